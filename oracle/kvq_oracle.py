@@ -1,0 +1,434 @@
+"""CPU oracle for quantize-on-write into a paged KV cache and for dequantizing
+paged decode attention.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+and the benchmark's CPU-baseline leg may import this module.  It is a plain,
+slow, deliberately unoptimised statement of what the GPU path computes, and it
+shares no code with that path.
+
+Sources (four web pages on KV-cache quantization; cited by title and section):
+  [P1] "Use Less Memory: Quantization and Offloading" (int8ai.com)
+  [P2] "12 KV Cache Quantization" (learning-materials, Inference Engineering)
+  [P3] "Quantized KV caches in production: FP8 vs INT8 vs INT4" (llms.blog)
+  [P4] "KV Cache Quantization" glossary entry (inferensys.com)
+
+Arithmetic precision.  The encoding steps (scale, quotient, rounding) are done
+in IEEE binary32 with round-to-nearest-even, and the scale is then rounded to
+binary16 for storage, exactly as the stored format requires; NumPy float32
+operations, ``np.rint`` and ``astype(np.float16)`` provide those roundings.
+Attention is computed in float64 over the dequantized values.
+
+Readings taken where the pages leave a step open (each is repeated at its use):
+  * the quotient divides by the STORED fp16 scale, so dequantization x_hat =
+    code * s reproduces what was divided by;
+  * "round" is round-half-to-even; INT8 codes are in [-127, 127] and INT4
+    codes in [-7, 7] (the symmetric clip range of [P1] section 2.1);
+  * FP8 is the OCP E4M3FN encoding (max 448, no infinities, S.1111.111 = NaN),
+    rounded to nearest-even and saturated at +-448.  [P1] section 2.3 prints
+    +-240, which is the maximum of the FNUZ variant, not of E4M3FN;
+  * a group whose fp16 scale is 0 (all-zero input, or a scale that underflows
+    fp16) stores scale 0 and all codes 0;
+  * INT4 packs two codes per byte, the even channel in the low nibble;
+  * KIVI-style keys: one fp16 scale and one fp16 zero point (= the group
+    minimum) per channel per 32-token group, unsigned codes 0..15; the rows of a
+    page wait in a per-sequence fp16 tail until the page's last row arrives.
+
+Parity unpinned: nothing here.  Every function below is pinned by a test in
+tests/test_oracle_*.py against the pages' worked example, closed forms,
+invariants, brute force or an independent library routine.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Formats
+# --------------------------------------------------------------------------
+
+INT8 = "int8"
+FP8_E4M3FN = "fp8_e4m3fn"
+INT4_G32 = "int4_g32"
+INT4_KIVI = "int4_kivi"
+
+SYM_FORMATS = (INT8, FP8_E4M3FN, INT4_G32)
+K_FORMATS = SYM_FORMATS + (INT4_KIVI,)
+V_FORMATS = SYM_FORMATS
+
+# Largest representable magnitude of each symmetric target ([P1] section 2.1
+# table: signed INT8 127, signed INT4 7; OCP E4M3FN 448).
+QMAX = {INT8: 127.0, INT4_G32: 7.0, FP8_E4M3FN: 448.0}
+
+# Channels per scale group along head_dim ([P2] section 5, "Where the scales
+# live": INT4 with group=32).  Per-token-per-head formats have one group = D.
+INT4_GROUP = 32
+
+# KIVI keys: tokens per quantization group along the sequence, and the number
+# of steps of the unsigned 4-bit range ([P4] asymmetric quantization maps
+# [min, max] onto the full integer range 0..15).
+KIVI_GROUP = 32
+KIVI_LEVELS = 15
+
+
+def groups_per_row(fmt: str, head_dim: int) -> int:
+    """Number of fp16 scales stored per (token, head) for a symmetric format."""
+    return head_dim // INT4_GROUP if fmt == INT4_G32 else 1
+
+
+def code_bytes_per_row(fmt: str, head_dim: int) -> int:
+    """Bytes of codes per (token, head): 1 B/element for 8-bit, 0.5 for 4-bit
+    ([P1] section 2.1 table, bytes per element)."""
+    return head_dim // 2 if fmt in (INT4_G32, INT4_KIVI) else head_dim
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3FN, written from the OCP 8-bit floating point definition:
+# 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0
+# holds subnormals m * 2^-9; no infinities; S.1111.111 is NaN, so the largest
+# finite magnitude is 1.75 * 2^8 = 448.  [P3] "Numerical Formats" gives the
+# 1-4-3 split and the 8 levels per power of two.
+# --------------------------------------------------------------------------
+
+E4M3FN_MAX_CODE = 0x7E  # 448
+
+
+def e4m3fn_value(code) -> np.ndarray:
+    """Exact float64 value of each E4M3FN byte (NaN for S.1111.111)."""
+    c = np.asarray(code, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3fn_encode(y) -> np.ndarray:
+    """Round float32 values to E4M3FN bytes: nearest, ties to the even code,
+    saturating at +-448.  The sign of zero (and of values that round to zero)
+    is kept.  NaN and infinite inputs are outside the contract."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y).astype(np.float64)  # exact
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # Subnormal range: the value is m * 2^-9; m = 8 lands on the smallest
+    # normal (code 0x08) by continuity of the encoding.
+    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)
+    nrm = ~sub
+    frac, exp = np.frexp(a[nrm])  # a = frac * 2^exp, frac in [0.5, 1)
+    e = exp.astype(np.int64) - 1  # a = (1 + f) * 2^e
+    mant = np.rint((2.0 * frac - 1.0) * 8.0).astype(np.int64)  # 0..8, ties even
+    # A mantissa that rounds up to 8 carries into the exponent, which the
+    # additive form below does by itself.
+    code[nrm] = ((e + 7) << 3) + mant
+    code = np.minimum(code, E4M3FN_MAX_CODE)  # saturate: 448 is the largest finite
+    code |= np.where(np.signbit(y), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# Symmetric quantization ([P1] section 2.1):
+#   s = max|x| / q_max;  x_q = clip(round(x / s), -q_max, q_max);  x_hat = x_q s
+# Granularity: per token per head ([P2] section 5 "Where the scales live":
+# k_scale (num_blocks, block_size, n_kv_heads) in FP16), or one scale per 32
+# channels for INT4 (same section: 4 groups x 2 bytes at head_dim 128).
+# --------------------------------------------------------------------------
+
+
+def quantize_sym(x16: np.ndarray, fmt: str):
+    """Quantize fp16 rows (..., D).  Returns (codes, scales):
+    codes int8 (INT8/INT4, values in [-q_max, q_max]) or uint8 (FP8 bytes),
+    shape (..., D); scales float16 of shape (..., D // group)."""
+    assert x16.dtype == np.float16
+    D = x16.shape[-1]
+    g = INT4_GROUP if fmt == INT4_G32 else D
+    x = x16.astype(np.float32).reshape(x16.shape[:-1] + (D // g, g))
+    amax = np.max(np.abs(x), axis=-1)  # exact
+    # Two roundings: the fp32 quotient, then fp16 for storage ([P1] section 2.1
+    # keeps s in FP32; [P1] Exercise 1 step 2 and [P2] section 5 store it as
+    # FP16).  The quotient below divides by the stored value.
+    s32 = amax / np.float32(QMAX[fmt])
+    s16 = s32.astype(np.float16)
+    s = s16.astype(np.float32)
+    zero = s == 0
+    safe = np.where(zero, np.float32(1.0), s)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = x / safe[..., None]  # IEEE binary32 quotient
+    if fmt == FP8_E4M3FN:
+        c = e4m3fn_encode(y)
+        c[np.broadcast_to(zero[..., None], c.shape)] = 0
+        codes = c.reshape(x16.shape)
+    else:
+        q = QMAX[fmt]
+        c = np.clip(np.rint(y), -q, q)  # rint: round half to even
+        c[np.broadcast_to(zero[..., None], c.shape)] = 0
+        codes = c.astype(np.int8).reshape(x16.shape)
+    return codes, s16
+
+
+def dequant_sym(codes: np.ndarray, scales16: np.ndarray, fmt: str) -> np.ndarray:
+    """x_hat = code * s in float64 ([P1] section 2.1, Exercise 1 step 4)."""
+    D = codes.shape[-1]
+    g = INT4_GROUP if fmt == INT4_G32 else D
+    if fmt == FP8_E4M3FN:
+        v = e4m3fn_value(codes)
+    else:
+        v = codes.astype(np.int8).astype(np.float64)
+    v = v.reshape(codes.shape[:-1] + (D // g, g))
+    return (v * scales16.astype(np.float64)[..., None]).reshape(codes.shape)
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte (0.5 B/element, [P1] section 2.1 table): byte j
+    holds channel 2j in its low nibble and channel 2j+1 in its high nibble.
+    Signed codes are stored as two's-complement nibbles."""
+    n = codes.astype(np.int64) & 0xF
+    return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray, signed: bool) -> np.ndarray:
+    p = packed.astype(np.int64)
+    lo, hi = p & 0xF, (p >> 4) & 0xF
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.int64)
+    out[..., 0::2], out[..., 1::2] = lo, hi
+    if signed:
+        out = np.where(out >= 8, out - 16, out)
+    return out
+
+
+# --------------------------------------------------------------------------
+# KIVI-style keys ([P2] section 5 "K is more sensitive than V": per-channel
+# quantization for K, per-token for V; [P3] "Numerical Formats": KIVI applies
+# per-channel quantization to keys; [P4]: asymmetric quantization maps the
+# observed min and max onto the full integer range).
+# One group = 32 consecutive tokens of one head; per channel:
+#   s = (max - min) / 15 (fp32, stored fp16),  z = min (stored fp16, exact),
+#   code = clip(round((x - z) / s), 0, 15),     x_hat = code * s + z.
+# --------------------------------------------------------------------------
+
+
+def kivi_quantize_group(x16: np.ndarray):
+    """x16: float16 (32, D) rows of one head.  Returns (codes uint8 (32, D) in
+    0..15, scale float16 (D,), zero float16 (D,))."""
+    assert x16.dtype == np.float16 and x16.shape[0] == KIVI_GROUP
+    x = x16.astype(np.float32)
+    mn = x.min(axis=0)
+    mx = x.max(axis=0)
+    s32 = (mx - mn) / np.float32(KIVI_LEVELS)  # fl32(fl32(mx - mn) / 15)
+    s16 = s32.astype(np.float16)
+    z16 = mn.astype(np.float16)  # exact: mn is an fp16 value
+    s = s16.astype(np.float32)
+    z = z16.astype(np.float32)
+    zero = s == 0
+    safe = np.where(zero, np.float32(1.0), s)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = (x - z) / safe  # fl32(fl32(x - z) / s)
+    c = np.clip(np.rint(y), 0, KIVI_LEVELS)
+    c[:, zero] = 0
+    return c.astype(np.uint8), s16, z16
+
+
+def kivi_dequant(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    return codes.astype(np.float64) * s16.astype(np.float64) + z16.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Paged cache ([P2] section 5: k_cache (num_blocks, block_size, n_kv_heads,
+# head_dim) with k_scale (num_blocks, block_size, n_kv_heads) in FP16; [P4]
+# PagedAttention: fixed-size, non-contiguous physical blocks).
+# --------------------------------------------------------------------------
+
+
+class OracleCache:
+    """NumPy mirror of the device cache buffers, in the same layouts:
+      codes  uint8  (num_blocks, block_size, H, D or D/2)
+      scales fp16   (num_blocks, block_size, H, groups)  symmetric formats
+             fp16   (num_blocks, H, D)                   KIVI keys
+      zeros  fp16   (num_blocks, H, D)                   KIVI keys only
+      k_tail, v_tail fp16 (max_seqs, block_size, H, D)   KIVI keys only
+    """
+
+    def __init__(self, num_blocks, block_size, n_kv_heads, head_dim, k_fmt, v_fmt, max_seqs=0):
+        assert k_fmt in K_FORMATS and v_fmt in V_FORMATS
+        if k_fmt == INT4_KIVI:
+            assert block_size == KIVI_GROUP
+        self.nb, self.bs, self.H, self.D = num_blocks, block_size, n_kv_heads, head_dim
+        self.k_fmt, self.v_fmt, self.max_seqs = k_fmt, v_fmt, max_seqs
+        nb, bs, H, D = num_blocks, block_size, n_kv_heads, head_dim
+        self.k_codes = np.zeros((nb, bs, H, code_bytes_per_row(k_fmt, D)), np.uint8)
+        self.v_codes = np.zeros((nb, bs, H, code_bytes_per_row(v_fmt, D)), np.uint8)
+        if k_fmt == INT4_KIVI:
+            self.k_scales = np.zeros((nb, H, D), np.float16)
+            self.k_zeros = np.zeros((nb, H, D), np.float16)
+            self.k_tail = np.zeros((max_seqs, bs, H, D), np.float16)
+            self.v_tail = np.zeros((max_seqs, bs, H, D), np.float16)
+        else:
+            self.k_scales = np.zeros((nb, bs, H, groups_per_row(k_fmt, D)), np.float16)
+            self.k_zeros = self.k_tail = self.v_tail = None
+        self.v_scales = np.zeros((nb, bs, H, groups_per_row(v_fmt, D)), np.float16)
+
+    def buffers(self):
+        out = {"k_codes": self.k_codes, "v_codes": self.v_codes,
+               "k_scales": self.k_scales, "v_scales": self.v_scales}
+        if self.k_fmt == INT4_KIVI:
+            out.update(k_zeros=self.k_zeros, k_tail=self.k_tail, v_tail=self.v_tail)
+        return out
+
+
+def _store_sym(codes_buf, scales_buf, fmt, x16_rows, slots, bs):
+    """Quantize (n, H, D) rows and scatter them to flat slots."""
+    codes, s16 = quantize_sym(x16_rows, fmt)
+    if fmt == INT4_G32:
+        stored = pack_int4(codes)
+    else:
+        stored = codes.view(np.uint8)
+    blk, off = slots // bs, slots % bs
+    codes_buf[blk, off] = stored
+    scales_buf[blk, off] = s16
+
+
+def write(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, seq_idx=None):
+    """Quantize-on-write of k, v (T, H, D) fp16 into the paged cache.
+
+    Token t goes to flat slot slot_mapping[t] = block * block_size + offset;
+    a negative slot means "skip".  Symmetric formats quantize each (token,
+    head) row on its own ([P2] section 5: per-token, per-head scaling).
+
+    KIVI keys: the rows of one page form one 32-token group.  A page is
+    quantized when its last row (offset block_size - 1) is written; its other
+    rows come from this call where present, else from the sequence's fp16
+    tail (rows written by earlier calls).  Rows of pages not completed by this
+    call are stored, K and V in fp16, in the tail of their sequence
+    (seq_idx[t]) at their page offset.  Completion reads the tail as it was
+    before this call.  V is quantized per token into its page in every case.
+    """
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    valid = np.nonzero(slots >= 0)[0]
+    bs = cache.bs
+    _store_sym(cache.v_codes, cache.v_scales, cache.v_fmt, v16[valid], slots[valid], bs)
+    if cache.k_fmt != INT4_KIVI:
+        _store_sym(cache.k_codes, cache.k_scales, cache.k_fmt, k16[valid], slots[valid], bs)
+        return
+    assert seq_idx is not None
+    seq_idx = np.asarray(seq_idx, dtype=np.int64)
+    pages = {}  # (seq, block) -> {offset: token index}
+    for t in valid:
+        key = (int(seq_idx[t]), int(slots[t] // bs))
+        off = int(slots[t] % bs)
+        assert off not in pages.setdefault(key, {}), "a slot written twice in one call"
+        pages[key][off] = t
+    tail_k_before = cache.k_tail.copy()
+    for (seq, blk), offs in pages.items():
+        if bs - 1 not in offs:
+            continue
+        rows = np.stack([k16[offs[j]] if j in offs else tail_k_before[seq, j] for j in range(bs)])
+        for h in range(cache.H):
+            c, s16, z16 = kivi_quantize_group(rows[:, h, :])
+            cache.k_codes[blk, :, h, :] = pack_int4(c)
+            cache.k_scales[blk, h] = s16
+            cache.k_zeros[blk, h] = z16
+    for (seq, blk), offs in pages.items():
+        if bs - 1 in offs:
+            continue
+        for off, t in offs.items():
+            cache.k_tail[seq, off] = k16[t]
+            cache.v_tail[seq, off] = v16[t]
+
+
+def _dequant_rows(cache: OracleCache, which: str, blk, off):
+    """float64 (n, H, D) rows of K or V at (block, offset) pairs (sym formats)."""
+    fmt = cache.k_fmt if which == "k" else cache.v_fmt
+    codes_buf = cache.k_codes if which == "k" else cache.v_codes
+    scales_buf = cache.k_scales if which == "k" else cache.v_scales
+    raw = codes_buf[blk, off]
+    if fmt == INT4_G32:
+        codes = unpack_int4(raw, signed=True)
+    elif fmt == FP8_E4M3FN:
+        codes = raw
+    else:
+        codes = raw.view(np.int8)
+    return dequant_sym(codes, scales_buf[blk, off], fmt)
+
+
+def gather_dequant(cache: OracleCache, block_table_row, L: int, seq: int):
+    """Dequantized K_hat, V_hat (L, H, D) float64 of one sequence, gathered
+    through its block-table row: token t lives at block
+    block_table_row[t // block_size], offset t % block_size.  For KIVI keys
+    the last L mod 32 tokens are read from the sequence's fp16 tail."""
+    bs = cache.bs
+    t = np.arange(L)
+    blk = np.asarray(block_table_row, dtype=np.int64)[t // bs]
+    off = t % bs
+    V = _dequant_rows(cache, "v", blk, off)
+    if cache.k_fmt != INT4_KIVI:
+        K = _dequant_rows(cache, "k", blk, off)
+        return K, V
+    nfull = (L // bs) * bs
+    K = np.empty((L, cache.H, cache.D), np.float64)
+    for p in range(nfull // bs):
+        b = blk[p * bs]
+        codes = unpack_int4(cache.k_codes[b], signed=False)  # (bs, H, D)
+        K[p * bs:(p + 1) * bs] = kivi_dequant(codes, cache.k_scales[b][None], cache.k_zeros[b][None])
+    K[nfull:] = cache.k_tail[seq, : L - nfull].astype(np.float64)
+    V[nfull:] = cache.v_tail[seq, : L - nfull].astype(np.float64)
+    return K, V
+
+
+def attention_fp64(q, K, V, sm_scale=None):
+    """One decode query per head against L cached tokens, float64:
+    o = softmax(q k^T * sm_scale) V  ([P2] section 5 "K is more sensitive than
+    V": softmax(q.k^T / sqrt(d)) and sum_i p_i v_i), with grouped-query
+    attention: query head hq reads KV head hq // G ([P4] GQA: groups of query
+    heads share one key/value head).
+    q: (Hq, D); K, V: (L, H, D).  Returns (Hq, D); zeros when L == 0."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq, D = q.shape
+    L, H, _ = K.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out = np.zeros((Hq, D), np.float64)
+    if L == 0:
+        return out
+    G = Hq // H
+    for hq in range(Hq):
+        h = hq // G
+        s = (K[:, h, :] @ q[hq]) * sm_scale
+        p = np.exp(s - s.max())
+        out[hq] = (p @ V[:, h, :]) / p.sum()
+    return out
+
+
+def decode_attn(cache: OracleCache, q, block_table, ctx_lens, sm_scale=None, seqs=None):
+    """Decode attention over the quantized paged cache, float64 (B, Hq, D).
+    For KIVI keys, batch row b reads tail row b.  `seqs` restricts the work to
+    a subset of batch rows (others are left zero)."""
+    q = np.asarray(q)
+    B = q.shape[0]
+    out = np.zeros(q.shape, np.float64)
+    for b in (range(B) if seqs is None else seqs):
+        L = int(ctx_lens[b])
+        K, V = gather_dequant(cache, block_table[b], L, b)
+        out[b] = attention_fp64(q[b], K, V, sm_scale)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Closed forms ([P1] Exercise 3 and [P3] "The Mathematics of KV Cache
+# Growth": bytes per token = 2 * layers * kv_heads * head_dim * bytes/element;
+# [P2] section 5 scale overheads).
+# --------------------------------------------------------------------------
+
+
+def kv_bytes_per_token(n_layers, n_kv_heads, head_dim, bytes_per_elem):
+    return 2 * n_layers * n_kv_heads * head_dim * bytes_per_elem
+
+
+def stored_bytes_per_token_head(fmt: str, head_dim: int) -> float:
+    """Codes + scale metadata per (token, head) as stored by OracleCache.
+    KIVI keys amortise one fp16 scale and one fp16 zero per channel over a
+    32-token group."""
+    if fmt == INT4_KIVI:
+        return head_dim / 2 + 2 * 2 * head_dim / KIVI_GROUP
+    return code_bytes_per_row(fmt, head_dim) + 2 * groups_per_row(fmt, head_dim)

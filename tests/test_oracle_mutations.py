@@ -1,0 +1,115 @@
+"""Planted mistakes in the oracle must fail its pins.  Each case builds a
+deliberately wrong variant of one oracle step (on the CPU) and checks that at
+least one pin in test_oracle_pins rejects it."""
+
+import types
+
+import numpy as np
+import pytest
+
+import oracle as o
+import test_oracle_pins as pins
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def _quantize_divide_by_fp32_scale(x16, fmt):
+    # Mistake: divide by the unrounded fp32 scale instead of the stored fp16 one.
+    D = x16.shape[-1]
+    g = o.INT4_GROUP if fmt == o.INT4_G32 else D
+    x = x16.astype(np.float32).reshape(x16.shape[:-1] + (D // g, g))
+    s32 = np.max(np.abs(x), axis=-1) / np.float32(o.QMAX[fmt])
+    s16 = s32.astype(np.float16)
+    safe = np.where(s32 == 0, np.float32(1), s32)
+    y = x / safe[..., None]
+    q = o.QMAX[fmt]
+    if fmt == o.FP8_E4M3FN:
+        return o.e4m3fn_encode(y).reshape(x16.shape), s16
+    return np.clip(np.rint(y), -q, q).astype(np.int8).reshape(x16.shape), s16
+
+
+def _quantize_round_half_up(x16, fmt):
+    # Mistake: round half away from zero.
+    x = x16.astype(np.float32)
+    s16 = (np.max(np.abs(x), axis=-1, keepdims=True) / np.float32(o.QMAX[fmt])).astype(np.float16)
+    y = x / s16.astype(np.float32)
+    c = np.sign(y) * np.floor(np.abs(y) + 0.5)
+    return np.clip(c, -127, 127).astype(np.int8), s16
+
+
+def _attention_wrong_gqa(q, K, V, sm_scale=None):
+    # Mistake: query head hq reads KV head hq % H instead of hq // G.
+    q = np.asarray(q, np.float64)
+    Hq, D = q.shape
+    H = K.shape[1]
+    out = np.zeros((Hq, D))
+    for hq in range(Hq):
+        h = hq % H
+        s = K[:, h, :] @ q[hq] / np.sqrt(D)
+        p = np.exp(s - s.max())
+        out[hq] = p @ V[:, h, :] / p.sum()
+    return out
+
+
+def test_wrong_qmax_fails(monkeypatch):
+    monkeypatch.setitem(o.kvq_oracle.QMAX, o.INT8, 128.0)
+    assert _fails(pins.check_worked_example, o.kvq_oracle.quantize_sym)
+
+
+def test_fp32_scale_divisor_fails():
+    assert _fails(pins.check_sym_invariants, _quantize_divide_by_fp32_scale, o.dequant_sym, (o.INT8,))
+
+
+def test_round_half_up_fails():
+    assert _fails(pins.check_round_half_even, _quantize_round_half_up)
+
+
+def test_no_saturation_fails(monkeypatch):
+    monkeypatch.setattr(o.kvq_oracle, "E4M3FN_MAX_CODE", 0x7F)
+    assert _fails(pins.check_fp8_specials, o.kvq_oracle.e4m3fn_encode)
+
+
+def test_wrong_fp8_exponent_bias_fails():
+    assert _fails(pins.check_fp8_bruteforce, lambda y: o.e4m3fn_encode(np.asarray(y, np.float32) * 2))
+
+
+def test_swapped_nibbles_fail():
+    assert _fails(pins.check_pack_order, lambda c: o.pack_int4(np.asarray(c)[..., ::-1]))
+
+
+def test_wrong_group_size_fails(monkeypatch):
+    monkeypatch.setattr(o.kvq_oracle, "INT4_GROUP", 64)
+    assert _fails(pins.check_closed_forms, o.kvq_oracle.stored_bytes_per_token_head)
+
+
+def test_wrong_kivi_levels_fail(monkeypatch):
+    monkeypatch.setattr(o.kvq_oracle, "KIVI_LEVELS", 16)
+    assert _fails(pins.check_kivi_invariants, o.kvq_oracle.kivi_quantize_group)
+
+
+def test_reversed_kivi_codes_fail():
+    def bad(x16):
+        c, s, z = o.kivi_quantize_group(x16)
+        return (15 - c).astype(np.uint8), s, z
+    assert _fails(pins.check_kivi_invariants, bad)
+
+
+def test_dropped_softmax_scale_fails(monkeypatch):
+    monkeypatch.setattr(o.kvq_oracle, "math", types.SimpleNamespace(sqrt=lambda x: 1.0))
+    assert _fails(pins.check_attention_vs_sdpa, o.kvq_oracle.attention_fp64)
+
+
+def test_wrong_gqa_mapping_fails():
+    assert _fails(pins.check_attention_vs_sdpa, _attention_wrong_gqa)
+
+
+@pytest.mark.parametrize("fmt", [o.INT8, o.INT4_G32])
+def test_unplanted_oracle_passes(fmt):
+    # Control: the real oracle passes the same checks.
+    pins.check_sym_invariants(o.quantize_sym, o.dequant_sym, (fmt,))

@@ -1,0 +1,418 @@
+"""Pins for the CPU oracle: values printed on the pages, closed forms,
+invariants, brute force and an independent library routine.  These run on the
+CPU only (no GPU, no HIP library)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+from conftest import read_golden
+
+RNG = np.random.default_rng(1234)
+
+# --------------------------------------------------------------------------
+# check_* helpers take the function under test so that tests/test_oracle_
+# mutations.py can show that planted mistakes fail them.
+# --------------------------------------------------------------------------
+
+
+def check_worked_example(quantize_sym=o.quantize_sym):
+    """'Use Less Memory', Exercise 1: k = [1.20, -0.45, 3.80, -2.10] in FP16,
+    per-token symmetric INT8 -> codes [40, -15, 127, -70]."""
+    g = read_golden("worked_example_int8.txt")
+    x16 = np.array([g["input"]], dtype=np.float16)
+    codes, s16 = quantize_sym(x16, o.INT8)
+    assert codes[0].tolist() == [int(c) for c in g["codes"]]
+    s = float(s16[0, 0])
+    # The page computes s from the decimal 3.80; the fp16 input is 3.8008 and
+    # the stored scale is fp16.  Within one fp16 ulp of the page's value.
+    assert abs(s - g["scale"]) <= 2.0 ** -16
+    xhat = codes[0].astype(np.float64) * s
+    # The page prints x_hat rounded to 5 decimals from its decimal s; the
+    # stored fp16 scale differs from that s by less than 2^-16, so each x_hat
+    # may differ by |code| * 2^-16 plus the printing's half unit.
+    assert np.all(np.abs(xhat - np.array(g["recon"])) <= np.abs(codes[0]) * 2.0 ** -16 + 5e-6)
+    # Errors as the page's table defines them: against the decimal originals.
+    orig = np.array(g["input"])
+    err = np.abs(xhat - orig)
+    assert err.max() <= g["max_abs_err"]
+    assert np.all(err <= np.array(g["abs_err"]) + np.abs(codes[0]) * 2.0 ** -16 + 5e-6)
+    rel = err / np.abs(orig)
+    assert rel.max() <= g["max_rel_err"] + 5e-5
+
+
+def check_round_half_even(quantize_sym=o.quantize_sym):
+    # s16 is exactly 2^-4 (7.9375 / 127); the other elements sit exactly on
+    # half-integers of the quotient, so rounding must go to the even code.
+    x16 = np.array([[7.9375, 0.15625, 0.21875, -0.15625, -0.21875, 0.03125]], np.float16)
+    codes, s16 = quantize_sym(x16, o.INT8)
+    assert float(s16[0, 0]) == 0.0625
+    assert codes[0].tolist() == [127, 2, 4, -2, -4, 0]
+
+
+def _bulk_rows(fmt, n=20000, D=128, seed=7):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, D)).astype(np.float32)
+    # mix of magnitudes: outlier channels, tiny rows, exact zeros, large rows
+    x[:, :4] *= 20
+    x[: n // 8] *= np.float32(1e-3)
+    x[n // 8: n // 4] *= np.float32(300)
+    x[-5:] = 0
+    x16 = x.astype(np.float16)
+    return x16
+
+
+def check_sym_invariants(quantize_sym=o.quantize_sym, dequant=o.dequant_sym, fmts=o.SYM_FORMATS):
+    for fmt in fmts:
+        x16 = _bulk_rows(fmt)
+        codes, s16 = quantize_sym(x16, fmt)
+        D = x16.shape[-1]
+        g = o.INT4_GROUP if fmt == o.INT4_G32 else D
+        x = x16.astype(np.float64).reshape(-1, D // g, g)
+        s = s16.astype(np.float64)
+        xhat = dequant(codes, s16, fmt).reshape(x.shape)
+        q = o.QMAX[fmt]
+        normal = s >= 2.0 ** -14  # s16 is a normal fp16 number
+        # 1. the largest-magnitude element lands on +-q_max ('Use Less Memory',
+        #    Exercise 1 step 3: "hits q_max exactly")
+        idx = np.argmax(np.abs(x), axis=-1)
+        top = np.take_along_axis(xhat, idx[..., None], -1)[..., 0]
+        topx = np.take_along_axis(x, idx[..., None], -1)[..., 0]
+        ok = normal & (topx != 0)
+        assert np.all(np.abs(top[ok] / s[ok]) == q), fmt
+        # 2. reconstruction error bound
+        err = np.abs(x - xhat)
+        if fmt == o.FP8_E4M3FN:
+            y = np.abs(x) / np.where(s == 0, 1, s)[..., None]
+            e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+            half_step = np.where(y < 2.0 ** -6, 2.0 ** -10, 2.0 ** (e - 4))
+            bound = s[..., None] * half_step * (1 + 2.0 ** -20)
+        else:
+            bound = s[..., None] * (0.5 + 2.0 ** -17)
+        bound = np.broadcast_to(bound, x.shape)
+        nz = np.broadcast_to((s > 0)[..., None], x.shape)
+        assert np.all(err[nz] <= bound[nz]), fmt
+        # 3. codes in range and carrying the sign of x
+        vals = xhat / np.where(s == 0, 1, s)[..., None]
+        assert np.all(np.abs(vals) <= q), fmt
+        assert np.all((vals == 0) | (np.sign(vals) == np.sign(x))), fmt
+        # 4. zero rows give scale 0 and code 0
+        assert np.all(s[-5:] == 0) and np.all(xhat[-5:] == 0)
+
+
+def check_fp8_bruteforce(encode=o.e4m3fn_encode):
+    # All finite E4M3FN values, magnitude side, by code.
+    mags = o.e4m3fn_value(np.arange(0x7F))  # codes 0x00..0x7E
+    assert mags[-1] == 448.0
+    # Every fp16 bit pattern (finite) taken as a quotient y, plus random fp32.
+    h = np.arange(0x10000, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    y = h[np.isfinite(h)].astype(np.float32)
+    rnd = (np.random.default_rng(5).standard_normal(200000) *
+           np.exp2(np.random.default_rng(6).uniform(-14, 10, 200000))).astype(np.float32)
+    y = np.concatenate([y, rnd])
+    a = np.abs(y).astype(np.float64)
+    # nearest finite magnitude, ties to the even code; beyond 448 saturate.
+    d = np.abs(a[:, None] - mags[None, :])
+    best = d.min(axis=1)
+    cand = d == best[:, None]
+    codes = np.arange(0x7F)
+    even_pick = np.where(cand & (codes[None, :] % 2 == 0), codes[None, :], 999).min(axis=1)
+    any_pick = np.where(cand, codes[None, :], 999).min(axis=1)
+    ties = cand.sum(axis=1) > 1
+    expect = np.where(ties, even_pick, any_pick)
+    expect = np.where(a > 448, 0x7E, expect) | np.where(np.signbit(y), 0x80, 0)
+    got = encode(y)
+    assert np.array_equal(got.astype(np.int64), expect.astype(np.int64))
+
+
+def check_fp8_specials(encode=o.e4m3fn_encode):
+    cases = [(448.0, 0x7E), (464.0, 0x7E), (465.0, 0x7E), (1e6, 0x7E), (-1e6, 0xFE),
+             (2.0 ** -9, 0x01), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (2.0 ** -6, 0x08),
+             (1.0, 0x38), (1.0625, 0x38), (1.1875, 0x3A), (-0.0, 0x80), (0.0, 0x00), (-1e-9, 0x80)]
+    for y, c in cases:
+        assert int(encode(np.array([y], np.float32))[0]) == c, (y, hex(c))
+
+
+def check_pack_order(pack=o.pack_int4):
+    assert pack(np.array([[1, 2]], np.int8))[0, 0] == 0x21
+    assert pack(np.array([[-1, 7]], np.int8))[0, 0] == 0x7F
+    assert pack(np.array([[-7, 0]], np.int8))[0, 0] == 0x09
+
+
+def check_closed_forms(stored=o.stored_bytes_per_token_head, kvb=o.kv_bytes_per_token):
+    g = read_golden("closed_forms.txt")
+    L, H, D = int(g["llama3_8b_layers"]), int(g["llama3_8b_kv_heads"]), int(g["llama3_8b_head_dim"])
+    assert kvb(L, H, D, 2) == g["bytes_per_token_fp16"]
+    assert kvb(L, H, D, 1) == g["bytes_per_token_fp8"]
+    assert kvb(L, H, D, 0.5) == g["bytes_per_token_int4"]
+    assert round(kvb(L, H, D, 2) * 32768 / 1e9, 2) == g["per_seq_gb_fp16_32k"]
+    assert round(kvb(L, H, D, 1) * 32768 / 1e9, 2) == g["per_seq_gb_fp8_32k"]
+    assert round(kvb(L, H, D, 0.5) * 32768 / 1e9, 2) == g["per_seq_gb_int4_32k"]
+    int8 = stored(o.INT8, 128)
+    assert int8 == g["int8_d128_data_bytes"] + g["int8_d128_scale_bytes"]
+    assert round(100 * (int8 - 128) / 128, 1) == g["int8_d128_overhead_pct"]
+    assert stored(o.FP8_E4M3FN, 128) == int8
+    i4 = stored(o.INT4_G32, 128)
+    assert i4 == g["int4_g32_d128_bytes"]
+    assert math.floor(10 * g["fp16_d128_bytes"] / i4) / 10 == g["int4_g32_ratio"]
+
+
+# --------------------------------------------------------------------------
+# Tests
+# --------------------------------------------------------------------------
+
+
+def test_worked_example():
+    check_worked_example()
+
+
+def test_round_half_even():
+    check_round_half_even()
+
+
+def test_sym_invariants():
+    check_sym_invariants()
+
+
+def test_fp8_bruteforce():
+    check_fp8_bruteforce()
+
+
+def test_fp8_specials():
+    check_fp8_specials()
+
+
+def test_fp8_decode_table():
+    vals = o.e4m3fn_value(np.arange(256))
+    fin = np.isfinite(vals)
+    assert fin.sum() == 254  # two NaN codes, no infinities
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF])
+    assert vals[0x7E] == 448.0 and vals[0xFE] == -448.0 and vals[0x01] == 2.0 ** -9
+    # 8 levels per power of two ('Quantized KV caches in production',
+    # Numerical Formats)
+    g = read_golden("closed_forms.txt")
+    octave = vals[(vals >= 1.0) & (vals < 2.0)]
+    assert len(octave) == g["e4m3_levels_per_octave"]
+    # every finite code round-trips through the encoder
+    codes = np.arange(256)[fin]
+    assert np.array_equal(o.e4m3fn_encode(vals[fin].astype(np.float32)), codes.astype(np.uint8))
+
+
+def test_fp8_matches_torch_cast():
+    # torch's CPU float8_e4m3fn cast is an independent RNE implementation; it
+    # does not saturate (gives NaN) from 464 up, so compare below that.
+    rng = np.random.default_rng(11)
+    y = (rng.standard_normal(400000) * np.exp2(rng.uniform(-16, 9, 400000))).astype(np.float32)
+    y = y[np.abs(y) < 464]
+    h = np.arange(0x10000, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    h = h[np.isfinite(h) & (np.abs(h) < 464)]
+    y = np.concatenate([y, h])
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.e4m3fn_encode(y), ref)
+
+
+def test_pack_int4():
+    check_pack_order()
+    c = np.array(np.meshgrid(np.arange(-7, 8), np.arange(-7, 8))).reshape(2, -1).T.astype(np.int8)
+    assert np.array_equal(o.unpack_int4(o.pack_int4(c), signed=True), c)
+    u = np.array(np.meshgrid(np.arange(16), np.arange(16))).reshape(2, -1).T.astype(np.uint8)
+    assert np.array_equal(o.unpack_int4(o.pack_int4(u), signed=False), u)
+
+
+def test_closed_forms():
+    check_closed_forms()
+
+
+def test_cache_buffer_sizes_match_closed_forms():
+    nb, bs, H, D = 6, 32, 2, 128
+    for kf, vf in [(o.INT8, o.INT8), (o.FP8_E4M3FN, o.INT4_G32), (o.INT4_KIVI, o.INT4_G32)]:
+        c = o.OracleCache(nb, bs, H, D, kf, vf, max_seqs=1)
+        k_bytes = c.k_codes.nbytes + c.k_scales.nbytes + (c.k_zeros.nbytes if c.k_zeros is not None else 0)
+        v_bytes = c.v_codes.nbytes + c.v_scales.nbytes
+        assert k_bytes / (nb * bs * H) == o.stored_bytes_per_token_head(kf, D)
+        assert v_bytes / (nb * bs * H) == o.stored_bytes_per_token_head(vf, D)
+    assert o.stored_bytes_per_token_head(o.INT4_KIVI, 128) == 80
+
+
+def check_kivi_invariants(kivi=o.kivi_quantize_group, deq=o.kivi_dequant):
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        x = rng.standard_normal((32, 64)).astype(np.float32)
+        x[:, :3] *= 20
+        x[:4] *= 10
+        x[:, 5] += 3  # skewed channel
+        x[:, 6] = 0.5  # constant channel -> scale 0
+        x16 = x.astype(np.float16)
+        c, s16, z16 = kivi(x16)
+        xf = x16.astype(np.float64)
+        s = s16.astype(np.float64)
+        assert c.min() >= 0 and c.max() <= 15
+        normal = s >= 2.0 ** -14
+        # [P4]: asymmetric quantization maps min and max to the integer range ends
+        amin = np.argmin(xf, axis=0)
+        amax = np.argmax(xf, axis=0)
+        cols = np.arange(64)
+        assert np.all(c[amin, cols][normal] == 0)
+        assert np.all(c[amax, cols][normal] == 15)
+        assert np.all(z16.astype(np.float64) == xf.min(axis=0))
+        xh = deq(c, s16, z16)
+        err = np.abs(xh - xf)
+        assert np.all(err[:, s > 0] <= (s * (0.5 + 2.0 ** -10))[None, s > 0])
+        assert np.all(xh[:, 6] == 0.5)
+
+
+def test_kivi_invariants():
+    check_kivi_invariants()
+
+
+def test_kivi_bruteforce_levels():
+    # The code is the nearest of the 16 levels z + c*s to x (checked on the
+    # fp32 quotient grid, so an exact tie cannot flip the decision).
+    rng = np.random.default_rng(9)
+    x16 = (rng.standard_normal((32, 16)) * 3).astype(np.float16)
+    c, s16, z16 = o.kivi_quantize_group(x16)
+    s, z = s16.astype(np.float64), z16.astype(np.float64)
+    levels = z[None, :, None] + np.arange(16)[None, None, :] * s[None, :, None]
+    d = np.abs(x16.astype(np.float64)[:, :, None] - levels)
+    best = d.min(axis=-1)
+    chosen = np.take_along_axis(d, c[..., None].astype(np.int64), -1)[..., 0]
+    assert np.all(chosen <= best + s[None, :] * 2.0 ** -18)
+
+
+# --------------------------------------------------------------------------
+# Attention and paging
+# --------------------------------------------------------------------------
+
+
+def _sdpa_fp64(q, K, V, G):
+    qt = torch.from_numpy(q)[None, :, None, :]  # (1, Hq, 1, D)
+    kt = torch.from_numpy(K.transpose(1, 0, 2).copy())[None]  # (1, H, L, D)
+    vt = torch.from_numpy(V.transpose(1, 0, 2).copy())[None]
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, enable_gqa=G > 1)
+    return out[0, :, 0, :].numpy()
+
+
+def check_attention_vs_sdpa(attn=o.attention_fp64):
+    rng = np.random.default_rng(21)
+    for (Hq, H, D, L) in [(4, 2, 64, 37), (8, 8, 32, 5), (16, 2, 128, 300), (6, 3, 16, 1)]:
+        q = rng.standard_normal((Hq, D))
+        K = rng.standard_normal((L, H, D)) * 3
+        V = rng.standard_normal((L, H, D))
+        ref = _sdpa_fp64(q, K, V, Hq // H)
+        got = attn(q, K, V)
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attention_vs_sdpa():
+    check_attention_vs_sdpa()
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(2)
+    K = rng.standard_normal((1, 2, 16))
+    V = rng.standard_normal((1, 2, 16))
+    q = rng.standard_normal((4, 16))
+    out = o.attention_fp64(q, K, V)
+    assert np.array_equal(out, V[0][[0, 0, 1, 1]])  # ctx 1 -> v_0 of the head
+    K = rng.standard_normal((50, 2, 16))
+    V = rng.standard_normal((50, 2, 16))
+    out = o.attention_fp64(np.zeros((4, 16)), K, V)
+    assert np.allclose(out, V.mean(axis=0)[[0, 0, 1, 1]], atol=1e-14)
+    assert np.array_equal(o.attention_fp64(q, K[:0], V[:0]), np.zeros((4, 16)))
+
+
+def _make_seq_cache(kf, vf, L, bs, H, D, table, seed=0, seqs=1):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((seqs * L, H, D)).astype(np.float16)
+    v = rng.standard_normal((seqs * L, H, D)).astype(np.float16)
+    nb = int(np.max(table)) + 1
+    c = o.OracleCache(nb, bs, H, D, kf, vf, max_seqs=seqs)
+    pos = np.tile(np.arange(L), seqs)
+    seq = np.repeat(np.arange(seqs), L)
+    slots = table[seq, pos // bs].astype(np.int64) * bs + pos % bs
+    o.write(c, k, v, slots, seq)
+    return c, k, v
+
+
+@pytest.mark.parametrize("kf,vf", [(o.INT8, o.INT8), (o.FP8_E4M3FN, o.FP8_E4M3FN), (o.INT8, o.INT4_G32),
+                                   (o.INT4_KIVI, o.INT4_G32)])
+def test_paged_gather_equals_direct_quantization(kf, vf):
+    # Writing through a shuffled block table and reading back through it gives
+    # exactly the dequantized rows in position order.
+    bs, H, D, L = (32 if kf == o.INT4_KIVI else 16), 2, 64, 101
+    npages = -(-L // bs)
+    table = np.random.default_rng(4).permutation(npages + 3)[:npages][None]
+    c, k, v = _make_seq_cache(kf, vf, L, bs, H, D, table)
+    K, V = o.gather_dequant(c, table[0], L, 0)
+    codes, s = o.quantize_sym(v, vf)
+    assert np.array_equal(V[: (L // bs) * bs if kf == o.INT4_KIVI else L],
+                          o.dequant_sym(codes, s, vf)[: (L // bs) * bs if kf == o.INT4_KIVI else L])
+    if kf == o.INT4_KIVI:
+        nf = (L // bs) * bs
+        for p in range(L // bs):
+            for h in range(H):
+                cc, ss, zz = o.kivi_quantize_group(k[p * bs:(p + 1) * bs, h])
+                assert np.array_equal(K[p * bs:(p + 1) * bs, h], o.kivi_dequant(cc, ss, zz))
+        assert np.array_equal(K[nf:], k[nf:].astype(np.float64))
+        assert np.array_equal(V[nf:], v[nf:].astype(np.float64))
+    else:
+        codes, s = o.quantize_sym(k, kf)
+        assert np.array_equal(K, o.dequant_sym(codes, s, kf))
+
+
+def test_block_permutation_invariance():
+    bs, H, D, L = 16, 2, 32, 77
+    n = -(-L // bs)
+    ident = np.arange(n)[None]
+    shuf = np.random.default_rng(8).permutation(n + 5)[:n][None]
+    q = np.random.default_rng(1).standard_normal((1, 4, D)).astype(np.float16)
+    c1, *_ = _make_seq_cache(o.INT8, o.INT4_G32, L, bs, H, D, ident)
+    c2, *_ = _make_seq_cache(o.INT8, o.INT4_G32, L, bs, H, D, shuf)
+    a = o.decode_attn(c1, q, ident, [L])
+    b = o.decode_attn(c2, q, shuf, [L])
+    assert np.array_equal(a, b)
+
+
+def test_negative_slots_are_skipped():
+    c = o.OracleCache(4, 16, 2, 32, o.INT8, o.INT8)
+    k = np.ones((3, 2, 32), np.float16)
+    o.write(c, k, k, np.array([-1, 5, -7]))
+    assert np.count_nonzero(c.k_codes) == 2 * 32 and np.all(c.k_codes[0, 5].view(np.int8) == 127)
+
+
+def test_kivi_incremental_equals_one_shot():
+    # A sequence written in one call, or token by token as in decoding, ends
+    # in the same cache state (codes, scales, zeros, the valid tail rows).
+    bs, H, D, L = 32, 2, 32, 75
+    n = -(-L // bs)
+    table = np.random.default_rng(12).permutation(n)[None]
+    a, k, v = _make_seq_cache(o.INT4_KIVI, o.INT4_G32, L, bs, H, D, table, seed=3)
+    b = o.OracleCache(n, bs, H, D, o.INT4_KIVI, o.INT4_G32, max_seqs=1)
+    pos = np.arange(L)
+    slots = table[0, pos // bs].astype(np.int64) * bs + pos % bs
+    # prefill of 40 tokens, then one token per call
+    o.write(b, k[:40], v[:40], slots[:40], np.zeros(40, np.int32))
+    for t in range(40, L):
+        o.write(b, k[t:t + 1], v[t:t + 1], slots[t:t + 1], np.zeros(1, np.int32))
+    for name in ("k_codes", "k_scales", "k_zeros", "v_codes", "v_scales"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+    m = L % bs
+    assert np.array_equal(a.k_tail[0, :m], b.k_tail[0, :m]) and np.array_equal(a.v_tail[0, :m], b.v_tail[0, :m])
+    q = np.random.default_rng(0).standard_normal((1, 4, D)).astype(np.float16)
+    assert np.array_equal(o.decode_attn(a, q, table, [L]), o.decode_attn(b, q, table, [L]))
+
+
+def test_quantized_attention_close_to_fp16_attention():
+    # Quality statistic sanity: INT8 per-token-head keys/values stay close to
+    # unquantized attention ('Use Less Memory', section 2.4: INT8 near-lossless).
+    bs, H, D, L = 16, 2, 64, 200
+    n = -(-L // bs)
+    table = np.arange(n)[None]
+    c, k, v = _make_seq_cache(o.INT8, o.INT8, L, bs, H, D, table, seed=5)
+    q = np.random.default_rng(6).standard_normal((1, 4, D)).astype(np.float16)
+    a = o.decode_attn(c, q, table, [L])[0]
+    ref = o.attention_fp64(q[0].astype(np.float64), k.astype(np.float64), v.astype(np.float64))
+    assert np.max(np.abs(a - ref)) < 2e-2
