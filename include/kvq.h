@@ -1,0 +1,168 @@
+/*
+ * kvq: quantize-on-write into a paged KV cache and dequantizing paged decode
+ * attention, for AMD Instinct MI355X (gfx950).
+ *
+ * The library stores keys and values of a transformer's KV cache as low-bit
+ * codes plus fp16 scales in fixed-size pages, and runs single-query (decode)
+ * attention that reads those pages through a block table and dequantizes them
+ * in registers.  Sources, cited by page title and section:
+ *   [P1] "Use Less Memory: Quantization and Offloading", section 2.1
+ *        (symmetric quantization: s = max|x| / q_max, x_q = clip(round(x/s),
+ *        -q_max, q_max), x_hat = x_q * s; q_max 127 for INT8, 7 for INT4),
+ *        section 2.2 (per-token / per-head granularity), section 2.3 (FP8).
+ *   [P2] "12 KV Cache Quantization", section 5: "Where the scales live"
+ *        (k_cache (num_blocks, block_size, n_kv_heads, head_dim) in
+ *        FP8/INT8/INT4, k_scale (num_blocks, block_size, n_kv_heads) in FP16;
+ *        INT4 with one FP16 scale per 32 channels), "K is more sensitive than
+ *        V" (softmax(q.k^T/sqrt(d)), sum_i p_i v_i; per-channel K, per-token V),
+ *        "The kernel side" (the attention kernel dequantizes while reading).
+ *   [P3] "Quantized KV caches in production: FP8 vs INT8 vs INT4", Numerical
+ *        Formats (E4M3 1-4-3 layout; KIVI per-channel keys / per-token values)
+ *        and Kernel Backends (dequantization on load; paged block allocator
+ *        keeping scale metadata beside the page tables).
+ *   [P4] "KV Cache Quantization" glossary: asymmetric quantization (min and
+ *        max onto the full integer range), PagedAttention, GQA.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them beyond the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it asynchronously; no entry point synchronizes.
+ *   - Return value: KVQ_OK (0) or a negative kvq_status.  Arguments are
+ *     validated on the host before anything is launched; on error nothing is
+ *     enqueued.  No C++ exception crosses this interface.
+ *   - Device-side ids are bounds-checked by the kernels: a slot outside
+ *     [0, num_blocks * block_size) is skipped by kvq_write, and a page whose
+ *     block id is outside [0, num_blocks) contributes nothing to attention.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1,  /* NULL pointer, non-positive size, bad enum   */
+  KVQ_ERR_UNSUPPORTED = -2,  /* format or head_dim not implemented          */
+  KVQ_ERR_SHAPE = -3,        /* shape rule broken (see kvq_cache)           */
+  KVQ_ERR_WORKSPACE = -4,    /* decode workspace NULL or too small          */
+  KVQ_ERR_NO_DEVICE = -5,    /* no HIP device visible                       */
+  KVQ_ERR_HIP = -6           /* a HIP runtime call or launch failed         */
+} kvq_status;
+
+/* Storage formats of a cache tensor.
+ * KVQ_INT8       symmetric, one fp16 scale per (token, head), q_max 127
+ *                ([P1] 2.1, [P2] 5).  Codes int8 in [-127, 127].
+ * KVQ_FP8_E4M3FN symmetric, one fp16 scale per (token, head); codes are OCP
+ *                E4M3FN bytes (bias 7, max 448, no infinities), q_max 448,
+ *                round-to-nearest-even, saturating.  ([P1] 2.3 prints +-240,
+ *                the maximum of the FNUZ variant; gfx950 uses OCP E4M3FN.)
+ * KVQ_INT4_G32   symmetric, one fp16 scale per 32 consecutive channels of a
+ *                (token, head) row, q_max 7; two codes per byte, even channel
+ *                in the low nibble, two's complement ([P2] 5).
+ * KVQ_INT4_KIVI  keys only: asymmetric per channel over the 32 tokens of a
+ *                page ([P2] 5, [P3], [P4]); requires block_size == 32.  Per
+ *                (page, head, channel): scale = fp16(fl32(max-min)/15), zero =
+ *                min (fp16), codes 0..15 unsigned nibbles (even channel low).
+ *                A page is quantized when its last row is written; until then
+ *                its rows (keys AND values) are kept in fp16 in the
+ *                sequence's tail.
+ * Every quotient x/s is the IEEE binary32 quotient by the STORED fp16 scale;
+ * an fp16 scale of 0 stores all-zero codes. */
+typedef enum kvq_dtype {
+  KVQ_INT8 = 1,
+  KVQ_FP8_E4M3FN = 2,
+  KVQ_INT4_G32 = 3,
+  KVQ_INT4_KIVI = 4
+} kvq_dtype;
+
+/* A paged, quantized KV cache for one attention layer.  All buffers are
+ * caller-allocated device memory, contiguous, in these layouts (nb =
+ * num_blocks, bs = block_size, H = n_kv_heads, D = head_dim):
+ *   k_codes / v_codes  uint8 (nb, bs, H, D)    INT8, FP8
+ *                      uint8 (nb, bs, H, D/2)  INT4_G32, INT4_KIVI
+ *   k_scales/v_scales  fp16  (nb, bs, H)       INT8, FP8
+ *                      fp16  (nb, bs, H, D/32) INT4_G32
+ *                      fp16  (nb, H, D)        INT4_KIVI (k only)
+ *   k_zeros            fp16  (nb, H, D)        INT4_KIVI only, else NULL
+ *   k_tail / v_tail    fp16  (max_seqs, bs, H, D)  INT4_KIVI only, else NULL;
+ *                      row r of a sequence's tail holds the fp16 key/value
+ *                      of its not-yet-quantized page at offset r.
+ * Token slot s (= block * bs + offset) of a page lives at [s / bs, s % bs].
+ * Shape rules: head_dim in {64, 128, 256}; INT4_KIVI only for keys, with
+ * block_size 32 and max_seqs > 0; values use INT8, FP8_E4M3FN or INT4_G32. */
+typedef struct kvq_cache {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t k_dtype; /* kvq_dtype */
+  int32_t v_dtype; /* kvq_dtype */
+  int32_t max_seqs;
+  int32_t reserved;
+  void* k_codes;
+  void* v_codes;
+  void* k_scales;
+  void* v_scales;
+  void* k_zeros;
+  void* k_tail;
+  void* v_tail;
+} kvq_cache;
+
+/* Quantize-on-write ([P1] 2.1-2.2, [P2] 5 "Where the scales live").
+ *   k, v          fp16 (num_tokens, H, D), row-major; read only.
+ *   slot_mapping  int64 (num_tokens): destination slot of each token;
+ *                 negative = skip the token.
+ *   seq_idx       int32 (num_tokens): tail row (sequence) of each token;
+ *                 required when k_dtype == KVQ_INT4_KIVI, else ignored.
+ * For KVQ_INT4_KIVI the rows of one page must appear in the call in slot
+ * order and consecutively (as a prefill chunk or one token per decode step
+ * does); a page is quantized when the call holds its last row, taking its
+ * earlier rows from this call or from the tail written by earlier calls.
+ * num_tokens == 0 is a no-op. */
+int kvq_write(const kvq_cache* cache, const void* k, const void* v,
+              const int64_t* slot_mapping, const int32_t* seq_idx,
+              int64_t num_tokens, void* stream);
+
+/* Bytes of device workspace kvq_decode_attn needs for these sizes (partial
+ * softmax states of the context splits).  pages_per_split 0 = automatic. */
+int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch,
+                               int32_t n_q_heads, int32_t max_blocks_per_seq,
+                               int32_t pages_per_split, size_t* bytes);
+
+/* Decode attention over the quantized pages ([P2] 5 "The kernel side";
+ * "K is more sensitive than V": o = softmax(q k^T * sm_scale) V).
+ *   q            fp16 (batch, n_q_heads, D)
+ *   block_table  int32 (batch, max_blocks_per_seq): physical block of each
+ *                page of each sequence; entries past the sequence's pages are
+ *                never read.
+ *   ctx_lens     int32 (batch): tokens of each sequence in the cache (0 gives
+ *                an all-zero output row).  For KVQ_INT4_KIVI keys the last
+ *                ctx_len % 32 tokens are read from tail row b (the batch row).
+ *   sm_scale     softmax scale; 0 means 1/sqrt(head_dim).
+ *   pages_per_split  pages per context split; 0 = automatic.
+ *   out          fp16 (batch, n_q_heads, D), written.
+ *   workspace    device scratch of at least kvq_decode_workspace_bytes().
+ * Query head hq reads KV head hq / (n_q_heads / n_kv_heads) ([P4] GQA).
+ * Scores and the softmax are accumulated in fp32; the result is rounded to
+ * fp16 once, to nearest-even.  The result does not depend on how the context
+ * is split except through fp32 rounding. */
+int kvq_decode_attn(const kvq_cache* cache, const void* q,
+                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* ctx_lens, int32_t batch, int32_t n_q_heads,
+                    float sm_scale, int32_t pages_per_split, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* kvq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

@@ -376,6 +376,29 @@ def gather_dequant(cache: OracleCache, block_table_row, L: int, seq: int):
     return K, V
 
 
+def dequantized_sequence(k16: np.ndarray, v16: np.ndarray, k_fmt: str, v_fmt: str, block_size: int = 32):
+    """K_hat, V_hat (L, H, D) float64 of one sequence written whole, without
+    paging: what gather_dequant returns for a sequence written in position
+    order.  KIVI keys: complete 32-token groups quantized per channel, the
+    last L mod 32 tokens (keys and values) kept in fp16."""
+    L = k16.shape[0]
+    codes, s = quantize_sym(v16, v_fmt)
+    V = dequant_sym(codes, s, v_fmt)
+    if k_fmt != INT4_KIVI:
+        codes, s = quantize_sym(k16, k_fmt)
+        return dequant_sym(codes, s, k_fmt), V
+    nfull = (L // KIVI_GROUP) * KIVI_GROUP
+    K = np.empty(k16.shape, np.float64)
+    for p in range(nfull // KIVI_GROUP):
+        sl = slice(p * KIVI_GROUP, (p + 1) * KIVI_GROUP)
+        for h in range(k16.shape[1]):
+            c, sc, z = kivi_quantize_group(k16[sl, h, :])
+            K[sl, h, :] = kivi_dequant(c, sc, z)
+    K[nfull:] = k16[nfull:].astype(np.float64)
+    V[nfull:] = v16[nfull:].astype(np.float64)
+    return K, V
+
+
 def attention_fp64(q, K, V, sm_scale=None):
     """One decode query per head against L cached tokens, float64:
     o = softmax(q k^T * sm_scale) V  ([P2] section 5 "K is more sensitive than

@@ -1,0 +1,190 @@
+"""ctypes binding of libkvq.so (see include/kvq.h for the contract).
+
+This layer only marshals arguments: it turns torch tensors into device
+pointers and the current torch stream into a hipStream_t, and allocates the
+caller-owned cache buffers with torch.  Every step of the computation runs in
+the HIP kernels; if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+KVQ_OK = 0
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_SHAPE",
+          -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_NO_DEVICE", -6: "KVQ_ERR_HIP"}
+DTYPES = {"int8": 1, "fp8_e4m3fn": 2, "int4_g32": 3, "int4_kivi": 4}
+
+# Functions declared in include/kvq.h (the symbol test checks this list
+# against the header).
+EXPORTS = ("kvq_write", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_status_string")
+
+
+class KvqCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("k_dtype", ctypes.c_int32), ("v_dtype", ctypes.c_int32),
+        ("max_seqs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+        ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("k_zeros", ctypes.c_void_p), ("k_tail", ctypes.c_void_p), ("v_tail", ctypes.c_void_p),
+    ]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, rc: int, what: str):
+        self.rc = rc
+        super().__init__(f"{what}: {STATUS.get(rc, rc)} ({status_string(rc)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvq.so from the package directory (built by build.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m quantized_paged_kv_write_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        cp = ctypes.POINTER(KvqCacheStruct)
+        L.kvq_write.argtypes = [cp, vp, vp, vp, vp, i64, vp]
+        L.kvq_write.restype = ctypes.c_int
+        L.kvq_decode_workspace_bytes.argtypes = [cp, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.kvq_decode_workspace_bytes.restype = ctypes.c_int
+        L.kvq_decode_attn.argtypes = [cp, vp, vp, i32, vp, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
+        L.kvq_decode_attn.restype = ctypes.c_int
+        L.kvq_status_string.argtypes = [ctypes.c_int]
+        L.kvq_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(rc: int) -> str:
+    return lib().kvq_status_string(rc).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, dtype, name, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+class PagedKVCache:
+    """One layer's quantized paged KV cache: caller-owned device buffers in
+    the layouts of include/kvq.h (codes uint8, scales/zeros/tails fp16)."""
+
+    def __init__(self, num_blocks, block_size, n_kv_heads, head_dim, k_dtype, v_dtype, max_seqs=0,
+                 device="cuda"):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.n_kv_heads, self.head_dim = int(n_kv_heads), int(head_dim)
+        self.k_dtype, self.v_dtype, self.max_seqs = k_dtype, v_dtype, int(max_seqs)
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        nb, bs, H, D = self.num_blocks, self.block_size, self.n_kv_heads, self.head_dim
+        z = lambda *shape, dt: torch.zeros(shape, dtype=dt, device=self.device)  # noqa: E731
+        half_row = lambda f: D // 2 if f in ("int4_g32", "int4_kivi") else D  # noqa: E731
+        groups = lambda f: D // 32 if f == "int4_g32" else 1  # noqa: E731
+        self.k_codes = z(nb, bs, H, half_row(k_dtype), dt=torch.uint8)
+        self.v_codes = z(nb, bs, H, half_row(v_dtype), dt=torch.uint8)
+        self.v_scales = z(nb, bs, H, groups(v_dtype), dt=torch.float16)
+        if k_dtype == "int4_kivi":
+            self.k_scales = z(nb, H, D, dt=torch.float16)
+            self.k_zeros = z(nb, H, D, dt=torch.float16)
+            self.k_tail = z(max(self.max_seqs, 1), bs, H, D, dt=torch.float16)
+            self.v_tail = z(max(self.max_seqs, 1), bs, H, D, dt=torch.float16)
+        else:
+            self.k_scales = z(nb, bs, H, groups(k_dtype), dt=torch.float16)
+            self.k_zeros = self.k_tail = self.v_tail = None
+
+    def struct(self) -> KvqCacheStruct:
+        return KvqCacheStruct(
+            self.num_blocks, self.block_size, self.n_kv_heads, self.head_dim,
+            DTYPES[self.k_dtype], DTYPES[self.v_dtype], self.max_seqs, 0,
+            _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scales), _ptr(self.v_scales),
+            _ptr(self.k_zeros), _ptr(self.k_tail), _ptr(self.v_tail))
+
+    def buffers(self) -> dict:
+        out = {"k_codes": self.k_codes, "v_codes": self.v_codes, "k_scales": self.k_scales,
+               "v_scales": self.v_scales}
+        if self.k_dtype == "int4_kivi":
+            out.update(k_zeros=self.k_zeros, k_tail=self.k_tail, v_tail=self.v_tail)
+        return out
+
+
+def write(cache: PagedKVCache, k, v, slot_mapping, seq_idx=None, stream=None):
+    """kvq_write: quantize fp16 k, v (T, H, D) into the cache at slot_mapping."""
+    dev = cache.device
+    _check(k, torch.float16, "k", dev)
+    _check(v, torch.float16, "v", dev)
+    _check(slot_mapping, torch.int64, "slot_mapping", dev)
+    if seq_idx is not None:
+        _check(seq_idx, torch.int32, "seq_idx", dev)
+    T = slot_mapping.numel()
+    if k.shape != (T, cache.n_kv_heads, cache.head_dim) or v.shape != k.shape:
+        raise ValueError(f"k/v must be ({T}, {cache.n_kv_heads}, {cache.head_dim})")
+    c = cache.struct()
+    rc = lib().kvq_write(ctypes.byref(c), _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(seq_idx), T, _stream(stream))
+    if rc != KVQ_OK:
+        raise KvqError(rc, "kvq_write")
+
+
+def decode_workspace_bytes(cache: PagedKVCache, batch, n_q_heads, max_blocks_per_seq, pages_per_split=0) -> int:
+    out = ctypes.c_size_t(0)
+    c = cache.struct()
+    rc = lib().kvq_decode_workspace_bytes(ctypes.byref(c), batch, n_q_heads, max_blocks_per_seq, pages_per_split,
+                                          ctypes.byref(out))
+    if rc != KVQ_OK:
+        raise KvqError(rc, "kvq_decode_workspace_bytes")
+    return out.value
+
+
+def decode_attn(cache: PagedKVCache, q, block_table, ctx_lens, sm_scale=0.0, pages_per_split=0, out=None,
+                workspace=None, stream=None):
+    """kvq_decode_attn: one decode step over the cache; returns out (B, Hq, D) fp16."""
+    dev = cache.device
+    _check(q, torch.float16, "q", dev)
+    _check(block_table, torch.int32, "block_table", dev)
+    _check(ctx_lens, torch.int32, "ctx_lens", dev)
+    B, Hq, D = q.shape
+    if D != cache.head_dim or block_table.dim() != 2 or block_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("shape mismatch between q, block_table and ctx_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, torch.float16, "out", dev)
+    need = decode_workspace_bytes(cache, B, Hq, block_table.shape[1], pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    c = cache.struct()
+    rc = lib().kvq_decode_attn(ctypes.byref(c), _ptr(q), _ptr(block_table), block_table.shape[1], _ptr(ctx_lens),
+                               B, Hq, float(sm_scale), pages_per_split, _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != KVQ_OK:
+        raise KvqError(rc, "kvq_decode_attn")
+    return out

@@ -1,0 +1,166 @@
+// C-ABI entry points: host-side validation, then launches on the caller's
+// stream.  Nothing here allocates device memory or synchronizes.
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace {
+
+using namespace kvq;
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool sym_fmt(int32_t f) { return f == KVQ_INT8 || f == KVQ_FP8_E4M3FN || f == KVQ_INT4_G32; }
+
+int check_cache(const kvq_cache* c) {
+  if (!c) return KVQ_ERR_INVALID_ARG;
+  if (c->num_blocks <= 0 || c->block_size <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0)
+    return KVQ_ERR_INVALID_ARG;
+  if (!(c->k_dtype >= KVQ_INT8 && c->k_dtype <= KVQ_INT4_KIVI)) return KVQ_ERR_INVALID_ARG;
+  if (!sym_fmt(c->v_dtype)) {
+    return (c->v_dtype == KVQ_INT4_KIVI) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
+  }
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (!is_pow2(c->block_size) || c->block_size < 8 || c->block_size > 128) return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)c->num_blocks * c->block_size * c->n_kv_heads >= (1ll << 31)) return KVQ_ERR_SHAPE;
+  if (!c->k_codes || !c->v_codes || !c->k_scales || !c->v_scales) return KVQ_ERR_INVALID_ARG;
+  if (c->k_dtype == KVQ_INT4_KIVI) {
+    if (c->block_size != 32) return KVQ_ERR_SHAPE;
+    if (c->max_seqs <= 0) return KVQ_ERR_SHAPE;
+    if (!c->k_zeros || !c->k_tail || !c->v_tail) return KVQ_ERR_INVALID_ARG;
+  }
+  return KVQ_OK;
+}
+
+int device_present() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return KVQ_ERR_NO_DEVICE;
+  return KVQ_OK;
+}
+
+struct SplitPlan {
+  int32_t pps;
+  int32_t splits;  // including the KIVI tail split
+};
+
+SplitPlan plan_splits(const kvq_cache& c, int32_t batch, int32_t max_blocks, int32_t requested) {
+  SplitPlan p;
+  p.pps = choose_pages_per_split(c, batch, max_blocks, requested);
+  p.splits = (max_blocks + p.pps - 1) / p.pps;
+  if (p.splits < 1) p.splits = 1;
+  if (c.k_dtype == KVQ_INT4_KIVI) p.splits += 1;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument (NULL pointer, non-positive size or unknown enum)";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported format, head_dim or block_size";
+    case KVQ_ERR_SHAPE: return "shape rule broken (KIVI needs block_size 32 and max_seqs > 0; sizes too large; "
+                               "n_q_heads not a multiple of n_kv_heads)";
+    case KVQ_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case KVQ_ERR_NO_DEVICE: return "no HIP device available";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown kvq status";
+}
+
+int kvq_write(const kvq_cache* cache, const void* k, const void* v, const int64_t* slot_mapping,
+              const int32_t* seq_idx, int64_t num_tokens, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != KVQ_OK) return rc;
+  if (cache->k_dtype == KVQ_INT4_G32) return KVQ_ERR_UNSUPPORTED;  // INT4 keys: KIVI only
+  if (num_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  if (num_tokens == 0) return KVQ_OK;
+  if (!k || !v || !slot_mapping) return KVQ_ERR_INVALID_ARG;
+  if (cache->k_dtype == KVQ_INT4_KIVI && !seq_idx) return KVQ_ERR_INVALID_ARG;
+  if (num_tokens * (int64_t)cache->n_kv_heads >= (1ll << 31)) return KVQ_ERR_SHAPE;
+  rc = device_present();
+  if (rc != KVQ_OK) return rc;
+  WriteArgs a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.slots = slot_mapping;
+  a.seq_idx = seq_idx;
+  a.T = num_tokens;
+  a.H = cache->n_kv_heads;
+  a.bs = cache->block_size;
+  a.capacity = (int64_t)cache->num_blocks * cache->block_size;
+  a.div_h = make_fastdiv((uint32_t)cache->n_kv_heads);
+  a.k_codes = static_cast<uint8_t*>(cache->k_codes);
+  a.k_scales = static_cast<uint16_t*>(cache->k_scales);
+  a.k_zeros = static_cast<uint16_t*>(cache->k_zeros);
+  a.v_codes = static_cast<uint8_t*>(cache->v_codes);
+  a.v_scales = static_cast<uint16_t*>(cache->v_scales);
+  a.k_tail = static_cast<uint16_t*>(cache->k_tail);
+  a.v_tail = static_cast<uint16_t*>(cache->v_tail);
+  a.max_seqs = cache->max_seqs;
+  return launch_write(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t n_q_heads,
+                               int32_t max_blocks_per_seq, int32_t pages_per_split, size_t* bytes) {
+  int rc = check_cache(cache);
+  if (rc != KVQ_OK) return rc;
+  if (!bytes || batch < 0 || n_q_heads <= 0 || max_blocks_per_seq <= 0 || pages_per_split < 0)
+    return KVQ_ERR_INVALID_ARG;
+  const SplitPlan p = plan_splits(*cache, batch, max_blocks_per_seq, pages_per_split);
+  *bytes = (size_t)batch * n_q_heads * p.splits * (cache->head_dim + 2) * sizeof(float);
+  return KVQ_OK;
+}
+
+int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* ctx_lens, int32_t batch, int32_t n_q_heads, float sm_scale,
+                    int32_t pages_per_split, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != KVQ_OK) return rc;
+  if (cache->k_dtype == KVQ_INT4_G32) return KVQ_ERR_UNSUPPORTED;
+  if (batch < 0 || n_q_heads <= 0 || max_blocks_per_seq <= 0 || pages_per_split < 0) return KVQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return KVQ_ERR_SHAPE;
+  const int32_t G = n_q_heads / cache->n_kv_heads;
+  if (G > 16) return KVQ_ERR_UNSUPPORTED;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return KVQ_ERR_INVALID_ARG;
+  if (batch == 0) return KVQ_OK;
+  if (cache->k_dtype == KVQ_INT4_KIVI && batch > cache->max_seqs) return KVQ_ERR_SHAPE;  // tail row per sequence
+  if (!q || !block_table || !ctx_lens || !out) return KVQ_ERR_INVALID_ARG;
+  size_t need = 0;
+  rc = kvq_decode_workspace_bytes(cache, batch, n_q_heads, max_blocks_per_seq, pages_per_split, &need);
+  if (rc != KVQ_OK) return rc;
+  if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+  rc = device_present();
+  if (rc != KVQ_OK) return rc;
+  const SplitPlan p = plan_splits(*cache, batch, max_blocks_per_seq, pages_per_split);
+  DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.max_blocks = max_blocks_per_seq;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.H = cache->n_kv_heads;
+  a.G = G;
+  a.bs = cache->block_size;
+  a.nb = cache->num_blocks;
+  const float scale = sm_scale == 0.0f ? 1.0f / sqrtf((float)cache->head_dim) : sm_scale;
+  a.qscale = scale * 1.4426950408889634f;  // log2(e): the softmax runs on exp2
+  a.k_codes = static_cast<const uint8_t*>(cache->k_codes);
+  a.k_scales = static_cast<const uint16_t*>(cache->k_scales);
+  a.k_zeros = static_cast<const uint16_t*>(cache->k_zeros);
+  a.v_codes = static_cast<const uint8_t*>(cache->v_codes);
+  a.v_scales = static_cast<const uint16_t*>(cache->v_scales);
+  a.k_tail = static_cast<const uint16_t*>(cache->k_tail);
+  a.v_tail = static_cast<const uint16_t*>(cache->v_tail);
+  a.max_seqs = cache->max_seqs;
+  a.pages_per_split = p.pps;
+  a.num_splits = p.splits;
+  a.part = static_cast<float*>(workspace);
+  a.out = static_cast<uint16_t*>(out);
+  return launch_decode(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // extern "C"

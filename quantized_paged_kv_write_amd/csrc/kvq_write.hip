@@ -1,0 +1,320 @@
+// Quantize-on-write into the paged cache (gfx950).
+//
+// Symmetric formats ("Use Less Memory: Quantization and Offloading", section
+// 2.1; "12 KV Cache Quantization", section 5 "Where the scales live"): every
+// (token, head) row is quantized on its own, one fp16 scale per row (INT8,
+// FP8 E4M3FN) or per 32 channels (INT4).  One pass streams the fp16 rows:
+// each lane owns 16 bytes (8 channels) of a row, a row is D/8 consecutive
+// lanes, the group max |x| is a lane-group reduction, and the codes of a row
+// leave as one contiguous store per lane.
+//
+// KIVI-style keys ("12 KV Cache Quantization", section 5 "K is more sensitive
+// than V"; "Quantized KV caches in production", Numerical Formats; the
+// glossary's asymmetric quantization): the 32 rows of a page are quantized
+// together per channel when the page's last row arrives (kivi_seal_kernel);
+// rows of unfinished pages wait in the sequence's fp16 tail, written by the
+// value pass after the seal kernel has read the previous tail.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT>
+__device__ __forceinline__ float qmax() {
+  return FMT == F_INT8 ? 127.0f : (FMT == F_FP8 ? 448.0f : 7.0f);
+}
+
+template <int FMT, int D>
+struct WShape {
+  static constexpr int LPR = D / 8;                      // lanes per row
+  static constexpr int RPP = 256 / LPR;                  // rows per pass of a block
+  static constexpr int LPG = FMT == F_INT4 ? 4 : LPR;    // lanes per scale group
+  static constexpr int CB = FMT == F_INT4 ? D / 2 : D;   // code bytes per row
+  static constexpr int NG = FMT == F_INT4 ? D / 32 : 1;  // scales per row
+};
+
+// Codes of 8 channels from their exact quotients y = x / s.
+template <int FMT>
+__device__ __forceinline__ u32x2 encode8(const float (&y)[8]) {
+  u32x2 out;
+  if constexpr (FMT == F_FP8) {
+    float c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = fminf(fmaxf(y[j], -448.0f), 448.0f);
+    out.x = fp8x4(c[0], c[1], c[2], c[3]);
+    out.y = fp8x4(c[4], c[5], c[6], c[7]);
+  } else if constexpr (FMT == F_INT8) {
+    uint32_t b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = (uint32_t)(int)__builtin_rintf(fminf(fmaxf(y[j], -127.0f), 127.0f)) & 0xFFu;
+    out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  } else {  // INT4: two's-complement nibbles, even channel low
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      w |= ((uint32_t)(int)__builtin_rintf(fminf(fmaxf(y[j], -7.0f), 7.0f)) & 0xFu) << (4 * j);
+    out.x = w;
+    out.y = 0;
+  }
+  return out;
+}
+
+template <int FMT, int D, int ITER, bool TAIL>
+__device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* __restrict__ src,
+                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+  using S = WShape<FMT, D>;
+  const int lir = threadIdx.x % S::LPR;
+  const uint32_t nrows = (uint32_t)(a.T * a.H);
+  const uint32_t row0 = blockIdx.x * (uint32_t)(S::RPP * ITER) + threadIdx.x / S::LPR;
+  u32x4 xin[ITER];
+  int64_t slot[ITER];
+  uint32_t tok[ITER];
+  // Issue every load of the block first so ITER rows per lane are in flight.
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const uint32_t r = row0 + i * S::RPP;
+    slot[i] = -1;
+    tok[i] = 0;
+    if (r < nrows) {
+      tok[i] = fastdiv(r, a.div_h);
+      slot[i] = a.slots[tok[i]];
+      xin[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)r * D) + lir);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const uint32_t r = row0 + i * S::RPP;
+    if (r >= nrows) continue;  // uniform over the lanes of a row
+    const int64_t s = slot[i];
+    const bool valid = s >= 0 && s < a.capacity;
+    float x[8];
+    unpack8(uint4{xin[i].x, xin[i].y, xin[i].z, xin[i].w}, x);
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+    am = group_max<S::LPG>(am);
+    // Scale: fp32 quotient, rounded once more to fp16 for storage; the codes
+    // divide by the stored value.
+    const float s32 = am / qmax<FMT>();
+    const uint32_t s16 = f2h_bits(s32);
+    const float sc = h2f(s16);
+    u32x2 enc = {0u, 0u};
+    if (sc != 0.0f) {
+      const float rc = 1.0f / sc;
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = exact_div(x[j], sc, rc);
+      enc = encode8<FMT>(y);
+    }
+    if (valid) {
+      const uint32_t h = r - tok[i] * (uint32_t)a.H;
+      const size_t orow = (size_t)s * a.H + h;
+      if constexpr (FMT == F_INT4) {
+        reinterpret_cast<uint32_t*>(codes + orow * S::CB)[lir] = enc.x;
+      } else {
+        reinterpret_cast<u32x2*>(codes + orow * S::CB)[lir] = enc;
+      }
+      if (lir % S::LPG == 0) scales[orow * S::NG + lir / S::LPG] = (uint16_t)s16;
+      if constexpr (TAIL) {
+        // KIVI keys: a row whose page is not completed within this call is
+        // kept in fp16 (key and value) in its sequence's tail.
+        const int off = (int)(s % a.bs);
+        const int64_t te = (int64_t)tok[i] + (a.bs - 1 - off);
+        const int32_t seq = a.seq_idx[tok[i]];
+        bool sealed = false;
+        if (te < a.T) sealed = a.seq_idx[te] == seq && a.slots[te] == s + (a.bs - 1 - off);
+        if (!sealed && seq >= 0 && seq < a.max_seqs) {
+          const size_t trow = ((size_t)seq * a.bs + off) * a.H + h;
+          reinterpret_cast<u32x4*>(a.v_tail + trow * D)[lir] = xin[i];
+          reinterpret_cast<u32x4*>(a.k_tail + trow * D)[lir] =
+              reinterpret_cast<const u32x4*>(a.k + (size_t)r * D)[lir];
+        }
+      }
+    }
+  }
+}
+
+// grid.y: 0 = keys, 1 = values (keys are skipped for KIVI: grid.y = 1 and
+// tensor0 = 1).
+template <int FK, int FV, int D, int ITER>
+__global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0) {
+  const int tensor = (int)blockIdx.y + tensor0;
+  if (tensor == 0) {
+    if constexpr (FK != F_KIVI) write_rows<FK, D, ITER, false>(a, a.k, a.k_codes, a.k_scales);
+  } else {
+    write_rows<FV, D, ITER, FK == F_KIVI>(a, a.v, a.v_codes, a.v_scales);
+  }
+}
+
+// Reductions across the row sets of a wave (lanes that share lane % NCH).
+template <int NCH>
+__device__ __forceinline__ float rowset_min(float v) {
+#pragma unroll
+  for (int m = NCH; m < 64; m <<= 1) v = fminf(v, __shfl_xor(v, m));
+  return v;
+}
+template <int NCH>
+__device__ __forceinline__ float rowset_max(float v) {
+#pragma unroll
+  for (int m = NCH; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// KIVI key pages.  Block (chunk of 32 call tokens, head h), one wave.  Every
+// token of the chunk that lands on the last row of a page completes that
+// page: its 32 key rows (from this call where present at the expected call
+// positions, else from the sequence's tail) are quantized per channel:
+//   s = fp16(fl32(max - min) / 15), z = min, code = clip(rint((x - z) / s), 0, 15).
+template <int D>
+__global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
+  constexpr int NCH = D / 8;     // lanes per row (8 channels each)
+  constexpr int RS = 64 / NCH;   // rows loaded side by side
+  constexpr int RPL = 32 / RS;   // rows per lane
+  const int h = (int)blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  const int lane = (int)threadIdx.x;
+  bool seal = false;
+  if (lane < 32) {
+    const int64_t t = t0 + lane;
+    if (t < a.T) {
+      const int64_t s = a.slots[t];
+      seal = s >= 0 && s < a.capacity && (s & 31) == 31;
+    }
+  }
+  uint64_t mask = __ballot(seal);
+  const int cc = lane % NCH, rs = lane / NCH;
+  while (mask) {
+    const int j = __ffsll((unsigned long long)mask) - 1;
+    mask &= mask - 1;
+    const int64_t te = t0 + j;
+    const int64_t se = a.slots[te];
+    const int32_t seq = a.seq_idx[te];
+    if (seq < 0 || seq >= a.max_seqs) continue;
+    const int64_t blk = se >> 5;
+    float x[RPL][8];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int row = rs + i * RS;
+      const int64_t ts = te - (31 - row);
+      bool in_call = false;
+      if (ts >= 0) in_call = a.seq_idx[ts] == seq && a.slots[ts] == se - (31 - row);
+      const uint16_t* src = in_call ? a.k + ((size_t)ts * a.H + h) * D
+                                    : a.k_tail + (((size_t)seq * 32 + row) * a.H + h) * D;
+      const u32x4 u = reinterpret_cast<const u32x4*>(src)[cc];
+      unpack8(uint4{u.x, u.y, u.z, u.w}, x[i]);
+    }
+    float mn[8], mx[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float lo = x[0][c], hi = x[0][c];
+#pragma unroll
+      for (int i = 1; i < RPL; ++i) {
+        lo = fminf(lo, x[i][c]);
+        hi = fmaxf(hi, x[i][c]);
+      }
+      mn[c] = rowset_min<NCH>(lo);
+      mx[c] = rowset_max<NCH>(hi);
+    }
+    uint32_t s16[8], z16[8];
+    float sc[8], rc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float range = mx[c] - mn[c];  // fl32(max - min)
+      s16[c] = f2h_bits(range / 15.0f);
+      z16[c] = f2h_bits(mn[c]);  // exact: mn is an fp16 value
+      sc[c] = h2f(s16[c]);
+      rc[c] = sc[c] != 0.0f ? 1.0f / sc[c] : 0.0f;
+    }
+    uint8_t* cbase = a.k_codes + (size_t)blk * 32 * a.H * (D / 2);
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int row = rs + i * RS;
+      uint32_t w = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t code = 0;
+        if (sc[c] != 0.0f) {
+          const float y = exact_div(x[i][c] - mn[c], sc[c], rc[c]);  // fl32(fl32(x - z) / s)
+          code = (uint32_t)(int)__builtin_rintf(fminf(fmaxf(y, 0.0f), 15.0f));
+        }
+        w |= code << (4 * c);
+      }
+      reinterpret_cast<uint32_t*>(cbase + ((size_t)row * a.H + h) * (D / 2))[cc] = w;
+    }
+    if (rs == 0) {
+      const size_t m = ((size_t)blk * a.H + h) * D + cc * 8;
+      u32x4 sv, zv;
+      sv.x = s16[0] | (s16[1] << 16); sv.y = s16[2] | (s16[3] << 16);
+      sv.z = s16[4] | (s16[5] << 16); sv.w = s16[6] | (s16[7] << 16);
+      zv.x = z16[0] | (z16[1] << 16); zv.y = z16[2] | (z16[3] << 16);
+      zv.z = z16[4] | (z16[5] << 16); zv.w = z16[6] | (z16[7] << 16);
+      *reinterpret_cast<u32x4*>(a.k_scales + m) = sv;
+      *reinterpret_cast<u32x4*>(a.k_zeros + m) = zv;
+    }
+  }
+}
+
+namespace {
+
+constexpr int kIter = 4;
+
+template <int FK, int FV, int D>
+hipError_t launch_sym(const WriteArgs& a, hipStream_t s) {
+  constexpr int RPP = 256 / (D / 8);
+  const int64_t rows = a.T * a.H;
+  const int64_t blocks = (rows + RPP * kIter - 1) / (RPP * kIter);
+  const int tensors = FK == F_KIVI ? 1 : 2;
+  const int tensor0 = FK == F_KIVI ? 1 : 0;
+  hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIter>), dim3((unsigned)blocks, tensors), dim3(256), 0, s, a,
+                     tensor0);
+  return hipGetLastError();
+}
+
+template <int FK, int FV, int D>
+hipError_t launch_all(const WriteArgs& a, hipStream_t s) {
+  if constexpr (FK == F_KIVI) {
+    const int64_t chunks = (a.T + 31) / 32;
+    hipLaunchKernelGGL((kivi_seal_kernel<D>), dim3((unsigned)chunks, a.H), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_sym<FK, FV, D>(a, s);
+}
+
+template <int FK, int FV>
+hipError_t by_dim(int D, const WriteArgs& a, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_all<FK, FV, 64>(a, s);
+    case 128: return launch_all<FK, FV, 128>(a, s);
+    case 256: return launch_all<FK, FV, 256>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FK>
+hipError_t by_v(int fv, int D, const WriteArgs& a, hipStream_t s) {
+  switch (fv) {
+    case F_INT8: return by_dim<FK, F_INT8>(D, a, s);
+    case F_FP8: return by_dim<FK, F_FP8>(D, a, s);
+    case F_INT4: return by_dim<FK, F_INT4>(D, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_write(const kvq_cache& c, const WriteArgs& a, hipStream_t s) {
+  switch (c.k_dtype) {
+    case F_INT8: return by_v<F_INT8>(c.v_dtype, c.head_dim, a, s);
+    case F_FP8: return by_v<F_FP8>(c.v_dtype, c.head_dim, a, s);
+    case F_INT4: return by_v<F_INT4>(c.v_dtype, c.head_dim, a, s);
+    case F_KIVI: return by_v<F_KIVI>(c.v_dtype, c.head_dim, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

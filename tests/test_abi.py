@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every function include/kvq.h declares, and
+rejects bad arguments on the host before anything is launched.  No compute
+call is made here (these tests must pass on a machine without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_paged_kv_write_amd as kvq
+from quantized_paged_kv_write_amd.binding import EXPORTS, KvqCacheStruct
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+OK, INVALID, UNSUPPORTED, SHAPE, WORKSPACE, NO_DEVICE = 0, -1, -2, -3, -4, -5
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_functions() == sorted(EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvq.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for rc in (OK, INVALID, UNSUPPORTED, SHAPE, WORKSPACE, NO_DEVICE, -6, 12345):
+        assert isinstance(kvq.status_string(rc), str) and kvq.status_string(rc)
+
+
+def _cache(**kw):
+    c = KvqCacheStruct(num_blocks=8, block_size=16, n_kv_heads=2, head_dim=128, k_dtype=1, v_dtype=1, max_seqs=0)
+    c.k_codes = c.v_codes = c.k_scales = c.v_scales = FAKE
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _write(c, T=4, seq=None):
+    return kvq.lib().kvq_write(ctypes.byref(c), FAKE, FAKE, FAKE, seq, T, None)
+
+
+def _ws(c, batch=1, hq=4, mb=4, pps=0):
+    out = ctypes.c_size_t(0)
+    rc = kvq.lib().kvq_decode_workspace_bytes(ctypes.byref(c), batch, hq, mb, pps, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_write_argument_errors():
+    L = kvq.lib()
+    assert L.kvq_write(None, FAKE, FAKE, FAKE, None, 4, None) == INVALID
+    assert _write(_cache(k_dtype=0)) == INVALID
+    assert _write(_cache(v_dtype=9)) == INVALID
+    assert _write(_cache(v_dtype=4)) == UNSUPPORTED  # KIVI is for keys only
+    assert _write(_cache(head_dim=96)) == UNSUPPORTED
+    assert _write(_cache(block_size=24)) == UNSUPPORTED
+    assert _write(_cache(num_blocks=0)) == INVALID
+    assert _write(_cache(k_codes=None)) == INVALID
+    assert _write(_cache(k_dtype=4, block_size=16, max_seqs=2)) == SHAPE  # KIVI needs 32-token pages
+    assert _write(_cache(k_dtype=4, block_size=32, max_seqs=0)) == SHAPE
+    assert _write(_cache(k_dtype=4, block_size=32, max_seqs=2)) == INVALID  # zeros / tails missing
+    assert _write(_cache(k_dtype=3)) == UNSUPPORTED  # INT4 group-32 keys not offered
+    assert _write(_cache(), T=-1) == INVALID
+    assert _write(_cache(), T=0) == OK  # no-op
+    assert L.kvq_write(ctypes.byref(_cache()), None, FAKE, FAKE, None, 4, None) == INVALID
+    kc = _cache(k_dtype=4, block_size=32, max_seqs=2, k_zeros=FAKE, k_tail=FAKE, v_tail=FAKE)
+    assert _write(kc, seq=None) == INVALID  # KIVI needs seq_idx
+
+
+def test_workspace_query():
+    rc, n = _ws(_cache(), batch=3, hq=4, mb=10, pps=4)
+    assert rc == OK and n == 3 * 4 * 3 * (128 + 2) * 4  # ceil(10/4) = 3 splits
+    rc, n = _ws(_cache(k_dtype=4, block_size=32, max_seqs=1, k_zeros=FAKE, k_tail=FAKE, v_tail=FAKE),
+                batch=1, hq=2, mb=8, pps=8)
+    assert rc == OK and n == 1 * 2 * 2 * 130 * 4  # one split + the fp16-tail split
+    assert _ws(_cache(), mb=0)[0] == INVALID
+    assert _ws(_cache(), pps=-1)[0] == INVALID
+
+
+def test_decode_argument_errors():
+    L = kvq.lib()
+    c = _cache()
+
+    def dec(batch=2, hq=4, mb=4, scale=0.0, pps=0, ws=FAKE, wsb=1 << 30, q=FAKE):
+        return L.kvq_decode_attn(ctypes.byref(c), q, FAKE, mb, FAKE, batch, hq, scale, pps, FAKE, ws, wsb, None)
+
+    assert dec(hq=3) == SHAPE            # not a multiple of n_kv_heads
+    assert dec(hq=2 * 17) == UNSUPPORTED  # G > 16
+    assert dec(scale=-1.0) == INVALID
+    assert dec(scale=float("nan")) == INVALID
+    assert dec(ws=None) == WORKSPACE
+    assert dec(wsb=16) == WORKSPACE
+    assert dec(q=None) == INVALID
+    assert dec(batch=0) == OK            # empty batch: nothing to do
+    assert dec(mb=0) == INVALID
+
+
+@pytest.mark.skipif(kvq.binding.torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_valid_call_without_device_reports_no_device():
+    assert _write(_cache()) == NO_DEVICE
+
+
+def test_fastdiv_constants_match_integer_division():
+    # The write kernel divides row indices by n_kv_heads with the round-up
+    # multiplier method; recompute its constants here and check exhaustively
+    # over the ranges the kernel sees (rows < 2^31).
+    import random
+    for d in list(range(1, 70)) + [96, 128, 255, 1000, 65535]:
+        s = 0
+        while (1 << s) < d:
+            s += 1
+        m = ((1 << 32) * ((1 << s) - d)) // d + 1
+        rnd = random.Random(d)
+        for n in [0, 1, d - 1, d, d + 1, 2 ** 31 - 1, 2 ** 31 - d] + [rnd.randrange(2 ** 31) for _ in range(2000)]:
+            q = ((n * m >> 32) + n) >> s
+            assert q == n // d, (d, n)

@@ -347,6 +347,8 @@ def test_paged_gather_equals_direct_quantization(kf, vf):
     table = np.random.default_rng(4).permutation(npages + 3)[:npages][None]
     c, k, v = _make_seq_cache(kf, vf, L, bs, H, D, table)
     K, V = o.gather_dequant(c, table[0], L, 0)
+    K2, V2 = o.dequantized_sequence(k, v, kf, vf)
+    assert np.array_equal(K, K2) and np.array_equal(V, V2)
     codes, s = o.quantize_sym(v, vf)
     assert np.array_equal(V[: (L // bs) * bs if kf == o.INT4_KIVI else L],
                           o.dequant_sym(codes, s, vf)[: (L // bs) * bs if kf == o.INT4_KIVI else L])
