@@ -1,0 +1,251 @@
+"""Benchmark: quantized paged decode on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one decode step of the workload's batch: quantize-on-write of the
+new token of every sequence into the paged cache (kvq_write), then decode
+attention over the whole cache (kvq_decode_attn).  The cache is filled before
+timing by a prefill write of all earlier tokens, which is timed on its own for
+the write bandwidth.  Prints one JSON line.
+
+value = decode KV-read bytes per step / step time (GB/s); the roofline entry
+is for the decode kernels (split-K attention + split merge), timed with HIP
+events on the stream they run on.  Bytes are algorithmic: what the method has
+to move (codes, scale metadata, block-table entries, q and out; for the write
+the fp16 K/V read, codes and metadata written, slot indices).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD specification
+
+
+def row_bytes(fmt: str, D: int) -> float:
+    """Stored bytes per (token, head): codes + fp16 scale metadata."""
+    if fmt == "int4_kivi":
+        return D / 2 + 2 * 2 * D / 32  # scale + zero per channel per 32-token page
+    if fmt == "int4_g32":
+        return D / 2 + 2 * D / 32
+    return D + 2
+
+
+def decode_bytes(w, ctx_lens) -> int:
+    H, D, bs = w.n_kv_heads, w.head_dim, w.block_size
+    per_tok = H * (row_bytes(w.k_dtype, D) + row_bytes(w.v_dtype, D))
+    total = 0.0
+    for L in ctx_lens:
+        if w.k_dtype == "int4_kivi":
+            nf = (L // 32) * 32
+            total += nf * per_tok + (L - nf) * H * D * 2 * 2  # fp16 tail rows
+        else:
+            total += L * per_tok
+        total += math.ceil(L / bs) * 4  # block-table entries
+    total += 2 * len(ctx_lens) * w.n_q_heads * D * 2  # q in, out
+    return int(total)
+
+
+def write_bytes(w, T: int) -> int:
+    H, D = w.n_kv_heads, w.head_dim
+    per = H * (2 * D * 2 + row_bytes(w.k_dtype, D) + row_bytes(w.v_dtype, D))
+    return int(T * (per + 8 + (4 if w.k_dtype == "int4_kivi" else 0)))
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The CPU oracle, single-threaded, on whole sequences of the same
+    workload until about budget_s seconds of decode work have been timed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as o
+
+    dec_t = wr_t = 0.0
+    dec_b = wr_b = 0
+    seqs = 0
+    with threadpool_limits(limits=1):
+        for b in range(w.batch):
+            L = inp.ctx_lens[b]
+            st = inp.seq_start[b]
+            k16 = inp.k[st:st + L].cpu().numpy()
+            v16 = inp.v[st:st + L].cpu().numpy()
+            npg = -(-L // w.block_size)
+            table = np.arange(npg, dtype=np.int64)[None]
+            pos = np.arange(L)
+            slots = table[0, pos // w.block_size] * w.block_size + pos % w.block_size
+            cache = o.OracleCache(npg, w.block_size, w.n_kv_heads, w.head_dim, w.k_dtype, w.v_dtype, max_seqs=1)
+            t0 = time.perf_counter()
+            o.write(cache, k16, v16, slots, np.zeros(L, np.int32))
+            t1 = time.perf_counter()
+            o.decode_attn(cache, inp.q[b:b + 1].cpu().numpy(), table, [L])
+            t2 = time.perf_counter()
+            wr_t += t1 - t0
+            dec_t += t2 - t1
+            wr_b += write_bytes(w, L)
+            dec_b += decode_bytes(w.with_(batch=1), [L])
+            seqs += 1
+            if dec_t + wr_t >= budget_s:
+                break
+    return {
+        "value": round(dec_b / dec_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{seqs} of {w.batch} sequences (ctx {inp.ctx_lens[0]}), decode step over their cache; "
+                  f"oracle write of the same sequences {wr_b / wr_t / 1e9:.4f} GB/s",
+        "decode_s": round(dec_t, 3), "write_s": round(wr_t, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_fp8")
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode and write kernels shard "
+              "by sequence or KV head with no communication, so run one process per GPU instead.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_paged_kv_write_amd as kvq
+    from quantized_paged_kv_write_amd import workloads as wl
+
+    dev = "cuda"
+    w = wl.WORKLOADS[args.workload]
+    seed = wl.ORDER.index(args.workload) + 1
+    print(f"[bench] workload {w.name}: B={w.batch} Hq={w.n_q_heads} H={w.n_kv_heads} D={w.head_dim} "
+          f"bs={w.block_size} K={w.k_dtype} V={w.v_dtype}", file=sys.stderr, flush=True)
+    inp = wl.make_inputs(w, seed, dev)
+    ctx = inp.ctx_lens
+    B = w.batch
+    cache = kvq.PagedKVCache(inp.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, w.k_dtype, w.v_dtype,
+                             max_seqs=B, device=dev)
+    pos = inp.positions
+    last = torch.tensor([inp.seq_start[b] + ctx[b] - 1 for b in range(B)])
+    pre_mask = torch.ones(pos.numel(), dtype=torch.bool)
+    pre_mask[last] = False
+    pre_idx = torch.nonzero(pre_mask)[:, 0].to(dev)
+    k_pre, v_pre = inp.k[pre_idx], inp.v[pre_idx]
+    s_pre = inp.slot_mapping.to(dev)[pre_idx]
+    q_pre = inp.seq_idx.to(dev)[pre_idx]
+    last_d = last.to(dev)
+    k_new, v_new = inp.k[last_d].contiguous(), inp.v[last_d].contiguous()
+    s_new = inp.slot_mapping.to(dev)[last_d].contiguous()
+    q_new = inp.seq_idx.to(dev)[last_d].contiguous()
+    q = inp.q
+    table = inp.block_table.to(dev)
+    ctx_d = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(kvq.decode_workspace_bytes(cache, B, w.n_q_heads, table.shape[1]), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- prefill write (cache fill), timed for the write bandwidth --------
+    kvq.write(cache, k_pre, v_pre, s_pre, q_pre)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.prefill_reps):
+        kvq.write(cache, k_pre, v_pre, s_pre, q_pre)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    write_ms = ev[0].elapsed_time(ev[1]) / args.prefill_reps
+    wbytes = write_bytes(w, pre_idx.numel())
+    print(f"[bench] prefill write of {pre_idx.numel()} tokens: {write_ms:.3f} ms, "
+          f"{wbytes / write_ms / 1e6:.1f} GB/s", file=sys.stderr, flush=True)
+
+    # ---- plain device copy: the achievable HBM ceiling ---------------------
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes * 5 / (ev[0].elapsed_time(ev[1]) * 1e6)
+    del src, dst
+
+    # ---- decode steps -------------------------------------------------------
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        kvq.write(cache, k_new, v_new, s_new, q_new)
+        if evs is not None:
+            evs[1].record(stream)
+        kvq.decode_attn(cache, q, table, ctx_d, out=out, workspace=ws)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    stepw_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    dbytes = decode_bytes(w, ctx)
+    value = dbytes / (ms_per_step * 1e6)
+    achieved = dbytes / (dec_ms * 1e6)
+    res = {
+        "metric": "quantized paged-decode KV-read GB/s (% HBM peak) + decode tok/s; write GB/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp8_e4m3fn": "fp8_e4m3fn", "int8": "int8"}.get(w.k_dtype, w.k_dtype) + "+" + w.v_dtype
+                 + " codes, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "ctx_lens": "fixed %d" % ctx[0] if len(set(ctx)) == 1
+                   else f"ragged {min(ctx)}..{max(ctx)} (mean {sum(ctx) / len(ctx):.0f})",
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "k_format": w.k_dtype, "v_format": w.v_dtype},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_kernels_ms": round(dec_ms, 4),
+        "decode_step_write_ms": round(stepw_ms, 4),
+        "decode_bytes_per_step": dbytes,
+        "decode_tok_s": round(B / (ms_per_step * 1e-3), 1),
+        "decode_tok_s_attention_only_all_layers": round(B / (ms_per_step * 1e-3 * w.n_layers), 1),
+        "write_GBps": round(wbytes / (write_ms * 1e6), 2),
+        "write_pct_hbm_peak": round(100 * wbytes / (write_ms * 1e6) / HBM_PEAK_GBPS, 2),
+        "write_ms": round(write_ms, 4),
+        "write_tokens": int(pre_idx.numel()),
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "decode_split_kernel + merge_kernel (one kvq_decode_attn call)"},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

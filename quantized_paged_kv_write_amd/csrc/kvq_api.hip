@@ -145,6 +145,8 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_
   a.H = cache->n_kv_heads;
   a.G = G;
   a.bs = cache->block_size;
+  a.log2_bs = 0;
+  while ((1 << a.log2_bs) < cache->block_size) ++a.log2_bs;
   a.nb = cache->num_blocks;
   const float scale = sm_scale == 0.0f ? 1.0f / sqrtf((float)cache->head_dim) : sm_scale;
   a.qscale = scale * 1.4426950408889634f;  // log2(e): the softmax runs on exp2
@@ -158,6 +160,7 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_
   a.max_seqs = cache->max_seqs;
   a.pages_per_split = p.pps;
   a.num_splits = p.splits;
+  a.quant_splits = p.splits - (cache->k_dtype == KVQ_INT4_KIVI ? 1 : 0);
   a.part = static_cast<float*>(workspace);
   a.out = static_cast<uint16_t*>(out);
   return launch_decode(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;

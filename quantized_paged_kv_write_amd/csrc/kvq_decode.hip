@@ -28,6 +28,8 @@
 //    fp32 throughout; each split stores (m, l, acc[D]).
 #include <math.h>
 
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -45,7 +47,7 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int TILE = 32;      // tokens per tile
 constexpr int MAX_WAVES = 8;  // KV heads per workgroup
-constexpr int MAX_PPS = 512;  // pages per split (block-table slice in LDS)
+constexpr int MAX_PPS = 256;  // pages per split (block-table slice in LDS)
 
 template <int FK, int D>
 struct KShape {
@@ -78,13 +80,11 @@ __device__ __forceinline__ void int8_to_h4(uint32_t d, uint32_t& lo, uint32_t& h
   lo = h2_bits(as_h2(a) - bias);
   hi = h2_bits(as_h2(b) - bias);
 }
-// FP8 E4M3FN -> fp32 (exact) -> fp16 (exact: every E4M3FN value is an fp16
-// value, so round-toward-zero packing is exact).
+// FP8 E4M3FN -> fp16, two codes per instruction (exact: every E4M3FN value
+// is an fp16 value; the scale operand 1.0 leaves the values unchanged).
 __device__ __forceinline__ void fp8_to_h4(uint32_t d, uint32_t& lo, uint32_t& hi) {
-  const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)d, false);
-  const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)d, true);
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f01[0], f01[1]));
-  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f23[0], f23[1]));
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true));
 }
 
 template <int FK>
@@ -126,7 +126,8 @@ __device__ __forceinline__ int key_channel(int j, int kb, int e) {
 // INT8: bf16(c + 128) (exact, <= 255); the +128 is removed afterwards with
 // the sum of the probabilities.  FP8: exact.  INT4: 128 + (n + 8) (exact).
 __device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
-  return (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u);
+  // upper halves of a (low word) and b (high word): one v_perm_b32
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x07060302u);
 }
 
 template <int FV>
@@ -134,14 +135,11 @@ __device__ __forceinline__ b8 value_operand_8bit(i2 t) {
   const uint32_t d0 = (uint32_t)t.x, d1 = (uint32_t)t.y;
   u4 r;
   if constexpr (FV == F_FP8) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, true);
-    r.x = bf16_pair_hi(a[0], a[1]);
-    r.y = bf16_pair_hi(b[0], b[1]);
-    r.z = bf16_pair_hi(c[0], c[1]);
-    r.w = bf16_pair_hi(d[0], d[1]);
+    // FP8 E4M3FN -> bf16, two codes per instruction (exact)
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
   } else {
     const uint32_t e0 = d0 ^ 0x80808080u, e1 = d1 ^ 0x80808080u;
     // (float)((x >> 8k) & 0xFF) is one v_cvt_f32_ubyte{k}
@@ -179,31 +177,167 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo, floa
   used = fh + (float)lo;
 }
 
+// Flat row index (slot * H + h) of token t0 + t and whether it is live: in the
+// context and on a page whose block id is valid.  The block id comes from
+// the split's block-table slice in LDS (s_blk[page - p0]).
+__device__ __forceinline__ uint32_t tile_row(const DecodeArgs& a, const int32_t* s_blk, int p0, int t, int t0,
+                                             int tok_end, int h, bool& live) {
+  const int tt = t0 + t;
+  const int lbs = a.log2_bs;
+  const int pg = tt >> lbs;
+  const bool in = tt < tok_end;
+  const int bid = in ? s_blk[pg - p0] : 0;
+  live = in && bid >= 0 && bid < a.nb;
+  const uint32_t blk = live ? (uint32_t)bid : 0u;
+  return ((blk << lbs) + (uint32_t)(tt & ((1 << lbs) - 1))) * (uint32_t)a.H + (uint32_t)h;
+}
+
+// ---- asynchronous copies global -> LDS ----------------------------------
+// global_load_lds_dword{,x4}: lane l of the instruction writes its 4 (16)
+// bytes at LDS address m0 + 4 l (16 l).  The loop below issues every global
+// read of a tile this way, so nothing it waits on lives in registers; the
+// compiler does not track these transfers, so the loop waits for them with
+// explicit s_waitcnt vmcnt(N) (loads complete in issue order).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_addr), "v"(src) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(lds_addr), "v"(src) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Swizzles of the 16-byte chunks of a tile row in LDS: chunk (row, col)
+// sits in slot row * CH + (col ^ swz(row)), so the rows one read instruction
+// touches fall in distinct bank groups.  Values are read with the 8-bit
+// transpose read (rows T_j), keys with 16-byte reads (16 consecutive rows).
+template <int CH>
+__device__ __forceinline__ int vswz(int row) {
+  return ((row & 3) | (((row >> 4) & 1) << 2)) & (CH - 1);
+}
+template <int CH>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (CH >= 8) return row & 7;
+  else if constexpr (CH == 4) return (row >> 1) & 3;
+  else return (row >> 2) & 1;
+}
+
 template <int FK, int FV, int D>
-__global__ __launch_bounds__(MAX_WAVES * 64) void decode_split_kernel(DecodeArgs a) {
+struct Stage {
   using KS = KShape<FK, D>;
   using VS = VShape<FV, D>;
-  __shared__ int32_t s_blk[MAX_PPS];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[MAX_WAVES][TILE * VS::RBP];
-  __shared__ float s_sk[MAX_WAVES][TILE];
-  __shared__ float s_sv[MAX_WAVES][TILE * VS::NG];
+  static constexpr int KT = TILE * KS::RB;          // key tile bytes
+  static constexpr int VT = TILE * VS::RB;          // value tile bytes
+  static constexpr int NLK = KT / 1024;             // 16-byte key chunks per lane (>= 1)
+  static constexpr int NLV = VT / 1024;
+  static constexpr int NGD = VS::NG > 1 ? VS::NG / 2 : 1;  // value-scale dwords per token
+  static constexpr int KIVI_BYTES = FK == F_KIVI ? 2 * D * 2 : 0;  // page scale + zero (fp16)
+  // byte offsets inside a stage
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_V = KT;
+  static constexpr int OFF_S = KT + VT;              // dword per token: key scale; then value-scale dwords
+  static constexpr int OFF_M = OFF_S + 4 * TILE * (1 + NGD);
+  static constexpr int BYTES = OFF_M + KIVI_BYTES;
+  // DMA instructions per tile: keys, values, scales, KIVI page metadata
+  static constexpr int NDMA = NLK + NLV + NGD + (FK == F_KIVI ? 1 : 0);
+};
 
-  const int split = (int)blockIdx.x, b = (int)blockIdx.z;
-  const int nw = (int)(blockDim.x >> 6);
-  const int w = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
-  const int h = (int)blockIdx.y * nw + w;
+// Start the copy of one tile (keys, values, per-token scales; KIVI page
+// scale/zero) into LDS stage `st`.  Masked rows copy from the start of the
+// buffer; their contents are never used unmasked (see the consumers).
+template <int FK, int FV, int D>
+__device__ __forceinline__ uint64_t issue_tile(const DecodeArgs& a, const int32_t* s_blk, int p0, int t0, int tok_end,
+                                               int h, uint8_t* st) {
+  using S = Stage<FK, FV, D>;
+  using KS = KShape<FK, D>;
+  using VS = VShape<FV, D>;
+  constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
+  const int lane = (int)threadIdx.x;
+  const uint32_t base = lds_addr(st);
+#pragma unroll
+  for (int i = 0; i < S::NLK; ++i) {
+    const int p = 64 * i + lane;  // LDS slot of this lane
+    const int row = p / CHK;
+    const int col = (p % CHK) ^ kswz<CHK>(row);
+    bool live;
+    const uint32_t r = tile_row(a, s_blk, p0, row, t0, tok_end, h, live);
+    dma16(a.k_codes + (live ? (size_t)r * KS::RB + col * 16 : 0), base + S::OFF_K + 1024 * i);
+  }
+#pragma unroll
+  for (int i = 0; i < S::NLV; ++i) {
+    const int p = 64 * i + lane;
+    const int row = p / VS::CH;
+    const int col = (p % VS::CH) ^ vswz<VS::CH>(row);
+    bool live;
+    const uint32_t r = tile_row(a, s_blk, p0, row, t0, tok_end, h, live);
+    dma16(a.v_codes + (live ? (size_t)r * VS::RB + col * 16 : 0), base + S::OFF_V + 1024 * i);
+  }
+  // scale dwords (LDS dword index): [t] the dword holding token t's key
+  // scale, [32 + t] the first value-scale dword of token t, [32 + 32 k + t]
+  // its value-scale dword k >= 1 (INT4 groups)
+  bool live;
+  const uint32_t r = tile_row(a, s_blk, p0, lane & 31, t0, tok_end, h, live);
+  const uint64_t live_mask = __ballot(live);
+  {
+    const uint16_t* src;
+    if (lane < 32) src = FK == F_KIVI ? a.v_scales : a.k_scales + (live ? (r & ~1u) : 0);
+    else src = a.v_scales + (live ? ((size_t)r * VS::NG & ~(size_t)1) : 0);
+    dma4(src, base + S::OFF_S);
+  }
+#pragma unroll
+  for (int g = 1; g < S::NGD; ++g) {
+    if (lane < 32) dma4(a.v_scales + (live ? (size_t)r * VS::NG + 2 * g : 0), base + S::OFF_S + 128 + 128 * g);
+  }
+  if constexpr (FK == F_KIVI) {
+    // the tile is one page (block_size 32): its D scales and D zeros
+    constexpr int CH = D * 2 / 16;
+    bool ok;
+    const uint32_t r0 = tile_row(a, s_blk, p0, 0, t0, tok_end, h, ok);
+    const size_t mrow = ((size_t)(r0 / (32u * (uint32_t)a.H)) * a.H + h) * D;
+    if (lane < 2 * CH) {
+      const uint16_t* src = (lane < CH ? a.k_scales : a.k_zeros) + (ok ? mrow + 8 * (lane % CH) : 0);
+      dma16(src, base + S::OFF_M);
+    }
+  }
+  return live_mask;
+}
+
+template <int FK, int FV, int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  using KS = KShape<FK, D>;
+  using VS = VShape<FV, D>;
+  using ST = Stage<FK, FV, D>;
+  constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
+  __shared__ int32_t s_blk[MAX_PPS];
+  // three stages: tile i is computed while tiles i+1 and i+2 are in flight
+  __shared__ __attribute__((aligned(16))) uint8_t s_st[3][ST::BYTES];
+
+  // Work unit (sequence, split, KV head); the KV heads of one (sequence,
+  // split) are consecutive workgroups of one XCD (workgroups are dealt to the
+  // 8 XCDs round robin), so they share the L2 lines of the page scales.
+  const uint32_t wg = blockIdx.x;
+  const uint32_t kk = wg >> 3;
+  const int h = (int)(kk % (uint32_t)a.H);
+  const uint32_t unit = (kk / (uint32_t)a.H) * 8 + (wg & 7);
+  if (unit >= (uint32_t)(a.B * a.quant_splits)) return;
+  const int b = (int)(unit / (uint32_t)a.quant_splits), split = (int)(unit % (uint32_t)a.quant_splits);
+
+  const int lane = (int)threadIdx.x;
   const int j = lane >> 4, n = lane & 15;
-  const int bs = a.bs;
+  const int bs = 1 << a.log2_bs;
   // ctx_len is clamped to what the block-table row can address
   const int L = min(max(a.ctx_lens[b], 0), a.max_blocks * bs);
   const int Lq = FK == F_KIVI ? (L & ~31) : L;  // tokens held in quantized pages
-  const int npages = (Lq + bs - 1) / bs;
+  const int npages = (Lq + bs - 1) >> a.log2_bs;
   const int p0 = split * a.pages_per_split;
   const int p1 = min(npages, p0 + a.pages_per_split);
-  for (int i = (int)threadIdx.x; i < p1 - p0; i += (int)blockDim.x)
-    s_blk[i] = a.block_table[(size_t)b * a.max_blocks + p0 + i];
-  __syncthreads();
-  if (h >= a.H) return;  // no barrier below this point
+  for (int i = lane; i < p1 - p0; i += 64) s_blk[i] = a.block_table[(size_t)b * a.max_blocks + p0 + i];
 
   const int G = a.G;
   const int hq0 = h * G;
@@ -214,112 +348,115 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void decode_split_kernel(DecodeArgs
 
   // Query operand (B of S^T = K Q^T): lane (j, n) holds query head n's
   // channels of k-slots 8j..8j+7 in the key operand's channel order.
-  const uint16_t* qrow = a.q + ((size_t)b * a.Hq + hq0 + n) * D;
+  const uint16_t* qrow = a.q + ((size_t)b * a.Hq + hq0 + (n < G ? n : 0)) * D;
   h8 qop[KS::KB];
 #pragma unroll
   for (int kb = 0; kb < KS::KB; ++kb) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint16_t bits = n < G ? qrow[key_channel<FK, D>(j, kb, e)] : (uint16_t)0;
-      qop[kb][e] = __builtin_bit_cast(_Float16, bits);
+      const uint16_t bits = qrow[key_channel<FK, D>(j, kb, e)];
+      qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < G ? bits : 0));
     }
   }
+  // the half of each scale dword that holds this (token, head)'s scale:
+  // (row index) & 1, which is h & 1 for an even head count
+  const bool h_odd = (a.H & 1) != 0;
 
-  uint8_t* sv = s_v[w];
+  // Value transpose reads: lane (j, i) points at row T_j[i / 2] of the value
+  // tile, byte 8 (i % 2) of the chunk, where T_j[e] = 16 (e / 4) + 4 j + e % 4
+  // is the token of k-slot e of lane group j.
+  const int trow = 16 * ((n >> 1) >> 2) + 4 * j + ((n >> 1) & 3);
+  const int tbase = ST::OFF_V + trow * VS::RB + 8 * (n & 1);
+  const int tswz = vswz<VS::CH>(trow);
+
   const int tok_begin = p0 * bs, tok_end = min(Lq, p1 * bs);
-  for (int t0 = tok_begin; t0 < tok_end; t0 += TILE) {
-    // ---- keys of the tile: lane (j, n) reads a quarter row of tokens n, 16+n
-    uint32_t kw[2][KS::NW];
-    bool kvalid[2];
+  const int ntiles = tok_end > tok_begin ? (tok_end - tok_begin + TILE - 1) / TILE : 0;
+  __syncthreads();  // s_blk visible (one wave: orders the LDS writes before the reads below)
+  uint64_t live[3] = {0, 0, 0};
+  if (ntiles > 0) live[0] = issue_tile<FK, FV, D>(a, s_blk, p0, tok_begin, tok_end, h, s_st[0]);
+  if (ntiles > 1) live[1] = issue_tile<FK, FV, D>(a, s_blk, p0, tok_begin + TILE, tok_end, h, s_st[1]);
+
+  int it = 0;
+  // One tile; S is the LDS stage holding it.
+  auto step = [&](auto stage) -> bool {
+    constexpr int S = decltype(stage)::value;
+    if (it >= ntiles) return false;
+    const int t0 = tok_begin + it * TILE;
+    uint8_t* cur = s_st[S];
+    // ---- wait for this tile's copies (the next tile's may stay in flight)
+    if (it + 1 < ntiles) wait_vmcnt<ST::NDMA>();
+    else wait_vmcnt<0>();
+    const uint64_t live_mask = live[S];
+    // ---- start the tile after next -----------------------------------------
+    if (it + 2 < ntiles)
+      live[(S + 2) % 3] = issue_tile<FK, FV, D>(a, s_blk, p0, t0 + 2 * TILE, tok_end, h, s_st[(S + 2) % 3]);
+
+    // ---- masked rows: zero FP8 value codes (a garbage byte may be a NaN code)
+    //      and every masked token's scales
+    if (live_mask != ~0ull) {
+      if constexpr (FV == F_FP8) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tt = t0 + 16 * u + n;
-      const int pg = tt / bs;
-      int blk = -1;
-      if (tt < tok_end) blk = s_blk[pg - p0];
-      kvalid[u] = blk >= 0 && blk < a.nb;
-      const uint8_t* src = a.k_codes + (((size_t)(kvalid[u] ? blk : 0) * bs + (tt - pg * bs)) * a.H + h) * KS::RB +
-                           j * KS::LB;
-#pragma unroll
-      for (int i = 0; i < KS::NW; i += 4) {
-        if constexpr (KS::NW >= 4) {
-          u4 v = kvalid[u] ? *reinterpret_cast<const u4*>(src + 4 * i) : u4{0u, 0u, 0u, 0u};
-          kw[u][i] = v.x; kw[u][i + 1] = v.y; kw[u][i + 2] = v.z; kw[u][i + 3] = v.w;
+        for (int i = 0; i < ST::NLV; ++i) {
+          const int p = 64 * i + lane;
+          if (!((live_mask >> (p / VS::CH)) & 1)) *reinterpret_cast<u4*>(cur + ST::OFF_V + 16 * p) = u4{0u, 0u, 0u, 0u};
         }
       }
-      if constexpr (KS::NW == 2) {
-        u2 v = kvalid[u] ? *reinterpret_cast<const u2*>(src) : u2{0u, 0u};
+      if (!((live_mask >> (lane & 31)) & 1)) {
+        reinterpret_cast<uint32_t*>(cur + ST::OFF_S)[lane] = 0u;
+#pragma unroll
+        for (int g = 1; g < ST::NGD; ++g)
+          if (lane < 32) reinterpret_cast<uint32_t*>(cur + ST::OFF_S + 128 + 128 * g)[lane] = 0u;
+      }
+    }
+
+    // ---- keys: lane (j, n) reads its quarter rows of tokens n, 16 + n --------
+    uint32_t kw[2][KS::NW];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = 16 * u + n;
+      if constexpr (KS::LB >= 16) {
+#pragma unroll
+        for (int q = 0; q < KS::LB / 16; ++q) {
+          const int col = (j * KS::LB / 16 + q) ^ kswz<CHK>(row);
+          const u4 v = *reinterpret_cast<const u4*>(cur + ST::OFF_K + (row * CHK + col) * 16);
+          kw[u][4 * q] = v.x; kw[u][4 * q + 1] = v.y; kw[u][4 * q + 2] = v.z; kw[u][4 * q + 3] = v.w;
+        }
+      } else {  // 8 bytes per lane (KIVI, head_dim 64)
+        const int col = ((j * KS::LB) / 16) ^ kswz<CHK>(row);
+        const u2 v = *reinterpret_cast<const u2*>(cur + ST::OFF_K + (row * CHK + col) * 16 + (j * KS::LB) % 16);
         kw[u][0] = v.x; kw[u][1] = v.y;
       }
     }
-    // ---- values of the tile -> LDS (zeros for masked rows) ---------------
-#pragma unroll
-    for (int i = 0; i < VS::NL; ++i) {
-      const int c = lane + 64 * i;
-      const int r = c / VS::CH, col = c % VS::CH;
-      const int tt = t0 + r;
-      const int pg = tt / bs;
-      int blk = -1;
-      if (tt < tok_end) blk = s_blk[pg - p0];
-      u4 v = {0u, 0u, 0u, 0u};
-      if (blk >= 0 && blk < a.nb)
-        v = *reinterpret_cast<const u4*>(a.v_codes + (((size_t)blk * bs + (tt - pg * bs)) * a.H + h) * VS::RB +
-                                         col * 16);
-      *reinterpret_cast<u4*>(sv + r * VS::RBP + col * 16) = v;
-    }
-    // ---- per-token scales -> LDS (0 for masked rows); live-token mask ----
-    uint64_t live_mask;
-    {
-      const int r = lane & 31;
-      const int tt = t0 + r;
-      const int pg = tt / bs;
-      int blk = -1;
-      if (tt < tok_end) blk = s_blk[pg - p0];
-      const bool ok = blk >= 0 && blk < a.nb;
-      live_mask = __ballot(ok);  // bit r: token t0 + r is in the context and its block id is valid
-      const size_t row = ((size_t)(ok ? blk : 0) * bs + (tt - pg * bs)) * a.H + h;
-      if (lane < 32) {
-        if constexpr (FK != F_KIVI) s_sk[w][r] = ok ? h2f(a.k_scales[row]) : 0.f;
-      } else {
-#pragma unroll
-        for (int g = 0; g < VS::NG; ++g) s_sv[w][r * VS::NG + g] = ok ? h2f(a.v_scales[row * VS::NG + g]) : 0.f;
-      }
-    }
 
-    // ---- KIVI: per-page query operand q * s (fp16 hi + lo) and q . z ------
+    // ---- KIVI: this page's query operand q * s (fp16 hi + lo) and q . z ----
     h8 qhi[KS::KB], qlo[KS::KB];
     float qz = 0.f;
     if constexpr (FK == F_KIVI) {
-      const int blk = s_blk[t0 / bs - p0];  // one page per tile (bs == 32)
-      const bool ok = blk >= 0 && blk < a.nb;
-      const size_t mrow = ((size_t)(ok ? blk : 0) * a.H + h) * D;
 #pragma unroll
       for (int kb = 0; kb < KS::KB; ++kb) {
-        // scales and zeros of the k-block's 8 channels: one 16-byte load each
-        const size_t cb = mrow + j * (D / 4) + 8 * kb;
-        const u4 sw = ok ? *reinterpret_cast<const u4*>(a.k_scales + cb) : u4{0u, 0u, 0u, 0u};
-        const u4 zw = ok ? *reinterpret_cast<const u4*>(a.k_zeros + cb) : u4{0u, 0u, 0u, 0u};
+        const int cb = j * (D / 4) + 8 * kb;
+        const u4 sw = *reinterpret_cast<const u4*>(cur + ST::OFF_M + 2 * cb);
+        const u4 zw = *reinterpret_cast<const u4*>(cur + ST::OFF_M + 2 * D + 2 * cb);
         float s8[8], z8[8];
         unpack8(uint4{sw.x, sw.y, sw.z, sw.w}, s8);
         unpack8(uint4{zw.x, zw.y, zw.z, zw.w}, z8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int ch = key_channel<FK, D>(j, kb, e) - (j * (D / 4) + 8 * kb);
+          const int ch = key_channel<FK, D>(j, kb, e) - cb;
           const float qv = (float)qop[kb][e];
-          const float s = s8[ch];
-          const float z = z8[ch];
-          const float qs = qv * s;
+          const float qs = qv * s8[ch];
           const _Float16 hi = (_Float16)qs;
           qhi[kb][e] = hi;
           qlo[kb][e] = (_Float16)(qs - (float)hi);
-          qz = __builtin_fmaf(qv, z, qz);
+          qz = __builtin_fmaf(qv, z8[ch], qz);
         }
       }
       qz += __shfl_xor(qz, 16);
       qz += __shfl_xor(qz, 32);
+      qz *= a.qscale;
     }
 
-    // ---- scores S^T[t][g] on the matrix cores ----------------------------
+    // ---- scores S^T[t][g] on the matrix cores ------------------------------
     f4 sc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -335,6 +472,7 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void decode_split_kernel(DecodeArgs
         }
       }
     }
+    const uint32_t* sdw = reinterpret_cast<const uint32_t*>(cur + ST::OFF_S);
     // lane (j, n): sc[u][r] = raw score of token 16u + 4j + r, query head n.
     float s[8];
     float tmax = -INFINITY;
@@ -343,12 +481,16 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void decode_split_kernel(DecodeArgs
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tr = 16 * u + 4 * j + r;
-        const bool live = (live_mask >> tr) & 1;
         float v;
-        if constexpr (FK == F_KIVI) v = (sc[u][r] + qz) * a.qscale;
-        else v = sc[u][r] * s_sk[w][tr] * a.qscale;
+        if constexpr (FK == F_KIVI) {
+          v = __builtin_fmaf(sc[u][r], a.qscale, qz);
+        } else {
+          const uint32_t d = sdw[tr];
+          const bool hi_half = h_odd ? ((tr + h) & 1) : (h & 1);
+          v = sc[u][r] * (h2f(hi_half ? d >> 16 : d & 0xFFFFu) * a.qscale);
+        }
         // a masked row's key codes may be anything: select, don't multiply
-        v = live ? v : -INFINITY;
+        v = ((live_mask >> tr) & 1) ? v : -INFINITY;
         s[4 * u + r] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -357,57 +499,68 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void decode_split_kernel(DecodeArgs
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);  // 0 on the first live tile
-    m_run = m_new;
+    // Rescale only when some head's running max moved (rare after the first
+    // tiles): alpha = 2^(m_old - m_new).
+    if (__ballot(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 on the first live tile
+      l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * j + r);
+#pragma unroll
+        for (int m = 0; m < VS::NPV; ++m) acc[m][r] *= ar;
+      }
+      m_run = m_new;
+    }
     float p[8];
-    float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(s[e] - m_use);
-      psum += p[e];
-    }
-    l_run = l_run * alpha + psum;
-    // rescale the accumulator: lane (j, n) holds query heads 4j + r
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ar = __shfl(alpha, 4 * j + r);
-#pragma unroll
-      for (int m = 0; m < VS::NPV; ++m) acc[m][r] *= ar;
+      p[e] = __builtin_amdgcn_exp2f(s[e] - m_use);  // exp2(-inf) = 0 for masked rows
+      l_run += p[e];
     }
 
-    // ---- P V on the matrix cores -----------------------------------------
-    // Token of k-slot e for lane group j: T_j[e] = 16 (e / 4) + 4 j + e % 4.
-    // tr8 addresses: lane (j, i) points at row T_j[i / 2], byte offset
-    // c0 + 8 (i % 2); lane (j, n) then receives byte c0 + n of the 8 rows.
-    const int trow = 16 * ((n >> 1) >> 2) + 4 * j + ((n >> 1) & 3);
-    const lds_u8* vbase = (const lds_u8*)(sv + trow * VS::RBP + 8 * (n & 1));
+    // value scale of token tr (group g)
+    auto vscale = [&](int tr, int g) -> float {
+      if constexpr (VS::NG == 1) {
+        const uint32_t d = sdw[32 + tr];
+        const bool hi_half = h_odd ? ((tr + h) & 1) : (h & 1);
+        return h2f(hi_half ? d >> 16 : d & 0xFFFFu);
+      } else {
+        // dword g/2 of the token's scales: dword 0 at [32 + t], dword k >= 1 at [32 + 32 k + t]
+        const uint32_t d = sdw[32 + 32 * (g >> 1) + tr];
+        return h2f((g & 1) ? d >> 16 : d & 0xFFFFu);
+      }
+    };
+
+    // ---- P V on the matrix cores -------------------------------------------
     if constexpr (FV == F_INT4) {
 #pragma unroll
       for (int grp = 0; grp < VS::NG; ++grp) {
-        __bf16 ah[8], al[8];
+        b8 A_hi, A_lo;
         float cs = 0.f;
         constexpr int ord[8] = {0, 2, 1, 3, 4, 6, 5, 7};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int slot = ord[e];
           const int tr = 16 * (slot >> 2) + 4 * j + (slot & 3);
+          __bf16 hi, lo;
           float used;
-          split_bf16(p[slot] * s_sv[w][tr * VS::NG + grp], ah[e], al[e], used);
+          split_bf16(p[slot] * vscale(tr, grp), hi, lo, used);
+          A_hi[e] = hi;
+          A_lo[e] = lo;
           cs += used;
         }
-        b8 A_hi, A_lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { A_hi[e] = ah[e]; A_lo[e] = al[e]; }
-        const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vbase + 16 * grp));
+        const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(cur + tbase + ((grp ^ tswz) << 4)));
         b8 ve, vo;
         value_operand_int4(raw, ve, vo);
-        // corr[g] = 136 * sum of the operand values of query head g
         cs += __shfl_xor(cs, 16);
         cs += __shfl_xor(cs, 32);
         acc[2 * grp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, ve, acc[2 * grp], 0, 0, 0);
         acc[2 * grp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, ve, acc[2 * grp], 0, 0, 0);
         acc[2 * grp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, vo, acc[2 * grp + 1], 0, 0, 0);
         acc[2 * grp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, vo, acc[2 * grp + 1], 0, 0, 0);
+        // remove the +136 bias of the value operand: 136 * sum of the operand
+        // values of query head 4j + r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float corr = 136.f * __shfl(cs, 4 * j + r);
@@ -423,14 +576,14 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void decode_split_kernel(DecodeArgs
         const int tr = 16 * (e >> 2) + 4 * j + (e & 3);
         __bf16 hi, lo;
         float used;
-        split_bf16(p[e] * s_sv[w][tr], hi, lo, used);
+        split_bf16(p[e] * vscale(tr, 0), hi, lo, used);
         A_hi[e] = hi;
         A_lo[e] = lo;
         cs += used;
       }
 #pragma unroll
       for (int m = 0; m < VS::NPV; ++m) {
-        const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vbase + 16 * m));
+        const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(cur + tbase + ((m ^ tswz) << 4)));
         const b8 vop = value_operand_8bit<FV>(raw);
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, vop, acc[m], 0, 0, 0);
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, vop, acc[m], 0, 0, 0);
@@ -446,9 +599,16 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void decode_split_kernel(DecodeArgs
         }
       }
     }
+    ++it;
+    return true;
+  };
+  for (;;) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
+    if (!step(std::integral_constant<int, 2>{})) break;
   }
 
-  // ---- write this split's softmax state ----------------------------------
+  // ---- write this split's softmax state ------------------------------------
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   const size_t stride = (size_t)D + 2;
@@ -522,41 +682,68 @@ __global__ __launch_bounds__(64) void kivi_tail_kernel(DecodeArgs a) {
 
 // Merge the splits of one (sequence, query head): M = max m_s,
 // out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), rounded to fp16.
+// Four waves share the splits; lanes own channels.
+constexpr int MERGE_WAVES = 4;
+
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
-  const int bh = (int)blockIdx.x, lane = (int)threadIdx.x;
+__global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   constexpr int CPL = D / 64;
+  __shared__ float s_m[MERGE_WAVES];
+  __shared__ float s_acc[MERGE_WAVES][D + 1];
+  const int bh = (int)blockIdx.x, tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int S = a.num_splits;
   const size_t stride = (size_t)D + 2;
-  const float* base = a.part + (size_t)bh * a.num_splits * stride;
+  const float* base = a.part + (size_t)bh * S * stride;
   float M = -INFINITY;
-  for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, base[s * stride]);
+  for (int s = tid; s < S; s += MERGE_WAVES * 64) M = fmaxf(M, base[s * stride]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) s_m[w] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MERGE_WAVES; ++i) M = fmaxf(M, s_m[i]);
   float accv[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) accv[c] = 0.f;
   float l = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < a.num_splits; ++s) {
-      const float ms = base[s * stride];
-      if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - M);
-      l = __builtin_fmaf(base[s * stride + 1], wgt, l);
+#pragma unroll 4
+    for (int s = w; s < S; s += MERGE_WAVES) {
+      const float* p = base + s * stride;
+      const float ms = p[0];
+      const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      l = __builtin_fmaf(p[1], wgt, l);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(base[s * stride + 2 + lane * CPL + c], wgt, accv[c]);
+      for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(p[2 + lane * CPL + c], wgt, accv[c]);
     }
   }
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) s_acc[w][lane * CPL + c] = accv[c];
+  if (lane == 0) s_acc[w][D] = l;
+  __syncthreads();
+  if (w != 0) return;
+  float lt = 0.f;
+#pragma unroll
+  for (int i = 0; i < MERGE_WAVES; ++i) lt += s_acc[i][D];
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   uint16_t* o = a.out + (size_t)bh * D;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) o[lane * CPL + c] = (uint16_t)f2h_bits(accv[c] * inv);
+  for (int c = 0; c < CPL; ++c) {
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < MERGE_WAVES; ++i) v += s_acc[i][lane * CPL + c];
+    o[lane * CPL + c] = (uint16_t)f2h_bits(v * inv);
+  }
 }
 
 namespace {
 
 template <int FK, int FV, int D>
-hipError_t launch3(const DecodeArgs& a, int nw, hipStream_t st) {
-  const int quant_splits = a.num_splits - (FK == F_KIVI ? 1 : 0);
-  const dim3 grid((unsigned)quant_splits, (unsigned)((a.H + nw - 1) / nw), (unsigned)a.B);
-  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D>), grid, dim3(nw * 64), 0, st, a);
+hipError_t launch3(const DecodeArgs& a, hipStream_t st) {
+  // one wave per (sequence, split, KV head); see decode_split_kernel for the order
+  const uint32_t units = (uint32_t)(a.B * a.quant_splits);
+  const uint32_t wgs = ((units + 7) / 8) * 8 * (uint32_t)a.H;
+  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D>), dim3(wgs), dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (FK == F_KIVI) {
@@ -564,26 +751,26 @@ hipError_t launch3(const DecodeArgs& a, int nw, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(MERGE_WAVES * 64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int FK, int FV>
-hipError_t by_dim(int D, const DecodeArgs& a, int nw, hipStream_t s) {
+hipError_t by_dim(int D, const DecodeArgs& a, hipStream_t s) {
   switch (D) {
-    case 64: return launch3<FK, FV, 64>(a, nw, s);
-    case 128: return launch3<FK, FV, 128>(a, nw, s);
-    case 256: return launch3<FK, FV, 256>(a, nw, s);
+    case 64: return launch3<FK, FV, 64>(a, s);
+    case 128: return launch3<FK, FV, 128>(a, s);
+    case 256: return launch3<FK, FV, 256>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int FK>
-hipError_t by_v(int fv, int D, const DecodeArgs& a, int nw, hipStream_t s) {
+hipError_t by_v(int fv, int D, const DecodeArgs& a, hipStream_t s) {
   switch (fv) {
-    case F_INT8: return by_dim<FK, F_INT8>(D, a, nw, s);
-    case F_FP8: return by_dim<FK, F_FP8>(D, a, nw, s);
-    case F_INT4: return by_dim<FK, F_INT4>(D, a, nw, s);
+    case F_INT8: return by_dim<FK, F_INT8>(D, a, s);
+    case F_FP8: return by_dim<FK, F_FP8>(D, a, s);
+    case F_INT4: return by_dim<FK, F_INT4>(D, a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -597,12 +784,11 @@ int32_t choose_pages_per_split(const kvq_cache& c, int32_t batch, int32_t max_bl
   if (pps <= 0) {
     // Enough workgroups to fill 256 CUs several times over, each holding
     // a few thousand tokens per KV head.
-    const int32_t head_groups = (c.n_kv_heads + MAX_WAVES - 1) / MAX_WAVES;
-    const int64_t target_wgs = 2048;
-    int64_t per_seq = (target_wgs + (int64_t)batch * head_groups - 1) / ((int64_t)batch * head_groups);
+    const int64_t target_units = 1024;  // (sequence, split) pairs; each runs n_kv_heads waves
+    int64_t per_seq = (target_units + batch - 1) / batch;
     if (per_seq < 1) per_seq = 1;
     pps = (int32_t)((max_blocks + per_seq - 1) / per_seq);
-    const int32_t min_pps = (256 + c.block_size - 1) / c.block_size;  // >= 256 tokens per split
+    const int32_t min_pps = (512 + c.block_size - 1) / c.block_size;  // >= 512 tokens per split
     if (pps < min_pps) pps = min_pps;
   }
   pps = ((pps + unit - 1) / unit) * unit;
@@ -611,12 +797,10 @@ int32_t choose_pages_per_split(const kvq_cache& c, int32_t batch, int32_t max_bl
 }
 
 hipError_t launch_decode(const kvq_cache& c, const DecodeArgs& a, hipStream_t s) {
-  int nw = 1;
-  while (nw < c.n_kv_heads && nw < MAX_WAVES) nw <<= 1;
   switch (c.k_dtype) {
-    case F_INT8: return by_v<F_INT8>(c.v_dtype, c.head_dim, a, nw, s);
-    case F_FP8: return by_v<F_FP8>(c.v_dtype, c.head_dim, a, nw, s);
-    case F_KIVI: return by_v<F_KIVI>(c.v_dtype, c.head_dim, a, nw, s);
+    case F_INT8: return by_v<F_INT8>(c.v_dtype, c.head_dim, a, s);
+    case F_FP8: return by_v<F_FP8>(c.v_dtype, c.head_dim, a, s);
+    case F_KIVI: return by_v<F_KIVI>(c.v_dtype, c.head_dim, a, s);
   }
   return hipErrorInvalidValue;
 }

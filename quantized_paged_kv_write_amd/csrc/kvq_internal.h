@@ -53,7 +53,7 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* ctx_lens;
   int32_t max_blocks;
-  int32_t B, Hq, H, G, bs, nb;
+  int32_t B, Hq, H, G, bs, log2_bs, nb;
   float qscale;  // sm_scale * log2(e)
   const uint8_t* k_codes;
   const uint16_t* k_scales;
@@ -64,7 +64,8 @@ struct DecodeArgs {
   const uint16_t* v_tail;
   int32_t max_seqs;
   int32_t pages_per_split;
-  int32_t num_splits;
+  int32_t num_splits;   // partial states per (sequence, query head), incl. the KIVI tail split
+  int32_t quant_splits;  // splits over quantized pages
   float* part;  // (B, Hq, num_splits, D + 2) fp32: m, l, acc[D]
   uint16_t* out;  // fp16 (B, Hq, D)
 };
