@@ -74,8 +74,9 @@ __device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(ui
 // INT8: (1024 + (c + 128)) - 1152 = c, exactly, in fp16.
 __device__ __forceinline__ void int8_to_h4(uint32_t d, uint32_t& lo, uint32_t& hi) {
   d ^= 0x80808080u;
-  const uint32_t a = (d & 0xFFu) | ((d & 0xFF00u) << 8) | 0x64006400u;
-  const uint32_t b = ((d >> 16) & 0xFFu) | ((d >> 8) & 0xFF0000u) | 0x64006400u;
+  // v_perm_b32: bytes [c0, 0x64, c1, 0x64] and [c2, 0x64, c3, 0x64]
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, d, 0x04010400u);
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, d, 0x04030402u);
   const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
   lo = h2_bits(as_h2(a) - bias);
   hi = h2_bits(as_h2(b) - bias);
@@ -169,12 +170,19 @@ __device__ __forceinline__ void value_operand_int4(i2 t, b8& even, b8& odd) {
   odd = __builtin_bit_cast(b8, od);
 }
 
-// x = hi + lo with hi = bf16_rne(x), lo = bf16_rne(x - hi).
-__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo, float& used) {
-  hi = (__bf16)x;
-  const float fh = (float)hi;
-  lo = (__bf16)(x - fh);
-  used = fh + (float)lo;
+// x = hi + lo with hi = bf16_rne(x), lo = bf16_rne(x - hi), two values at a
+// time (v_cvt_pk_bf16_f32); `used` is what the operands hold, hi + lo.
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_bf16x2(f2 x, uint32_t& hi, uint32_t& lo, f2& used) {
+  const bf2 h = __builtin_convertvector(x, bf2);
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  const f2 fh = {__builtin_bit_cast(float, hb << 16), __builtin_bit_cast(float, hb & 0xFFFF0000u)};
+  const bf2 l = __builtin_convertvector(x - fh, bf2);
+  const uint32_t lb = __builtin_bit_cast(uint32_t, l);
+  hi = hb;
+  lo = lb;
+  used = fh + f2{__builtin_bit_cast(float, lb << 16), __builtin_bit_cast(float, lb & 0xFFFF0000u)};
 }
 
 // Flat row index (slot * H + h) of token t0 + t and whether it is live: in the
@@ -241,16 +249,17 @@ struct Stage {
   // byte offsets inside a stage
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = KT;
-  static constexpr int OFF_S = KT + VT;              // dword per token: key scale; then value-scale dwords
+  static constexpr int OFF_S = KT + VT;              // raw scale dwords (see issue_tile)
   static constexpr int OFF_M = OFF_S + 4 * TILE * (1 + NGD);
   static constexpr int BYTES = OFF_M + KIVI_BYTES;
   // DMA instructions per tile: keys, values, scales, KIVI page metadata
   static constexpr int NDMA = NLK + NLV + NGD + (FK == F_KIVI ? 1 : 0);
 };
 
-// Start the copy of one tile (keys, values, per-token scales; KIVI page
-// scale/zero) into LDS stage `st`.  Masked rows copy from the start of the
-// buffer; their contents are never used unmasked (see the consumers).
+// Start the copy of one tile (keys, values, per-token scale dwords; KIVI
+// page scale/zero) into LDS stage `st`; returns the live-token mask (bit t
+// and t + 32: token t0 + t is in the context on a valid page).  Masked rows
+// copy from the start of the buffer; those bytes are never used unmasked.
 template <int FK, int FV, int D>
 __device__ __forceinline__ uint64_t issue_tile(const DecodeArgs& a, const int32_t* s_blk, int p0, int t0, int tok_end,
                                                int h, uint8_t* st) {
@@ -260,45 +269,45 @@ __device__ __forceinline__ uint64_t issue_tile(const DecodeArgs& a, const int32_
   constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
   const int lane = (int)threadIdx.x;
   const uint32_t base = lds_addr(st);
+  // row index of token `lane & 31`, or ~0 when masked; shared with shuffles
+  bool live;
+  const uint32_t r_own = tile_row(a, s_blk, p0, lane & 31, t0, tok_end, h, live);
+  const uint64_t live_mask = __ballot(live);
+  const uint32_t rl = live ? r_own : ~0u;
 #pragma unroll
   for (int i = 0; i < S::NLK; ++i) {
     const int p = 64 * i + lane;  // LDS slot of this lane
     const int row = p / CHK;
     const int col = (p % CHK) ^ kswz<CHK>(row);
-    bool live;
-    const uint32_t r = tile_row(a, s_blk, p0, row, t0, tok_end, h, live);
-    dma16(a.k_codes + (live ? (size_t)r * KS::RB + col * 16 : 0), base + S::OFF_K + 1024 * i);
+    const uint32_t r = (uint32_t)__shfl((int)rl, row);
+    dma16(a.k_codes + (r != ~0u ? (size_t)r * KS::RB + col * 16 : 0), base + S::OFF_K + 1024 * i);
   }
 #pragma unroll
   for (int i = 0; i < S::NLV; ++i) {
     const int p = 64 * i + lane;
     const int row = p / VS::CH;
     const int col = (p % VS::CH) ^ vswz<VS::CH>(row);
-    bool live;
-    const uint32_t r = tile_row(a, s_blk, p0, row, t0, tok_end, h, live);
-    dma16(a.v_codes + (live ? (size_t)r * VS::RB + col * 16 : 0), base + S::OFF_V + 1024 * i);
+    const uint32_t r = (uint32_t)__shfl((int)rl, row);
+    dma16(a.v_codes + (r != ~0u ? (size_t)r * VS::RB + col * 16 : 0), base + S::OFF_V + 1024 * i);
   }
   // scale dwords (LDS dword index): [t] the dword holding token t's key
   // scale, [32 + t] the first value-scale dword of token t, [32 + 32 k + t]
   // its value-scale dword k >= 1 (INT4 groups)
-  bool live;
-  const uint32_t r = tile_row(a, s_blk, p0, lane & 31, t0, tok_end, h, live);
-  const uint64_t live_mask = __ballot(live);
   {
     const uint16_t* src;
-    if (lane < 32) src = FK == F_KIVI ? a.v_scales : a.k_scales + (live ? (r & ~1u) : 0);
-    else src = a.v_scales + (live ? ((size_t)r * VS::NG & ~(size_t)1) : 0);
+    if (lane < 32) src = FK == F_KIVI ? a.v_scales : a.k_scales + (live ? (r_own & ~1u) : 0);
+    else src = a.v_scales + (live ? ((size_t)r_own * VS::NG & ~(size_t)1) : 0);
     dma4(src, base + S::OFF_S);
   }
 #pragma unroll
   for (int g = 1; g < S::NGD; ++g) {
-    if (lane < 32) dma4(a.v_scales + (live ? (size_t)r * VS::NG + 2 * g : 0), base + S::OFF_S + 128 + 128 * g);
+    if (lane < 32) dma4(a.v_scales + (live ? (size_t)r_own * VS::NG + 2 * g : 0), base + S::OFF_S + 128 + 128 * g);
   }
   if constexpr (FK == F_KIVI) {
     // the tile is one page (block_size 32): its D scales and D zeros
     constexpr int CH = D * 2 / 16;
-    bool ok;
-    const uint32_t r0 = tile_row(a, s_blk, p0, 0, t0, tok_end, h, ok);
+    const uint32_t r0 = (uint32_t)__shfl((int)rl, 0);
+    const bool ok = r0 != ~0u;
     const size_t mrow = ((size_t)(r0 / (32u * (uint32_t)a.H)) * a.H + h) * D;
     if (lane < 2 * CH) {
       const uint16_t* src = (lane < CH ? a.k_scales : a.k_zeros) + (ok ? mrow + 8 * (lane % CH) : 0);
@@ -314,9 +323,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using VS = VShape<FV, D>;
   using ST = Stage<FK, FV, D>;
   constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
+  constexpr int NCS = FV == F_INT4 ? VS::NG : 1;  // bias-correction sums kept per value group
   __shared__ int32_t s_blk[MAX_PPS];
   // three stages: tile i is computed while tiles i+1 and i+2 are in flight
   __shared__ __attribute__((aligned(16))) uint8_t s_st[3][ST::BYTES];
+  // this tile's scales as fp32: key scale x sm_scale x log2 e, value scales
+  __shared__ __attribute__((aligned(16))) float s_fk[TILE];
+  __shared__ __attribute__((aligned(16))) float s_fv[TILE * VS::NG];
 
   // Work unit (sequence, split, KV head); the KV heads of one (sequence,
   // split) are consecutive workgroups of one XCD (workgroups are dealt to the
@@ -345,6 +358,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int m = 0; m < VS::NPV; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  float cs_run[NCS];  // sum of the probability operands (hi + lo) of query head n, per value group
+#pragma unroll
+  for (int g = 0; g < NCS; ++g) cs_run[g] = 0.f;
 
   // Query operand (B of S^T = K Q^T): lane (j, n) holds query head n's
   // channels of k-slots 8j..8j+7 in the key operand's channel order.
@@ -358,8 +374,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < G ? bits : 0));
     }
   }
-  // the half of each scale dword that holds this (token, head)'s scale:
-  // (row index) & 1, which is h & 1 for an even head count
+  // the half of a scale dword holding this (token, head)'s scale is
+  // (row index) & 1: h & 1 for an even head count, (t + h) & 1 otherwise
   const bool h_odd = (a.H & 1) != 0;
 
   // Value transpose reads: lane (j, i) points at row T_j[i / 2] of the value
@@ -371,7 +387,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   const int tok_begin = p0 * bs, tok_end = min(Lq, p1 * bs);
   const int ntiles = tok_end > tok_begin ? (tok_end - tok_begin + TILE - 1) / TILE : 0;
-  __syncthreads();  // s_blk visible (one wave: orders the LDS writes before the reads below)
+  __syncthreads();  // s_blk written before it is read below
   uint64_t live[3] = {0, 0, 0};
   if (ntiles > 0) live[0] = issue_tile<FK, FV, D>(a, s_blk, p0, tok_begin, tok_end, h, s_st[0]);
   if (ntiles > 1) live[1] = issue_tile<FK, FV, D>(a, s_blk, p0, tok_begin + TILE, tok_end, h, s_st[1]);
@@ -391,21 +407,44 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if (it + 2 < ntiles)
       live[(S + 2) % 3] = issue_tile<FK, FV, D>(a, s_blk, p0, t0 + 2 * TILE, tok_end, h, s_st[(S + 2) % 3]);
 
-    // ---- masked rows: zero FP8 value codes (a garbage byte may be a NaN code)
-    //      and every masked token's scales
-    if (live_mask != ~0ull) {
-      if constexpr (FV == F_FP8) {
-#pragma unroll
-        for (int i = 0; i < ST::NLV; ++i) {
-          const int p = 64 * i + lane;
-          if (!((live_mask >> (p / VS::CH)) & 1)) *reinterpret_cast<u4*>(cur + ST::OFF_V + 16 * p) = u4{0u, 0u, 0u, 0u};
+    // ---- scales -> fp32 (0 for masked tokens); FP8 codes of masked value
+    //      rows zeroed (a garbage byte may be a NaN code)
+    {
+      const uint32_t* sdw = reinterpret_cast<const uint32_t*>(cur + ST::OFF_S);
+      const int t = lane & 31;
+      const bool lv = (live_mask >> t) & 1;
+      const bool hi_half = h_odd ? ((t + h) & 1) : (h & 1);
+      if (lane < 32) {
+        if constexpr (FK != F_KIVI) {
+          const uint32_t d = sdw[t];
+          s_fk[t] = lv ? h2f(hi_half ? d >> 16 : d & 0xFFFFu) * a.qscale : 0.f;
         }
       }
-      if (!((live_mask >> (lane & 31)) & 1)) {
-        reinterpret_cast<uint32_t*>(cur + ST::OFF_S)[lane] = 0u;
+      if constexpr (VS::NG == 1) {
+        if (lane >= 32) {
+          const uint32_t d = sdw[32 + t];
+          s_fv[t] = lv ? h2f(hi_half ? d >> 16 : d & 0xFFFFu) : 0.f;
+        }
+      } else {
+        // value scales of (token t, group g): dword g/2 of the token, half g&1
+        // lanes 0..31 take the even dwords of token t, lanes 32..63 the odd ones
 #pragma unroll
-        for (int g = 1; g < ST::NGD; ++g)
-          if (lane < 32) reinterpret_cast<uint32_t*>(cur + ST::OFF_S + 128 + 128 * g)[lane] = 0u;
+        for (int gd = 0; gd < VS::NG / 2; ++gd) {
+          if ((lane >> 5) == (gd & 1)) {
+            const uint32_t d = sdw[32 + 32 * gd + t];
+            s_fv[t * VS::NG + 2 * gd] = lv ? h2f(d & 0xFFFFu) : 0.f;
+            s_fv[t * VS::NG + 2 * gd + 1] = lv ? h2f(d >> 16) : 0.f;
+          }
+        }
+      }
+      if constexpr (FV == F_FP8) {
+        if (live_mask != ~0ull) {
+#pragma unroll
+          for (int i = 0; i < ST::NLV; ++i) {
+            const int p = 64 * i + lane;
+            if (!((live_mask >> (p / VS::CH)) & 1)) *reinterpret_cast<u4*>(cur + ST::OFF_V + 16 * p) = u4{0u, 0u, 0u, 0u};
+          }
+        }
       }
     }
 
@@ -472,23 +511,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         }
       }
     }
-    const uint32_t* sdw = reinterpret_cast<const uint32_t*>(cur + ST::OFF_S);
     // lane (j, n): sc[u][r] = raw score of token 16u + 4j + r, query head n.
     float s[8];
     float tmax = -INFINITY;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      f4 ks4 = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (FK != F_KIVI) ks4 = *reinterpret_cast<const f4*>(&s_fk[16 * u + 4 * j]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tr = 16 * u + 4 * j + r;
         float v;
-        if constexpr (FK == F_KIVI) {
-          v = __builtin_fmaf(sc[u][r], a.qscale, qz);
-        } else {
-          const uint32_t d = sdw[tr];
-          const bool hi_half = h_odd ? ((tr + h) & 1) : (h & 1);
-          v = sc[u][r] * (h2f(hi_half ? d >> 16 : d & 0xFFFFu) * a.qscale);
-        }
+        if constexpr (FK == F_KIVI) v = __builtin_fmaf(sc[u][r], a.qscale, qz);
+        else v = sc[u][r] * ks4[r];
         // a masked row's key codes may be anything: select, don't multiply
         v = ((live_mask >> tr) & 1) ? v : -INFINITY;
         s[4 * u + r] = v;
@@ -505,6 +540,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 on the first live tile
       l_run *= alpha;
 #pragma unroll
+      for (int g = 0; g < NCS; ++g) cs_run[g] *= alpha;
+#pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float ar = __shfl(alpha, 4 * j + r);
 #pragma unroll
@@ -519,84 +556,55 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       l_run += p[e];
     }
 
-    // value scale of token tr (group g)
-    auto vscale = [&](int tr, int g) -> float {
-      if constexpr (VS::NG == 1) {
-        const uint32_t d = sdw[32 + tr];
-        const bool hi_half = h_odd ? ((tr + h) & 1) : (h & 1);
-        return h2f(hi_half ? d >> 16 : d & 0xFFFFu);
-      } else {
-        // dword g/2 of the token's scales: dword 0 at [32 + t], dword k >= 1 at [32 + 32 k + t]
-        const uint32_t d = sdw[32 + 32 * (g >> 1) + tr];
-        return h2f((g & 1) ? d >> 16 : d & 0xFFFFu);
-      }
-    };
-
     // ---- P V on the matrix cores -------------------------------------------
+    // Probability operand of lane (j, n): 8 k-slots (tokens T_j[e]) of query
+    // head n times the value scale, as bf16 hi + lo.  Value operands hold
+    // exact codes, biased to non-negative for INT8/INT4; the bias times the
+    // probability sum is removed once, after the last tile (cs_run).
     if constexpr (FV == F_INT4) {
+      // element order [0, 2, 1, 3, 4, 6, 5, 7] (see value_operand_int4)
 #pragma unroll
       for (int grp = 0; grp < VS::NG; ++grp) {
-        b8 A_hi, A_lo;
-        float cs = 0.f;
-        constexpr int ord[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+        uint32_t ah[4], al[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int slot = ord[e];
-          const int tr = 16 * (slot >> 2) + 4 * j + (slot & 3);
-          __bf16 hi, lo;
-          float used;
-          split_bf16(p[slot] * vscale(tr, grp), hi, lo, used);
-          A_hi[e] = hi;
-          A_lo[e] = lo;
-          cs += used;
+        for (int q = 0; q < 4; ++q) {
+          // pair q: slots (0,2) (1,3) (4,6) (5,7)
+          const int s0 = (q >> 1) * 4 + (q & 1), s1 = s0 + 2;
+          const int t0_ = 16 * (s0 >> 2) + 4 * j + (s0 & 3), t1_ = 16 * (s1 >> 2) + 4 * j + (s1 & 3);
+          f2 used;
+          split_bf16x2(f2{p[s0] * s_fv[t0_ * VS::NG + grp], p[s1] * s_fv[t1_ * VS::NG + grp]}, ah[q], al[q], used);
+          cs_run[grp] += used.x + used.y;
         }
+        const b8 A_hi = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
+        const b8 A_lo = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
         const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(cur + tbase + ((grp ^ tswz) << 4)));
         b8 ve, vo;
         value_operand_int4(raw, ve, vo);
-        cs += __shfl_xor(cs, 16);
-        cs += __shfl_xor(cs, 32);
         acc[2 * grp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, ve, acc[2 * grp], 0, 0, 0);
         acc[2 * grp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, ve, acc[2 * grp], 0, 0, 0);
         acc[2 * grp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, vo, acc[2 * grp + 1], 0, 0, 0);
         acc[2 * grp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, vo, acc[2 * grp + 1], 0, 0, 0);
-        // remove the +136 bias of the value operand: 136 * sum of the operand
-        // values of query head 4j + r
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float corr = 136.f * __shfl(cs, 4 * j + r);
-          acc[2 * grp][r] -= corr;
-          acc[2 * grp + 1][r] -= corr;
-        }
       }
     } else {
-      b8 A_hi, A_lo;
-      float cs = 0.f;
+      f4 vs4[2];
+      vs4[0] = *reinterpret_cast<const f4*>(&s_fv[4 * j]);
+      vs4[1] = *reinterpret_cast<const f4*>(&s_fv[16 + 4 * j]);
+      uint32_t ah[4], al[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tr = 16 * (e >> 2) + 4 * j + (e & 3);
-        __bf16 hi, lo;
-        float used;
-        split_bf16(p[e] * vscale(tr, 0), hi, lo, used);
-        A_hi[e] = hi;
-        A_lo[e] = lo;
-        cs += used;
+      for (int q = 0; q < 4; ++q) {  // pair q: slots 2q, 2q + 1
+        const int u = q >> 1, r0 = 2 * (q & 1);
+        f2 used;
+        split_bf16x2(f2{p[2 * q] * vs4[u][r0], p[2 * q + 1] * vs4[u][r0 + 1]}, ah[q], al[q], used);
+        if constexpr (FV == F_INT8) cs_run[0] += used.x + used.y;
       }
+      const b8 A_hi = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
+      const b8 A_lo = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
 #pragma unroll
       for (int m = 0; m < VS::NPV; ++m) {
         const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(cur + tbase + ((m ^ tswz) << 4)));
         const b8 vop = value_operand_8bit<FV>(raw);
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, vop, acc[m], 0, 0, 0);
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, vop, acc[m], 0, 0, 0);
-      }
-      if constexpr (FV == F_INT8) {
-        cs += __shfl_xor(cs, 16);
-        cs += __shfl_xor(cs, 32);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float corr = 128.f * __shfl(cs, 4 * j + r);
-#pragma unroll
-          for (int m = 0; m < VS::NPV; ++m) acc[m][r] -= corr;
-        }
       }
     }
     ++it;
@@ -606,6 +614,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if (!step(std::integral_constant<int, 0>{})) break;
     if (!step(std::integral_constant<int, 1>{})) break;
     if (!step(std::integral_constant<int, 2>{})) break;
+  }
+
+  // ---- remove the value-operand bias: acc[g][ch] -= bias * sum of the
+  //      probability operands of query head g (INT8 +128, INT4 +136) -------
+  if constexpr (FV != F_FP8) {
+    constexpr float bias = FV == F_INT8 ? 128.f : 136.f;
+#pragma unroll
+    for (int g = 0; g < NCS; ++g) {
+      float cs = cs_run[g];
+      cs += __shfl_xor(cs, 16);
+      cs += __shfl_xor(cs, 32);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float corr = bias * __shfl(cs, 4 * j + r);
+        if constexpr (FV == F_INT8) {
+#pragma unroll
+          for (int m = 0; m < VS::NPV; ++m) acc[m][r] -= corr;
+        } else {
+          acc[2 * g][r] -= corr;
+          acc[2 * g + 1][r] -= corr;
+        }
+      }
+    }
   }
 
   // ---- write this split's softmax state ------------------------------------
