@@ -28,6 +28,75 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD specification
+DECODE_SRC = os.path.join(ROOT, "quantized_paged_kv_write_amd", "csrc", "kvq_decode.hip")
+CAL_ELEMS = 1 << 28  # calibration kernel: negate 1 GiB of fp32 (reads 1 GiB, writes 1 GiB)
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_profile_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.json")
+
+
+def load_traffic(workload: str):
+    """HBM bytes per decode call from the committed counter summary, or None
+    when there is none or the decode kernels changed since it was taken."""
+    path = traffic_profile_path(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("decode_source_sha256_16") != decode_source_hash():
+        return None
+    return d["hbm_bytes_per_decode_call"]
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str, command: str) -> dict:
+    """Reduce two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) to HBM bytes per decode call, calibrated by the counters of the
+    elementwise negation of CAL_ELEMS fp32 values that bench.py launches
+    (algorithmically 4 CAL_ELEMS bytes read and written)."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(vals, key):
+        ks = [k for k in vals if key in k]
+        if not ks:
+            raise SystemExit(f"no kernel matching {key!r} in the counter file")
+        v = [x for k in ks for x in vals[k]]
+        return sum(v) / len(v), len(v)
+
+    cal_bytes = 4.0 * CAL_ELEMS
+    cal_f, _ = pick(f, "neg_kernel")
+    cal_w, _ = pick(w, "neg_kernel")
+    kf, kw = cal_bytes / cal_f, cal_bytes / cal_w
+    out = {"workload": workload, "decode_source_sha256_16": decode_source_hash(), "command": command,
+           "calibration": {"kernel": "elementwise negation of 2^28 fp32", "bytes_each_way": cal_bytes,
+                           "fetch_counter_bytes": cal_f, "write_counter_bytes": cal_w,
+                           "fetch_factor": kf, "write_factor": kw}, "kernels": {}}
+    total = 0.0
+    for key in ("decode_split_kernel", "kivi_tail_kernel", "merge_kernel"):
+        if not any(key in k for k in f):
+            continue
+        fb, nf = pick(f, key)
+        wb, nw = pick(w, key)
+        out["kernels"][key] = {"fetch_bytes": fb * kf, "write_bytes": wb * kw, "launches": nf}
+        total += fb * kf + wb * kw
+    out["hbm_bytes_per_decode_call"] = total
+    return out
 
 
 def row_bytes(fmt: str, D: int) -> float:
@@ -111,7 +180,17 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="reduce two rocprofv3 counter CSVs to profiles/decode_<workload>_hbm_traffic.json")
+    ap.add_argument("--pmc-command", default="", help="the command that produced the counter CSVs")
     args = ap.parse_args()
+    if args.pmc_summary:
+        d = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.pmc_command)
+        os.makedirs(os.path.dirname(traffic_profile_path(args.workload)), exist_ok=True)
+        with open(traffic_profile_path(args.workload), "w") as f:
+            json.dump(d, f, indent=1)
+        print(json.dumps(d, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode and write kernels shard "
               "by sequence or KV head with no communication, so run one process per GPU instead.", file=sys.stderr)
@@ -179,6 +258,11 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * nbytes * 5 / (ev[0].elapsed_time(ev[1]) * 1e6)
     del src, dst
+    # known-size kernel for calibrating the FETCH_SIZE / WRITE_SIZE counters
+    cal = torch.ones(CAL_ELEMS, dtype=torch.float32, device=dev)
+    cal = cal.neg()
+    torch.cuda.synchronize()
+    del cal
 
     # ---- decode steps -------------------------------------------------------
     def step(evs=None):
@@ -238,7 +322,7 @@ def main():
         "write_tokens": int(pre_idx.numel()),
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w.name),
                      "kernel": "decode_split_kernel + merge_kernel (one kvq_decode_attn call)"},
     }
     if not args.no_cpu_baseline:
