@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_8b_fp8")
     ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed decode calls after the cache fill, before any timing")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -234,6 +236,18 @@ def main():
     # ---- prefill write (cache fill), timed for the write bandwidth --------
     kvq.write(cache, k_pre, v_pre, s_pre, q_pre)
     torch.cuda.synchronize()
+    # Settle: after idle time or a different heavy kernel, decode calls run
+    # at a varying, slower rate for tens of milliseconds (clock and power
+    # management adjusting), so untimed decode calls run for a fixed time
+    # before each timed phase.
+    def settle():
+        t_settle = time.perf_counter() + args.settle
+        while time.perf_counter() < t_settle:
+            for _ in range(8):
+                kvq.decode_attn(cache, q, table, ctx_d, out=out, workspace=ws)
+            torch.cuda.synchronize()
+
+    settle()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(args.prefill_reps):
@@ -275,6 +289,7 @@ def main():
         if evs is not None:
             evs[2].record(stream)
 
+    settle()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -299,6 +314,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -50,7 +50,7 @@ typedef enum kvq_status {
   KVQ_ERR_INVALID_ARG = -1,  /* NULL pointer, non-positive size, bad enum   */
   KVQ_ERR_UNSUPPORTED = -2,  /* format or head_dim not implemented          */
   KVQ_ERR_SHAPE = -3,        /* shape rule broken (see kvq_cache)           */
-  KVQ_ERR_WORKSPACE = -4,    /* decode workspace NULL or too small          */
+  KVQ_ERR_WORKSPACE = -4,    /* decode workspace NULL, too small, unaligned */
   KVQ_ERR_NO_DEVICE = -5,    /* no HIP device visible                       */
   KVQ_ERR_HIP = -6           /* a HIP runtime call or launch failed         */
 } kvq_status;
@@ -129,11 +129,15 @@ int kvq_write(const kvq_cache* cache, const void* k, const void* v,
               const int64_t* slot_mapping, const int32_t* seq_idx,
               int64_t num_tokens, void* stream);
 
-/* Bytes of device workspace kvq_decode_attn needs for these sizes (partial
- * softmax states of the context splits).  pages_per_split 0 = automatic. */
+/* Bytes of device workspace kvq_decode_attn needs for these sizes and this
+ * split_tokens (see below): the work partition and the partial softmax
+ * states of the pieces the context is cut into.  Depends only on the
+ * arguments, not on the device or on ctx_lens.  KVQ_ERR_SHAPE if
+ * max_blocks_per_seq * block_size reaches 2^30 tokens or the call's tile
+ * count (batch x that / 32) reaches 2^30. */
 int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch,
                                int32_t n_q_heads, int32_t max_blocks_per_seq,
-                               int32_t pages_per_split, size_t* bytes);
+                               int32_t split_tokens, size_t* bytes);
 
 /* Decode attention over the quantized pages ([P2] 5 "The kernel side";
  * "K is more sensitive than V": o = softmax(q k^T * sm_scale) V).
@@ -142,20 +146,31 @@ int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch,
  *                page of each sequence; entries past the sequence's pages are
  *                never read.
  *   ctx_lens     int32 (batch): tokens of each sequence in the cache (0 gives
- *                an all-zero output row).  For KVQ_INT4_KIVI keys the last
- *                ctx_len % 32 tokens are read from tail row b (the batch row).
+ *                an all-zero output row; values above max_blocks_per_seq *
+ *                block_size are clamped to it).  For KVQ_INT4_KIVI keys the
+ *                last ctx_len % 32 tokens are read from tail row b (the batch
+ *                row).
  *   sm_scale     softmax scale; 0 means 1/sqrt(head_dim).
- *   pages_per_split  pages per context split; 0 = automatic.
+ *   split_tokens work partition.  The quantized tokens of all sequences,
+ *                in 32-token tiles, are numbered sequence after sequence and
+ *                cut into equal shares, each read by one wave per KV head
+ *                (a share may end in one sequence and go on in the next).
+ *                0 = automatic: as many shares as fill the GPU's resident
+ *                waves once (at least 4 tiles each); > 0 = shares of
+ *                ceil(split_tokens / 32) tiles.
  *   out          fp16 (batch, n_q_heads, D), written.
- *   workspace    device scratch of at least kvq_decode_workspace_bytes().
+ *   workspace    device scratch of at least kvq_decode_workspace_bytes()
+ *                for the same arguments, 16-byte aligned; its contents on
+ *                entry do not matter.
  * Query head hq reads KV head hq / (n_q_heads / n_kv_heads) ([P4] GQA).
  * Scores and the softmax are accumulated in fp32; the result is rounded to
- * fp16 once, to nearest-even.  The result does not depend on how the context
- * is split except through fp32 rounding. */
+ * fp16 once, to nearest-even.  The result does not depend on the partition
+ * except through fp32 rounding, and a given partition gives bitwise the same
+ * result on every call. */
 int kvq_decode_attn(const kvq_cache* cache, const void* q,
                     const int32_t* block_table, int32_t max_blocks_per_seq,
                     const int32_t* ctx_lens, int32_t batch, int32_t n_q_heads,
-                    float sm_scale, int32_t pages_per_split, void* out,
+                    float sm_scale, int32_t split_tokens, void* out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */

@@ -155,17 +155,17 @@ def write(cache: PagedKVCache, k, v, slot_mapping, seq_idx=None, stream=None):
         raise KvqError(rc, "kvq_write")
 
 
-def decode_workspace_bytes(cache: PagedKVCache, batch, n_q_heads, max_blocks_per_seq, pages_per_split=0) -> int:
+def decode_workspace_bytes(cache: PagedKVCache, batch, n_q_heads, max_blocks_per_seq, split_tokens=0) -> int:
     out = ctypes.c_size_t(0)
     c = cache.struct()
-    rc = lib().kvq_decode_workspace_bytes(ctypes.byref(c), batch, n_q_heads, max_blocks_per_seq, pages_per_split,
+    rc = lib().kvq_decode_workspace_bytes(ctypes.byref(c), batch, n_q_heads, max_blocks_per_seq, split_tokens,
                                           ctypes.byref(out))
     if rc != KVQ_OK:
         raise KvqError(rc, "kvq_decode_workspace_bytes")
     return out.value
 
 
-def decode_attn(cache: PagedKVCache, q, block_table, ctx_lens, sm_scale=0.0, pages_per_split=0, out=None,
+def decode_attn(cache: PagedKVCache, q, block_table, ctx_lens, sm_scale=0.0, split_tokens=0, out=None,
                 workspace=None, stream=None):
     """kvq_decode_attn: one decode step over the cache; returns out (B, Hq, D) fp16."""
     dev = cache.device
@@ -178,12 +178,12 @@ def decode_attn(cache: PagedKVCache, q, block_table, ctx_lens, sm_scale=0.0, pag
     if out is None:
         out = torch.empty_like(q)
     _check(out, torch.float16, "out", dev)
-    need = decode_workspace_bytes(cache, B, Hq, block_table.shape[1], pages_per_split)
+    need = decode_workspace_bytes(cache, B, Hq, block_table.shape[1], split_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     c = cache.struct()
     rc = lib().kvq_decode_attn(ctypes.byref(c), _ptr(q), _ptr(block_table), block_table.shape[1], _ptr(ctx_lens),
-                               B, Hq, float(sm_scale), pages_per_split, _ptr(out), _ptr(workspace),
+                               B, Hq, float(sm_scale), split_tokens, _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != KVQ_OK:
         raise KvqError(rc, "kvq_decode_attn")

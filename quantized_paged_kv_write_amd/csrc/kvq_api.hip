@@ -38,20 +38,6 @@ int device_present() {
   return KVQ_OK;
 }
 
-struct SplitPlan {
-  int32_t pps;
-  int32_t splits;  // including the KIVI tail split
-};
-
-SplitPlan plan_splits(const kvq_cache& c, int32_t batch, int32_t max_blocks, int32_t requested) {
-  SplitPlan p;
-  p.pps = choose_pages_per_split(c, batch, max_blocks, requested);
-  p.splits = (max_blocks + p.pps - 1) / p.pps;
-  if (p.splits < 1) p.splits = 1;
-  if (c.k_dtype == KVQ_INT4_KIVI) p.splits += 1;
-  return p;
-}
-
 }  // namespace
 
 extern "C" {
@@ -63,7 +49,7 @@ const char* kvq_status_string(int status) {
     case KVQ_ERR_UNSUPPORTED: return "unsupported format, head_dim or block_size";
     case KVQ_ERR_SHAPE: return "shape rule broken (KIVI needs block_size 32 and max_seqs > 0; sizes too large; "
                                "n_q_heads not a multiple of n_kv_heads)";
-    case KVQ_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case KVQ_ERR_WORKSPACE: return "decode workspace missing, too small or not 16-byte aligned";
     case KVQ_ERR_NO_DEVICE: return "no HIP device available";
     case KVQ_ERR_HIP: return "HIP runtime error";
   }
@@ -104,23 +90,24 @@ int kvq_write(const kvq_cache* cache, const void* k, const void* v, const int64_
 }
 
 int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t n_q_heads,
-                               int32_t max_blocks_per_seq, int32_t pages_per_split, size_t* bytes) {
+                               int32_t max_blocks_per_seq, int32_t split_tokens, size_t* bytes) {
   int rc = check_cache(cache);
   if (rc != KVQ_OK) return rc;
-  if (!bytes || batch < 0 || n_q_heads <= 0 || max_blocks_per_seq <= 0 || pages_per_split < 0)
+  if (!bytes || batch < 0 || n_q_heads <= 0 || max_blocks_per_seq <= 0 || split_tokens < 0)
     return KVQ_ERR_INVALID_ARG;
-  const SplitPlan p = plan_splits(*cache, batch, max_blocks_per_seq, pages_per_split);
-  *bytes = (size_t)batch * n_q_heads * p.splits * (cache->head_dim + 2) * sizeof(float);
+  DecodePlan p;
+  if (!plan_decode(*cache, batch, n_q_heads, max_blocks_per_seq, split_tokens, &p)) return KVQ_ERR_SHAPE;
+  *bytes = p.bytes;
   return KVQ_OK;
 }
 
 int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
                     const int32_t* ctx_lens, int32_t batch, int32_t n_q_heads, float sm_scale,
-                    int32_t pages_per_split, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                    int32_t split_tokens, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_cache(cache);
   if (rc != KVQ_OK) return rc;
   if (cache->k_dtype == KVQ_INT4_G32) return KVQ_ERR_UNSUPPORTED;
-  if (batch < 0 || n_q_heads <= 0 || max_blocks_per_seq <= 0 || pages_per_split < 0) return KVQ_ERR_INVALID_ARG;
+  if (batch < 0 || n_q_heads <= 0 || max_blocks_per_seq <= 0 || split_tokens < 0) return KVQ_ERR_INVALID_ARG;
   if (n_q_heads % cache->n_kv_heads != 0) return KVQ_ERR_SHAPE;
   const int32_t G = n_q_heads / cache->n_kv_heads;
   if (G > 16) return KVQ_ERR_UNSUPPORTED;
@@ -128,13 +115,12 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_
   if (batch == 0) return KVQ_OK;
   if (cache->k_dtype == KVQ_INT4_KIVI && batch > cache->max_seqs) return KVQ_ERR_SHAPE;  // tail row per sequence
   if (!q || !block_table || !ctx_lens || !out) return KVQ_ERR_INVALID_ARG;
-  size_t need = 0;
-  rc = kvq_decode_workspace_bytes(cache, batch, n_q_heads, max_blocks_per_seq, pages_per_split, &need);
-  if (rc != KVQ_OK) return rc;
-  if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+  DecodePlan p;
+  if (!plan_decode(*cache, batch, n_q_heads, max_blocks_per_seq, split_tokens, &p)) return KVQ_ERR_SHAPE;
+  if (!workspace || workspace_bytes < p.bytes) return KVQ_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return KVQ_ERR_WORKSPACE;
   rc = device_present();
   if (rc != KVQ_OK) return rc;
-  const SplitPlan p = plan_splits(*cache, batch, max_blocks_per_seq, pages_per_split);
   DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.block_table = block_table;
@@ -158,10 +144,11 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_
   a.k_tail = static_cast<const uint16_t*>(cache->k_tail);
   a.v_tail = static_cast<const uint16_t*>(cache->v_tail);
   a.max_seqs = cache->max_seqs;
-  a.pages_per_split = p.pps;
-  a.num_splits = p.splits;
-  a.quant_splits = p.splits - (cache->k_dtype == KVQ_INT4_KIVI ? 1 : 0);
-  a.part = static_cast<float*>(workspace);
+  a.share_tiles = p.share_tiles;
+  a.max_shares = p.max_shares;
+  a.num_shares = p.max_shares;  // the launcher may use fewer
+  a.plan = static_cast<int32_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.plan_bytes);
   a.out = static_cast<uint16_t*>(out);
   return launch_decode(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }

@@ -28,7 +28,10 @@
 //    fp32 throughout; each split stores (m, l, acc[D]).
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -46,8 +49,10 @@ typedef __attribute__((address_space(3))) i2 lds_i2;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int TILE = 32;      // tokens per tile
-constexpr int MAX_WAVES = 8;  // KV heads per workgroup
-constexpr int MAX_PPS = 256;  // pages per split (block-table slice in LDS)
+// Balanced partition: at most this many waves, and at least this many tiles
+// per share unless the caller asks for a size.
+constexpr int AUTO_MAX_WAVES = 4096;
+constexpr int AUTO_MIN_TILES = 4;
 
 template <int FK, int D>
 struct KShape {
@@ -185,16 +190,15 @@ __device__ __forceinline__ void split_bf16x2(f2 x, uint32_t& hi, uint32_t& lo, f
   used = fh + f2{__builtin_bit_cast(float, lb << 16), __builtin_bit_cast(float, lb & 0xFFFF0000u)};
 }
 
-// Flat row index (slot * H + h) of token t0 + t and whether it is live: in the
-// context and on a page whose block id is valid.  The block id comes from
-// the split's block-table slice in LDS (s_blk[page - p0]).
-__device__ __forceinline__ uint32_t tile_row(const DecodeArgs& a, const int32_t* s_blk, int p0, int t, int t0,
-                                             int tok_end, int h, bool& live) {
+// Flat row index (slot * H + h) of token t0 + t of a sequence and whether it
+// is live: in the context and on a page whose block id is valid.  ids[t] is
+// the block id of that token's page (copied into LDS ahead of the tile).
+__device__ __forceinline__ uint32_t tile_row(const DecodeArgs& a, const int32_t* ids, int t, int t0, int tok_end,
+                                             int h, bool& live) {
   const int tt = t0 + t;
   const int lbs = a.log2_bs;
-  const int pg = tt >> lbs;
   const bool in = tt < tok_end;
-  const int bid = in ? s_blk[pg - p0] : 0;
+  const int bid = in ? ids[t] : 0;
   live = in && bid >= 0 && bid < a.nb;
   const uint32_t blk = live ? (uint32_t)bid : 0u;
   return ((blk << lbs) + (uint32_t)(tt & ((1 << lbs) - 1))) * (uint32_t)a.H + (uint32_t)h;
@@ -254,15 +258,39 @@ struct Stage {
   static constexpr int BYTES = OFF_M + KIVI_BYTES;
   // DMA instructions per tile: keys, values, scales, KIVI page metadata
   static constexpr int NDMA = NLK + NLV + NGD + (FK == F_KIVI ? 1 : 0);
+  // Pipeline depth: NST stages (NST - 1 tiles in flight while one is
+  // computed), as many as fit beside the other LDS arrays in a quarter of a
+  // CU's 160 KB, so one wave per SIMD fits; 3 to 6, and the copies of
+  // NST - 2 tiles must fit the 6-bit vmcnt.
+  static constexpr int LDS_WAVE = 160 * 1024 / 4;
+  static constexpr int OTHER = 8 * TILE * 4 + TILE * 4 + TILE * VS::NG * 4;  // id ring, scale arrays
+  static constexpr int NST_FIT = (LDS_WAVE - OTHER) / BYTES;
+  static constexpr int NST_VM = 63 / NDMA + 2;
+  static constexpr int NST = NST_FIT < 3 ? 3 : (NST_FIT > 6 ? (NST_VM < 6 ? NST_VM : 6) : (NST_VM < NST_FIT ? NST_VM : NST_FIT));
+  static constexpr int RING = NST <= 4 ? 4 : 8;  // block-id ring slots (power of two >= NST)
 };
+
+// s_waitcnt vmcnt(k * N) for a run-time k in [0, KMAX].
+template <int N, int KMAX>
+__device__ __forceinline__ void wait_groups(int k) {
+  if constexpr (KMAX > 0) {
+    if (k >= KMAX) {
+      wait_vmcnt<KMAX * N>();
+      return;
+    }
+    wait_groups<N, KMAX - 1>(k);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
 
 // Start the copy of one tile (keys, values, per-token scale dwords; KIVI
 // page scale/zero) into LDS stage `st`; returns the live-token mask (bit t
 // and t + 32: token t0 + t is in the context on a valid page).  Masked rows
 // copy from the start of the buffer; those bytes are never used unmasked.
 template <int FK, int FV, int D>
-__device__ __forceinline__ uint64_t issue_tile(const DecodeArgs& a, const int32_t* s_blk, int p0, int t0, int tok_end,
-                                               int h, uint8_t* st) {
+__device__ __forceinline__ uint64_t issue_tile(const DecodeArgs& a, const int32_t* ids, int t0, int tok_end, int h,
+                                               uint8_t* st) {
   using S = Stage<FK, FV, D>;
   using KS = KShape<FK, D>;
   using VS = VShape<FV, D>;
@@ -271,7 +299,7 @@ __device__ __forceinline__ uint64_t issue_tile(const DecodeArgs& a, const int32_
   const uint32_t base = lds_addr(st);
   // row index of token `lane & 31`, or ~0 when masked; shared with shuffles
   bool live;
-  const uint32_t r_own = tile_row(a, s_blk, p0, lane & 31, t0, tok_end, h, live);
+  const uint32_t r_own = tile_row(a, ids, lane & 31, t0, tok_end, h, live);
   const uint64_t live_mask = __ballot(live);
   const uint32_t rl = live ? r_own : ~0u;
 #pragma unroll
@@ -317,6 +345,61 @@ __device__ __forceinline__ uint64_t issue_tile(const DecodeArgs& a, const int32_
   return live_mask;
 }
 
+// Sequence b of the tile numbering owns tiles [lo, hi) and holds lq tokens in
+// quantized pages.  Lane i of the window registers holds, for sequence
+// wb + i, the end of its tile range (hi) and lq; a cursor reads them with
+// readlane, so moving to the next sequence costs no memory access (a refill
+// after 64 sequences does).
+struct SeqCursor {
+  int b, wb, lo, hi, lq;
+  int win_hi, win_lq;  // per lane
+};
+
+template <int FK>
+__device__ __forceinline__ int seq_tokens(const DecodeArgs& a, int b) {
+  // ctx_len clamped to what the block-table row addresses; KIVI: whole pages
+  const int L = min(max(a.ctx_lens[b], 0), a.max_blocks << a.log2_bs);
+  return FK == F_KIVI ? (L & ~31) : L;
+}
+
+template <int FK>
+__device__ __forceinline__ void fill_window(SeqCursor& c, const DecodeArgs& a, int wb) {
+  const int lane = (int)threadIdx.x, sb = wb + lane;
+  c.wb = wb;
+  c.win_hi = sb < a.B ? a.plan[2 + sb] : INT_MAX;
+  c.win_lq = sb < a.B ? seq_tokens<FK>(a, sb) : 0;
+}
+
+__device__ __forceinline__ int rdlane(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
+
+// Move the cursor to the sequence holding tile x (x >= the current tile and
+// x < the number of tiles, so the loop ends on a valid sequence).
+template <int FK>
+__device__ __forceinline__ void seek(SeqCursor& c, const DecodeArgs& a, int x) {
+  if (x < c.hi) return;
+  do {
+    ++c.b;
+    if (c.b - c.wb >= 64) fill_window<FK>(c, a, c.b);
+    c.lo = c.hi;
+    c.hi = rdlane(c.win_hi, c.b - c.wb);
+  } while (x >= c.hi);
+  c.lq = rdlane(c.win_lq, c.b - c.wb);
+}
+
+// Copy the block ids of the 32 tokens of tile x (of the cursor's sequence)
+// into LDS: lane t < 32 fetches the block-table entry of token t's page.
+template <int RING>
+__device__ __forceinline__ void issue_ids(const DecodeArgs& a, const SeqCursor& c, int x, uint32_t ring) {
+  const int lane = (int)threadIdx.x;
+  if (lane < TILE) {
+    const int tok = TILE * (x - c.lo) + lane;
+    const int pg = tok < c.lq ? tok >> a.log2_bs : 0;
+    // slot x % RING of the ring; wave-uniform (it follows the tile counter)
+    dma4(a.block_table + (size_t)c.b * a.max_blocks + pg,
+         __builtin_amdgcn_readfirstlane(ring + (uint32_t)(x & (RING - 1)) * (TILE * 4)));
+  }
+}
+
 template <int FK, int FV, int D>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using KS = KShape<FK, D>;
@@ -324,34 +407,39 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using ST = Stage<FK, FV, D>;
   constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
   constexpr int NCS = FV == F_INT4 ? VS::NG : 1;  // bias-correction sums kept per value group
-  __shared__ int32_t s_blk[MAX_PPS];
-  // three stages: tile i is computed while tiles i+1 and i+2 are in flight
-  __shared__ __attribute__((aligned(16))) uint8_t s_st[3][ST::BYTES];
+  constexpr int NST = ST::NST, RING = ST::RING;
+  // NST stages: tile x is computed while tiles x + 1 .. x + NST - 1 are in flight
+  __shared__ __attribute__((aligned(16))) uint8_t s_st[NST][ST::BYTES];
+  // block ids of the tokens of tile x in slot x % RING (fetched NST - 1 tiles ahead of the tile)
+  __shared__ __attribute__((aligned(16))) int32_t s_ids[RING][TILE];
   // this tile's scales as fp32: key scale x sm_scale x log2 e, value scales
   __shared__ __attribute__((aligned(16))) float s_fk[TILE];
   __shared__ __attribute__((aligned(16))) float s_fv[TILE * VS::NG];
 
-  // Work unit (sequence, split, KV head); the KV heads of one (sequence,
-  // split) are consecutive workgroups of one XCD (workgroups are dealt to the
-  // 8 XCDs round robin), so they share the L2 lines of the page scales.
+  // Wave (share, KV head).  The KV heads of one share are consecutive
+  // workgroups of one XCD (workgroups are dealt to the 8 XCDs round robin),
+  // so they read the same page-scale lines of its L2 at about the same time.
   const uint32_t wg = blockIdx.x;
   const uint32_t kk = wg >> 3;
   const int h = (int)(kk % (uint32_t)a.H);
-  const uint32_t unit = (kk / (uint32_t)a.H) * 8 + (wg & 7);
-  if (unit >= (uint32_t)(a.B * a.quant_splits)) return;
-  const int b = (int)(unit / (uint32_t)a.quant_splits), split = (int)(unit % (uint32_t)a.quant_splits);
+  const int share = (int)((kk / (uint32_t)a.H) * 8 + (wg & 7));
+  if (share >= a.num_shares) return;
+  const int S = a.plan[0];
+  const int total = a.plan[1 + a.B];
+  const int x_begin = share * S;
+  if (x_begin >= total) return;
+  const int x_end = min(x_begin + S, total);
+
+  SeqCursor cc;  // tile being computed
+  cc.b = a.plan[2 + a.B + share];
+  cc.lo = a.plan[1 + cc.b];
+  fill_window<FK>(cc, a, cc.b);
+  cc.hi = rdlane(cc.win_hi, 0);
+  cc.lq = rdlane(cc.win_lq, 0);
+  SeqCursor ci = cc, cd = cc;  // tile being issued, block ids being fetched
 
   const int lane = (int)threadIdx.x;
   const int j = lane >> 4, n = lane & 15;
-  const int bs = 1 << a.log2_bs;
-  // ctx_len is clamped to what the block-table row can address
-  const int L = min(max(a.ctx_lens[b], 0), a.max_blocks * bs);
-  const int Lq = FK == F_KIVI ? (L & ~31) : L;  // tokens held in quantized pages
-  const int npages = (Lq + bs - 1) >> a.log2_bs;
-  const int p0 = split * a.pages_per_split;
-  const int p1 = min(npages, p0 + a.pages_per_split);
-  for (int i = lane; i < p1 - p0; i += 64) s_blk[i] = a.block_table[(size_t)b * a.max_blocks + p0 + i];
-
   const int G = a.G;
   const int hq0 = h * G;
   f4 acc[VS::NPV];
@@ -361,19 +449,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   float cs_run[NCS];  // sum of the probability operands (hi + lo) of query head n, per value group
 #pragma unroll
   for (int g = 0; g < NCS; ++g) cs_run[g] = 0.f;
-
-  // Query operand (B of S^T = K Q^T): lane (j, n) holds query head n's
-  // channels of k-slots 8j..8j+7 in the key operand's channel order.
-  const uint16_t* qrow = a.q + ((size_t)b * a.Hq + hq0 + (n < G ? n : 0)) * D;
+  // Query operand (B of S^T = K Q^T), loaded at the start of each sequence's
+  // piece: lane (j, n) holds query head n's channels of k-slots 8j..8j+7 in
+  // the key operand's channel order.
   h8 qop[KS::KB];
-#pragma unroll
-  for (int kb = 0; kb < KS::KB; ++kb) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t bits = qrow[key_channel<FK, D>(j, kb, e)];
-      qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < G ? bits : 0));
-    }
-  }
+  bool piece_start = true;
+
   // the half of a scale dword holding this (token, head)'s scale is
   // (row index) & 1: h & 1 for an even head count, (t + h) & 1 otherwise
   const bool h_odd = (a.H & 1) != 0;
@@ -385,27 +466,107 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int tbase = ST::OFF_V + trow * VS::RB + 8 * (n & 1);
   const int tswz = vswz<VS::CH>(trow);
 
-  const int tok_begin = p0 * bs, tok_end = min(Lq, p1 * bs);
-  const int ntiles = tok_end > tok_begin ? (tok_end - tok_begin + TILE - 1) / TILE : 0;
-  __syncthreads();  // s_blk written before it is read below
-  uint64_t live[3] = {0, 0, 0};
-  if (ntiles > 0) live[0] = issue_tile<FK, FV, D>(a, s_blk, p0, tok_begin, tok_end, h, s_st[0]);
-  if (ntiles > 1) live[1] = issue_tile<FK, FV, D>(a, s_blk, p0, tok_begin + TILE, tok_end, h, s_st[1]);
+  // Copies are issued in groups, one per tile y: the block ids of tile
+  // y + NST - 1, then tile y itself (NDMA copies).  Loads complete in issue
+  // order, so once at most k NDMA copies are outstanding, with k the number
+  // of groups issued after tile y's, tile y and every earlier id copy are in
+  // LDS (the id copies of the later groups only make the wait longer).
+  const uint32_t ring = lds_addr(&s_ids[0][0]);
+  for (int y = x_begin; y < x_begin + NST - 1 && y < x_end; ++y) {
+    seek<FK>(cd, a, y);
+    issue_ids<RING>(a, cd, y, ring);
+  }
+  wait_vmcnt<0>();
+  auto issue_group = [&](int y, uint8_t* st) __attribute__((always_inline)) -> uint64_t {
+    if (y + NST - 1 < x_end) {
+      seek<FK>(cd, a, y + NST - 1);
+      issue_ids<RING>(a, cd, y + NST - 1, ring);
+    }
+    seek<FK>(ci, a, y);
+    return issue_tile<FK, FV, D>(a, s_ids[y & (RING - 1)], TILE * (y - ci.lo), ci.lq, h, st);
+  };
+  uint64_t live[NST];
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) live[i] = x_begin + i < x_end ? issue_group(x_begin + i, s_st[i]) : 0;
 
-  int it = 0;
-  // One tile; S is the LDS stage holding it.
-  auto step = [&](auto stage) -> bool {
-    constexpr int S = decltype(stage)::value;
-    if (it >= ntiles) return false;
-    const int t0 = tok_begin + it * TILE;
-    uint8_t* cur = s_st[S];
-    // ---- wait for this tile's copies (the next tile's may stay in flight)
-    if (it + 1 < ntiles) wait_vmcnt<ST::NDMA>();
-    else wait_vmcnt<0>();
-    const uint64_t live_mask = live[S];
-    // ---- start the tile after next -----------------------------------------
-    if (it + 2 < ntiles)
-      live[(S + 2) % 3] = issue_tile<FK, FV, D>(a, s_blk, p0, t0 + 2 * TILE, tok_end, h, s_st[(S + 2) % 3]);
+  // Write the softmax state of sequence b's piece (record share + b) and
+  // reset it for the next piece.
+  auto write_piece = [&](int b) __attribute__((always_inline)) {
+    // remove the value-operand bias: acc[g][ch] -= bias * sum of the
+    // probability operands of query head g (INT8 +128, INT4 +136)
+    if constexpr (FV != F_FP8) {
+      constexpr float bias = FV == F_INT8 ? 128.f : 136.f;
+#pragma unroll
+      for (int g = 0; g < NCS; ++g) {
+        float cs = cs_run[g];
+        cs += __shfl_xor(cs, 16);
+        cs += __shfl_xor(cs, 32);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float corr = bias * __shfl(cs, 4 * j + r);
+          if constexpr (FV == F_INT8) {
+#pragma unroll
+            for (int m = 0; m < VS::NPV; ++m) acc[m][r] -= corr;
+          } else {
+            acc[2 * g][r] -= corr;
+            acc[2 * g + 1][r] -= corr;
+          }
+        }
+      }
+    }
+    float l = l_run;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const size_t stride = (size_t)D + 2;
+    float* pbase = a.part + ((size_t)(share + b) * a.Hq + hq0) * stride;
+    if (j == 0 && n < G) {
+      pbase[n * stride] = m_run;
+      pbase[n * stride + 1] = l;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * j + r;
+      if (g < G) {
+#pragma unroll
+        for (int m = 0; m < VS::NPV; ++m) {
+          const int ch = FV == F_INT4 ? 32 * (m >> 1) + 2 * n + (m & 1) : 16 * m + n;
+          pbase[g * stride + 2 + ch] = acc[m][r];
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < VS::NPV; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int g = 0; g < NCS; ++g) cs_run[g] = 0.f;
+    piece_start = true;
+  };
+
+  int x = x_begin;
+  // One tile; S_ is the LDS stage holding it.
+  auto step = [&](auto stage) __attribute__((always_inline)) -> bool {
+    constexpr int S_ = decltype(stage)::value;
+    if (x >= x_end) return false;
+    uint8_t* cur = s_st[S_];
+    // ---- wait for this tile's copies (the next group may stay in flight) ----
+    wait_groups<ST::NDMA, NST - 2>(x_end - 1 - x);
+    const uint64_t live_mask = live[S_];
+    // ---- start tile x + NST - 1 ---------------------------------------------
+    if (x + NST - 1 < x_end) live[(S_ + NST - 1) % NST] = issue_group(x + NST - 1, s_st[(S_ + NST - 1) % NST]);
+    // ---- first tile of a sequence's piece: its query operand ---------------
+    if (piece_start) {
+      const uint16_t* qrow = a.q + ((size_t)cc.b * a.Hq + hq0 + (n < G ? n : 0)) * D;
+#pragma unroll
+      for (int kb = 0; kb < KS::KB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t bits = qrow[key_channel<FK, D>(j, kb, e)];
+          qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < G ? bits : 0));
+        }
+      }
+      piece_start = false;
+    }
 
     // ---- scales -> fp32 (0 for masked tokens); FP8 codes of masked value
     //      rows zeroed (a garbage byte may be a NaN code)
@@ -607,73 +768,31 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, vop, acc[m], 0, 0, 0);
       }
     }
-    ++it;
+    // ---- last tile of the piece: write its softmax state ---------------------
+    if (x + 1 == x_end || x + 1 == cc.hi) {
+      write_piece(cc.b);
+      if (x + 1 < x_end) seek<FK>(cc, a, x + 1);
+    }
+    ++x;
     return true;
   };
-  for (;;) {
-    if (!step(std::integral_constant<int, 0>{})) break;
-    if (!step(std::integral_constant<int, 1>{})) break;
-    if (!step(std::integral_constant<int, 2>{})) break;
-  }
-
-  // ---- remove the value-operand bias: acc[g][ch] -= bias * sum of the
-  //      probability operands of query head g (INT8 +128, INT4 +136) -------
-  if constexpr (FV != F_FP8) {
-    constexpr float bias = FV == F_INT8 ? 128.f : 136.f;
-#pragma unroll
-    for (int g = 0; g < NCS; ++g) {
-      float cs = cs_run[g];
-      cs += __shfl_xor(cs, 16);
-      cs += __shfl_xor(cs, 32);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float corr = bias * __shfl(cs, 4 * j + r);
-        if constexpr (FV == F_INT8) {
-#pragma unroll
-          for (int m = 0; m < VS::NPV; ++m) acc[m][r] -= corr;
-        } else {
-          acc[2 * g][r] -= corr;
-          acc[2 * g + 1][r] -= corr;
-        }
-      }
-    }
-  }
-
-  // ---- write this split's softmax state ------------------------------------
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  const size_t stride = (size_t)D + 2;
-  float* pbase = a.part + (((size_t)b * a.Hq + hq0) * a.num_splits + split) * stride;
-  const size_t hstride = (size_t)a.num_splits * stride;
-  if (j == 0 && n < G) {
-    pbase[n * hstride] = m_run;
-    pbase[n * hstride + 1] = l_run;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int g = 4 * j + r;
-    if (g < G) {
-#pragma unroll
-      for (int m = 0; m < VS::NPV; ++m) {
-        const int ch = FV == F_INT4 ? 32 * (m >> 1) + 2 * n + (m & 1) : 16 * m + n;
-        pbase[g * hstride + 2 + ch] = acc[m][r];
-      }
-    }
+  auto round = [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) -> bool {
+    return (step(std::integral_constant<int, I>{}) && ...);
+  };
+  while (round(std::make_integer_sequence<int, NST>{})) {
   }
 }
 
 // KIVI fp16 tail: the last ctx_len % 32 tokens of each sequence, keys and
-// values in fp16, as one extra split (index num_splits - 1).  One wave per
+// values in fp16, as one more record (max_shares + B + b).  One wave per
 // (sequence, KV head); plain fp32 arithmetic.
 template <int D>
 __global__ __launch_bounds__(64) void kivi_tail_kernel(DecodeArgs a) {
   const int b = (int)blockIdx.x, h = (int)blockIdx.y, lane = (int)threadIdx.x;
   const int L = min(max(a.ctx_lens[b], 0), a.max_blocks * 32);
   const int nt = b < a.max_seqs ? (L & 31) : 0;  // tail rows exist only for b < max_seqs
-  const int split = a.num_splits - 1;
   const size_t stride = (size_t)D + 2;
-  const size_t hstride = (size_t)a.num_splits * stride;
-  float* pbase = a.part + (((size_t)b * a.Hq + h * a.G) * a.num_splits + split) * stride;
+  float* pbase = a.part + ((size_t)(a.max_shares + a.B + b) * a.Hq + h * a.G) * stride;
   constexpr int CPL = D / 64;  // channels per lane for the value accumulation
   for (int g = 0; g < a.G; ++g) {
     const uint16_t* qrow = a.q + ((size_t)b * a.Hq + h * a.G + g) * D;
@@ -701,7 +820,7 @@ __global__ __launch_bounds__(64) void kivi_tail_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(pt, h2f(vrow[lane * CPL + c]), accv[c]);
     }
-    float* dst = pbase + g * hstride;
+    float* dst = pbase + g * stride;
     if (lane == 0) {
       dst[0] = mx;
       dst[1] = l;
@@ -711,22 +830,32 @@ __global__ __launch_bounds__(64) void kivi_tail_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the splits of one (sequence, query head): M = max m_s,
-// out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), rounded to fp16.
-// Four waves share the splits; lanes own channels.
+// Merge the pieces of one (sequence, query head): M = max m_r,
+// out = sum_r acc_r 2^(m_r - M) / sum_r l_r 2^(m_r - M), rounded to fp16.
+// Sequence b's tiles [P_b, P_b+1) lie in shares P_b / S .. (P_b+1 - 1) / S,
+// whose pieces are records share + b; a KIVI tail adds record
+// max_shares + B + b.  Four waves share the records; lanes own channels.
 constexpr int MERGE_WAVES = 4;
 
-template <int D>
+template <int D, bool KIVI>
 __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   constexpr int CPL = D / 64;
   __shared__ float s_m[MERGE_WAVES];
   __shared__ float s_acc[MERGE_WAVES][D + 1];
   const int bh = (int)blockIdx.x, tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int S = a.num_splits;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq;
+  const int S = a.plan[0];
+  const int t0 = a.plan[1 + b], t1 = a.plan[2 + b];
+  const int first = t1 > t0 ? t0 / S : 0;
+  const int npieces = t1 > t0 ? (t1 - 1) / S - first + 1 : 0;
+  const int nrec = npieces + (KIVI ? 1 : 0);
   const size_t stride = (size_t)D + 2;
-  const float* base = a.part + (size_t)bh * S * stride;
+  auto rec = [&](int i) -> const float* {
+    const size_t r = i < npieces ? (size_t)(first + i + b) : (size_t)(a.max_shares + a.B + b);
+    return a.part + (r * a.Hq + hq) * stride;
+  };
   float M = -INFINITY;
-  for (int s = tid; s < S; s += MERGE_WAVES * 64) M = fmaxf(M, base[s * stride]);
+  for (int i = tid; i < nrec; i += MERGE_WAVES * 64) M = fmaxf(M, rec(i)[0]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) s_m[w] = M;
@@ -739,8 +868,8 @@ __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   float l = 0.f;
   if (M != -INFINITY) {
 #pragma unroll 4
-    for (int s = w; s < S; s += MERGE_WAVES) {
-      const float* p = base + s * stride;
+    for (int i = w; i < nrec; i += MERGE_WAVES) {
+      const float* p = rec(i);
       const float ms = p[0];
       const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
       l = __builtin_fmaf(p[1], wgt, l);
@@ -767,22 +896,127 @@ __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   }
 }
 
+// The partition of one call: tiles per sequence, their prefix sums, the
+// share size S and the sequence holding each share's first tile (plan
+// layout in DecodeArgs).  One workgroup; sequences in chunks of 1024.
+constexpr int PLAN_THREADS = 1024;
+
+template <bool KIVI>
+__device__ __forceinline__ int seq_tiles(const DecodeArgs& a, int b) {
+  const int L = min(max(a.ctx_lens[b], 0), a.max_blocks << a.log2_bs);
+  const int Lq = KIVI ? (L & ~31) : L;
+  return (Lq + TILE - 1) / TILE;
+}
+
+// Exclusive prefix sum over the workgroup; returns the workgroup total.
+__device__ __forceinline__ int block_scan(int v, int& excl, int* s_tot) {
+  const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) s_tot[w] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < PLAN_THREADS / 64; ++i) {
+    before += i < w ? s_tot[i] : 0;
+    all += s_tot[i];
+  }
+  __syncthreads();  // s_tot is reused by the next chunk
+  excl = before + incl - v;
+  return all;
+}
+
+template <bool KIVI>
+__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(DecodeArgs a) {
+  __shared__ int s_tot[PLAN_THREADS / 64];
+  const int tid = (int)threadIdx.x;
+  int* pre = a.plan + 1;
+  int carry = 0;
+  for (int c = 0; c < a.B; c += PLAN_THREADS) {
+    const int b = c + tid;
+    const int n = b < a.B ? seq_tiles<KIVI>(a, b) : 0;
+    int excl;
+    const int all = block_scan(n, excl, s_tot);
+    if (b < a.B) pre[b] = carry + excl;
+    carry += all;
+  }
+  const int total = carry;
+  int S = a.share_tiles;
+  if (S <= 0) S = max((total + a.num_shares - 1) / a.num_shares, AUTO_MIN_TILES);
+  if (tid == 0) {
+    pre[a.B] = total;
+    a.plan[0] = S;
+  }
+  // share i starts in the sequence whose tiles [P_b, P_b + n_b) hold i S
+  int* first = a.plan + 2 + a.B;
+  carry = 0;
+  for (int c = 0; c < a.B; c += PLAN_THREADS) {
+    const int b = c + tid;
+    const int n = b < a.B ? seq_tiles<KIVI>(a, b) : 0;
+    int excl;
+    const int all = block_scan(n, excl, s_tot);
+    const int p = carry + excl;
+    if (n > 0) {
+      const int i1 = min((p + n + S - 1) / S, a.num_shares);
+      for (int i = (p + S - 1) / S; i < i1; ++i) first[i] = b;
+    }
+    carry += all;
+  }
+}
+
 namespace {
 
+// Waves of decode_split_kernel<FK, FV, D> to run at once on the current
+// device: one per SIMD (4 per compute unit), or the occupancy if lower.
+// Every wave gets the same work, so two waves sharing a SIMD would hold the
+// whole launch back.  Cached per device.
 template <int FK, int FV, int D>
-hipError_t launch3(const DecodeArgs& a, hipStream_t st) {
-  // one wave per (sequence, split, KV head); see decode_split_kernel for the order
-  const uint32_t units = (uint32_t)(a.B * a.quant_splits);
-  const uint32_t wgs = ((units + 7) / 8) * 8 * (uint32_t)a.H;
-  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D>), dim3(wgs), dim3(64), 0, st, a);
+int resident_waves() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D>, 64, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int w = std::min(per_cu, 4) * cus;
+  if (dev >= 0 && dev < 64 && w > 0) cache[dev].store(w, std::memory_order_relaxed);
+  return w;
+}
+
+template <int FK, int FV, int D>
+hipError_t launch3(DecodeArgs a, hipStream_t st) {
+  if (a.share_tiles <= 0) {
+    // balanced: all waves the same length, all resident at once
+    const int w = resident_waves<FK, FV, D>();
+    if (w <= 0) return hipErrorInvalidDevice;
+    a.num_shares = min(a.max_shares, max(1, w / a.H));
+  } else {
+    a.num_shares = a.max_shares;
+  }
+  hipLaunchKernelGGL((plan_kernel<FK == F_KIVI>), dim3(1), dim3(PLAN_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // one wave per (share, KV head); see decode_split_kernel for the order
+  const uint32_t wgs = (((uint32_t)a.num_shares + 7) / 8) * 8 * (uint32_t)a.H;
+  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D>), dim3(wgs), dim3(64), 0, st, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (FK == F_KIVI) {
     hipLaunchKernelGGL((kivi_tail_kernel<D>), dim3((unsigned)a.B, (unsigned)a.H), dim3(64), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(MERGE_WAVES * 64), 0, st, a);
+  hipLaunchKernelGGL((merge_kernel<D, FK == F_KIVI>), dim3((unsigned)(a.B * a.Hq)), dim3(MERGE_WAVES * 64), 0, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -808,23 +1042,30 @@ hipError_t by_v(int fv, int D, const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int32_t choose_pages_per_split(const kvq_cache& c, int32_t batch, int32_t max_blocks, int32_t requested) {
-  // Tiles are 32 tokens, so a split is a whole number of tiles.
-  const int32_t unit = c.block_size >= 32 ? 1 : 32 / c.block_size;
-  int32_t pps = requested;
-  if (pps <= 0) {
-    // Enough workgroups to fill 256 CUs several times over, each holding
-    // a few thousand tokens per KV head.
-    const int64_t target_units = 1024;  // (sequence, split) pairs; each runs n_kv_heads waves
-    int64_t per_seq = (target_units + batch - 1) / batch;
-    if (per_seq < 1) per_seq = 1;
-    pps = (int32_t)((max_blocks + per_seq - 1) / per_seq);
-    const int32_t min_pps = (512 + c.block_size - 1) / c.block_size;  // >= 512 tokens per split
-    if (pps < min_pps) pps = min_pps;
+bool plan_decode(const kvq_cache& c, int32_t batch, int32_t n_q_heads, int32_t max_blocks, int32_t split_tokens,
+                 DecodePlan* p) {
+  const int64_t max_tok = (int64_t)max_blocks * c.block_size;  // tokens one block-table row addresses
+  if (max_tok >= (1ll << 30)) return false;
+  const int64_t bound = (int64_t)batch * ((max_tok + TILE - 1) / TILE);  // tiles of the call, at most
+  if (bound >= (1ll << 30)) return false;
+  int64_t shares;
+  if (split_tokens > 0) {
+    const int64_t S = ((int64_t)split_tokens + TILE - 1) / TILE;
+    shares = (bound + S - 1) / S;
+    p->share_tiles = (int32_t)S;
+  } else {
+    shares = std::min<int64_t>((AUTO_MAX_WAVES + c.n_kv_heads - 1) / c.n_kv_heads,
+                               (bound + AUTO_MIN_TILES - 1) / AUTO_MIN_TILES);
+    p->share_tiles = 0;
   }
-  pps = ((pps + unit - 1) / unit) * unit;
-  if (pps > MAX_PPS) pps = (MAX_PPS / unit) * unit;
-  return pps;
+  if (shares < 1) shares = 1;
+  if (shares > (1 << 24)) return false;
+  p->max_shares = (int32_t)shares;
+  const size_t ints = 2 + (size_t)batch + (size_t)shares;
+  p->plan_bytes = (ints * sizeof(int32_t) + 255) / 256 * 256;
+  p->records = (size_t)shares + batch + (c.k_dtype == KVQ_INT4_KIVI ? batch : 0);
+  p->bytes = p->plan_bytes + p->records * n_q_heads * ((size_t)c.head_dim + 2) * sizeof(float);
+  return true;
 }
 
 hipError_t launch_decode(const kvq_cache& c, const DecodeArgs& a, hipStream_t s) {

@@ -63,18 +63,38 @@ struct DecodeArgs {
   const uint16_t* k_tail;
   const uint16_t* v_tail;
   int32_t max_seqs;
-  int32_t pages_per_split;
-  int32_t num_splits;   // partial states per (sequence, query head), incl. the KIVI tail split
-  int32_t quant_splits;  // splits over quantized pages
-  float* part;  // (B, Hq, num_splits, D + 2) fp32: m, l, acc[D]
+  // Work partition.  The quantized tiles (32 tokens) of all sequences are
+  // numbered sequence by sequence; share i covers tiles [i S, (i + 1) S) and
+  // is processed by n_kv_heads waves, one per KV head.
+  int32_t share_tiles;  // S requested by the caller; 0 = balanced over num_shares
+  int32_t num_shares;   // shares launched (<= max_shares)
+  int32_t max_shares;   // shares the workspace was laid out for
+  // Workspace: plan ints, then the partial softmax records.
+  //   plan[0]              S used by this call
+  //   plan[1 + b]          first tile of sequence b (b = 0..B; plan[1 + B] = all tiles)
+  //   plan[2 + B + i]      sequence holding the first tile of share i
+  int32_t* plan;
+  // Record r, query head hq: part[(r Hq + hq) (D + 2) ...] = m, l, acc[D] (fp32).
+  // Records: share i's piece of sequence b -> i + b; KIVI fp16 tail of b -> max_shares + B + b.
+  float* part;
   uint16_t* out;  // fp16 (B, Hq, D)
 };
+
+// Workspace layout of one decode call (host side, no device needed).
+struct DecodePlan {
+  int32_t share_tiles;   // requested S (0 = balanced)
+  int32_t max_shares;    // upper bound on the shares any launch of this call uses
+  size_t plan_bytes;     // plan ints, rounded up to 256 bytes
+  size_t records;        // partial records
+  size_t bytes;          // total workspace
+};
+// Returns false if the sizes overflow the ranges the kernels index with.
+bool plan_decode(const kvq_cache& c, int32_t batch, int32_t n_q_heads, int32_t max_blocks, int32_t split_tokens,
+                 DecodePlan* plan);
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_write(const kvq_cache& c, const WriteArgs& a, hipStream_t s);
 hipError_t launch_decode(const kvq_cache& c, const DecodeArgs& a, hipStream_t s);
 
-// Context split used by decode for given sizes (shared by the workspace query).
-int32_t choose_pages_per_split(const kvq_cache& c, int32_t batch, int32_t max_blocks, int32_t requested);
 
 }  // namespace kvq

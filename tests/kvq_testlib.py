@@ -66,11 +66,11 @@ def write_both(inp: wl.Inputs, dev, orc, device):
     o.write(orc, to_np16(inp.k), to_np16(inp.v), inp.slot_mapping.numpy(), inp.seq_idx.numpy())
 
 
-def decode_both(inp: wl.Inputs, dev, orc, device, pages_per_split=0, sm_scale=0.0):
+def decode_both(inp: wl.Inputs, dev, orc, device, split_tokens=0, sm_scale=0.0):
     import quantized_paged_kv_write_amd as kvq
     ctx = torch.tensor(inp.ctx_lens, dtype=torch.int32)
     out = kvq.decode_attn(dev, inp.q.to(device), inp.block_table.to(device), ctx.to(device), sm_scale=sm_scale,
-                          pages_per_split=pages_per_split)
+                          split_tokens=split_tokens)
     torch.cuda.synchronize()
     ref = o.decode_attn(orc, to_np16(inp.q), inp.block_table.numpy(), inp.ctx_lens,
                         sm_scale=None if sm_scale == 0 else sm_scale)

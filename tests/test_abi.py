@@ -79,13 +79,25 @@ def test_write_argument_errors():
 
 
 def test_workspace_query():
-    rc, n = _ws(_cache(), batch=3, hq=4, mb=10, pps=4)
-    assert rc == OK and n == 3 * 4 * 3 * (128 + 2) * 4  # ceil(10/4) = 3 splits
+    # Layout: plan ints (2 + batch + shares, padded to 256 bytes), then
+    # (shares + batch [+ batch for KIVI tails]) records of n_q_heads x (D + 2) fp32.
+    # bs 16, mb 10: 160 tokens = 5 tiles per sequence, 15 for the call; shares of
+    # 64 tokens = 2 tiles -> 8 shares; 13 ints -> 256 bytes; 11 records.
+    rc, n = _ws(_cache(), batch=3, hq=4, mb=10, pps=64)
+    assert rc == OK and n == 256 + 11 * 4 * 130 * 4
+    # KIVI: 8 pages of 32 tokens = 8 tiles, one share of 8 tiles; records 1 + 1 + 1 tail.
     rc, n = _ws(_cache(k_dtype=4, block_size=32, max_seqs=1, k_zeros=FAKE, k_tail=FAKE, v_tail=FAKE),
-                batch=1, hq=2, mb=8, pps=8)
-    assert rc == OK and n == 1 * 2 * 2 * 130 * 4  # one split + the fp16-tail split
+                batch=1, hq=2, mb=8, pps=256)
+    assert rc == OK and n == 256 + 3 * 2 * 130 * 4
+    # automatic: min(ceil(4096 / H), ceil(tiles / 4)) shares = min(2048, 250); 254 ints -> 1024 bytes
+    rc, n = _ws(_cache(), batch=2, hq=4, mb=1000, pps=0)
+    assert rc == OK and n == 1024 + 252 * 4 * 130 * 4
+    # a split size that is not a multiple of 32 rounds up to whole tiles
+    assert _ws(_cache(), batch=3, hq=4, mb=10, pps=33) == _ws(_cache(), batch=3, hq=4, mb=10, pps=64)
     assert _ws(_cache(), mb=0)[0] == INVALID
     assert _ws(_cache(), pps=-1)[0] == INVALID
+    assert _ws(_cache(), mb=1 << 26)[0] == SHAPE            # 2^30 tokens in one block-table row
+    assert _ws(_cache(), batch=1 << 25, mb=64)[0] == SHAPE  # 2^30 tiles in the call
 
 
 def test_decode_argument_errors():
@@ -101,6 +113,7 @@ def test_decode_argument_errors():
     assert dec(scale=float("nan")) == INVALID
     assert dec(ws=None) == WORKSPACE
     assert dec(wsb=16) == WORKSPACE
+    assert dec(ws=ctypes.c_void_p(0x1004)) == WORKSPACE  # not 16-byte aligned
     assert dec(q=None) == INVALID
     assert dec(batch=0) == OK            # empty batch: nothing to do
     assert dec(mb=0) == INVALID

@@ -63,14 +63,33 @@ def test_decode_block_sizes(bs):
 def test_decode_split_invariance_and_determinism(kf, vf):
     inp, dev, orc = _setup(kf, vf, 128, [1000, 2047, 65], seed=3)
     outs = []
-    for pps in (0, 2, 4, 8, 30):
-        got, ref = decode_both(inp, dev, orc, DEV, pages_per_split=pps)
-        assert decode_error(got, ref)[0] <= ATOL, pps
+    # automatic, one tile per share, shares that end inside a sequence, one share per sequence or more
+    for st in (0, 32, 96, 256, 1000, 4096):
+        got, ref = decode_both(inp, dev, orc, DEV, split_tokens=st)
+        assert decode_error(got, ref)[0] <= ATOL, st
         outs.append(got)
     for a in outs[1:]:
         assert np.max(np.abs(a - outs[0])) <= 2 * ATOL
-    again, _ = decode_both(inp, dev, orc, DEV, pages_per_split=4)
+    again, _ = decode_both(inp, dev, orc, DEV, split_tokens=96)
     assert np.array_equal(again, outs[2])  # run-to-run bitwise
+
+
+@pytest.mark.parametrize("kf,vf", [("int8", "int8"), ("fp8_e4m3fn", "int4_g32"), ("int4_kivi", "int4_g32")])
+@pytest.mark.parametrize("split_tokens", [0, 32, 4096])
+def test_decode_many_short_sequences(kf, vf, split_tokens):
+    # 150 sequences of 0..70 tokens: shares run across many sequence ends
+    # (4096 tokens = 128 tiles holds more than 64 sequences, so a wave walks
+    # past its first window of sequence bounds), with empty sequences between.
+    g = np.random.default_rng(11)
+    ctx = [int(x) for x in g.integers(0, 71, size=150)]
+    for i in (0, 1, 2, 40, 41, 149):
+        ctx[i] = 0
+    inp, dev, orc = _setup(kf, vf, 64, ctx, seed=21, extra=5)
+    got, ref = decode_both(inp, dev, orc, DEV, split_tokens=split_tokens)
+    err, err16 = decode_error(got, ref)
+    assert err <= ATOL, (err, err16)
+    for i in (0, 1, 2, 40, 41, 149):
+        assert np.all(got[i] == 0)
 
 
 def test_decode_custom_sm_scale():
