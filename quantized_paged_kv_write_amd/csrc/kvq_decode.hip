@@ -8,24 +8,30 @@
 // glossary, GQA).
 //
 // How (MI355X design, not the pages' Hopper kernels):
-//  * Split-K over the context: a workgroup owns (context split, up to 8 KV
-//    heads, sequence); wave w handles one KV head and all G query heads that
-//    read it.  Splits are whole pages, so ragged batches stay balanced; a
-//    second kernel merges the per-split softmax states.
-//  * Tiles of 32 tokens.  Scores S^T = K Q^T run on the matrix cores
-//    (v_mfma_f32_16x16x32_f16): the 8-bit/4-bit key codes become exact fp16
-//    operands (q is fp16 already), so the products are exact and only the
-//    fp32 accumulation rounds; the per-token key scale is applied to the
-//    fp32 score afterwards (q.k_hat = s_k (q.codes)).
-//  * Values: the tile's value pages are staged in LDS and read back with the
-//    8-bit transpose read (ds_read_b64_tr_b8), which hands each lane one
-//    channel (INT8/FP8) or one channel pair (INT4) of 8 tokens, the layout
-//    the matrix core wants for P V.  Value codes become exact bf16 operands;
-//    the probabilities times the per-token value scale are split into two
-//    bf16 terms (hi + lo, relative error <= 2^-18), so P V costs two MFMAs per
-//    16 channels and keeps fp32-level accuracy.
+//  * Work partition: the quantized 32-token tiles of all sequences are
+//    numbered sequence after sequence and cut into equal shares (a small plan
+//    kernel computes the cut on the device).  A share is read by one wave per
+//    KV head, which handles all G query heads reading that head.  By default
+//    there is one wave per SIMD, all resident at once with the same amount
+//    of work, so no wave waits for a later round.  A wave writes one partial
+//    softmax state per sequence piece it covers; a merge kernel combines them.
+//  * Data path: a tile's key and value rows, scales and block ids are loaded
+//    into registers several tiles ahead (the compiler tracks the loads, and
+//    every step issues the same loads so its waits stay exact), then stored
+//    into one LDS stage in a swizzled layout and read back as MFMA operands.
+//  * Scores S^T = K Q^T run on the matrix cores (v_mfma_f32_16x16x32_f16):
+//    the 8-bit/4-bit key codes become exact fp16 operands (q is fp16
+//    already), so the products are exact and only the fp32 accumulation
+//    rounds; the per-token key scale is applied to the fp32 score afterwards
+//    (q.k_hat = s_k (q.codes)).
+//  * Values are read back with the 8-bit transpose read (ds_read_b64_tr_b8),
+//    which hands each lane one channel (INT8/FP8) or one channel pair (INT4)
+//    of 8 tokens, the layout the matrix core wants for P V.  Value codes
+//    become exact bf16 operands; the probabilities times the per-token value
+//    scale are split into two bf16 terms (hi + lo, relative error <= 2^-18),
+//    so P V costs two MFMAs per 16 channels and keeps fp32-level accuracy.
 //  * Online softmax in the log2 domain (q pre-multiplied by sm_scale*log2 e),
-//    fp32 throughout; each split stores (m, l, acc[D]).
+//    fp32 throughout; each piece stores (m, l, acc[D]).
 #include <math.h>
 
 #include <algorithm>
@@ -191,38 +197,14 @@ __device__ __forceinline__ void split_bf16x2(f2 x, uint32_t& hi, uint32_t& lo, f
 }
 
 // Flat row index (slot * H + h) of token t0 + t of a sequence and whether it
-// is live: in the context and on a page whose block id is valid.  ids[t] is
-// the block id of that token's page (copied into LDS ahead of the tile).
-__device__ __forceinline__ uint32_t tile_row(const DecodeArgs& a, const int32_t* ids, int t, int t0, int tok_end,
-                                             int h, bool& live) {
+// is live: in the context and on a page whose block id (bid) is valid.
+__device__ __forceinline__ uint32_t tile_row(const DecodeArgs& a, int bid, int t, int t0, int tok_end, int h,
+                                             bool& live) {
   const int tt = t0 + t;
   const int lbs = a.log2_bs;
-  const bool in = tt < tok_end;
-  const int bid = in ? ids[t] : 0;
-  live = in && bid >= 0 && bid < a.nb;
+  live = tt < tok_end && bid >= 0 && bid < a.nb;
   const uint32_t blk = live ? (uint32_t)bid : 0u;
   return ((blk << lbs) + (uint32_t)(tt & ((1 << lbs) - 1))) * (uint32_t)a.H + (uint32_t)h;
-}
-
-// ---- asynchronous copies global -> LDS ----------------------------------
-// global_load_lds_dword{,x4}: lane l of the instruction writes its 4 (16)
-// bytes at LDS address m0 + 4 l (16 l).  The loop below issues every global
-// read of a tile this way, so nothing it waits on lives in registers; the
-// compiler does not track these transfers, so the loop waits for them with
-// explicit s_waitcnt vmcnt(N) (loads complete in issue order).
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_addr), "v"(src) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(lds_addr), "v"(src) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // Swizzles of the 16-byte chunks of a tile row in LDS: chunk (row, col)
@@ -253,96 +235,108 @@ struct Stage {
   // byte offsets inside a stage
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = KT;
-  static constexpr int OFF_S = KT + VT;              // raw scale dwords (see issue_tile)
+  static constexpr int OFF_S = KT + VT;              // raw scale dwords (see load_tile)
   static constexpr int OFF_M = OFF_S + 4 * TILE * (1 + NGD);
   static constexpr int BYTES = OFF_M + KIVI_BYTES;
-  // DMA instructions per tile: keys, values, scales, KIVI page metadata
-  static constexpr int NDMA = NLK + NLV + NGD + (FK == F_KIVI ? 1 : 0);
-  // Pipeline depth: NST stages (NST - 1 tiles in flight while one is
-  // computed), as many as fit beside the other LDS arrays in a quarter of a
-  // CU's 160 KB, so one wave per SIMD fits; 3 to 6, and the copies of
-  // NST - 2 tiles must fit the 6-bit vmcnt.
-  static constexpr int LDS_WAVE = 160 * 1024 / 4;
-  static constexpr int OTHER = 8 * TILE * 4 + TILE * 4 + TILE * VS::NG * 4;  // id ring, scale arrays
-  static constexpr int NST_FIT = (LDS_WAVE - OTHER) / BYTES;
-  static constexpr int NST_VM = 63 / NDMA + 2;
-  static constexpr int NST = NST_FIT < 3 ? 3 : (NST_FIT > 6 ? (NST_VM < 6 ? NST_VM : 6) : (NST_VM < NST_FIT ? NST_VM : NST_FIT));
-  static constexpr int RING = NST <= 4 ? 4 : 8;  // block-id ring slots (power of two >= NST)
+  // Registers one lane needs for a tile in flight (TileRegs); NS tiles are
+  // held at once (NS - 1 in flight while one is stored to LDS and computed),
+  // 2 to 4 within about 136 registers.
+  static constexpr int TILE_REGS = 4 * (NLK + NLV) + NGD + (FK == F_KIVI ? 4 : 0);
+  static constexpr int NS_FIT = 136 / TILE_REGS;
+  static constexpr int NS = NS_FIT < 2 ? 2 : (NS_FIT > 4 ? 4 : NS_FIT);
 };
 
-// s_waitcnt vmcnt(k * N) for a run-time k in [0, KMAX].
-template <int N, int KMAX>
-__device__ __forceinline__ void wait_groups(int k) {
-  if constexpr (KMAX > 0) {
-    if (k >= KMAX) {
-      wait_vmcnt<KMAX * N>();
-      return;
-    }
-    wait_groups<N, KMAX - 1>(k);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
-// Start the copy of one tile (keys, values, per-token scale dwords; KIVI
-// page scale/zero) into LDS stage `st`; returns the live-token mask (bit t
-// and t + 32: token t0 + t is in the context on a valid page).  Masked rows
-// copy from the start of the buffer; those bytes are never used unmasked.
+// One tile's global data in registers: the 16-byte chunks of its key and
+// value rows, its scale dwords and (KIVI) its page's scales and zeros.  Each
+// lane holds exactly what it later stores into the LDS stage.
 template <int FK, int FV, int D>
-__device__ __forceinline__ uint64_t issue_tile(const DecodeArgs& a, const int32_t* ids, int t0, int tok_end, int h,
-                                               uint8_t* st) {
+struct TileRegs {
+  using S = Stage<FK, FV, D>;
+  u4 k[S::NLK];
+  u4 v[S::NLV];
+  uint32_t s[S::NGD];
+  u4 m;  // KIVI only
+};
+
+// Load one tile (keys, values, per-token scale dwords; KIVI page scales and
+// zeros) into registers; bid is the block id of token lane % 32's page.
+// Returns the live-token mask (bit t and t + 32: token t0 + t is in the
+// context on a valid page).  Every load is issued by every lane, so each
+// tile costs the same number of loads: masked rows and idle lanes read the
+// start of the buffer, and those bytes are never used unmasked.
+template <int FK, int FV, int D>
+__device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int t0, int tok_end, int h,
+                                              TileRegs<FK, FV, D>& r) {
   using S = Stage<FK, FV, D>;
   using KS = KShape<FK, D>;
   using VS = VShape<FV, D>;
   constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
   const int lane = (int)threadIdx.x;
-  const uint32_t base = lds_addr(st);
   // row index of token `lane & 31`, or ~0 when masked; shared with shuffles
   bool live;
-  const uint32_t r_own = tile_row(a, ids, lane & 31, t0, tok_end, h, live);
+  const uint32_t r_own = tile_row(a, bid, lane & 31, t0, tok_end, h, live);
   const uint64_t live_mask = __ballot(live);
   const uint32_t rl = live ? r_own : ~0u;
 #pragma unroll
   for (int i = 0; i < S::NLK; ++i) {
-    const int p = 64 * i + lane;  // LDS slot of this lane
+    const int p = 64 * i + lane;  // LDS chunk slot this lane stores
     const int row = p / CHK;
     const int col = (p % CHK) ^ kswz<CHK>(row);
-    const uint32_t r = (uint32_t)__shfl((int)rl, row);
-    dma16(a.k_codes + (r != ~0u ? (size_t)r * KS::RB + col * 16 : 0), base + S::OFF_K + 1024 * i);
+    const uint32_t rr = (uint32_t)__shfl((int)rl, row);
+    r.k[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u4*>(a.k_codes + (rr != ~0u ? (size_t)rr * KS::RB + col * 16 : 0)));
   }
 #pragma unroll
   for (int i = 0; i < S::NLV; ++i) {
     const int p = 64 * i + lane;
     const int row = p / VS::CH;
     const int col = (p % VS::CH) ^ vswz<VS::CH>(row);
-    const uint32_t r = (uint32_t)__shfl((int)rl, row);
-    dma16(a.v_codes + (r != ~0u ? (size_t)r * VS::RB + col * 16 : 0), base + S::OFF_V + 1024 * i);
+    const uint32_t rr = (uint32_t)__shfl((int)rl, row);
+    r.v[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u4*>(a.v_codes + (rr != ~0u ? (size_t)rr * VS::RB + col * 16 : 0)));
   }
   // scale dwords (LDS dword index): [t] the dword holding token t's key
   // scale, [32 + t] the first value-scale dword of token t, [32 + 32 k + t]
-  // its value-scale dword k >= 1 (INT4 groups)
+  // its value-scale dword k >= 1 (INT4 groups; lanes < 32)
   {
     const uint16_t* src;
     if (lane < 32) src = FK == F_KIVI ? a.v_scales : a.k_scales + (live ? (r_own & ~1u) : 0);
     else src = a.v_scales + (live ? ((size_t)r_own * VS::NG & ~(size_t)1) : 0);
-    dma4(src, base + S::OFF_S);
+    r.s[0] = *reinterpret_cast<const uint32_t*>(src);
   }
 #pragma unroll
-  for (int g = 1; g < S::NGD; ++g) {
-    if (lane < 32) dma4(a.v_scales + (live ? (size_t)r_own * VS::NG + 2 * g : 0), base + S::OFF_S + 128 + 128 * g);
-  }
+  for (int g = 1; g < S::NGD; ++g)
+    r.s[g] = *reinterpret_cast<const uint32_t*>(a.v_scales +
+                                                (live && lane < 32 ? (size_t)r_own * VS::NG + 2 * g : 0));
   if constexpr (FK == F_KIVI) {
     // the tile is one page (block_size 32): its D scales and D zeros
     constexpr int CH = D * 2 / 16;
     const uint32_t r0 = (uint32_t)__shfl((int)rl, 0);
-    const bool ok = r0 != ~0u;
+    const bool ok = r0 != ~0u && lane < 2 * CH;
     const size_t mrow = ((size_t)(r0 / (32u * (uint32_t)a.H)) * a.H + h) * D;
-    if (lane < 2 * CH) {
-      const uint16_t* src = (lane < CH ? a.k_scales : a.k_zeros) + (ok ? mrow + 8 * (lane % CH) : 0);
-      dma16(src, base + S::OFF_M);
-    }
+    const uint16_t* src = (lane < CH ? a.k_scales : a.k_zeros) + (ok ? mrow + 8 * (lane % CH) : 0);
+    r.m = *reinterpret_cast<const u4*>(src);
   }
   return live_mask;
+}
+
+// Store a loaded tile into the LDS stage `st` (layout of Stage).
+template <int FK, int FV, int D>
+__device__ __forceinline__ void store_tile(const TileRegs<FK, FV, D>& r, uint8_t* st) {
+  using S = Stage<FK, FV, D>;
+  const int lane = (int)threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < S::NLK; ++i) reinterpret_cast<u4*>(st + S::OFF_K)[64 * i + lane] = r.k[i];
+#pragma unroll
+  for (int i = 0; i < S::NLV; ++i) reinterpret_cast<u4*>(st + S::OFF_V)[64 * i + lane] = r.v[i];
+  uint32_t* sd = reinterpret_cast<uint32_t*>(st + S::OFF_S);
+  sd[lane] = r.s[0];
+#pragma unroll
+  for (int g = 1; g < S::NGD; ++g)
+    if (lane < 32) sd[32 + 32 * g + lane] = r.s[g];
+  if constexpr (FK == F_KIVI) {
+    if (lane < D / 4) reinterpret_cast<u4*>(st + S::OFF_M)[lane] = r.m;
+  }
 }
 
 // Sequence b of the tile numbering owns tiles [lo, hi) and holds lq tokens in
@@ -386,18 +380,12 @@ __device__ __forceinline__ void seek(SeqCursor& c, const DecodeArgs& a, int x) {
   c.lq = rdlane(c.win_lq, c.b - c.wb);
 }
 
-// Copy the block ids of the 32 tokens of tile x (of the cursor's sequence)
-// into LDS: lane t < 32 fetches the block-table entry of token t's page.
-template <int RING>
-__device__ __forceinline__ void issue_ids(const DecodeArgs& a, const SeqCursor& c, int x, uint32_t ring) {
-  const int lane = (int)threadIdx.x;
-  if (lane < TILE) {
-    const int tok = TILE * (x - c.lo) + lane;
-    const int pg = tok < c.lq ? tok >> a.log2_bs : 0;
-    // slot x % RING of the ring; wave-uniform (it follows the tile counter)
-    dma4(a.block_table + (size_t)c.b * a.max_blocks + pg,
-         __builtin_amdgcn_readfirstlane(ring + (uint32_t)(x & (RING - 1)) * (TILE * 4)));
-  }
+// Block id of the page of token x * 32 + lane % 32 of the cursor's sequence
+// (entry 0 of its row past the sequence's end; those tokens are masked).
+__device__ __forceinline__ int load_ids(const DecodeArgs& a, const SeqCursor& c, int x) {
+  const int tok = TILE * (x - c.lo) + ((int)threadIdx.x & 31);
+  const int pg = tok < c.lq ? tok >> a.log2_bs : 0;
+  return a.block_table[(size_t)c.b * a.max_blocks + pg];
 }
 
 template <int FK, int FV, int D>
@@ -407,11 +395,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using ST = Stage<FK, FV, D>;
   constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
   constexpr int NCS = FV == F_INT4 ? VS::NG : 1;  // bias-correction sums kept per value group
-  constexpr int NST = ST::NST, RING = ST::RING;
-  // NST stages: tile x is computed while tiles x + 1 .. x + NST - 1 are in flight
-  __shared__ __attribute__((aligned(16))) uint8_t s_st[NST][ST::BYTES];
-  // block ids of the tokens of tile x in slot x % RING (fetched NST - 1 tiles ahead of the tile)
-  __shared__ __attribute__((aligned(16))) int32_t s_ids[RING][TILE];
+  // NS tiles held in registers: tile x is stored to LDS and computed while
+  // tiles x + 1 .. x + P are in flight
+  constexpr int NS = ST::NS, P = NS - 1;
+  constexpr int L = NS > 2 ? 2 : 1;  // block ids are loaded L tiles ahead of their tile
+  __shared__ __attribute__((aligned(16))) uint8_t s_st[ST::BYTES];
   // this tile's scales as fp32: key scale x sm_scale x log2 e, value scales
   __shared__ __attribute__((aligned(16))) float s_fk[TILE];
   __shared__ __attribute__((aligned(16))) float s_fv[TILE * VS::NG];
@@ -466,28 +454,31 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int tbase = ST::OFF_V + trow * VS::RB + 8 * (n & 1);
   const int tswz = vswz<VS::CH>(trow);
 
-  // Copies are issued in groups, one per tile y: the block ids of tile
-  // y + NST - 1, then tile y itself (NDMA copies).  Loads complete in issue
-  // order, so once at most k NDMA copies are outstanding, with k the number
-  // of groups issued after tile y's, tile y and every earlier id copy are in
-  // LDS (the id copies of the later groups only make the wait longer).
-  const uint32_t ring = lds_addr(&s_ids[0][0]);
-  for (int y = x_begin; y < x_begin + NST - 1 && y < x_end; ++y) {
-    seek<FK>(cd, a, y);
-    issue_ids<RING>(a, cd, y, ring);
-  }
-  wait_vmcnt<0>();
-  auto issue_group = [&](int y, uint8_t* st) __attribute__((always_inline)) -> uint64_t {
-    if (y + NST - 1 < x_end) {
-      seek<FK>(cd, a, y + NST - 1);
-      issue_ids<RING>(a, cd, y + NST - 1, ring);
-    }
-    seek<FK>(ci, a, y);
-    return issue_tile<FK, FV, D>(a, s_ids[y & (RING - 1)], TILE * (y - ci.lo), ci.lq, h, st);
-  };
-  uint64_t live[NST];
+  // Loads are issued in groups, one per tile y: the block ids of tile y + L,
+  // then tile y itself (with the ids loaded L groups earlier).  Every group
+  // issues the same loads, tiles past the share's end reload its last tile,
+  // so the compiler's load counters are exact and only wait for the tile
+  // being stored.  Registers rotate over NS slots: slot (y - x_begin) % NS.
+  TileRegs<FK, FV, D> regs[NS];
+  uint64_t live[NS];
+  int ids[NS];
+  const int x_last = x_end - 1;
 #pragma unroll
-  for (int i = 0; i < NST - 1; ++i) live[i] = x_begin + i < x_end ? issue_group(x_begin + i, s_st[i]) : 0;
+  for (int i = 0; i < L; ++i) {
+    const int y = min(x_begin + i, x_last);
+    seek<FK>(cd, a, y);
+    ids[i] = load_ids(a, cd, y);
+  }
+  auto load_group = [&](int y, int& ids_out, int ids_in, TileRegs<FK, FV, D>& r) __attribute__((always_inline)) {
+    const int yi = min(y + L, x_last);
+    seek<FK>(cd, a, yi);
+    ids_out = load_ids(a, cd, yi);
+    const int yc = min(y, x_last);
+    seek<FK>(ci, a, yc);
+    return load_tile<FK, FV, D>(a, ids_in, TILE * (yc - ci.lo), ci.lq, h, r);
+  };
+#pragma unroll
+  for (int i = 0; i < P; ++i) live[i] = load_group(x_begin + i, ids[(i + L) % NS], ids[i], regs[i]);
 
   // Write the softmax state of sequence b's piece (record share + b) and
   // reset it for the next piece.
@@ -543,17 +534,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     piece_start = true;
   };
 
-  int x = x_begin;
-  // One tile; S_ is the LDS stage holding it.
-  auto step = [&](auto stage) __attribute__((always_inline)) -> bool {
+  int xr = x_begin;  // first tile of the current round
+  // Step S_ of a round: tile x = xr + S_, held in register slot S_.
+  auto step = [&](auto stage) __attribute__((always_inline)) {
     constexpr int S_ = decltype(stage)::value;
-    if (x >= x_end) return false;
-    uint8_t* cur = s_st[S_];
-    // ---- wait for this tile's copies (the next group may stay in flight) ----
-    wait_groups<ST::NDMA, NST - 2>(x_end - 1 - x);
+    const int x = xr + S_;
+    // ---- start tile x + P ---------------------------------------------------
+    live[(S_ + P) % NS] = load_group(x + P, ids[(S_ + P + L) % NS], ids[(S_ + P) % NS], regs[(S_ + P) % NS]);
+    if (x >= x_end) return;
+    // ---- tile x into LDS ------------------------------------------------------
+    uint8_t* cur = s_st;
+    store_tile<FK, FV, D>(regs[S_], cur);
     const uint64_t live_mask = live[S_];
-    // ---- start tile x + NST - 1 ---------------------------------------------
-    if (x + NST - 1 < x_end) live[(S_ + NST - 1) % NST] = issue_group(x + NST - 1, s_st[(S_ + NST - 1) % NST]);
     // ---- first tile of a sequence's piece: its query operand ---------------
     if (piece_start) {
       const uint16_t* qrow = a.q + ((size_t)cc.b * a.Hq + hq0 + (n < G ? n : 0)) * D;
@@ -773,14 +765,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       write_piece(cc.b);
       if (x + 1 < x_end) seek<FK>(cc, a, x + 1);
     }
-    ++x;
-    return true;
   };
-  auto round = [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) -> bool {
-    return (step(std::integral_constant<int, I>{}) && ...);
+  auto round = [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) {
+    (step(std::integral_constant<int, I>{}), ...);
   };
-  while (round(std::make_integer_sequence<int, NST>{})) {
-  }
+  for (; xr < x_end; xr += NS) round(std::make_integer_sequence<int, NS>{});
 }
 
 // KIVI fp16 tail: the last ctx_len % 32 tokens of each sequence, keys and
