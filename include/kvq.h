@@ -134,7 +134,8 @@ int kvq_write(const kvq_cache* cache, const void* k, const void* v,
  * states of the pieces the context is cut into.  Depends only on the
  * arguments, not on the device or on ctx_lens.  KVQ_ERR_SHAPE if
  * max_blocks_per_seq * block_size reaches 2^30 tokens or the call's tile
- * count (batch x that / 32) reaches 2^30. */
+ * count (batch x that / (32 / HP)) reaches 2^30, or n_q_heads is not a
+ * multiple of n_kv_heads. */
 int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch,
                                int32_t n_q_heads, int32_t max_blocks_per_seq,
                                int32_t split_tokens, size_t* bytes);
@@ -151,13 +152,16 @@ int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch,
  *                last ctx_len % 32 tokens are read from tail row b (the batch
  *                row).
  *   sm_scale     softmax scale; 0 means 1/sqrt(head_dim).
- *   split_tokens work partition.  The quantized tokens of all sequences,
- *                in 32-token tiles, are numbered sequence after sequence and
- *                cut into equal shares, each read by one wave per KV head
+ *   split_tokens work partition.  One wave reads HP consecutive KV heads
+ *                (HP = 4, 2 or 1: the most with HP x n_q_heads/n_kv_heads
+ *                <= 16 that divides n_kv_heads; 1 for KVQ_INT4_KIVI keys), in
+ *                tiles of 32 (token, head) rows = 32 / HP tokens.  The tiles
+ *                of all sequences are numbered sequence after sequence and
+ *                cut into equal shares, each read by n_kv_heads / HP waves
  *                (a share may end in one sequence and go on in the next).
  *                0 = automatic: as many shares as fill the GPU's resident
  *                waves once (at least 4 tiles each); > 0 = shares of
- *                ceil(split_tokens / 32) tiles.
+ *                ceil(split_tokens / (32 / HP)) tiles.
  *   out          fp16 (batch, n_q_heads, D), written.
  *   workspace    device scratch of at least kvq_decode_workspace_bytes()
  *                for the same arguments, 16-byte aligned; its contents on

@@ -144,6 +144,7 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_
   a.k_tail = static_cast<const uint16_t*>(cache->k_tail);
   a.v_tail = static_cast<const uint16_t*>(cache->v_tail);
   a.max_seqs = cache->max_seqs;
+  a.hp_log2 = heads_per_wave_log2(*cache, G);
   a.share_tiles = p.share_tiles;
   a.max_shares = p.max_shares;
   a.num_shares = p.max_shares;  // the launcher may use fewer

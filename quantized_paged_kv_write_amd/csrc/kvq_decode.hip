@@ -196,15 +196,18 @@ __device__ __forceinline__ void split_bf16x2(f2 x, uint32_t& hi, uint32_t& lo, f
   used = fh + f2{__builtin_bit_cast(float, lb << 16), __builtin_bit_cast(float, lb & 0xFFFF0000u)};
 }
 
-// Flat row index (slot * H + h) of token t0 + t of a sequence and whether it
-// is live: in the context and on a page whose block id (bid) is valid.
-__device__ __forceinline__ uint32_t tile_row(const DecodeArgs& a, int bid, int t, int t0, int tok_end, int h,
+// Tile row rho (0..31) is token t0 + rho / HP of the sequence, KV head
+// h0 + rho % HP (HP = 2^hp_log2 heads per wave).  Returns its flat row index
+// (slot * H + head) and whether it is live: in the context and on a page
+// whose block id (bid) is valid.
+__device__ __forceinline__ uint32_t tile_row(const DecodeArgs& a, int bid, int rho, int t0, int tok_end, int h0,
                                              bool& live) {
-  const int tt = t0 + t;
+  const int tt = t0 + (rho >> a.hp_log2);
   const int lbs = a.log2_bs;
   live = tt < tok_end && bid >= 0 && bid < a.nb;
   const uint32_t blk = live ? (uint32_t)bid : 0u;
-  return ((blk << lbs) + (uint32_t)(tt & ((1 << lbs) - 1))) * (uint32_t)a.H + (uint32_t)h;
+  const uint32_t head = (uint32_t)(h0 + (rho & ((1 << a.hp_log2) - 1)));
+  return ((blk << lbs) + (uint32_t)(tt & ((1 << lbs) - 1))) * (uint32_t)a.H + head;
 }
 
 // Swizzles of the 16-byte chunks of a tile row in LDS: chunk (row, col)
@@ -238,12 +241,15 @@ struct Stage {
   static constexpr int OFF_S = KT + VT;              // raw scale dwords (see load_tile)
   static constexpr int OFF_M = OFF_S + 4 * TILE * (1 + NGD);
   static constexpr int BYTES = OFF_M + KIVI_BYTES;
-  // Registers one lane needs for a tile in flight (TileRegs); NS tiles are
-  // held at once (NS - 1 in flight while one is stored to LDS and computed),
-  // 2 to 4 within about 136 registers.
-  static constexpr int TILE_REGS = 4 * (NLK + NLV) + NGD + (FK == F_KIVI ? 4 : 0);
+  // Waves per SIMD and register slots for tiles.  Head dims up to 128 run
+  // two waves per SIMD (each within 256 registers), so one wave's compute
+  // hides the other's waits; a wave then holds NS = 2 tiles (one in flight
+  // while one is stored to LDS and computed).  Head dim 256 runs one wave per
+  // SIMD with up to 4 tiles held, within about 136 registers.
+  static constexpr int WPE = D <= 128 ? 2 : 1;
+  static constexpr int TILE_REGS = 4 * (NLK + NLV) + NGD + 1 + (FK == F_KIVI ? 4 : 0);
   static constexpr int NS_FIT = 136 / TILE_REGS;
-  static constexpr int NS = NS_FIT < 2 ? 2 : (NS_FIT > 4 ? 4 : NS_FIT);
+  static constexpr int NS = WPE == 2 ? 2 : (NS_FIT < 2 ? 2 : (NS_FIT > 4 ? 4 : NS_FIT));
 };
 
 // One tile's global data in registers: the 16-byte chunks of its key and
@@ -255,6 +261,7 @@ struct TileRegs {
   u4 k[S::NLK];
   u4 v[S::NLV];
   uint32_t s[S::NGD];
+  uint32_t par;  // bit rho: row rho's 16-bit scale is the high half of its dword
   u4 m;  // KIVI only
 };
 
@@ -265,7 +272,7 @@ struct TileRegs {
 // tile costs the same number of loads: masked rows and idle lanes read the
 // start of the buffer, and those bytes are never used unmasked.
 template <int FK, int FV, int D>
-__device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int t0, int tok_end, int h,
+__device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int t0, int tok_end, int h0,
                                               TileRegs<FK, FV, D>& r) {
   using S = Stage<FK, FV, D>;
   using KS = KShape<FK, D>;
@@ -274,7 +281,7 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
   const int lane = (int)threadIdx.x;
   // row index of token `lane & 31`, or ~0 when masked; shared with shuffles
   bool live;
-  const uint32_t r_own = tile_row(a, bid, lane & 31, t0, tok_end, h, live);
+  const uint32_t r_own = tile_row(a, bid, lane & 31, t0, tok_end, h0, live);
   const uint64_t live_mask = __ballot(live);
   const uint32_t rl = live ? r_own : ~0u;
 #pragma unroll
@@ -295,14 +302,16 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
     r.v[i] = __builtin_nontemporal_load(
         reinterpret_cast<const u4*>(a.v_codes + (rr != ~0u ? (size_t)rr * VS::RB + col * 16 : 0)));
   }
-  // scale dwords (LDS dword index): [t] the dword holding token t's key
-  // scale, [32 + t] the first value-scale dword of token t, [32 + 32 k + t]
-  // its value-scale dword k >= 1 (INT4 groups; lanes < 32)
+  // scale dwords (LDS dword index): [rho] the dword holding row rho's key
+  // scale, [32 + rho] the first value-scale dword of row rho, [32 + 32 k +
+  // rho] its value-scale dword k >= 1 (INT4 groups; lanes < 32).  A lone
+  // fp16 scale sits in half (flat row & 1) of its dword (par).
   {
     const uint16_t* src;
     if (lane < 32) src = FK == F_KIVI ? a.v_scales : a.k_scales + (live ? (r_own & ~1u) : 0);
     else src = a.v_scales + (live ? ((size_t)r_own * VS::NG & ~(size_t)1) : 0);
     r.s[0] = *reinterpret_cast<const uint32_t*>(src);
+    r.par = (uint32_t)__ballot(live && (r_own & 1u));
   }
 #pragma unroll
   for (int g = 1; g < S::NGD; ++g)
@@ -313,7 +322,7 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
     constexpr int CH = D * 2 / 16;
     const uint32_t r0 = (uint32_t)__shfl((int)rl, 0);
     const bool ok = r0 != ~0u && lane < 2 * CH;
-    const size_t mrow = ((size_t)(r0 / (32u * (uint32_t)a.H)) * a.H + h) * D;
+    const size_t mrow = ((size_t)(r0 / (32u * (uint32_t)a.H)) * a.H + h0) * D;
     const uint16_t* src = (lane < CH ? a.k_scales : a.k_zeros) + (ok ? mrow + 8 * (lane % CH) : 0);
     r.m = *reinterpret_cast<const u4*>(src);
   }
@@ -380,16 +389,17 @@ __device__ __forceinline__ void seek(SeqCursor& c, const DecodeArgs& a, int x) {
   c.lq = rdlane(c.win_lq, c.b - c.wb);
 }
 
-// Block id of the page of token x * 32 + lane % 32 of the cursor's sequence
-// (entry 0 of its row past the sequence's end; those tokens are masked).
+// Block id of the page of tile row lane % 32 of tile x of the cursor's
+// sequence (entry 0 of its row past the sequence's end; those rows are masked).
 __device__ __forceinline__ int load_ids(const DecodeArgs& a, const SeqCursor& c, int x) {
-  const int tok = TILE * (x - c.lo) + ((int)threadIdx.x & 31);
+  const int tok = ((TILE * (x - c.lo)) >> a.hp_log2) + (((int)threadIdx.x & 31) >> a.hp_log2);
   const int pg = tok < c.lq ? tok >> a.log2_bs : 0;
   return a.block_table[(size_t)c.b * a.max_blocks + pg];
 }
 
 template <int FK, int FV, int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Stage<FK, FV, D>::WPE, Stage<FK, FV, D>::WPE)))
+void decode_split_kernel(DecodeArgs a) {
   using KS = KShape<FK, D>;
   using VS = VShape<FV, D>;
   using ST = Stage<FK, FV, D>;
@@ -404,13 +414,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float s_fk[TILE];
   __shared__ __attribute__((aligned(16))) float s_fv[TILE * VS::NG];
 
-  // Wave (share, KV head).  The KV heads of one share are consecutive
-  // workgroups of one XCD (workgroups are dealt to the 8 XCDs round robin),
-  // so they read the same page-scale lines of its L2 at about the same time.
+  // Wave (share, group of HP KV heads).  The head groups of one share are
+  // consecutive workgroups of one XCD (workgroups are dealt to the 8 XCDs
+  // round robin), so they read the same page-scale lines of its L2 at about
+  // the same time.
   const uint32_t wg = blockIdx.x;
   const uint32_t kk = wg >> 3;
-  const int h = (int)(kk % (uint32_t)a.H);
-  const int share = (int)((kk / (uint32_t)a.H) * 8 + (wg & 7));
+  const uint32_t groups = (uint32_t)(a.H >> a.hp_log2);
+  const int h0 = (int)(kk % groups) << a.hp_log2;  // first KV head of the wave
+  const int share = (int)((kk / groups) * 8 + (wg & 7));
   if (share >= a.num_shares) return;
   const int S = a.plan[0];
   const int total = a.plan[1 + a.B];
@@ -428,8 +440,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   const int lane = (int)threadIdx.x;
   const int j = lane >> 4, n = lane & 15;
+  // MFMA column n (query operand, scores, output rows) is query head
+  // hq0 + n: KV head h0 + n / G, for n < NC = HP G (at most 16).
   const int G = a.G;
-  const int hq0 = h * G;
+  const int NC = G << a.hp_log2;
+  const int hq0 = h0 * G;
+  // tile rows whose KV head is column n's (all rows when HP = 1)
+  const int hp_mask = (1 << a.hp_log2) - 1;
+  uint32_t colmask = 0;
+  if (n < NC) {
+#pragma unroll
+    for (int rho = 0; rho < 32; ++rho) colmask |= ((rho & hp_mask) == n / G ? 1u : 0u) << rho;
+  }
   f4 acc[VS::NPV];
 #pragma unroll
   for (int m = 0; m < VS::NPV; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
@@ -442,10 +464,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // the key operand's channel order.
   h8 qop[KS::KB];
   bool piece_start = true;
-
-  // the half of a scale dword holding this (token, head)'s scale is
-  // (row index) & 1: h & 1 for an even head count, (t + h) & 1 otherwise
-  const bool h_odd = (a.H & 1) != 0;
 
   // Value transpose reads: lane (j, i) points at row T_j[i / 2] of the value
   // tile, byte 8 (i % 2) of the chunk, where T_j[e] = 16 (e / 4) + 4 j + e % 4
@@ -475,7 +493,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     ids_out = load_ids(a, cd, yi);
     const int yc = min(y, x_last);
     seek<FK>(ci, a, yc);
-    return load_tile<FK, FV, D>(a, ids_in, TILE * (yc - ci.lo), ci.lq, h, r);
+    return load_tile<FK, FV, D>(a, ids_in, (TILE * (yc - ci.lo)) >> a.hp_log2, ci.lq, h0, r);
   };
 #pragma unroll
   for (int i = 0; i < P; ++i) live[i] = load_group(x_begin + i, ids[(i + L) % NS], ids[i], regs[i]);
@@ -510,14 +528,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     l += __shfl_xor(l, 32);
     const size_t stride = (size_t)D + 2;
     float* pbase = a.part + ((size_t)(share + b) * a.Hq + hq0) * stride;
-    if (j == 0 && n < G) {
+    if (j == 0 && n < NC) {
       pbase[n * stride] = m_run;
       pbase[n * stride + 1] = l;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int g = 4 * j + r;
-      if (g < G) {
+      if (g < NC) {
 #pragma unroll
         for (int m = 0; m < VS::NPV; ++m) {
           const int ch = FV == F_INT4 ? 32 * (m >> 1) + 2 * n + (m & 1) : 16 * m + n;
@@ -546,15 +564,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     uint8_t* cur = s_st;
     store_tile<FK, FV, D>(regs[S_], cur);
     const uint64_t live_mask = live[S_];
+    const uint32_t par = regs[S_].par;
     // ---- first tile of a sequence's piece: its query operand ---------------
     if (piece_start) {
-      const uint16_t* qrow = a.q + ((size_t)cc.b * a.Hq + hq0 + (n < G ? n : 0)) * D;
+      const uint16_t* qrow = a.q + ((size_t)cc.b * a.Hq + hq0 + (n < NC ? n : 0)) * D;
 #pragma unroll
       for (int kb = 0; kb < KS::KB; ++kb) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint16_t bits = qrow[key_channel<FK, D>(j, kb, e)];
-          qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < G ? bits : 0));
+          qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < NC ? bits : 0));
         }
       }
       piece_start = false;
@@ -566,7 +585,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       const uint32_t* sdw = reinterpret_cast<const uint32_t*>(cur + ST::OFF_S);
       const int t = lane & 31;
       const bool lv = (live_mask >> t) & 1;
-      const bool hi_half = h_odd ? ((t + h) & 1) : (h & 1);
+      const bool hi_half = (par >> t) & 1;
       if (lane < 32) {
         if constexpr (FK != F_KIVI) {
           const uint32_t d = sdw[t];
@@ -664,7 +683,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         }
       }
     }
-    // lane (j, n): sc[u][r] = raw score of token 16u + 4j + r, query head n.
+    // lane (j, n): sc[u][r] = raw score of tile row 16u + 4j + r, column n.
+    const uint32_t vmask = (uint32_t)live_mask & colmask;
     float s[8];
     float tmax = -INFINITY;
 #pragma unroll
@@ -677,8 +697,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         float v;
         if constexpr (FK == F_KIVI) v = __builtin_fmaf(sc[u][r], a.qscale, qz);
         else v = sc[u][r] * ks4[r];
-        // a masked row's key codes may be anything: select, don't multiply
-        v = ((live_mask >> tr) & 1) ? v : -INFINITY;
+        // a masked row's key codes may be anything, and a row of another KV
+        // head than column n's does not belong to it: select, don't multiply
+        v = ((vmask >> tr) & 1) ? v : -INFINITY;
         s[4 * u + r] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -894,7 +915,8 @@ template <bool KIVI>
 __device__ __forceinline__ int seq_tiles(const DecodeArgs& a, int b) {
   const int L = min(max(a.ctx_lens[b], 0), a.max_blocks << a.log2_bs);
   const int Lq = KIVI ? (L & ~31) : L;
-  return (Lq + TILE - 1) / TILE;
+  const int tt = TILE >> a.hp_log2;  // tokens per tile
+  return (Lq + tt - 1) / tt;
 }
 
 // Exclusive prefix sum over the workgroup; returns the workgroup total.
@@ -960,9 +982,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(DecodeArgs a) {
 namespace {
 
 // Waves of decode_split_kernel<FK, FV, D> to run at once on the current
-// device: one per SIMD (4 per compute unit), or the occupancy if lower.
-// Every wave gets the same work, so two waves sharing a SIMD would hold the
-// whole launch back.  Cached per device.
+// device: WPE per SIMD (4 WPE per compute unit), or the occupancy if lower.
+// Every wave gets the same work, so a SIMD holding more waves than the
+// others would hold the whole launch back.  Cached per device.
 template <int FK, int FV, int D>
 int resident_waves() {
   static std::atomic<int> cache[64];
@@ -976,7 +998,7 @@ int resident_waves() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D>, 64, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  const int w = std::min(per_cu, 4) * cus;
+  const int w = std::min(per_cu, 4 * Stage<FK, FV, D>::WPE) * cus;
   if (dev >= 0 && dev < 64 && w > 0) cache[dev].store(w, std::memory_order_relaxed);
   return w;
 }
@@ -987,15 +1009,15 @@ hipError_t launch3(DecodeArgs a, hipStream_t st) {
     // balanced: all waves the same length, all resident at once
     const int w = resident_waves<FK, FV, D>();
     if (w <= 0) return hipErrorInvalidDevice;
-    a.num_shares = min(a.max_shares, max(1, w / a.H));
+    a.num_shares = min(a.max_shares, max(1, w / (a.H >> a.hp_log2)));
   } else {
     a.num_shares = a.max_shares;
   }
   hipLaunchKernelGGL((plan_kernel<FK == F_KIVI>), dim3(1), dim3(PLAN_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // one wave per (share, KV head); see decode_split_kernel for the order
-  const uint32_t wgs = (((uint32_t)a.num_shares + 7) / 8) * 8 * (uint32_t)a.H;
+  // one wave per (share, group of HP KV heads); see decode_split_kernel for the order
+  const uint32_t wgs = (((uint32_t)a.num_shares + 7) / 8) * 8 * (uint32_t)(a.H >> a.hp_log2);
   hipLaunchKernelGGL((decode_split_kernel<FK, FV, D>), dim3(wgs), dim3(64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1031,20 +1053,31 @@ hipError_t by_v(int fv, int D, const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int32_t heads_per_wave_log2(const kvq_cache& c, int32_t G) {
+  // KIVI tiles are whole 32-token pages of one head (their page scales)
+  if (c.k_dtype == KVQ_INT4_KIVI) return 0;
+  int32_t l = 0;
+  while (l < 2 && ((2 << l) * G) <= 16 && c.n_kv_heads % (2 << l) == 0) ++l;
+  return l;
+}
+
 bool plan_decode(const kvq_cache& c, int32_t batch, int32_t n_q_heads, int32_t max_blocks, int32_t split_tokens,
                  DecodePlan* p) {
+  if (n_q_heads <= 0 || n_q_heads % c.n_kv_heads != 0) return false;
+  const int32_t hp_log2 = heads_per_wave_log2(c, n_q_heads / c.n_kv_heads);
+  const int32_t tile_tokens = TILE >> hp_log2;
+  const int32_t groups = c.n_kv_heads >> hp_log2;  // waves per share
   const int64_t max_tok = (int64_t)max_blocks * c.block_size;  // tokens one block-table row addresses
   if (max_tok >= (1ll << 30)) return false;
-  const int64_t bound = (int64_t)batch * ((max_tok + TILE - 1) / TILE);  // tiles of the call, at most
+  const int64_t bound = (int64_t)batch * ((max_tok + tile_tokens - 1) / tile_tokens);  // tiles of the call, at most
   if (bound >= (1ll << 30)) return false;
   int64_t shares;
   if (split_tokens > 0) {
-    const int64_t S = ((int64_t)split_tokens + TILE - 1) / TILE;
+    const int64_t S = ((int64_t)split_tokens + tile_tokens - 1) / tile_tokens;
     shares = (bound + S - 1) / S;
     p->share_tiles = (int32_t)S;
   } else {
-    shares = std::min<int64_t>((AUTO_MAX_WAVES + c.n_kv_heads - 1) / c.n_kv_heads,
-                               (bound + AUTO_MIN_TILES - 1) / AUTO_MIN_TILES);
+    shares = std::min<int64_t>((AUTO_MAX_WAVES + groups - 1) / groups, (bound + AUTO_MIN_TILES - 1) / AUTO_MIN_TILES);
     p->share_tiles = 0;
   }
   if (shares < 1) shares = 1;

@@ -63,9 +63,12 @@ struct DecodeArgs {
   const uint16_t* k_tail;
   const uint16_t* v_tail;
   int32_t max_seqs;
-  // Work partition.  The quantized tiles (32 tokens) of all sequences are
-  // numbered sequence by sequence; share i covers tiles [i S, (i + 1) S) and
-  // is processed by n_kv_heads waves, one per KV head.
+  // A wave handles HP = 2^hp_log2 consecutive KV heads; a tile is 32 rows,
+  // (token, head) pairs: 32 / HP tokens of those HP heads.
+  int32_t hp_log2;
+  // Work partition.  The tiles of all sequences are numbered sequence by
+  // sequence; share i covers tiles [i S, (i + 1) S) and is processed by
+  // n_kv_heads / HP waves, one per group of HP KV heads.
   int32_t share_tiles;  // S requested by the caller; 0 = balanced over num_shares
   int32_t num_shares;   // shares launched (<= max_shares)
   int32_t max_shares;   // shares the workspace was laid out for
@@ -91,6 +94,9 @@ struct DecodePlan {
 // Returns false if the sizes overflow the ranges the kernels index with.
 bool plan_decode(const kvq_cache& c, int32_t batch, int32_t n_q_heads, int32_t max_blocks, int32_t split_tokens,
                  DecodePlan* plan);
+
+// log2 of the KV heads one decode wave handles for G query heads per KV head.
+int32_t heads_per_wave_log2(const kvq_cache& c, int32_t G);
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_write(const kvq_cache& c, const WriteArgs& a, hipStream_t s);

@@ -81,21 +81,24 @@ def test_write_argument_errors():
 def test_workspace_query():
     # Layout: plan ints (2 + batch + shares, padded to 256 bytes), then
     # (shares + batch [+ batch for KIVI tails]) records of n_q_heads x (D + 2) fp32.
-    # bs 16, mb 10: 160 tokens = 5 tiles per sequence, 15 for the call; shares of
-    # 64 tokens = 2 tiles -> 8 shares; 13 ints -> 256 bytes; 11 records.
+    # Tiles are 32 (token, head) rows of HP heads: here 2 KV heads x 2 query
+    # heads each -> HP = 2, 16 tokens per tile.
+    # mb 10 x bs 16 = 160 tokens = 10 tiles per sequence, 30 for the call; shares of
+    # 64 tokens = 4 tiles -> 8 shares; 13 ints -> 256 bytes; 11 records.
     rc, n = _ws(_cache(), batch=3, hq=4, mb=10, pps=64)
     assert rc == OK and n == 256 + 11 * 4 * 130 * 4
-    # KIVI: 8 pages of 32 tokens = 8 tiles, one share of 8 tiles; records 1 + 1 + 1 tail.
+    # KIVI (one head per wave, 32-token tiles): 8 pages = 8 tiles, one share; records 1 + 1 + 1 tail.
     rc, n = _ws(_cache(k_dtype=4, block_size=32, max_seqs=1, k_zeros=FAKE, k_tail=FAKE, v_tail=FAKE),
                 batch=1, hq=2, mb=8, pps=256)
     assert rc == OK and n == 256 + 3 * 2 * 130 * 4
-    # automatic: min(ceil(4096 / H), ceil(tiles / 4)) shares = min(2048, 250); 254 ints -> 1024 bytes
+    # automatic: min(ceil(4096 / (H / HP)), ceil(tiles / 4)) shares = min(4096, 500); 504 ints -> 2048 bytes
     rc, n = _ws(_cache(), batch=2, hq=4, mb=1000, pps=0)
-    assert rc == OK and n == 1024 + 252 * 4 * 130 * 4
-    # a split size that is not a multiple of 32 rounds up to whole tiles
-    assert _ws(_cache(), batch=3, hq=4, mb=10, pps=33) == _ws(_cache(), batch=3, hq=4, mb=10, pps=64)
+    assert rc == OK and n == 2048 + 502 * 4 * 130 * 4
+    # a split size rounds up to whole tiles (16 tokens here)
+    assert _ws(_cache(), batch=3, hq=4, mb=10, pps=33) == _ws(_cache(), batch=3, hq=4, mb=10, pps=48)
     assert _ws(_cache(), mb=0)[0] == INVALID
     assert _ws(_cache(), pps=-1)[0] == INVALID
+    assert _ws(_cache(), hq=3)[0] == SHAPE                  # not a multiple of n_kv_heads
     assert _ws(_cache(), mb=1 << 26)[0] == SHAPE            # 2^30 tokens in one block-table row
     assert _ws(_cache(), batch=1 << 25, mb=64)[0] == SHAPE  # 2^30 tiles in the call
 
