@@ -88,7 +88,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, command: str) -> 
                            "fetch_counter_bytes": cal_f, "write_counter_bytes": cal_w,
                            "fetch_factor": kf, "write_factor": kw}, "kernels": {}}
     total = 0.0
-    for key in ("decode_split_kernel", "kivi_tail_kernel", "merge_kernel"):
+    for key in ("plan_kernel", "decode_split_kernel", "kivi_tail_kernel", "merge_kernel"):
         if not any(key in k for k in f):
             continue
         fb, nf = pick(f, key)
@@ -339,7 +339,7 @@ def main():
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w.name),
-                     "kernel": "decode_split_kernel + merge_kernel (one kvq_decode_attn call)"},
+                     "kernel": "plan_kernel + decode_split_kernel + merge_kernel (one kvq_decode_attn call)"},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
