@@ -397,7 +397,9 @@ __device__ __forceinline__ int load_ids(const DecodeArgs& a, const SeqCursor& c,
   return a.block_table[(size_t)c.b * a.max_blocks + pg];
 }
 
-template <int FK, int FV, int D>
+// HPC: KV heads per wave (a.hp_log2 == log2 HPC).  Lane (j, n) keeps only the
+// scores of its column's head: rows 16 u + 4 j + r with r = hn (mod HPC).
+template <int FK, int FV, int D, int HPC>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Stage<FK, FV, D>::WPE, Stage<FK, FV, D>::WPE)))
 void decode_split_kernel(DecodeArgs a) {
   using KS = KShape<FK, D>;
@@ -446,7 +448,8 @@ void decode_split_kernel(DecodeArgs a) {
   const int NC = G << a.hp_log2;
   const int hq0 = h0 * G;
   // tile rows whose KV head is column n's (all rows when HP = 1)
-  const int hp_mask = (1 << a.hp_log2) - 1;
+  const int hp_mask = HPC - 1;
+  const int hn = n < NC ? n / G : 0;  // column n's head within the wave
   uint32_t colmask = 0;
   if (n < NC) {
 #pragma unroll
@@ -683,24 +686,31 @@ void decode_split_kernel(DecodeArgs a) {
         }
       }
     }
-    // lane (j, n): sc[u][r] = raw score of tile row 16u + 4j + r, column n.
+    // lane (j, n): sc[u][r] = raw score of tile row 16u + 4j + r, column n;
+    // only rows r = hn + HPC i (i < NU) hold column n's head.
+    constexpr int NU = 4 / HPC;
     const uint32_t vmask = (uint32_t)live_mask & colmask;
-    float s[8];
+    float s[2][NU];
+    int rows[2][NU];
     float tmax = -INFINITY;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      f4 ks4 = f4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (FK != F_KIVI) ks4 = *reinterpret_cast<const f4*>(&s_fk[16 * u + 4 * j]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int i = 0; i < NU; ++i) {
+        const int r = HPC == 1 ? i : hn + HPC * i;
         const int tr = 16 * u + 4 * j + r;
+        rows[u][i] = tr;
+        float raw;
+        if constexpr (HPC == 1) raw = sc[u][i];
+        else if constexpr (HPC == 2) raw = hn ? sc[u][2 * i + 1] : sc[u][2 * i];
+        else raw = hn == 0 ? sc[u][0] : hn == 1 ? sc[u][1] : hn == 2 ? sc[u][2] : sc[u][3];
         float v;
-        if constexpr (FK == F_KIVI) v = __builtin_fmaf(sc[u][r], a.qscale, qz);
-        else v = sc[u][r] * ks4[r];
+        if constexpr (FK == F_KIVI) v = __builtin_fmaf(raw, a.qscale, qz);
+        else v = raw * s_fk[tr];
         // a masked row's key codes may be anything, and a row of another KV
         // head than column n's does not belong to it: select, don't multiply
         v = ((vmask >> tr) & 1) ? v : -INFINITY;
-        s[4 * u + r] = v;
+        s[u][i] = v;
         tmax = fmaxf(tmax, v);
       }
     }
@@ -723,31 +733,72 @@ void decode_split_kernel(DecodeArgs a) {
       }
       m_run = m_new;
     }
-    float p[8];
+    float p[2][NU];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(s[e] - m_use);  // exp2(-inf) = 0 for masked rows
-      l_run += p[e];
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int i = 0; i < NU; ++i) {
+        p[u][i] = __builtin_amdgcn_exp2f(s[u][i] - m_use);  // exp2(-inf) = 0 for masked rows
+        l_run += p[u][i];
+      }
     }
 
     // ---- P V on the matrix cores -------------------------------------------
-    // Probability operand of lane (j, n): 8 k-slots (tokens T_j[e]) of query
-    // head n times the value scale, as bf16 hi + lo.  Value operands hold
-    // exact codes, biased to non-negative for INT8/INT4; the bias times the
-    // probability sum is removed once, after the last tile (cs_run).
+    // Probability operand of lane (j, n): 8 k-slots (tile rows T_j[e]) of
+    // column n times the value scale, as bf16 hi + lo; slots of rows of other
+    // heads are 0.  Value operands hold exact codes, biased to non-negative
+    // for INT8/INT4; the bias times the probability sum is removed once,
+    // after the last tile (cs_run).
+    // Place bf16 x (low half of b) into half `hi` of a dword.
+    auto at_half = [](uint32_t b, bool hi) __attribute__((always_inline)) { return hi ? b << 16 : b & 0xFFFFu; };
     if constexpr (FV == F_INT4) {
-      // element order [0, 2, 1, 3, 4, 6, 5, 7] (see value_operand_int4)
+      // dword q holds slots (q >> 1) 4 + (q & 1) (rows r = q & 1, low half) and
+      // that + 2 (r = (q & 1) + 2, high half) of u = q >> 1 (value_operand_int4)
 #pragma unroll
       for (int grp = 0; grp < VS::NG; ++grp) {
         uint32_t ah[4], al[4];
+        if constexpr (HPC == 1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          // pair q: slots (0,2) (1,3) (4,6) (5,7)
-          const int s0 = (q >> 1) * 4 + (q & 1), s1 = s0 + 2;
-          const int t0_ = 16 * (s0 >> 2) + 4 * j + (s0 & 3), t1_ = 16 * (s1 >> 2) + 4 * j + (s1 & 3);
+          for (int q = 0; q < 4; ++q) {
+            const int u = q >> 1, r0 = q & 1;
+            f2 used;
+            split_bf16x2(f2{p[u][r0] * s_fv[rows[u][r0] * VS::NG + grp],
+                            p[u][r0 + 2] * s_fv[rows[u][r0 + 2] * VS::NG + grp]},
+                         ah[q], al[q], used);
+            cs_run[grp] += used.x + used.y;
+          }
+        } else if constexpr (HPC == 2) {
+          // rows hn, hn + 2 of u share dword 2 u + hn
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            uint32_t h, l;
+            f2 used;
+            split_bf16x2(f2{p[u][0] * s_fv[rows[u][0] * VS::NG + grp], p[u][1] * s_fv[rows[u][1] * VS::NG + grp]}, h, l,
+                         used);
+            cs_run[grp] += used.x + used.y;
+            ah[2 * u] = hn ? 0u : h;
+            ah[2 * u + 1] = hn ? h : 0u;
+            al[2 * u] = hn ? 0u : l;
+            al[2 * u + 1] = hn ? l : 0u;
+          }
+        } else {
+          // row hn of u: dword 2 u + (hn & 1), half hn >> 1
+          uint32_t h, l;
           f2 used;
-          split_bf16x2(f2{p[s0] * s_fv[t0_ * VS::NG + grp], p[s1] * s_fv[t1_ * VS::NG + grp]}, ah[q], al[q], used);
+          split_bf16x2(f2{p[0][0] * s_fv[rows[0][0] * VS::NG + grp], p[1][0] * s_fv[rows[1][0] * VS::NG + grp]}, h, l,
+                       used);
           cs_run[grp] += used.x + used.y;
+          const bool up = hn >> 1, odd = hn & 1;
+          const uint32_t h0 = at_half(h, up), h1 = at_half(h >> 16, up);
+          const uint32_t l0 = at_half(l, up), l1 = at_half(l >> 16, up);
+          ah[0] = odd ? 0u : h0;
+          ah[1] = odd ? h0 : 0u;
+          ah[2] = odd ? 0u : h1;
+          ah[3] = odd ? h1 : 0u;
+          al[0] = odd ? 0u : l0;
+          al[1] = odd ? l0 : 0u;
+          al[2] = odd ? 0u : l1;
+          al[3] = odd ? l1 : 0u;
         }
         const b8 A_hi = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
         const b8 A_lo = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
@@ -760,16 +811,46 @@ void decode_split_kernel(DecodeArgs a) {
         acc[2 * grp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, vo, acc[2 * grp + 1], 0, 0, 0);
       }
     } else {
-      f4 vs4[2];
-      vs4[0] = *reinterpret_cast<const f4*>(&s_fv[4 * j]);
-      vs4[1] = *reinterpret_cast<const f4*>(&s_fv[16 + 4 * j]);
+      // dword q holds slots 2q, 2q + 1: rows r = 2 (q & 1), 2 (q & 1) + 1 of u = q >> 1
       uint32_t ah[4], al[4];
+      if constexpr (HPC == 1) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {  // pair q: slots 2q, 2q + 1
-        const int u = q >> 1, r0 = 2 * (q & 1);
+        for (int q = 0; q < 4; ++q) {
+          const int u = q >> 1, r0 = 2 * (q & 1);
+          f2 used;
+          split_bf16x2(f2{p[u][r0] * s_fv[rows[u][r0]], p[u][r0 + 1] * s_fv[rows[u][r0 + 1]]}, ah[q], al[q], used);
+          if constexpr (FV == F_INT8) cs_run[0] += used.x + used.y;
+        }
+      } else if constexpr (HPC == 2) {
+        // row hn + 2 i of u: dword 2 u + i, half hn
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          uint32_t h, l;
+          f2 used;
+          split_bf16x2(f2{p[u][0] * s_fv[rows[u][0]], p[u][1] * s_fv[rows[u][1]]}, h, l, used);
+          if constexpr (FV == F_INT8) cs_run[0] += used.x + used.y;
+          ah[2 * u] = at_half(h, hn);
+          ah[2 * u + 1] = at_half(h >> 16, hn);
+          al[2 * u] = at_half(l, hn);
+          al[2 * u + 1] = at_half(l >> 16, hn);
+        }
+      } else {
+        // row hn of u: dword 2 u + (hn >> 1), half hn & 1
+        uint32_t h, l;
         f2 used;
-        split_bf16x2(f2{p[2 * q] * vs4[u][r0], p[2 * q + 1] * vs4[u][r0 + 1]}, ah[q], al[q], used);
+        split_bf16x2(f2{p[0][0] * s_fv[rows[0][0]], p[1][0] * s_fv[rows[1][0]]}, h, l, used);
         if constexpr (FV == F_INT8) cs_run[0] += used.x + used.y;
+        const bool odd = hn & 1, up = hn >> 1;
+        const uint32_t h0 = at_half(h, odd), h1 = at_half(h >> 16, odd);
+        const uint32_t l0 = at_half(l, odd), l1 = at_half(l >> 16, odd);
+        ah[0] = up ? 0u : h0;
+        ah[1] = up ? h0 : 0u;
+        ah[2] = up ? 0u : h1;
+        ah[3] = up ? h1 : 0u;
+        al[0] = up ? 0u : l0;
+        al[1] = up ? l0 : 0u;
+        al[2] = up ? 0u : l1;
+        al[3] = up ? l1 : 0u;
       }
       const b8 A_hi = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
       const b8 A_lo = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
@@ -985,7 +1066,7 @@ namespace {
 // device: WPE per SIMD (4 WPE per compute unit), or the occupancy if lower.
 // Every wave gets the same work, so a SIMD holding more waves than the
 // others would hold the whole launch back.  Cached per device.
-template <int FK, int FV, int D>
+template <int FK, int FV, int D, int HPC>
 int resident_waves() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -995,7 +1076,7 @@ int resident_waves() {
     if (c > 0) return c;
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D>, 64, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D, HPC>, 64, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   const int w = std::min(per_cu, 4 * Stage<FK, FV, D>::WPE) * cus;
@@ -1003,11 +1084,11 @@ int resident_waves() {
   return w;
 }
 
-template <int FK, int FV, int D>
-hipError_t launch3(DecodeArgs a, hipStream_t st) {
+template <int FK, int FV, int D, int HPC>
+hipError_t launch4(DecodeArgs a, hipStream_t st) {
   if (a.share_tiles <= 0) {
     // balanced: all waves the same length, all resident at once
-    const int w = resident_waves<FK, FV, D>();
+    const int w = resident_waves<FK, FV, D, HPC>();
     if (w <= 0) return hipErrorInvalidDevice;
     a.num_shares = min(a.max_shares, max(1, w / (a.H >> a.hp_log2)));
   } else {
@@ -1018,7 +1099,7 @@ hipError_t launch3(DecodeArgs a, hipStream_t st) {
   if (e != hipSuccess) return e;
   // one wave per (share, group of HP KV heads); see decode_split_kernel for the order
   const uint32_t wgs = (((uint32_t)a.num_shares + 7) / 8) * 8 * (uint32_t)(a.H >> a.hp_log2);
-  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D>), dim3(wgs), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D, HPC>), dim3(wgs), dim3(64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (FK == F_KIVI) {
@@ -1029,6 +1110,18 @@ hipError_t launch3(DecodeArgs a, hipStream_t st) {
   hipLaunchKernelGGL((merge_kernel<D, FK == F_KIVI>), dim3((unsigned)(a.B * a.Hq)), dim3(MERGE_WAVES * 64), 0, st,
                      a);
   return hipGetLastError();
+}
+
+template <int FK, int FV, int D>
+hipError_t launch3(const DecodeArgs& a, hipStream_t st) {
+  // KIVI keys always run one head per wave (heads_per_wave_log2)
+  if constexpr (FK == F_KIVI) return launch4<FK, FV, D, 1>(a, st);
+  switch (a.hp_log2) {
+    case 0: return launch4<FK, FV, D, 1>(a, st);
+    case 1: return launch4<FK, FV, D, 2>(a, st);
+    case 2: return launch4<FK, FV, D, 4>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int FK, int FV>
