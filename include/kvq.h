@@ -154,7 +154,7 @@ int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch,
  *   sm_scale     softmax scale; 0 means 1/sqrt(head_dim).
  *   split_tokens work partition.  One wave reads HP consecutive KV heads
  *                (HP = 4, 2 or 1: the most with HP x n_q_heads/n_kv_heads
- *                <= 16 that divides n_kv_heads; 1 for KVQ_INT4_KIVI keys), in
+ *                <= 16 that divides n_kv_heads), in
  *                tiles of 32 (token, head) rows = 32 / HP tokens.  The tiles
  *                of all sequences are numbered sequence after sequence and
  *                cut into equal shares, each read by n_kv_heads / HP waves

@@ -234,7 +234,8 @@ struct Stage {
   static constexpr int NLK = KT / 1024;             // 16-byte key chunks per lane (>= 1)
   static constexpr int NLV = VT / 1024;
   static constexpr int NGD = VS::NG > 1 ? VS::NG / 2 : 1;  // value-scale dwords per token
-  static constexpr int KIVI_BYTES = FK == F_KIVI ? 2 * D * 2 : 0;  // page scale + zero (fp16)
+  // KIVI: the page's scales, then its zeros, of up to 4 KV heads (fp16)
+  static constexpr int KIVI_BYTES = FK == F_KIVI ? 4 * 2 * D * 2 : 0;
   // byte offsets inside a stage
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = KT;
@@ -247,22 +248,25 @@ struct Stage {
   // while one is stored to LDS and computed).  Head dim 256 runs one wave per
   // SIMD with up to 4 tiles held, within about 136 registers.
   static constexpr int WPE = D <= 128 ? 2 : 1;
-  static constexpr int TILE_REGS = 4 * (NLK + NLV) + NGD + 1 + (FK == F_KIVI ? 4 : 0);
+  static constexpr int TILE_REGS = 4 * (NLK + NLV) + NGD + 1 + (FK == F_KIVI ? 4 * (D / 64) : 0);
   static constexpr int NS_FIT = 136 / TILE_REGS;
   static constexpr int NS = WPE == 2 ? 2 : (NS_FIT < 2 ? 2 : (NS_FIT > 4 ? 4 : NS_FIT));
 };
 
 // One tile's global data in registers: the 16-byte chunks of its key and
-// value rows, its scale dwords and (KIVI) its page's scales and zeros.  Each
-// lane holds exactly what it later stores into the LDS stage.
-template <int FK, int FV, int D>
+// value rows, its scale dwords and (KIVI) its page's scales and zeros for the
+// wave's HPC heads.  Each lane holds exactly what it later stores into the
+// LDS stage.
+template <int FK, int FV, int D, int HPC>
 struct TileRegs {
   using S = Stage<FK, FV, D>;
+  static constexpr int MCH = FK == F_KIVI ? HPC * D / 4 : 0;  // 16-byte chunks of page metadata
+  static constexpr int KM = (MCH + 63) / 64;                  // per lane
   u4 k[S::NLK];
   u4 v[S::NLV];
   uint32_t s[S::NGD];
   uint32_t par;  // bit rho: row rho's 16-bit scale is the high half of its dword
-  u4 m;  // KIVI only
+  u4 m[KM > 0 ? KM : 1];
 };
 
 // Load one tile (keys, values, per-token scale dwords; KIVI page scales and
@@ -271,9 +275,9 @@ struct TileRegs {
 // context on a valid page).  Every load is issued by every lane, so each
 // tile costs the same number of loads: masked rows and idle lanes read the
 // start of the buffer, and those bytes are never used unmasked.
-template <int FK, int FV, int D>
+template <int FK, int FV, int D, int HPC>
 __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int t0, int tok_end, int h0,
-                                              TileRegs<FK, FV, D>& r) {
+                                              TileRegs<FK, FV, D, HPC>& r) {
   using S = Stage<FK, FV, D>;
   using KS = KShape<FK, D>;
   using VS = VShape<FV, D>;
@@ -318,20 +322,27 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
     r.s[g] = *reinterpret_cast<const uint32_t*>(a.v_scales +
                                                 (live && lane < 32 ? (size_t)r_own * VS::NG + 2 * g : 0));
   if constexpr (FK == F_KIVI) {
-    // the tile is one page (block_size 32): its D scales and D zeros
-    constexpr int CH = D * 2 / 16;
+    // the tile lies in one page (block_size 32): the D scales of heads
+    // h0 .. h0 + HPC - 1 (contiguous), then their D zeros; chunk c of 16 bytes
+    using TR = TileRegs<FK, FV, D, HPC>;
+    constexpr int HALF = HPC * D / 8;  // chunks of scales
     const uint32_t r0 = (uint32_t)__shfl((int)rl, 0);
-    const bool ok = r0 != ~0u && lane < 2 * CH;
+    const bool ok = r0 != ~0u;
     const size_t mrow = ((size_t)(r0 / (32u * (uint32_t)a.H)) * a.H + h0) * D;
-    const uint16_t* src = (lane < CH ? a.k_scales : a.k_zeros) + (ok ? mrow + 8 * (lane % CH) : 0);
-    r.m = *reinterpret_cast<const u4*>(src);
+#pragma unroll
+    for (int k = 0; k < TR::KM; ++k) {
+      const int c = 64 * k + lane;
+      const bool use = ok && c < TR::MCH;
+      const uint16_t* src = (c < HALF ? a.k_scales : a.k_zeros) + (use ? mrow + 8 * (c < HALF ? c : c - HALF) : 0);
+      r.m[k] = *reinterpret_cast<const u4*>(src);
+    }
   }
   return live_mask;
 }
 
 // Store a loaded tile into the LDS stage `st` (layout of Stage).
-template <int FK, int FV, int D>
-__device__ __forceinline__ void store_tile(const TileRegs<FK, FV, D>& r, uint8_t* st) {
+template <int FK, int FV, int D, int HPC>
+__device__ __forceinline__ void store_tile(const TileRegs<FK, FV, D, HPC>& r, uint8_t* st) {
   using S = Stage<FK, FV, D>;
   const int lane = (int)threadIdx.x;
 #pragma unroll
@@ -344,7 +355,10 @@ __device__ __forceinline__ void store_tile(const TileRegs<FK, FV, D>& r, uint8_t
   for (int g = 1; g < S::NGD; ++g)
     if (lane < 32) sd[32 + 32 * g + lane] = r.s[g];
   if constexpr (FK == F_KIVI) {
-    if (lane < D / 4) reinterpret_cast<u4*>(st + S::OFF_M)[lane] = r.m;
+    using TR = TileRegs<FK, FV, D, HPC>;
+#pragma unroll
+    for (int k = 0; k < TR::KM; ++k)
+      if (64 * k + lane < TR::MCH) reinterpret_cast<u4*>(st + S::OFF_M)[64 * k + lane] = r.m[k];
   }
 }
 
@@ -467,6 +481,9 @@ void decode_split_kernel(DecodeArgs a) {
   // the key operand's channel order.
   h8 qop[KS::KB];
   bool piece_start = true;
+  // KIVI: q * s of the current page (fp16 hi + lo) and q . z, column n's head
+  h8 qhi[FK == F_KIVI ? KS::KB : 1], qlo[FK == F_KIVI ? KS::KB : 1];
+  float qz = 0.f;
 
   // Value transpose reads: lane (j, i) points at row T_j[i / 2] of the value
   // tile, byte 8 (i % 2) of the chunk, where T_j[e] = 16 (e / 4) + 4 j + e % 4
@@ -480,7 +497,7 @@ void decode_split_kernel(DecodeArgs a) {
   // issues the same loads, tiles past the share's end reload its last tile,
   // so the compiler's load counters are exact and only wait for the tile
   // being stored.  Registers rotate over NS slots: slot (y - x_begin) % NS.
-  TileRegs<FK, FV, D> regs[NS];
+  TileRegs<FK, FV, D, HPC> regs[NS];
   uint64_t live[NS];
   int ids[NS];
   const int x_last = x_end - 1;
@@ -490,13 +507,13 @@ void decode_split_kernel(DecodeArgs a) {
     seek<FK>(cd, a, y);
     ids[i] = load_ids(a, cd, y);
   }
-  auto load_group = [&](int y, int& ids_out, int ids_in, TileRegs<FK, FV, D>& r) __attribute__((always_inline)) {
+  auto load_group = [&](int y, int& ids_out, int ids_in, TileRegs<FK, FV, D, HPC>& r) __attribute__((always_inline)) {
     const int yi = min(y + L, x_last);
     seek<FK>(cd, a, yi);
     ids_out = load_ids(a, cd, yi);
     const int yc = min(y, x_last);
     seek<FK>(ci, a, yc);
-    return load_tile<FK, FV, D>(a, ids_in, (TILE * (yc - ci.lo)) >> a.hp_log2, ci.lq, h0, r);
+    return load_tile<FK, FV, D, HPC>(a, ids_in, (TILE * (yc - ci.lo)) >> a.hp_log2, ci.lq, h0, r);
   };
 #pragma unroll
   for (int i = 0; i < P; ++i) live[i] = load_group(x_begin + i, ids[(i + L) % NS], ids[i], regs[i]);
@@ -565,10 +582,11 @@ void decode_split_kernel(DecodeArgs a) {
     if (x >= x_end) return;
     // ---- tile x into LDS ------------------------------------------------------
     uint8_t* cur = s_st;
-    store_tile<FK, FV, D>(regs[S_], cur);
+    store_tile<FK, FV, D, HPC>(regs[S_], cur);
     const uint64_t live_mask = live[S_];
     const uint32_t par = regs[S_].par;
     // ---- first tile of a sequence's piece: its query operand ---------------
+    const bool new_piece = piece_start;
     if (piece_start) {
       const uint16_t* qrow = a.q + ((size_t)cc.b * a.Hq + hq0 + (n < NC ? n : 0)) * D;
 #pragma unroll
@@ -642,32 +660,34 @@ void decode_split_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- KIVI: this page's query operand q * s (fp16 hi + lo) and q . z ----
-    h8 qhi[KS::KB], qlo[KS::KB];
-    float qz = 0.f;
+    // ---- KIVI: the page's query operand q * s (fp16 hi + lo) and q . z for
+    //      column n's head, once per page (a page is HPC tiles) ---------------
     if constexpr (FK == F_KIVI) {
+      if (new_piece || ((x - cc.lo) & (HPC - 1)) == 0) {
+        qz = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KS::KB; ++kb) {
-        const int cb = j * (D / 4) + 8 * kb;
-        const u4 sw = *reinterpret_cast<const u4*>(cur + ST::OFF_M + 2 * cb);
-        const u4 zw = *reinterpret_cast<const u4*>(cur + ST::OFF_M + 2 * D + 2 * cb);
-        float s8[8], z8[8];
-        unpack8(uint4{sw.x, sw.y, sw.z, sw.w}, s8);
-        unpack8(uint4{zw.x, zw.y, zw.z, zw.w}, z8);
+        for (int kb = 0; kb < KS::KB; ++kb) {
+          const int cb = j * (D / 4) + 8 * kb;
+          const u4 sw = *reinterpret_cast<const u4*>(cur + ST::OFF_M + 2 * (hn * D + cb));
+          const u4 zw = *reinterpret_cast<const u4*>(cur + ST::OFF_M + 2 * (HPC * D + hn * D + cb));
+          float s8[8], z8[8];
+          unpack8(uint4{sw.x, sw.y, sw.z, sw.w}, s8);
+          unpack8(uint4{zw.x, zw.y, zw.z, zw.w}, z8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = key_channel<FK, D>(j, kb, e) - cb;
-          const float qv = (float)qop[kb][e];
-          const float qs = qv * s8[ch];
-          const _Float16 hi = (_Float16)qs;
-          qhi[kb][e] = hi;
-          qlo[kb][e] = (_Float16)(qs - (float)hi);
-          qz = __builtin_fmaf(qv, z8[ch], qz);
+          for (int e = 0; e < 8; ++e) {
+            const int ch = key_channel<FK, D>(j, kb, e) - cb;
+            const float qv = (float)qop[kb][e];
+            const float qs = qv * s8[ch];
+            const _Float16 hi = (_Float16)qs;
+            qhi[kb][e] = hi;
+            qlo[kb][e] = (_Float16)(qs - (float)hi);
+            qz = __builtin_fmaf(qv, z8[ch], qz);
+          }
         }
+        qz += __shfl_xor(qz, 16);
+        qz += __shfl_xor(qz, 32);
+        qz *= a.qscale;
       }
-      qz += __shfl_xor(qz, 16);
-      qz += __shfl_xor(qz, 32);
-      qz *= a.qscale;
     }
 
     // ---- scores S^T[t][g] on the matrix cores ------------------------------
@@ -1114,8 +1134,6 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
 
 template <int FK, int FV, int D>
 hipError_t launch3(const DecodeArgs& a, hipStream_t st) {
-  // KIVI keys always run one head per wave (heads_per_wave_log2)
-  if constexpr (FK == F_KIVI) return launch4<FK, FV, D, 1>(a, st);
   switch (a.hp_log2) {
     case 0: return launch4<FK, FV, D, 1>(a, st);
     case 1: return launch4<FK, FV, D, 2>(a, st);
@@ -1147,8 +1165,6 @@ hipError_t by_v(int fv, int D, const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 int32_t heads_per_wave_log2(const kvq_cache& c, int32_t G) {
-  // KIVI tiles are whole 32-token pages of one head (their page scales)
-  if (c.k_dtype == KVQ_INT4_KIVI) return 0;
   int32_t l = 0;
   while (l < 2 && ((2 << l) * G) <= 16 && c.n_kv_heads % (2 << l) == 0) ++l;
   return l;

@@ -53,10 +53,11 @@ def test_decode_gqa_group_sizes(G):
 
 
 @pytest.mark.parametrize("H,G", [(8, 4), (4, 4), (8, 8), (8, 2), (8, 1), (6, 2), (4, 16)])
-@pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32")])
+@pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("int4_kivi", "int4_g32")])
 def test_decode_head_groups(H, G, kf, vf):
     # a wave reads HP = 4, 2 or 1 KV heads (the most with HP G <= 16 and
-    # H % HP == 0): (token, head) tile rows, head-matched score columns
+    # H % HP == 0): (token, head) tile rows, head-matched score columns; for
+    # KIVI keys a 32-token page spans HP tiles (the page's q * s is reused)
     inp, dev, orc = _setup(kf, vf, 128, [0, 9, 130, 611], H=H, G=G, seed=H * 16 + G)
     for st in (0, 64):
         got, ref = decode_both(inp, dev, orc, DEV, split_tokens=st)
