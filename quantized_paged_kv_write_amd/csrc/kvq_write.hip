@@ -20,6 +20,9 @@
 namespace kvq {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 hv2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ hv2 as_hv2(uint32_t u) { return __builtin_bit_cast(hv2, u); }
+__device__ __forceinline__ uint32_t hv2_bits(hv2 v) { return __builtin_bit_cast(uint32_t, v); }
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int FMT>
@@ -150,30 +153,21 @@ __global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0
   }
 }
 
-// Reductions across the row sets of a wave (lanes that share lane % NCH).
-template <int NCH>
-__device__ __forceinline__ float rowset_min(float v) {
-#pragma unroll
-  for (int m = NCH; m < 64; m <<= 1) v = fminf(v, __shfl_xor(v, m));
-  return v;
-}
-template <int NCH>
-__device__ __forceinline__ float rowset_max(float v) {
-#pragma unroll
-  for (int m = NCH; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
-
 // KIVI key pages.  Block (chunk of 32 call tokens, head h), one wave.  Every
 // token of the chunk that lands on the last row of a page completes that
 // page: its 32 key rows (from this call where present at the expected call
 // positions, else from the sequence's tail) are quantized per channel:
 //   s = fp16(fl32(max - min) / 15), z = min, code = clip(rint((x - z) / s), 0, 15).
+// Each lane owns PPL channel pairs of every row (rows are split over RG row
+// groups when a row has fewer pairs than the wave has lanes), so one row is
+// one coalesced load across the wave and the per-channel min and max stay in
+// registers.
 template <int D>
 __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
-  constexpr int NCH = D / 8;     // lanes per row (8 channels each)
-  constexpr int RS = 64 / NCH;   // rows loaded side by side
-  constexpr int RPL = 32 / RS;   // rows per lane
+  constexpr int PPL = D >= 256 ? D / 128 : 1;  // channel pairs per lane
+  constexpr int LPR = D / 2 / PPL;             // lanes per row
+  constexpr int RG = 64 / LPR;                 // row groups
+  constexpr int RPL = 32 / RG;                 // rows per lane
   const int h = (int)blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * 32;
   const int lane = (int)threadIdx.x;
@@ -186,7 +180,7 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
     }
   }
   uint64_t mask = __ballot(seal);
-  const int cc = lane % NCH, rs = lane / NCH;
+  const int pl = lane % LPR, g = lane / LPR;
   while (mask) {
     const int j = __ffsll((unsigned long long)mask) - 1;
     mask &= mask - 1;
@@ -195,34 +189,47 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
     const int32_t seq = a.seq_idx[te];
     if (seq < 0 || seq >= a.max_seqs) continue;
     const int64_t blk = se >> 5;
-    float x[RPL][8];
+    // row r of the page is in this call at position te - 31 + r when that
+    // token belongs to the same sequence and slot; otherwise it is in the tail
+    bool inc = false;
+    if (lane < 32) {
+      const int64_t ts = te - 31 + lane;
+      if (ts >= 0) inc = a.seq_idx[ts] == seq && a.slots[ts] == se - 31 + lane;
+    }
+    const uint64_t incall = __ballot(inc);
+    uint32_t x[RPL][PPL];  // fp16 channel pairs, even channel in the low half
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const int row = rs + i * RS;
-      const int64_t ts = te - (31 - row);
-      bool in_call = false;
-      if (ts >= 0) in_call = a.seq_idx[ts] == seq && a.slots[ts] == se - (31 - row);
-      const uint16_t* src = in_call ? a.k + ((size_t)ts * a.H + h) * D
-                                    : a.k_tail + (((size_t)seq * 32 + row) * a.H + h) * D;
-      const u32x4 u = reinterpret_cast<const u32x4*>(src)[cc];
-      unpack8(uint4{u.x, u.y, u.z, u.w}, x[i]);
-    }
-    float mn[8], mx[8];
+      const int row = g + RG * i;
+      const uint16_t* src = ((incall >> row) & 1) ? a.k + ((size_t)(te - 31 + row) * a.H + h) * D
+                                                  : a.k_tail + (((size_t)seq * 32 + row) * a.H + h) * D;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float lo = x[0][c], hi = x[0][c];
+      for (int q = 0; q < PPL; ++q) x[i][q] = reinterpret_cast<const uint32_t*>(src)[pl * PPL + q];
+    }
+    // per-channel min and max on the packed fp16 pairs (exact)
+    float mn[2 * PPL], mx[2 * PPL];
+#pragma unroll
+    for (int q = 0; q < PPL; ++q) {
+      hv2 lo = as_hv2(x[0][q]), hi = lo;
 #pragma unroll
       for (int i = 1; i < RPL; ++i) {
-        lo = fminf(lo, x[i][c]);
-        hi = fmaxf(hi, x[i][c]);
+        lo = __builtin_elementwise_min(lo, as_hv2(x[i][q]));
+        hi = __builtin_elementwise_max(hi, as_hv2(x[i][q]));
       }
-      mn[c] = rowset_min<NCH>(lo);
-      mx[c] = rowset_max<NCH>(hi);
-    }
-    uint32_t s16[8], z16[8];
-    float sc[8], rc[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+      for (int m = LPR; m < 64; m <<= 1) {
+        lo = __builtin_elementwise_min(lo, as_hv2((uint32_t)__shfl_xor((int)hv2_bits(lo), m)));
+        hi = __builtin_elementwise_max(hi, as_hv2((uint32_t)__shfl_xor((int)hv2_bits(hi), m)));
+      }
+      mn[2 * q] = (float)lo.x;
+      mn[2 * q + 1] = (float)lo.y;
+      mx[2 * q] = (float)hi.x;
+      mx[2 * q + 1] = (float)hi.y;
+    }
+    uint32_t s16[2 * PPL], z16[2 * PPL];
+    float sc[2 * PPL], rc[2 * PPL];
+#pragma unroll
+    for (int c = 0; c < 2 * PPL; ++c) {
       const float range = mx[c] - mn[c];  // fl32(max - min)
       s16[c] = f2h_bits(range / 15.0f);
       z16[c] = f2h_bits(mn[c]);  // exact: mn is an fp16 value
@@ -232,28 +239,29 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
     uint8_t* cbase = a.k_codes + (size_t)blk * 32 * a.H * (D / 2);
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const int row = rs + i * RS;
+      const int row = g + RG * i;
       uint32_t w = 0;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < 2 * PPL; ++c) {
         uint32_t code = 0;
         if (sc[c] != 0.0f) {
-          const float y = exact_div(x[i][c] - mn[c], sc[c], rc[c]);  // fl32(fl32(x - z) / s)
+          const float v = h2f((c & 1) ? x[i][c >> 1] >> 16 : x[i][c >> 1] & 0xFFFFu);
+          const float y = exact_div(v - mn[c], sc[c], rc[c]);  // fl32(fl32(x - z) / s)
           code = (uint32_t)(int)__builtin_rintf(fminf(fmaxf(y, 0.0f), 15.0f));
         }
         w |= code << (4 * c);
       }
-      reinterpret_cast<uint32_t*>(cbase + ((size_t)row * a.H + h) * (D / 2))[cc] = w;
+      uint8_t* dst = cbase + ((size_t)row * a.H + h) * (D / 2) + pl * PPL;
+      if constexpr (PPL == 1) *dst = (uint8_t)w;
+      else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
     }
-    if (rs == 0) {
-      const size_t m = ((size_t)blk * a.H + h) * D + cc * 8;
-      u32x4 sv, zv;
-      sv.x = s16[0] | (s16[1] << 16); sv.y = s16[2] | (s16[3] << 16);
-      sv.z = s16[4] | (s16[5] << 16); sv.w = s16[6] | (s16[7] << 16);
-      zv.x = z16[0] | (z16[1] << 16); zv.y = z16[2] | (z16[3] << 16);
-      zv.z = z16[4] | (z16[5] << 16); zv.w = z16[6] | (z16[7] << 16);
-      *reinterpret_cast<u32x4*>(a.k_scales + m) = sv;
-      *reinterpret_cast<u32x4*>(a.k_zeros + m) = zv;
+    if (g == 0) {
+      const size_t m = ((size_t)blk * a.H + h) * D + 2 * PPL * pl;
+#pragma unroll
+      for (int q = 0; q < PPL; ++q) {
+        reinterpret_cast<uint32_t*>(a.k_scales + m)[q] = s16[2 * q] | (s16[2 * q + 1] << 16);
+        reinterpret_cast<uint32_t*>(a.k_zeros + m)[q] = z16[2 * q] | (z16[2 * q + 1] << 16);
+      }
     }
   }
 }
