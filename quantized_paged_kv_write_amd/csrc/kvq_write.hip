@@ -171,30 +171,35 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
   const int h = (int)blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * 32;
   const int lane = (int)threadIdx.x;
-  bool seal = false;
-  if (lane < 32) {
-    const int64_t t = t0 + lane;
-    if (t < a.T) {
-      const int64_t s = a.slots[t];
-      seal = s >= 0 && s < a.capacity && (s & 31) == 31;
-    }
+  // slot and sequence of the chunk's token `lane` (lanes < 32)
+  int64_t my_slot = -1;
+  int32_t my_seq = -1;
+  if (lane < 32 && t0 + lane < a.T) {
+    my_slot = a.slots[t0 + lane];
+    my_seq = a.seq_idx[t0 + lane];
   }
-  uint64_t mask = __ballot(seal);
+  uint64_t mask = __ballot(my_slot >= 0 && my_slot < a.capacity && (my_slot & 31) == 31);
   const int pl = lane % LPR, g = lane / LPR;
   while (mask) {
     const int j = __ffsll((unsigned long long)mask) - 1;
     mask &= mask - 1;
     const int64_t te = t0 + j;
-    const int64_t se = a.slots[te];
-    const int32_t seq = a.seq_idx[te];
+    const int64_t se = ((int64_t)__shfl((int)(my_slot >> 32), j) << 32) | (uint32_t)__shfl((int)my_slot, j);
+    const int32_t seq = __shfl(my_seq, j);
     if (seq < 0 || seq >= a.max_seqs) continue;
     const int64_t blk = se >> 5;
     // row r of the page is in this call at position te - 31 + r when that
-    // token belongs to the same sequence and slot; otherwise it is in the tail
+    // token belongs to the same sequence and slot; otherwise it is in the
+    // tail.  A page ending on the chunk's last token has its rows in this
+    // chunk (already loaded); others look them up.
     bool inc = false;
     if (lane < 32) {
-      const int64_t ts = te - 31 + lane;
-      if (ts >= 0) inc = a.seq_idx[ts] == seq && a.slots[ts] == se - 31 + lane;
+      if (j == 31) {
+        inc = my_seq == seq && my_slot == se - 31 + lane;
+      } else {
+        const int64_t ts = te - 31 + lane;
+        if (ts >= 0) inc = a.seq_idx[ts] == seq && a.slots[ts] == se - 31 + lane;
+      }
     }
     const uint64_t incall = __ballot(inc);
     uint32_t x[RPL][PPL];  // fp16 channel pairs, even channel in the low half
