@@ -389,6 +389,30 @@ __device__ __forceinline__ void fill_window(SeqCursor& c, const DecodeArgs& a, i
 
 __device__ __forceinline__ int rdlane(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
 
+// The plan of a batch of at most 64 sequences, computed by one wave: lane b
+// holds sequence b's quantized tokens (lq), tiles (n) and first tile (excl);
+// returns the tiles of the whole batch.
+template <int FK>
+__device__ __forceinline__ int wave_plan(const DecodeArgs& a, int& lq, int& n, int& excl) {
+  const int lane = (int)threadIdx.x & 63;
+  lq = lane < a.B ? seq_tokens<FK>(a, lane) : 0;
+  const int tt = TILE >> a.hp_log2;
+  n = (lq + tt - 1) / tt;
+  int incl = n;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  excl = incl - n;
+  return rdlane(incl, 63);
+}
+
+// Tiles per share: requested, or the balanced share of num_shares.
+__device__ __forceinline__ int share_size(const DecodeArgs& a, int total) {
+  return a.share_tiles > 0 ? a.share_tiles : max((total + a.num_shares - 1) / a.num_shares, AUTO_MIN_TILES);
+}
+
 // Move the cursor to the sequence holding tile x (x >= the current tile and
 // x < the number of tiles, so the loop ends on a valid sequence).
 template <int FK>
@@ -440,18 +464,35 @@ void decode_split_kernel(DecodeArgs a) {
   const int h0 = (int)(kk % groups) << a.hp_log2;  // first KV head of the wave
   const int share = (int)((kk / groups) * 8 + (wg & 7));
   if (share >= a.num_shares) return;
-  const int S = a.plan[0];
-  const int total = a.plan[1 + a.B];
-  const int x_begin = share * S;
-  if (x_begin >= total) return;
-  const int x_end = min(x_begin + S, total);
-
   SeqCursor cc;  // tile being computed
-  cc.b = a.plan[2 + a.B + share];
-  cc.lo = a.plan[1 + cc.b];
-  fill_window<FK>(cc, a, cc.b);
-  cc.hi = rdlane(cc.win_hi, 0);
-  cc.lq = rdlane(cc.win_lq, 0);
+  int S, total;
+  if (a.inline_plan) {
+    // one window holds the whole batch
+    int lq, nt, excl;
+    total = wave_plan<FK>(a, lq, nt, excl);
+    S = share_size(a, total);
+    if (share * S >= total) return;
+    const int lane = (int)threadIdx.x;
+    cc.wb = 0;
+    cc.win_hi = lane < a.B ? excl + nt : INT_MAX;
+    cc.win_lq = lq;
+    // first sequence whose tiles end after the share's first tile
+    cc.b = __popcll(__ballot(lane < a.B && excl + nt <= share * S));
+    cc.lo = rdlane(excl, cc.b);
+    cc.hi = rdlane(cc.win_hi, cc.b);
+    cc.lq = rdlane(cc.win_lq, cc.b);
+  } else {
+    S = a.plan[0];
+    total = a.plan[1 + a.B];
+    if (share * S >= total) return;
+    cc.b = a.plan[2 + a.B + share];
+    cc.lo = a.plan[1 + cc.b];
+    fill_window<FK>(cc, a, cc.b);
+    cc.hi = rdlane(cc.win_hi, 0);
+    cc.lq = rdlane(cc.win_lq, 0);
+  }
+  const int x_begin = share * S;
+  const int x_end = min(x_begin + S, total);
   SeqCursor ci = cc, cd = cc;  // tile being issued, block ids being fetched
 
   const int lane = (int)threadIdx.x;
@@ -894,58 +935,13 @@ void decode_split_kernel(DecodeArgs a) {
   for (; xr < x_end; xr += NS) round(std::make_integer_sequence<int, NS>{});
 }
 
-// KIVI fp16 tail: the last ctx_len % 32 tokens of each sequence, keys and
-// values in fp16, as one more record (max_shares + B + b).  One wave per
-// (sequence, KV head); plain fp32 arithmetic.
-template <int D>
-__global__ __launch_bounds__(64) void kivi_tail_kernel(DecodeArgs a) {
-  const int b = (int)blockIdx.x, h = (int)blockIdx.y, lane = (int)threadIdx.x;
-  const int L = min(max(a.ctx_lens[b], 0), a.max_blocks * 32);
-  const int nt = b < a.max_seqs ? (L & 31) : 0;  // tail rows exist only for b < max_seqs
-  const size_t stride = (size_t)D + 2;
-  float* pbase = a.part + ((size_t)(a.max_shares + a.B + b) * a.Hq + h * a.G) * stride;
-  constexpr int CPL = D / 64;  // channels per lane for the value accumulation
-  for (int g = 0; g < a.G; ++g) {
-    const uint16_t* qrow = a.q + ((size_t)b * a.Hq + h * a.G + g) * D;
-    float sc = -INFINITY;
-    if (lane < nt) {
-      const uint16_t* krow = a.k_tail + (((size_t)b * 32 + lane) * a.H + h) * D;
-      float dot = 0.f;
-      for (int c = 0; c < D; ++c) dot = __builtin_fmaf(h2f(qrow[c]), h2f(krow[c]), dot);
-      sc = dot * a.qscale;
-    }
-    float mx = sc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float mu = mx == -INFINITY ? 0.f : mx;
-    const float pv = exp2f(sc - mu);
-    float l = pv;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
-    float accv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) accv[c] = 0.f;
-    for (int t = 0; t < nt; ++t) {
-      const float pt = __shfl(pv, t);
-      const uint16_t* vrow = a.v_tail + (((size_t)b * 32 + t) * a.H + h) * D;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(pt, h2f(vrow[lane * CPL + c]), accv[c]);
-    }
-    float* dst = pbase + g * stride;
-    if (lane == 0) {
-      dst[0] = mx;
-      dst[1] = l;
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) dst[2 + lane * CPL + c] = accv[c];
-  }
-}
-
 // Merge the pieces of one (sequence, query head): M = max m_r,
 // out = sum_r acc_r 2^(m_r - M) / sum_r l_r 2^(m_r - M), rounded to fp16.
 // Sequence b's tiles [P_b, P_b+1) lie in shares P_b / S .. (P_b+1 - 1) / S,
-// whose pieces are records share + b; a KIVI tail adds record
-// max_shares + B + b.  Four waves share the records; lanes own channels.
+// whose pieces are records share + b.  For KIVI keys the last ctx_len % 32
+// tokens (fp16 keys and values in tail row b) are one more piece, computed
+// here by wave 0 in plain fp32.  Four waves share the records; lanes own
+// channels.
 constexpr int MERGE_WAVES = 4;
 
 template <int D, bool KIVI>
@@ -953,19 +949,67 @@ __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   constexpr int CPL = D / 64;
   __shared__ float s_m[MERGE_WAVES];
   __shared__ float s_acc[MERGE_WAVES][D + 1];
+  __shared__ float s_tail[D + 2];  // KIVI tail piece: m, l, acc[D]
   const int bh = (int)blockIdx.x, tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int b = bh / a.Hq, hq = bh - b * a.Hq;
-  const int S = a.plan[0];
-  const int t0 = a.plan[1 + b], t1 = a.plan[2 + b];
+  int S, t0, t1;
+  if (a.inline_plan) {
+    int lq, nt, excl;
+    const int total = wave_plan<KIVI ? F_KIVI : F_INT8>(a, lq, nt, excl);
+    S = share_size(a, total);
+    t0 = rdlane(excl, b);
+    t1 = t0 + rdlane(nt, b);
+  } else {
+    S = a.plan[0];
+    t0 = a.plan[1 + b];
+    t1 = a.plan[2 + b];
+  }
   const int first = t1 > t0 ? t0 / S : 0;
-  const int npieces = t1 > t0 ? (t1 - 1) / S - first + 1 : 0;
-  const int nrec = npieces + (KIVI ? 1 : 0);
+  const int nrec = t1 > t0 ? (t1 - 1) / S - first + 1 : 0;
   const size_t stride = (size_t)D + 2;
-  auto rec = [&](int i) -> const float* {
-    const size_t r = i < npieces ? (size_t)(first + i + b) : (size_t)(a.max_shares + a.B + b);
-    return a.part + (r * a.Hq + hq) * stride;
-  };
-  float M = -INFINITY;
+  auto rec = [&](int i) -> const float* { return a.part + ((size_t)(first + i + b) * a.Hq + hq) * stride; };
+  float tm = -INFINITY;  // the tail piece's max (KIVI)
+  if constexpr (KIVI) {
+    if (w == 0) {
+      const int L = min(max(a.ctx_lens[b], 0), a.max_blocks * 32);
+      const int nt = b < a.max_seqs ? (L & 31) : 0;  // tail rows exist only for b < max_seqs
+      const int h = hq / a.G;
+      const uint16_t* qrow = a.q + ((size_t)b * a.Hq + hq) * D;
+      float sc = -INFINITY;
+      if (lane < nt) {
+        const uint16_t* krow = a.k_tail + (((size_t)b * 32 + lane) * a.H + h) * D;
+        float dot = 0.f;
+        for (int c = 0; c < D; ++c) dot = __builtin_fmaf(h2f(qrow[c]), h2f(krow[c]), dot);
+        sc = dot * a.qscale;
+      }
+      float mx = sc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float mu = mx == -INFINITY ? 0.f : mx;
+      const float pv = exp2f(sc - mu);
+      float l = pv;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+      float accv[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) accv[c] = 0.f;
+      for (int t = 0; t < nt; ++t) {
+        const float pt = __shfl(pv, t);
+        const uint16_t* vrow = a.v_tail + (((size_t)b * 32 + t) * a.H + h) * D;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(pt, h2f(vrow[lane * CPL + c]), accv[c]);
+      }
+      if (lane == 0) {
+        s_tail[0] = mx;
+        s_tail[1] = l;
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) s_tail[2 + lane * CPL + c] = accv[c];
+    }
+    __syncthreads();
+    tm = s_tail[0];
+  }
+  float M = tm;
   for (int i = tid; i < nrec; i += MERGE_WAVES * 64) M = fmaxf(M, rec(i)[0]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
@@ -986,6 +1030,12 @@ __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
       l = __builtin_fmaf(p[1], wgt, l);
 #pragma unroll
       for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(p[2 + lane * CPL + c], wgt, accv[c]);
+    }
+    if (KIVI && w == 0 && tm != -INFINITY) {
+      const float wgt = exp2f(tm - M);
+      l = __builtin_fmaf(s_tail[1], wgt, l);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(s_tail[2 + lane * CPL + c], wgt, accv[c]);
     }
   }
 #pragma unroll
@@ -1114,19 +1164,19 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
   } else {
     a.num_shares = a.max_shares;
   }
-  hipLaunchKernelGGL((plan_kernel<FK == F_KIVI>), dim3(1), dim3(PLAN_THREADS), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // Up to 64 sequences, every wave derives the plan from ctx_lens itself.
+  a.inline_plan = a.B <= 64 ? 1 : 0;
+  hipError_t e;
+  if (!a.inline_plan) {
+    hipLaunchKernelGGL((plan_kernel<FK == F_KIVI>), dim3(1), dim3(PLAN_THREADS), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // one wave per (share, group of HP KV heads); see decode_split_kernel for the order
   const uint32_t wgs = (((uint32_t)a.num_shares + 7) / 8) * 8 * (uint32_t)(a.H >> a.hp_log2);
   hipLaunchKernelGGL((decode_split_kernel<FK, FV, D, HPC>), dim3(wgs), dim3(64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (FK == F_KIVI) {
-    hipLaunchKernelGGL((kivi_tail_kernel<D>), dim3((unsigned)a.B, (unsigned)a.H), dim3(64), 0, st, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   hipLaunchKernelGGL((merge_kernel<D, FK == F_KIVI>), dim3((unsigned)(a.B * a.Hq)), dim3(MERGE_WAVES * 64), 0, st,
                      a);
   return hipGetLastError();
@@ -1194,7 +1244,7 @@ bool plan_decode(const kvq_cache& c, int32_t batch, int32_t n_q_heads, int32_t m
   p->max_shares = (int32_t)shares;
   const size_t ints = 2 + (size_t)batch + (size_t)shares;
   p->plan_bytes = (ints * sizeof(int32_t) + 255) / 256 * 256;
-  p->records = (size_t)shares + batch + (c.k_dtype == KVQ_INT4_KIVI ? batch : 0);
+  p->records = (size_t)shares + batch;
   p->bytes = p->plan_bytes + p->records * n_q_heads * ((size_t)c.head_dim + 2) * sizeof(float);
   return true;
 }

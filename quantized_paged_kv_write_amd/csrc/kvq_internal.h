@@ -70,6 +70,7 @@ struct DecodeArgs {
   // sequence; share i covers tiles [i S, (i + 1) S) and is processed by
   // n_kv_heads / HP waves, one per group of HP KV heads.
   int32_t share_tiles;  // S requested by the caller; 0 = balanced over num_shares
+  int32_t inline_plan;  // B <= 64: the kernels derive the plan from ctx_lens themselves
   int32_t num_shares;   // shares launched (<= max_shares)
   int32_t max_shares;   // shares the workspace was laid out for
   // Workspace: plan ints, then the partial softmax records.
@@ -78,7 +79,7 @@ struct DecodeArgs {
   //   plan[2 + B + i]      sequence holding the first tile of share i
   int32_t* plan;
   // Record r, query head hq: part[(r Hq + hq) (D + 2) ...] = m, l, acc[D] (fp32).
-  // Records: share i's piece of sequence b -> i + b; KIVI fp16 tail of b -> max_shares + B + b.
+  // Records: share i's piece of sequence b -> i + b.
   float* part;
   uint16_t* out;  // fp16 (B, Hq, D)
 };

@@ -80,17 +80,18 @@ def test_write_argument_errors():
 
 def test_workspace_query():
     # Layout: plan ints (2 + batch + shares, padded to 256 bytes), then
-    # (shares + batch [+ batch for KIVI tails]) records of n_q_heads x (D + 2) fp32.
+    # (shares + batch) records of n_q_heads x (D + 2) fp32.
     # Tiles are 32 (token, head) rows of HP heads: here 2 KV heads x 2 query
     # heads each -> HP = 2, 16 tokens per tile.
     # mb 10 x bs 16 = 160 tokens = 10 tiles per sequence, 30 for the call; shares of
     # 64 tokens = 4 tiles -> 8 shares; 13 ints -> 256 bytes; 11 records.
     rc, n = _ws(_cache(), batch=3, hq=4, mb=10, pps=64)
     assert rc == OK and n == 256 + 11 * 4 * 130 * 4
-    # KIVI (one head per wave, 32-token tiles): 8 pages = 8 tiles, one share; records 1 + 1 + 1 tail.
+    # KIVI, 1 query head per KV head -> HP 2, 16-token tiles: 8 pages = 16 tiles, one
+    # share of 256 tokens; records 1 + 1.
     rc, n = _ws(_cache(k_dtype=4, block_size=32, max_seqs=1, k_zeros=FAKE, k_tail=FAKE, v_tail=FAKE),
                 batch=1, hq=2, mb=8, pps=256)
-    assert rc == OK and n == 256 + 3 * 2 * 130 * 4
+    assert rc == OK and n == 256 + 2 * 2 * 130 * 4
     # automatic: min(ceil(4096 / (H / HP)), ceil(tiles / 4)) shares = min(4096, 500); 504 ints -> 2048 bytes
     rc, n = _ws(_cache(), batch=2, hq=4, mb=1000, pps=0)
     assert rc == OK and n == 2048 + 502 * 4 * 130 * 4
