@@ -940,11 +940,10 @@ void decode_split_kernel(DecodeArgs a) {
 // Sequence b's tiles [P_b, P_b+1) lie in shares P_b / S .. (P_b+1 - 1) / S,
 // whose pieces are records share + b.  For KIVI keys the last ctx_len % 32
 // tokens (fp16 keys and values in tail row b) are one more piece, computed
-// here by wave 0 in plain fp32.  Four waves share the records; lanes own
+// here by wave 0 in plain fp32.  MW waves share the records (16 when the
+// grid is small, so a few long record lists still fill the GPU); lanes own
 // channels.
-constexpr int MERGE_WAVES = 4;
-
-template <int D, bool KIVI>
+template <int D, bool KIVI, int MERGE_WAVES>
 __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   constexpr int CPL = D / 64;
   __shared__ float s_m[MERGE_WAVES];
@@ -1177,8 +1176,10 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
   hipLaunchKernelGGL((decode_split_kernel<FK, FV, D, HPC>), dim3(wgs), dim3(64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<D, FK == F_KIVI>), dim3((unsigned)(a.B * a.Hq)), dim3(MERGE_WAVES * 64), 0, st,
-                     a);
+  if (a.B * a.Hq < 512)
+    hipLaunchKernelGGL((merge_kernel<D, FK == F_KIVI, 16>), dim3((unsigned)(a.B * a.Hq)), dim3(16 * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, FK == F_KIVI, 4>), dim3((unsigned)(a.B * a.Hq)), dim3(4 * 64), 0, st, a);
   return hipGetLastError();
 }
 
