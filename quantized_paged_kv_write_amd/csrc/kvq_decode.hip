@@ -273,8 +273,9 @@ struct TileRegs {
 // zeros) into registers; bid is the block id of token lane % 32's page.
 // Returns the live-token mask (bit t and t + 32: token t0 + t is in the
 // context on a valid page).  Every load is issued by every lane, so each
-// tile costs the same number of loads: masked rows and idle lanes read the
-// start of the buffer, and those bytes are never used unmasked.
+// tile costs the same number of loads: masked rows read flat row 0 (every
+// cache has at least one block) and idle lanes the start of the buffer;
+// those bytes are never used unmasked.
 template <int FK, int FV, int D, int HPC>
 __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int t0, int tok_end, int h0,
                                               TileRegs<FK, FV, D, HPC>& r) {
@@ -287,7 +288,7 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
   bool live;
   const uint32_t r_own = tile_row(a, bid, lane & 31, t0, tok_end, h0, live);
   const uint64_t live_mask = __ballot(live);
-  const uint32_t rl = live ? r_own : ~0u;
+  const uint32_t rl = live ? r_own : 0u;
 #pragma unroll
   for (int i = 0; i < S::NLK; ++i) {
     const int p = 64 * i + lane;  // LDS chunk slot this lane stores
@@ -295,7 +296,7 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
     const int col = (p % CHK) ^ kswz<CHK>(row);
     const uint32_t rr = (uint32_t)__shfl((int)rl, row);
     r.k[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const u4*>(a.k_codes + (rr != ~0u ? (size_t)rr * KS::RB + col * 16 : 0)));
+        reinterpret_cast<const u4*>(a.k_codes + (size_t)rr * KS::RB + col * 16));
   }
 #pragma unroll
   for (int i = 0; i < S::NLV; ++i) {
@@ -304,7 +305,7 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
     const int col = (p % VS::CH) ^ vswz<VS::CH>(row);
     const uint32_t rr = (uint32_t)__shfl((int)rl, row);
     r.v[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const u4*>(a.v_codes + (rr != ~0u ? (size_t)rr * VS::RB + col * 16 : 0)));
+        reinterpret_cast<const u4*>(a.v_codes + (size_t)rr * VS::RB + col * 16));
   }
   // scale dwords (LDS dword index): [rho] the dword holding row rho's key
   // scale, [32 + rho] the first value-scale dword of row rho, [32 + 32 k +
@@ -327,12 +328,11 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
     using TR = TileRegs<FK, FV, D, HPC>;
     constexpr int HALF = HPC * D / 8;  // chunks of scales
     const uint32_t r0 = (uint32_t)__shfl((int)rl, 0);
-    const bool ok = r0 != ~0u;
     const size_t mrow = ((size_t)(r0 / (32u * (uint32_t)a.H)) * a.H + h0) * D;
 #pragma unroll
     for (int k = 0; k < TR::KM; ++k) {
       const int c = 64 * k + lane;
-      const bool use = ok && c < TR::MCH;
+      const bool use = c < TR::MCH;
       const uint16_t* src = (c < HALF ? a.k_scales : a.k_zeros) + (use ? mrow + 8 * (c < HALF ? c : c - HALF) : 0);
       r.m[k] = *reinterpret_cast<const u4*>(src);
     }
@@ -509,6 +509,29 @@ void decode_split_kernel(DecodeArgs a) {
   if (n < NC) {
 #pragma unroll
     for (int rho = 0; rho < 32; ++rho) colmask |= ((rho & hp_mask) == n / G ? 1u : 0u) << rho;
+  }
+  // v_perm selectors that place the bf16 probabilities of column n's rows
+  // into the probability operand (slots of other heads' rows get 0): psel[q]
+  // builds operand dword q from the packed pair of split_bf16x2.
+  uint32_t psel[4] = {0u, 0u, 0u, 0u};
+  {
+    // move half `from` of a dword to half `to`, zero the other half
+    auto half_sel = [](int from, bool to) __attribute__((always_inline)) {
+      const uint32_t v = (uint32_t)((2 * from + 1) << 8 | 2 * from);
+      return to ? v << 16 | 0x0C0Cu : 0x0C0C0000u | v;
+    };
+    if constexpr (HPC == 4) {
+      // one row per u: row hn of u = q >> 1 sits in the dword q with
+      // q & 1 == (INT4: hn & 1; 8-bit: hn >> 1), half (INT4: hn >> 1; 8-bit: hn & 1)
+      const int dsel = FV == F_INT4 ? (hn & 1) : (hn >> 1);
+      const bool hsel = FV == F_INT4 ? (hn >> 1) : (hn & 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) psel[q] = (q & 1) == dsel ? half_sel(q >> 1, hsel) : 0x0C0C0C0Cu;
+    } else if constexpr (HPC == 2 && FV != F_INT4) {
+      // rows hn + 2 i of u: dword 2 u + i, half hn (from half i of u's pair)
+      psel[0] = half_sel(0, hn);
+      psel[1] = half_sel(1, hn);
+    }
   }
   f4 acc[VS::NPV];
 #pragma unroll
@@ -810,8 +833,7 @@ void decode_split_kernel(DecodeArgs a) {
     // heads are 0.  Value operands hold exact codes, biased to non-negative
     // for INT8/INT4; the bias times the probability sum is removed once,
     // after the last tile (cs_run).
-    // Place bf16 x (low half of b) into half `hi` of a dword.
-    auto at_half = [](uint32_t b, bool hi) __attribute__((always_inline)) { return hi ? b << 16 : b & 0xFFFFu; };
+    auto place = [](uint32_t b, uint32_t sel) __attribute__((always_inline)) { return __builtin_amdgcn_perm(b, b, sel); };
     if constexpr (FV == F_INT4) {
       // dword q holds slots (q >> 1) 4 + (q & 1) (rows r = q & 1, low half) and
       // that + 2 (r = (q & 1) + 2, high half) of u = q >> 1 (value_operand_int4)
@@ -843,23 +865,17 @@ void decode_split_kernel(DecodeArgs a) {
             al[2 * u + 1] = hn ? l : 0u;
           }
         } else {
-          // row hn of u: dword 2 u + (hn & 1), half hn >> 1
+          // row hn of u: dword 2 u + (hn & 1), half hn >> 1 (psel)
           uint32_t h, l;
           f2 used;
           split_bf16x2(f2{p[0][0] * s_fv[rows[0][0] * VS::NG + grp], p[1][0] * s_fv[rows[1][0] * VS::NG + grp]}, h, l,
                        used);
           cs_run[grp] += used.x + used.y;
-          const bool up = hn >> 1, odd = hn & 1;
-          const uint32_t h0 = at_half(h, up), h1 = at_half(h >> 16, up);
-          const uint32_t l0 = at_half(l, up), l1 = at_half(l >> 16, up);
-          ah[0] = odd ? 0u : h0;
-          ah[1] = odd ? h0 : 0u;
-          ah[2] = odd ? 0u : h1;
-          ah[3] = odd ? h1 : 0u;
-          al[0] = odd ? 0u : l0;
-          al[1] = odd ? l0 : 0u;
-          al[2] = odd ? 0u : l1;
-          al[3] = odd ? l1 : 0u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            ah[q] = place(h, psel[q]);
+            al[q] = place(l, psel[q]);
+          }
         }
         const b8 A_hi = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
         const b8 A_lo = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
@@ -890,10 +906,10 @@ void decode_split_kernel(DecodeArgs a) {
           f2 used;
           split_bf16x2(f2{p[u][0] * s_fv[rows[u][0]], p[u][1] * s_fv[rows[u][1]]}, h, l, used);
           if constexpr (FV == F_INT8) cs_run[0] += used.x + used.y;
-          ah[2 * u] = at_half(h, hn);
-          ah[2 * u + 1] = at_half(h >> 16, hn);
-          al[2 * u] = at_half(l, hn);
-          al[2 * u + 1] = at_half(l >> 16, hn);
+          ah[2 * u] = place(h, psel[0]);
+          ah[2 * u + 1] = place(h, psel[1]);
+          al[2 * u] = place(l, psel[0]);
+          al[2 * u + 1] = place(l, psel[1]);
         }
       } else {
         // row hn of u: dword 2 u + (hn >> 1), half hn & 1
@@ -901,17 +917,11 @@ void decode_split_kernel(DecodeArgs a) {
         f2 used;
         split_bf16x2(f2{p[0][0] * s_fv[rows[0][0]], p[1][0] * s_fv[rows[1][0]]}, h, l, used);
         if constexpr (FV == F_INT8) cs_run[0] += used.x + used.y;
-        const bool odd = hn & 1, up = hn >> 1;
-        const uint32_t h0 = at_half(h, odd), h1 = at_half(h >> 16, odd);
-        const uint32_t l0 = at_half(l, odd), l1 = at_half(l >> 16, odd);
-        ah[0] = up ? 0u : h0;
-        ah[1] = up ? h0 : 0u;
-        ah[2] = up ? 0u : h1;
-        ah[3] = up ? h1 : 0u;
-        al[0] = up ? 0u : l0;
-        al[1] = up ? l0 : 0u;
-        al[2] = up ? 0u : l1;
-        al[3] = up ? l1 : 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ah[q] = place(h, psel[q]);
+          al[q] = place(l, psel[q]);
+        }
       }
       const b8 A_hi = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
       const b8 A_lo = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
