@@ -103,14 +103,16 @@ template <int FK>
 __device__ __forceinline__ h8 key_operand(const uint32_t* w, int kb) {
   u4 r;
   if constexpr (FK == F_KIVI) {
-    // 8 unsigned nibbles of one dword; pair i = channels (i, i + 4):
-    // (1024 + n) - 1024 = n exactly.
-    const uint32_t d = w[kb];
-    const h2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
-    r.x = h2_bits(as_h2((d & 0x000F000Fu) | 0x64006400u) - bias);
-    r.y = h2_bits(as_h2(((d >> 4) & 0x000F000Fu) | 0x64006400u) - bias);
-    r.z = h2_bits(as_h2(((d >> 8) & 0x000F000Fu) | 0x64006400u) - bias);
-    r.w = h2_bits(as_h2(((d >> 12) & 0x000F000Fu) | 0x64006400u) - bias);
+    // 8 unsigned nibbles of one dword; pair i = channels (i, i + 4).  A
+    // nibble in mantissa bits 0-3 of an fp16 is the subnormal n 2^-24, in
+    // bits 4-7 it is 16 n 2^-24, both exact: even channels (x, z) give
+    // n 2^-24, odd channels (y, w) 16 n 2^-24; the query operand of even
+    // channels carries the factor 16 instead.
+    const uint32_t d = w[kb], t = d >> 8;
+    r.x = d & 0x000F000Fu;
+    r.y = d & 0x00F000F0u;
+    r.z = t & 0x000F000Fu;
+    r.w = t & 0x00F000F0u;
   } else {
     uint32_t x0, x1, x2, x3;
     if constexpr (FK == F_FP8) {
@@ -164,36 +166,46 @@ __device__ __forceinline__ b8 value_operand_8bit(i2 t) {
 }
 
 // INT4: 8 bytes = 8 tokens of a channel pair; element order of both operands
-// is tokens [0, 2, 1, 3, 4, 6, 5, 7].
+// is tokens [0, 2, 1, 3, 4, 6, 5, 7].  Each operand dword is one v_bitop3:
+// bits under the mask 0x000F000F take the code nibble xor 8 (code + 8), the
+// others the bf16 128 pattern, giving bf16 128 + (code + 8) exactly.
+__device__ __forceinline__ uint32_t int4_pair_bf16(uint32_t x) {
+  // f(x, m, c) = m ? x ^ c : c (truth table of x = 0xF0, m = 0xCC, c = 0xAA)
+  return __builtin_amdgcn_bitop3_b32(x, 0x000F000Fu, 0x43084308u, 0x6A);
+}
 __device__ __forceinline__ void value_operand_int4(i2 t, b8& even, b8& odd) {
-  const uint32_t d0 = (uint32_t)t.x ^ 0x88888888u, d1 = (uint32_t)t.y ^ 0x88888888u;
-  const uint32_t m = 0x000F000Fu, o = 0x43004300u;
+  const uint32_t d0 = (uint32_t)t.x, d1 = (uint32_t)t.y;
   u4 e, od;
-  e.x = (d0 & m) | o;
-  e.y = ((d0 >> 8) & m) | o;
-  e.z = (d1 & m) | o;
-  e.w = ((d1 >> 8) & m) | o;
-  od.x = ((d0 >> 4) & m) | o;
-  od.y = ((d0 >> 12) & m) | o;
-  od.z = ((d1 >> 4) & m) | o;
-  od.w = ((d1 >> 12) & m) | o;
+  e.x = int4_pair_bf16(d0);
+  e.y = int4_pair_bf16(d0 >> 8);
+  e.z = int4_pair_bf16(d1);
+  e.w = int4_pair_bf16(d1 >> 8);
+  od.x = int4_pair_bf16(d0 >> 4);
+  od.y = int4_pair_bf16(d0 >> 12);
+  od.z = int4_pair_bf16(d1 >> 4);
+  od.w = int4_pair_bf16(d1 >> 12);
   even = __builtin_bit_cast(b8, e);
   odd = __builtin_bit_cast(b8, od);
 }
 
 // x = hi + lo with hi = bf16_rne(x), lo = bf16_rne(x - hi), two values at a
-// time (v_cvt_pk_bf16_f32); `used` is what the operands hold, hi + lo.
+// time (v_cvt_pk_bf16_f32).
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void split_bf16x2(f2 x, uint32_t& hi, uint32_t& lo, f2& used) {
+__device__ __forceinline__ void split_bf16x2(f2 x, uint32_t& hi, uint32_t& lo) {
   const bf2 h = __builtin_convertvector(x, bf2);
   const uint32_t hb = __builtin_bit_cast(uint32_t, h);
   const f2 fh = {__builtin_bit_cast(float, hb << 16), __builtin_bit_cast(float, hb & 0xFFFF0000u)};
   const bf2 l = __builtin_convertvector(x - fh, bf2);
-  const uint32_t lb = __builtin_bit_cast(uint32_t, l);
   hi = hb;
-  lo = lb;
-  used = fh + f2{__builtin_bit_cast(float, lb << 16), __builtin_bit_cast(float, lb & 0xFFFF0000u)};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+// cs + the four bf16 values of a split pair (what the operands hold), with
+// two v_dot2_f32_bf16 against (1, 1)
+__device__ __forceinline__ float add_split(float cs, uint32_t hi, uint32_t lo) {
+  const bf2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  cs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, hi), one, cs, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, lo), one, cs, false);
 }
 
 // Tile row rho (0..31) is token t0 + rho / HP of the sequence, KV head
@@ -547,7 +559,7 @@ void decode_split_kernel(DecodeArgs a) {
   bool piece_start = true;
   // KIVI: q * s of the current page (fp16 hi + lo) and q . z, column n's head
   h8 qhi[FK == F_KIVI ? KS::KB : 1], qlo[FK == F_KIVI ? KS::KB : 1];
-  float qz = 0.f;
+  float qz = 0.f, kmul = 0.f;  // score = raw kmul + qz
 
   // Value transpose reads: lane (j, i) points at row T_j[i / 2] of the value
   // tile, byte 8 (i % 2) of the chunk, where T_j[e] = 16 (e / 4) + 4 j + e % 4
@@ -725,10 +737,15 @@ void decode_split_kernel(DecodeArgs a) {
     }
 
     // ---- KIVI: the page's query operand q * s (fp16 hi + lo) and q . z for
-    //      column n's head, once per page (a page is HPC tiles) ---------------
+    //      column n's head, once per page (a page is HPC tiles).  q * s is
+    //      scaled by a power of two F (per column) so that its largest
+    //      magnitude times 16 lies in [2^14, 2^15): the fp16 operands neither
+    //      overflow nor lose digits to subnormals. --------------------------
     if constexpr (FK == F_KIVI) {
       if (new_piece || ((x - cc.lo) & (HPC - 1)) == 0) {
         qz = 0.f;
+        float qs[KS::KB][8];
+        float mx = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KS::KB; ++kb) {
           const int cb = j * (D / 4) + 8 * kb;
@@ -741,16 +758,32 @@ void decode_split_kernel(DecodeArgs a) {
           for (int e = 0; e < 8; ++e) {
             const int ch = key_channel<FK, D>(j, kb, e) - cb;
             const float qv = (float)qop[kb][e];
-            const float qs = qv * s8[ch];
-            const _Float16 hi = (_Float16)qs;
-            qhi[kb][e] = hi;
-            qlo[kb][e] = (_Float16)(qs - (float)hi);
+            qs[kb][e] = qv * s8[ch];
+            mx = fmaxf(mx, fabsf(qs[kb][e]));
             qz = __builtin_fmaf(qv, z8[ch], qz);
           }
         }
         qz += __shfl_xor(qz, 16);
         qz += __shfl_xor(qz, 32);
         qz *= a.qscale;
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // mx < 2^ex; F = 2^(11 - ex), so 16 F mx < 2^15
+        const int ex = mx > 0.f ? min(max(__builtin_amdgcn_frexp_expf(mx), -100), 100) : 0;
+        const float f_odd = __builtin_ldexpf(1.f, 11 - ex), f_even = 16.f * f_odd;
+        // raw = 2^-24 16 F sum n q s
+        kmul = a.qscale * __builtin_ldexpf(1.f, 20 - (11 - ex));
+#pragma unroll
+        for (int kb = 0; kb < KS::KB; ++kb) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            // slots e = 2, 3, 6, 7 hold odd channels (16 n 2^-24 keys)
+            const float xs = qs[kb][e] * ((e & 2) ? f_odd : f_even);
+            const _Float16 hi = (_Float16)xs;
+            qhi[kb][e] = hi;
+            qlo[kb][e] = (_Float16)(xs - (float)hi);
+          }
+        }
       }
     }
 
@@ -789,7 +822,7 @@ void decode_split_kernel(DecodeArgs a) {
         else if constexpr (HPC == 2) raw = hn ? sc[u][2 * i + 1] : sc[u][2 * i];
         else raw = hn == 0 ? sc[u][0] : hn == 1 ? sc[u][1] : hn == 2 ? sc[u][2] : sc[u][3];
         float v;
-        if constexpr (FK == F_KIVI) v = __builtin_fmaf(raw, a.qscale, qz);
+        if constexpr (FK == F_KIVI) v = __builtin_fmaf(raw, kmul, qz);
         else v = raw * s_fk[tr];
         // a masked row's key codes may be anything, and a row of another KV
         // head than column n's does not belong to it: select, don't multiply
@@ -844,21 +877,18 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int u = q >> 1, r0 = q & 1;
-            f2 used;
             split_bf16x2(f2{p[u][r0] * s_fv[rows[u][r0] * VS::NG + grp],
                             p[u][r0 + 2] * s_fv[rows[u][r0 + 2] * VS::NG + grp]},
-                         ah[q], al[q], used);
-            cs_run[grp] += used.x + used.y;
+                         ah[q], al[q]);
+            cs_run[grp] = add_split(cs_run[grp], ah[q], al[q]);
           }
         } else if constexpr (HPC == 2) {
           // rows hn, hn + 2 of u share dword 2 u + hn
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             uint32_t h, l;
-            f2 used;
-            split_bf16x2(f2{p[u][0] * s_fv[rows[u][0] * VS::NG + grp], p[u][1] * s_fv[rows[u][1] * VS::NG + grp]}, h, l,
-                         used);
-            cs_run[grp] += used.x + used.y;
+            split_bf16x2(f2{p[u][0] * s_fv[rows[u][0] * VS::NG + grp], p[u][1] * s_fv[rows[u][1] * VS::NG + grp]}, h, l);
+            cs_run[grp] = add_split(cs_run[grp], h, l);
             ah[2 * u] = hn ? 0u : h;
             ah[2 * u + 1] = hn ? h : 0u;
             al[2 * u] = hn ? 0u : l;
@@ -867,10 +897,8 @@ void decode_split_kernel(DecodeArgs a) {
         } else {
           // row hn of u: dword 2 u + (hn & 1), half hn >> 1 (psel)
           uint32_t h, l;
-          f2 used;
-          split_bf16x2(f2{p[0][0] * s_fv[rows[0][0] * VS::NG + grp], p[1][0] * s_fv[rows[1][0] * VS::NG + grp]}, h, l,
-                       used);
-          cs_run[grp] += used.x + used.y;
+          split_bf16x2(f2{p[0][0] * s_fv[rows[0][0] * VS::NG + grp], p[1][0] * s_fv[rows[1][0] * VS::NG + grp]}, h, l);
+          cs_run[grp] = add_split(cs_run[grp], h, l);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             ah[q] = place(h, psel[q]);
@@ -894,18 +922,16 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int u = q >> 1, r0 = 2 * (q & 1);
-          f2 used;
-          split_bf16x2(f2{p[u][r0] * s_fv[rows[u][r0]], p[u][r0 + 1] * s_fv[rows[u][r0 + 1]]}, ah[q], al[q], used);
-          if constexpr (FV == F_INT8) cs_run[0] += used.x + used.y;
+          split_bf16x2(f2{p[u][r0] * s_fv[rows[u][r0]], p[u][r0 + 1] * s_fv[rows[u][r0 + 1]]}, ah[q], al[q]);
+          if constexpr (FV == F_INT8) cs_run[0] = add_split(cs_run[0], ah[q], al[q]);
         }
       } else if constexpr (HPC == 2) {
         // row hn + 2 i of u: dword 2 u + i, half hn
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           uint32_t h, l;
-          f2 used;
-          split_bf16x2(f2{p[u][0] * s_fv[rows[u][0]], p[u][1] * s_fv[rows[u][1]]}, h, l, used);
-          if constexpr (FV == F_INT8) cs_run[0] += used.x + used.y;
+          split_bf16x2(f2{p[u][0] * s_fv[rows[u][0]], p[u][1] * s_fv[rows[u][1]]}, h, l);
+          if constexpr (FV == F_INT8) cs_run[0] = add_split(cs_run[0], h, l);
           ah[2 * u] = place(h, psel[0]);
           ah[2 * u + 1] = place(h, psel[1]);
           al[2 * u] = place(l, psel[0]);
@@ -914,9 +940,8 @@ void decode_split_kernel(DecodeArgs a) {
       } else {
         // row hn of u: dword 2 u + (hn >> 1), half hn & 1
         uint32_t h, l;
-        f2 used;
-        split_bf16x2(f2{p[0][0] * s_fv[rows[0][0]], p[1][0] * s_fv[rows[1][0]]}, h, l, used);
-        if constexpr (FV == F_INT8) cs_run[0] += used.x + used.y;
+        split_bf16x2(f2{p[0][0] * s_fv[rows[0][0]], p[1][0] * s_fv[rows[1][0]]}, h, l);
+        if constexpr (FV == F_INT8) cs_run[0] = add_split(cs_run[0], h, l);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           ah[q] = place(h, psel[q]);
