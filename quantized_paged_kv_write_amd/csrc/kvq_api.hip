@@ -86,6 +86,9 @@ int kvq_write(const kvq_cache* cache, const void* k, const void* v, const int64_
   a.k_tail = static_cast<uint16_t*>(cache->k_tail);
   a.v_tail = static_cast<uint16_t*>(cache->v_tail);
   a.max_seqs = cache->max_seqs;
+  // KIVI seal waves: one per call token for small calls (decode steps), one
+  // per 32 tokens otherwise
+  a.seal_chunk = num_tokens <= 2048 ? 1 : 32;
   return launch_write(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

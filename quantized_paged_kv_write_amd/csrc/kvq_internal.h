@@ -46,6 +46,7 @@ struct WriteArgs {
   uint16_t* k_tail;
   uint16_t* v_tail;
   int32_t max_seqs;
+  int32_t seal_chunk;  // KIVI: call tokens per seal wave (32, or 1 for small calls)
 };
 
 struct DecodeArgs {

@@ -76,7 +76,9 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
   u32x4 xin[ITER];
   int64_t slot[ITER];
   uint32_t tok[ITER];
-  // Issue every load of the block first so ITER rows per lane are in flight.
+  // Issue every load of the block first so ITER rows per lane are in flight:
+  // the slots, then the rows (loads complete in issue order, so the tail
+  // lookups below wait for the slots only).
 #pragma unroll
   for (int i = 0; i < ITER; ++i) {
     const uint32_t r = row0 + i * S::RPP;
@@ -85,7 +87,33 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
     if (r < nrows) {
       tok[i] = fastdiv(r, a.div_h);
       slot[i] = a.slots[tok[i]];
-      xin[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)r * D) + lir);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const uint32_t r = row0 + i * S::RPP;
+    if (r < nrows) xin[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)r * D) + lir);
+  }
+  // KIVI keys: whether the row's page is completed within this call (its
+  // last row is at the matching call position), looked up while the rows
+  // are in flight.  Rows of pages left open go to the sequence's fp16 tail.
+  bool to_tail[ITER];
+  int32_t tseq[ITER];
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    to_tail[i] = false;
+    tseq[i] = -1;
+    if constexpr (TAIL) {
+      const int64_t sl = slot[i];
+      if (row0 + i * S::RPP < nrows && sl >= 0 && sl < a.capacity) {
+        const int off = (int)(sl % a.bs);
+        const int64_t te = (int64_t)tok[i] + (a.bs - 1 - off);
+        const int32_t seq = a.seq_idx[tok[i]];
+        bool sealed = false;
+        if (te < a.T) sealed = a.seq_idx[te] == seq && a.slots[te] == sl + (a.bs - 1 - off);
+        to_tail[i] = !sealed && seq >= 0 && seq < a.max_seqs;
+        tseq[i] = seq;
+      }
     }
   }
 #pragma unroll
@@ -125,13 +153,9 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
       if constexpr (TAIL) {
         // KIVI keys: a row whose page is not completed within this call is
         // kept in fp16 (key and value) in its sequence's tail.
-        const int off = (int)(s % a.bs);
-        const int64_t te = (int64_t)tok[i] + (a.bs - 1 - off);
-        const int32_t seq = a.seq_idx[tok[i]];
-        bool sealed = false;
-        if (te < a.T) sealed = a.seq_idx[te] == seq && a.slots[te] == s + (a.bs - 1 - off);
-        if (!sealed && seq >= 0 && seq < a.max_seqs) {
-          const size_t trow = ((size_t)seq * a.bs + off) * a.H + h;
+        if (to_tail[i]) {
+          const int off = (int)(s % a.bs);
+          const size_t trow = ((size_t)tseq[i] * a.bs + off) * a.H + h;
           reinterpret_cast<u32x4*>(a.v_tail + trow * D)[lir] = xin[i];
           reinterpret_cast<u32x4*>(a.k_tail + trow * D)[lir] =
               reinterpret_cast<const u32x4*>(a.k + (size_t)r * D)[lir];
@@ -153,15 +177,20 @@ __global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0
   }
 }
 
-// KIVI key pages.  Block (chunk of 32 call tokens, head h), one wave.  Every
-// token of the chunk that lands on the last row of a page completes that
-// page: its 32 key rows (from this call where present at the expected call
-// positions, else from the sequence's tail) are quantized per channel:
+// KIVI key pages.  Block (chunk of C call tokens, head h), one wave; C = 32
+// for large calls (a chunk then holds about one page end) and 1 for small
+// ones (a decode step may complete a page in every sequence at once, and
+// each page gets its own wave).  Every token of the chunk that lands on the
+// last row of a page completes that page: its 32 key rows (from this call
+// where present at the expected call positions, else from the sequence's
+// tail) are quantized per channel:
 //   s = fp16(fl32(max - min) / 15), z = min, code = clip(rint((x - z) / s), 0, 15).
 // Each lane owns PPL channel pairs of every row (rows are split over RG row
 // groups when a row has fewer pairs than the wave has lanes), so one row is
 // one coalesced load across the wave and the per-channel min and max stay in
-// registers.
+// registers.  The rows are loaded from the call positions while the check
+// that they hold the page's tokens is in flight; rows that fail it are
+// reloaded from the tail.
 template <int D>
 __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
   constexpr int PPL = D >= 256 ? D / 128 : 1;  // channel pairs per lane
@@ -169,12 +198,13 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
   constexpr int RG = 64 / LPR;                 // row groups
   constexpr int RPL = 32 / RG;                 // rows per lane
   const int h = (int)blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  const int C = a.seal_chunk;
+  const int64_t t0 = (int64_t)blockIdx.x * C;
   const int lane = (int)threadIdx.x;
-  // slot and sequence of the chunk's token `lane` (lanes < 32)
+  // slot and sequence of the chunk's token `lane` (lanes < C)
   int64_t my_slot = -1;
   int32_t my_seq = -1;
-  if (lane < 32 && t0 + lane < a.T) {
+  if (lane < C && t0 + lane < a.T) {
     my_slot = a.slots[t0 + lane];
     my_seq = a.seq_idx[t0 + lane];
   }
@@ -194,22 +224,33 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
     // chunk (already loaded); others look them up.
     bool inc = false;
     if (lane < 32) {
-      if (j == 31) {
+      if (C == 32 && j == 31) {
         inc = my_seq == seq && my_slot == se - 31 + lane;
       } else {
         const int64_t ts = te - 31 + lane;
         if (ts >= 0) inc = a.seq_idx[ts] == seq && a.slots[ts] == se - 31 + lane;
       }
     }
-    const uint64_t incall = __ballot(inc);
     uint32_t x[RPL][PPL];  // fp16 channel pairs, even channel in the low half
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const int row = g + RG * i;
-      const uint16_t* src = ((incall >> row) & 1) ? a.k + ((size_t)(te - 31 + row) * a.H + h) * D
-                                                  : a.k_tail + (((size_t)seq * 32 + row) * a.H + h) * D;
+      const int64_t ts = te - 31 + row;  // call position of the row (before the call: a dummy read)
+      const uint16_t* src = a.k + ((size_t)(ts >= 0 ? ts : 0) * a.H + h) * D;
 #pragma unroll
       for (int q = 0; q < PPL; ++q) x[i][q] = reinterpret_cast<const uint32_t*>(src)[pl * PPL + q];
+    }
+    const uint64_t incall = __ballot(inc);
+    if ((uint32_t)incall != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        const int row = g + RG * i;
+        if (!((incall >> row) & 1)) {
+          const uint16_t* src = a.k_tail + (((size_t)seq * 32 + row) * a.H + h) * D;
+#pragma unroll
+          for (int q = 0; q < PPL; ++q) x[i][q] = reinterpret_cast<const uint32_t*>(src)[pl * PPL + q];
+        }
+      }
     }
     // per-channel min and max on the packed fp16 pairs (exact)
     float mn[2 * PPL], mx[2 * PPL];
@@ -290,7 +331,7 @@ hipError_t launch_sym(const WriteArgs& a, hipStream_t s) {
 template <int FK, int FV, int D>
 hipError_t launch_all(const WriteArgs& a, hipStream_t s) {
   if constexpr (FK == F_KIVI) {
-    const int64_t chunks = (a.T + 31) / 32;
+    const int64_t chunks = (a.T + a.seal_chunk - 1) / a.seal_chunk;
     hipLaunchKernelGGL((kivi_seal_kernel<D>), dim3((unsigned)chunks, a.H), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

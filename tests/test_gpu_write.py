@@ -145,6 +145,28 @@ def test_write_kivi_incremental_decode_steps():
     assert compare_buffers(dev, orc) == {}
 
 
+def test_write_kivi_large_calls():
+    # Calls of more than 2048 tokens (one seal wave per 32 call tokens):
+    # sequences start inside a chunk, pages straddle the two calls (their
+    # first rows come from the tail), and short sequences stay in the tail.
+    ctx = [3000, 2500, 1700, 45, 7]
+    inp = _small("int4_kivi", "int4_g32", 128, 32, ctx, seed=17)
+    dev, orc = new_caches(inp.num_blocks, 32, 2, 128, "int4_kivi", "int4_g32", len(ctx), DEV, seed=18)
+    import quantized_paged_kv_write_amd as kvq
+    cut = [int(0.6 * L) + 5 for L in ctx]
+    first = np.concatenate([np.arange(st, st + min(c, L)) for st, L, c in zip(inp.seq_start, ctx, cut)])
+    rest = np.concatenate([np.arange(st + min(c, L), st + L) for st, L, c in zip(inp.seq_start, ctx, cut)])
+    assert len(first) > 2048 and len(rest) > 2048
+    for sel in (first, rest):
+        idx = torch.from_numpy(sel)
+        k, v = inp.k[idx], inp.v[idx]
+        s, q = inp.slot_mapping[idx], inp.seq_idx[idx]
+        kvq.write(dev, k.to(DEV), v.to(DEV), s.to(DEV), q.to(DEV))
+        o.write(orc, to_np16(k), to_np16(v), s.numpy(), q.numpy())
+    torch.cuda.synchronize()
+    assert compare_buffers(dev, orc) == {}
+
+
 @pytest.mark.parametrize("name", wl.ORDER[1:])
 def test_write_full_size_sampled(name):
     """The full workload written in one call on the GPU; sampled rows (and,
