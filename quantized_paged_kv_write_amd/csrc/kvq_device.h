@@ -31,15 +31,32 @@ __device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
 }
 
 // IEEE binary32 quotient x / s (round to nearest even) from r = RN(1/s):
-// y0 = RN(x r) is within one ulp of x/s, the residual x - y0 s is exact under
-// FMA, and RN(y0 + r * residual) is the correctly rounded quotient
+// y0 = RN(x r) is within one ulp of x/s, the residual y0 s - x is exact under
+// FMA, and RN(y0 - r * residual) is the correctly rounded quotient
 // (Markstein's theorem; "Handbook of Floating-Point Arithmetic", division by
-// FMA).  Checked bit-exact against IEEE division for every fp16 x and every
-// fp16 s, and on 1.4e9 random fp32 differences of fp16 values.
+// FMA).  Written with the residual's sign flipped so that x = -0 gives -0.
+// Checked bit-exact (signed zeros included) against IEEE division on gfx950
+// for every fp16 x and every positive finite fp16 s with r from recip_fp16.
 __device__ __forceinline__ float exact_div(float x, float s, float r) {
   const float y0 = x * r;
-  const float e = __builtin_fmaf(-y0, s, x);
-  return __builtin_fmaf(e, r, y0);
+  const float e = __builtin_fmaf(y0, s, -x);
+  return __builtin_fmaf(e, -r, y0);
+}
+
+// RN(1/s) for a positive finite fp16 value s: the hardware reciprocal and
+// one Newton step, e = 1 - s r0 (exact under FMA), r0 + r0 e.  Equal to IEEE
+// 1/s for every positive finite fp16 s (checked exhaustively on gfx950).
+__device__ __forceinline__ float recip_fp16(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, r0, 1.0f);
+  return __builtin_fmaf(r0, e, r0);
+}
+
+// Round-to-nearest-even integer of |y| < 2^22 in the low bits of the result:
+// y + 1.5 2^23 is rounded by the add (ulp 1), and its low 8 bits are the
+// integer's two's-complement low byte.
+__device__ __forceinline__ uint32_t rne_low_bits(float y) {
+  return __builtin_bit_cast(uint32_t, y + 12582912.0f);
 }
 
 // Four fp32 values -> four OCP E4M3FN bytes, nearest-even (gfx950 hardware
@@ -51,17 +68,25 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
-// Max / sum over groups of N consecutive lanes (N a power of two <= 64).
+// Lane exchange within rows of 16 lanes (DPP): quad_perm [1,0,3,2] (xor 1),
+// [2,3,0,1] (xor 2), row_half_mirror (lane i of 8 reads 7 - i), row_mirror
+// (lane i of 16 reads 15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+// Max over aligned groups of N consecutive lanes (N a power of two <= 64).
+// Up to 16 lanes: butterflies on the DPP exchanges (after the two quad
+// steps a lane holds its quad's max, the half-row mirror pairs the two
+// quads of 8 lanes, the row mirror the two halves of 16); beyond, shuffles.
 template <int N>
 __device__ __forceinline__ float group_max(float v) {
+  if constexpr (N >= 2) v = fmaxf(v, dpp<0xB1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp<0x4E>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp<0x141>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp<0x140>(v));
 #pragma unroll
-  for (int m = 1; m < N; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
-template <int N>
-__device__ __forceinline__ float group_min(float v) {
-#pragma unroll
-  for (int m = 1; m < N; m <<= 1) v = fminf(v, __shfl_xor(v, m));
+  for (int m = 16; m < N; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
 }
 

@@ -29,6 +29,12 @@ template <int FMT>
 __device__ __forceinline__ float qmax() {
   return FMT == F_INT8 ? 127.0f : (FMT == F_FP8 ? 448.0f : 7.0f);
 }
+// RN(1 / q_max), rounded once at compile time
+template <int FMT>
+__device__ __forceinline__ float inv_qmax() {
+  constexpr float r = FMT == F_INT8 ? 1.0f / 127.0f : (FMT == F_FP8 ? 1.0f / 448.0f : 1.0f / 7.0f);
+  return r;
+}
 
 template <int FMT, int D>
 struct WShape {
@@ -50,17 +56,26 @@ __device__ __forceinline__ u32x2 encode8(const float (&y)[8]) {
     out.x = fp8x4(c[0], c[1], c[2], c[3]);
     out.y = fp8x4(c[4], c[5], c[6], c[7]);
   } else if constexpr (FMT == F_INT8) {
+    // clip, round half to even (rne_low_bits), low bytes gathered by v_perm
     uint32_t b[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = (uint32_t)(int)__builtin_rintf(fminf(fmaxf(y[j], -127.0f), 127.0f)) & 0xFFu;
-    out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-    out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    for (int j = 0; j < 8; ++j) b[j] = rne_low_bits(__builtin_amdgcn_fmed3f(y[j], -127.0f, 127.0f));
+    out.x = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u),
+                                  __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u), 0x05040100u);
+    out.y = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0C0C0400u),
+                                  __builtin_amdgcn_perm(b[5], b[4], 0x0C0C0400u), 0x05040100u);
   } else {  // INT4: two's-complement nibbles, even channel low
-    uint32_t w = 0;
+    uint32_t p[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      w |= ((uint32_t)(int)__builtin_rintf(fminf(fmaxf(y[j], -7.0f), 7.0f)) & 0xFu) << (4 * j);
-    out.x = w;
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = rne_low_bits(__builtin_amdgcn_fmed3f(y[2 * j], -7.0f, 7.0f));
+      const uint32_t hi = rne_low_bits(__builtin_amdgcn_fmed3f(y[2 * j + 1], -7.0f, 7.0f));
+      // byte = low nibble of lo | low nibble of hi << 4: m ? lo : hi << 4 with
+      // m = 0x0F (truth table of lo = 0xF0, hi = 0xCC, m = 0xAA)
+      p[j] = __builtin_amdgcn_bitop3_b32(lo, hi << 4, 0x0Fu, 0xE4);
+    }
+    out.x = __builtin_amdgcn_perm(__builtin_amdgcn_perm(p[3], p[2], 0x0C0C0400u),
+                                  __builtin_amdgcn_perm(p[1], p[0], 0x0C0C0400u), 0x05040100u);
     out.y = 0;
   }
   return out;
@@ -95,25 +110,22 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
     if (r < nrows) xin[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)r * D) + lir);
   }
   // KIVI keys: whether the row's page is completed within this call (its
-  // last row is at the matching call position), looked up while the rows
-  // are in flight.  Rows of pages left open go to the sequence's fp16 tail.
-  bool to_tail[ITER];
-  int32_t tseq[ITER];
+  // last row is at the matching call position).  The lookups are issued
+  // while the rows are in flight and compared only when the row is stored.
+  // Rows of pages left open go to the sequence's fp16 tail.
+  constexpr int NT = TAIL ? ITER : 1;
+  int32_t tseq[NT], tseq_e[NT];
+  int64_t tslot_e[NT], te_[NT];
+  if constexpr (TAIL) {
 #pragma unroll
-  for (int i = 0; i < ITER; ++i) {
-    to_tail[i] = false;
-    tseq[i] = -1;
-    if constexpr (TAIL) {
-      const int64_t sl = slot[i];
-      if (row0 + i * S::RPP < nrows && sl >= 0 && sl < a.capacity) {
-        const int off = (int)(sl % a.bs);
-        const int64_t te = (int64_t)tok[i] + (a.bs - 1 - off);
-        const int32_t seq = a.seq_idx[tok[i]];
-        bool sealed = false;
-        if (te < a.T) sealed = a.seq_idx[te] == seq && a.slots[te] == sl + (a.bs - 1 - off);
-        to_tail[i] = !sealed && seq >= 0 && seq < a.max_seqs;
-        tseq[i] = seq;
-      }
+    for (int i = 0; i < ITER; ++i) {
+      const int64_t sl = slot[i] >= 0 ? slot[i] : 0;
+      const int64_t te = (int64_t)tok[i] + (a.bs - 1 - (int)(sl % a.bs));
+      const int64_t tc = te < a.T ? te : a.T - 1;  // in bounds; compared below
+      te_[i] = te;
+      tseq[i] = a.seq_idx[tok[i]];
+      tseq_e[i] = a.seq_idx[tc];
+      tslot_e[i] = a.slots[tc];
     }
   }
 #pragma unroll
@@ -130,12 +142,12 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
     am = group_max<S::LPG>(am);
     // Scale: fp32 quotient, rounded once more to fp16 for storage; the codes
     // divide by the stored value.
-    const float s32 = am / qmax<FMT>();
+    const float s32 = exact_div(am, qmax<FMT>(), inv_qmax<FMT>());
     const uint32_t s16 = f2h_bits(s32);
     const float sc = h2f(s16);
     u32x2 enc = {0u, 0u};
     if (sc != 0.0f) {
-      const float rc = 1.0f / sc;
+      const float rc = recip_fp16(sc);
       float y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = exact_div(x[j], sc, rc);
@@ -153,9 +165,11 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
       if constexpr (TAIL) {
         // KIVI keys: a row whose page is not completed within this call is
         // kept in fp16 (key and value) in its sequence's tail.
-        if (to_tail[i]) {
-          const int off = (int)(s % a.bs);
-          const size_t trow = ((size_t)tseq[i] * a.bs + off) * a.H + h;
+        const int off = (int)(s % a.bs);
+        const int32_t seq = tseq[i];
+        const bool sealed = te_[i] < a.T && tseq_e[i] == seq && tslot_e[i] == s + (a.bs - 1 - off);
+        if (!sealed && seq >= 0 && seq < a.max_seqs) {
+          const size_t trow = ((size_t)seq * a.bs + off) * a.H + h;
           reinterpret_cast<u32x4*>(a.v_tail + trow * D)[lir] = xin[i];
           reinterpret_cast<u32x4*>(a.k_tail + trow * D)[lir] =
               reinterpret_cast<const u32x4*>(a.k + (size_t)r * D)[lir];
@@ -197,9 +211,14 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
   constexpr int LPR = D / 2 / PPL;             // lanes per row
   constexpr int RG = 64 / LPR;                 // row groups
   constexpr int RPL = 32 / RG;                 // rows per lane
-  const int h = (int)blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round robin in dispatch order (x
+  // fastest): workgroup (x, y) runs on XCD x % 8.  The H waves of one chunk
+  // (whose code rows share cache lines) are workgroups (8 h + c, y) of
+  // chunk 8 y + c: same XCD, same L2.
+  const int h = (int)(blockIdx.x >> 3);
+  const int64_t chunk = (int64_t)blockIdx.y * 8 + (blockIdx.x & 7);
   const int C = a.seal_chunk;
-  const int64_t t0 = (int64_t)blockIdx.x * C;
+  const int64_t t0 = chunk * C;
   const int lane = (int)threadIdx.x;
   // slot and sequence of the chunk's token `lane` (lanes < C)
   int64_t my_slot = -1;
@@ -280,7 +299,7 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
       s16[c] = f2h_bits(range / 15.0f);
       z16[c] = f2h_bits(mn[c]);  // exact: mn is an fp16 value
       sc[c] = h2f(s16[c]);
-      rc[c] = sc[c] != 0.0f ? 1.0f / sc[c] : 0.0f;
+      rc[c] = sc[c] != 0.0f ? recip_fp16(sc[c]) : 0.0f;
     }
     uint8_t* cbase = a.k_codes + (size_t)blk * 32 * a.H * (D / 2);
 #pragma unroll
@@ -293,7 +312,7 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
         if (sc[c] != 0.0f) {
           const float v = h2f((c & 1) ? x[i][c >> 1] >> 16 : x[i][c >> 1] & 0xFFFFu);
           const float y = exact_div(v - mn[c], sc[c], rc[c]);  // fl32(fl32(x - z) / s)
-          code = (uint32_t)(int)__builtin_rintf(fminf(fmaxf(y, 0.0f), 15.0f));
+          code = rne_low_bits(__builtin_amdgcn_fmed3f(y, 0.0f, 15.0f)) & 0xFu;  // clip, round half to even
         }
         w |= code << (4 * c);
       }
@@ -332,7 +351,8 @@ template <int FK, int FV, int D>
 hipError_t launch_all(const WriteArgs& a, hipStream_t s) {
   if constexpr (FK == F_KIVI) {
     const int64_t chunks = (a.T + a.seal_chunk - 1) / a.seal_chunk;
-    hipLaunchKernelGGL((kivi_seal_kernel<D>), dim3((unsigned)chunks, a.H), dim3(64), 0, s, a);
+    const int64_t groups = (chunks + 7) / 8;  // chunks padded to a multiple of 8 (extra waves find no token)
+    hipLaunchKernelGGL((kivi_seal_kernel<D>), dim3((unsigned)(8 * a.H), (unsigned)groups), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

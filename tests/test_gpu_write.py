@@ -52,8 +52,9 @@ def test_write_block_sizes(bs):
 
 
 def _edge_rows(D, rng):
-    """Rows that stress the encoders: zeros, -0, max fp16, subnormals, scales
-    that underflow fp16, exact half-way quotients, single spikes."""
+    """Rows that stress the encoders: zeros, -0 (alone and beside nonzero
+    values: FP8 keeps the sign of zero), max fp16, subnormals, scales that
+    underflow fp16, exact half-way quotients, single spikes."""
     rows = []
     rows.append(np.zeros(D))
     rows.append(-np.zeros(D))
@@ -67,6 +68,7 @@ def _edge_rows(D, rng):
     r = np.zeros(D); r[5] = -1.0; rows.append(r)                 # one spike
     r = rng.standard_normal(D); r[::7] *= 300; rows.append(r)
     rows.append(np.linspace(-1, 1, D) * 3.5)
+    r = rng.standard_normal(D); r[::3] = -0.0; r[1::5] = 0.0; rows.append(r)  # signed zeros, scale != 0
     return np.stack(rows).astype(np.float16)
 
 
