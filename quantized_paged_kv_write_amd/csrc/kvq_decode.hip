@@ -749,18 +749,16 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int kb = 0; kb < KS::KB; ++kb) {
           const int cb = j * (D / 4) + 8 * kb;
-          const u4 sw = *reinterpret_cast<const u4*>(cur + ST::OFF_M + 2 * (hn * D + cb));
-          const u4 zw = *reinterpret_cast<const u4*>(cur + ST::OFF_M + 2 * (HPC * D + hn * D + cb));
-          float s8[8], z8[8];
-          unpack8(uint4{sw.x, sw.y, sw.z, sw.w}, s8);
-          unpack8(uint4{zw.x, zw.y, zw.z, zw.w}, z8);
+          // fp16 scales and zeros of 8 channels; the products take the fp16
+          // operands directly (mixed-precision FMA, exact in fp32)
+          const h8 s8 = *reinterpret_cast<const h8*>(cur + ST::OFF_M + 2 * (hn * D + cb));
+          const h8 z8 = *reinterpret_cast<const h8*>(cur + ST::OFF_M + 2 * (HPC * D + hn * D + cb));
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int ch = key_channel<FK, D>(j, kb, e) - cb;
-            const float qv = (float)qop[kb][e];
-            qs[kb][e] = qv * s8[ch];
+            qs[kb][e] = __builtin_fmaf((float)qop[kb][e], (float)s8[ch], 0.f);
             mx = fmaxf(mx, fabsf(qs[kb][e]));
-            qz = __builtin_fmaf(qv, z8[ch], qz);
+            qz = __builtin_fmaf((float)qop[kb][e], (float)z8[ch], qz);
           }
         }
         qz += __shfl_xor(qz, 16);
@@ -781,7 +779,7 @@ void decode_split_kernel(DecodeArgs a) {
             const float xs = qs[kb][e] * ((e & 2) ? f_odd : f_even);
             const _Float16 hi = (_Float16)xs;
             qhi[kb][e] = hi;
-            qlo[kb][e] = (_Float16)(xs - (float)hi);
+            qlo[kb][e] = (_Float16)__builtin_fmaf((float)hi, -1.0f, xs);  // xs - hi exactly, then rounded
           }
         }
       }
