@@ -137,12 +137,12 @@ __device__ __forceinline__ int key_channel(int j, int kb, int e) {
 }
 
 // ---- value operands: 8 exact bf16 values, 8 tokens of one channel ----------
-// INT8: bf16(c + 128) (exact, <= 255); the +128 is removed afterwards with
-// the sum of the probabilities.  FP8: exact.  INT4: 128 + (n + 8) (exact).
-__device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
-  // upper halves of a (low word) and b (high word): one v_perm_b32
-  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x07060302u);
-}
+// FP8: the exact value.  INT8 and INT4: the unsigned code u (c + 128, or
+// c + 8 for INT4) as the bf16 bit pattern u, which is exactly u 2^-133 for
+// every u < 256 (subnormal below 128; from 128 on the smallest exponent
+// continues the same spacing).  The probability operand carries 2^60 so the
+// products stay normal fp32; the offset times the probability sum is removed
+// once per piece (cs_run), and the scale factors with it.
 
 template <int FV>
 __device__ __forceinline__ b8 value_operand_8bit(i2 t) {
@@ -155,35 +155,37 @@ __device__ __forceinline__ b8 value_operand_8bit(i2 t) {
     r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
     r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
   } else {
+    // bytes c + 128 into zero-padded halves: [u0, 0, u1, 0] per dword
     const uint32_t e0 = d0 ^ 0x80808080u, e1 = d1 ^ 0x80808080u;
-    // (float)((x >> 8k) & 0xFF) is one v_cvt_f32_ubyte{k}
-    r.x = bf16_pair_hi((float)(e0 & 0xFFu), (float)((e0 >> 8) & 0xFFu));
-    r.y = bf16_pair_hi((float)((e0 >> 16) & 0xFFu), (float)(e0 >> 24));
-    r.z = bf16_pair_hi((float)(e1 & 0xFFu), (float)((e1 >> 8) & 0xFFu));
-    r.w = bf16_pair_hi((float)((e1 >> 16) & 0xFFu), (float)(e1 >> 24));
+    r.x = __builtin_amdgcn_perm(0u, e0, 0x0C010C00u);
+    r.y = __builtin_amdgcn_perm(0u, e0, 0x0C030C02u);
+    r.z = __builtin_amdgcn_perm(0u, e1, 0x0C010C00u);
+    r.w = __builtin_amdgcn_perm(0u, e1, 0x0C030C02u);
   }
   return __builtin_bit_cast(b8, r);
 }
 
 // INT4: 8 bytes = 8 tokens of a channel pair; element order of both operands
-// is tokens [0, 2, 1, 3, 4, 6, 5, 7].  Each operand dword is one v_bitop3:
-// bits under the mask 0x000F000F take the code nibble xor 8 (code + 8), the
-// others the bf16 128 pattern, giving bf16 128 + (code + 8) exactly.
-__device__ __forceinline__ uint32_t int4_pair_bf16(uint32_t x) {
-  // f(x, m, c) = m ? x ^ c : c (truth table of x = 0xF0, m = 0xCC, c = 0xAA)
-  return __builtin_amdgcn_bitop3_b32(x, 0x000F000Fu, 0x43084308u, 0x6A);
+// is tokens [0, 2, 1, 3, 4, 6, 5, 7].  Each operand dword is one v_bitop3,
+// (x ^ c) & m: the even channel's nibbles xor 8 (code + 8) stay in bits 0-3
+// of each half (u 2^-133), the odd channel's in bits 4-7 (16 u 2^-133).
+template <uint32_t M, uint32_t C>
+__device__ __forceinline__ uint32_t int4_pair(uint32_t x) {
+  // f(x, m, c) = m & (x ^ c) (truth table of x = 0xF0, m = 0xCC, c = 0xAA)
+  return __builtin_amdgcn_bitop3_b32(x, M, C, 0x48);
 }
 __device__ __forceinline__ void value_operand_int4(i2 t, b8& even, b8& odd) {
-  const uint32_t d0 = (uint32_t)t.x, d1 = (uint32_t)t.y;
+  const uint32_t d0 = (uint32_t)t.x, d1 = (uint32_t)t.y, d0s = d0 >> 8, d1s = d1 >> 8;
+  constexpr uint32_t ME = 0x000F000Fu, CE = 0x00080008u, MO = 0x00F000F0u, CO = 0x00800080u;
   u4 e, od;
-  e.x = int4_pair_bf16(d0);
-  e.y = int4_pair_bf16(d0 >> 8);
-  e.z = int4_pair_bf16(d1);
-  e.w = int4_pair_bf16(d1 >> 8);
-  od.x = int4_pair_bf16(d0 >> 4);
-  od.y = int4_pair_bf16(d0 >> 12);
-  od.z = int4_pair_bf16(d1 >> 4);
-  od.w = int4_pair_bf16(d1 >> 12);
+  e.x = int4_pair<ME, CE>(d0);
+  e.y = int4_pair<ME, CE>(d0s);
+  e.z = int4_pair<ME, CE>(d1);
+  e.w = int4_pair<ME, CE>(d1s);
+  od.x = int4_pair<MO, CO>(d0);
+  od.y = int4_pair<MO, CO>(d0s);
+  od.z = int4_pair<MO, CO>(d1);
+  od.w = int4_pair<MO, CO>(d1s);
   even = __builtin_bit_cast(b8, e);
   odd = __builtin_bit_cast(b8, od);
 }
@@ -457,6 +459,8 @@ void decode_split_kernel(DecodeArgs a) {
   using ST = Stage<FK, FV, D>;
   constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
   constexpr int NCS = FV == F_INT4 ? VS::NG : 1;  // bias-correction sums kept per value group
+  // value scales carry 2^60 for the INT8 / INT4 value operands (u 2^-133)
+  constexpr float VSC = FV == F_FP8 ? 1.f : 0x1p60f;
   // NS tiles held in registers: tile x is stored to LDS and computed while
   // tiles x + 1 .. x + P are in flight
   constexpr int NS = ST::NS, P = NS - 1;
@@ -597,10 +601,12 @@ void decode_split_kernel(DecodeArgs a) {
   // Write the softmax state of sequence b's piece (record share + b) and
   // reset it for the next piece.
   auto write_piece = [&](int b) __attribute__((always_inline)) {
-    // remove the value-operand bias: acc[g][ch] -= bias * sum of the
-    // probability operands of query head g (INT8 +128, INT4 +136)
+    // remove the value-operand offset and scale factors: with P = 2^60 p s
+    // and value operands u 2^-133 (u = c + 128) the true sum is
+    // 2^73 acc - 2^-53 cs; INT4 (u = c + 8): even channels 2^73 acc - 2^-57 cs,
+    // odd channels (16 u 2^-133) 2^69 acc - 2^-57 cs; cs = sum of the
+    // probability operands of query head g
     if constexpr (FV != F_FP8) {
-      constexpr float bias = FV == F_INT8 ? 128.f : 136.f;
 #pragma unroll
       for (int g = 0; g < NCS; ++g) {
         float cs = cs_run[g];
@@ -608,13 +614,15 @@ void decode_split_kernel(DecodeArgs a) {
         cs += __shfl_xor(cs, 32);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float corr = bias * __shfl(cs, 4 * j + r);
+          const float csr = __shfl(cs, 4 * j + r);
           if constexpr (FV == F_INT8) {
+            const float corr = csr * 0x1p-53f;
 #pragma unroll
-            for (int m = 0; m < VS::NPV; ++m) acc[m][r] -= corr;
+            for (int m = 0; m < VS::NPV; ++m) acc[m][r] = __builtin_fmaf(acc[m][r], 0x1p73f, -corr);
           } else {
-            acc[2 * g][r] -= corr;
-            acc[2 * g + 1][r] -= corr;
+            const float corr = csr * 0x1p-57f;
+            acc[2 * g][r] = __builtin_fmaf(acc[2 * g][r], 0x1p73f, -corr);
+            acc[2 * g + 1][r] = __builtin_fmaf(acc[2 * g + 1][r], 0x1p69f, -corr);
           }
         }
       }
@@ -692,7 +700,7 @@ void decode_split_kernel(DecodeArgs a) {
       if constexpr (VS::NG == 1) {
         if (lane >= 32) {
           const uint32_t d = sdw[32 + t];
-          s_fv[t] = lv ? h2f(hi_half ? d >> 16 : d & 0xFFFFu) : 0.f;
+          s_fv[t] = lv ? h2f(hi_half ? d >> 16 : d & 0xFFFFu) * VSC : 0.f;
         }
       } else {
         // value scales of (token t, group g): dword g/2 of the token, half g&1
@@ -701,8 +709,8 @@ void decode_split_kernel(DecodeArgs a) {
         for (int gd = 0; gd < VS::NG / 2; ++gd) {
           if ((lane >> 5) == (gd & 1)) {
             const uint32_t d = sdw[32 + 32 * gd + t];
-            s_fv[t * VS::NG + 2 * gd] = lv ? h2f(d & 0xFFFFu) : 0.f;
-            s_fv[t * VS::NG + 2 * gd + 1] = lv ? h2f(d >> 16) : 0.f;
+            s_fv[t * VS::NG + 2 * gd] = lv ? h2f(d & 0xFFFFu) * VSC : 0.f;
+            s_fv[t * VS::NG + 2 * gd + 1] = lv ? h2f(d >> 16) * VSC : 0.f;
           }
         }
       }
