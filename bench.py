@@ -4,9 +4,11 @@
 
 One step is one decode step of the workload's batch: quantize-on-write of the
 new token of every sequence into the paged cache (kvq_write), then decode
-attention over the whole cache (kvq_decode_attn).  The cache is filled before
-timing by a prefill write of all earlier tokens, which is timed on its own for
-the write bandwidth.  Prints one JSON line.
+attention over the whole cache (kvq_decode_attn).  Two identical caches are
+filled before timing by a prefill write of all earlier tokens (the write into
+the first is timed on its own for the write bandwidth); consecutive timed steps
+alternate between them, so no call reads what the previous one left in the
+memory-side cache.  Prints one JSON line.
 
 value = decode KV-read bytes per step / step time (GB/s); the roofline entry
 is for the decode kernels (split-K attention + split merge), timed with HIP
@@ -180,6 +182,9 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed decode calls after the cache fill, before any timing")
+    ap.add_argument("--caches", type=int, default=2, choices=(1, 2),
+                    help="identical caches the timed decode steps alternate between, so that no call reads "
+                         "data the previous call left in the memory-side cache")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -211,8 +216,9 @@ def main():
     inp = wl.make_inputs(w, seed, dev)
     ctx = inp.ctx_lens
     B = w.batch
-    cache = kvq.PagedKVCache(inp.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, w.k_dtype, w.v_dtype,
-                             max_seqs=B, device=dev)
+    caches = [kvq.PagedKVCache(inp.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, w.k_dtype, w.v_dtype,
+                               max_seqs=B, device=dev) for _ in range(args.caches)]
+    cache = caches[0]
     pos = inp.positions
     last = torch.tensor([inp.seq_start[b] + ctx[b] - 1 for b in range(B)])
     pre_mask = torch.ones(pos.numel(), dtype=torch.bool)
@@ -234,7 +240,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     # ---- prefill write (cache fill), timed for the write bandwidth --------
-    kvq.write(cache, k_pre, v_pre, s_pre, q_pre)
+    for c in caches:
+        kvq.write(c, k_pre, v_pre, s_pre, q_pre)
     torch.cuda.synchronize()
     # Settle: after idle time or a different heavy kernel, decode calls run
     # at a varying, slower rate for tens of milliseconds (clock and power
@@ -243,8 +250,8 @@ def main():
     def settle():
         t_settle = time.perf_counter() + args.settle
         while time.perf_counter() < t_settle:
-            for _ in range(8):
-                kvq.decode_attn(cache, q, table, ctx_d, out=out, workspace=ws)
+            for i in range(8):
+                kvq.decode_attn(caches[i % len(caches)], q, table, ctx_d, out=out, workspace=ws)
             torch.cuda.synchronize()
 
     settle()
@@ -279,25 +286,30 @@ def main():
     del cal
 
     # ---- decode steps -------------------------------------------------------
-    def step(evs=None):
+    # Step i writes the new token of every sequence into cache i % caches and
+    # decodes it: consecutive steps read different (identical) caches, so a
+    # call never reuses what the previous one left in the 256 MB memory-side
+    # cache (the steps' working sets are 0.45-1.8 GB).
+    def step(i, evs=None):
+        c = caches[i % len(caches)]
         if evs is not None:
             evs[0].record(stream)
-        kvq.write(cache, k_new, v_new, s_new, q_new)
+        kvq.write(c, k_new, v_new, s_new, q_new)
         if evs is not None:
             evs[1].record(stream)
-        kvq.decode_attn(cache, q, table, ctx_d, out=out, workspace=ws)
+        kvq.decode_attn(c, q, table, ctx_d, out=out, workspace=ws)
         if evs is not None:
             evs[2].record(stream)
 
     settle()
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
@@ -315,6 +327,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_s": args.settle,
+        "timed_caches": len(caches),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
