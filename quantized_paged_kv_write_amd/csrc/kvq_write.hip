@@ -308,12 +308,13 @@ __global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
       uint32_t w = 0;
 #pragma unroll
       for (int c = 0; c < 2 * PPL; ++c) {
-        uint32_t code = 0;
-        if (sc[c] != 0.0f) {
-          const float v = h2f((c & 1) ? x[i][c >> 1] >> 16 : x[i][c >> 1] & 0xFFFFu);
-          const float y = exact_div(v - mn[c], sc[c], rc[c]);  // fl32(fl32(x - z) / s)
-          code = rne_low_bits(__builtin_amdgcn_fmed3f(y, 0.0f, 15.0f)) & 0xFu;  // clip, round half to even
-        }
+        // fl32(x - z) by one mixed-precision FMA on the fp16 x; then
+        // fl32(. / s).  No branch on s = 0: with r = 0 the division of the
+        // non-negative difference gives +0, so the code is 0.
+        const _Float16 xv = __builtin_bit_cast(hv2, x[i][c >> 1])[c & 1];
+        const float d = __builtin_fmaf((float)xv, 1.0f, -mn[c]);
+        const float y = exact_div(d, sc[c], rc[c]);
+        const uint32_t code = rne_low_bits(__builtin_amdgcn_fmed3f(y, 0.0f, 15.0f)) & 0xFu;  // clip, round half to even
         w |= code << (4 * c);
       }
       uint8_t* dst = cbase + ((size_t)row * a.H + h) * (D / 2) + pl * PPL;
