@@ -290,7 +290,14 @@ struct TileRegs {
 // tile costs the same number of loads: masked rows read flat row 0 (every
 // cache has at least one block) and idle lanes the start of the buffer;
 // those bytes are never used unmasked.
-template <int FK, int FV, int D, int HPC>
+//
+// OP (one page): the tile's 32 / HPC tokens lie in one page (block_size is
+// a multiple of them; tiles start at multiples of them), so bid is the same
+// on every lane and tile row rho is flat row row0 + (rho / HPC) H + rho % HPC:
+// a uniform page base plus a per-lane constant, with no row exchange between
+// lanes.  Rows past the context are read from the same page (page 0 when bid
+// is out of range), so every address stays inside the cache; they are masked.
+template <int FK, int FV, int D, int HPC, bool OP>
 __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int t0, int tok_end, int h0,
                                               TileRegs<FK, FV, D, HPC>& r) {
   using S = Stage<FK, FV, D>;
@@ -298,6 +305,60 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
   using VS = VShape<FV, D>;
   constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
   const int lane = (int)threadIdx.x;
+  if constexpr (OP) {
+    constexpr int hp = HPC == 4 ? 2 : HPC == 2 ? 1 : 0;
+    const int bu = __builtin_amdgcn_readfirstlane(bid);
+    const bool bok = bu >= 0 && bu < a.nb;
+    const uint32_t blk = bok ? (uint32_t)bu : 0u;
+    const uint32_t row0 = ((blk << a.log2_bs) + (uint32_t)(t0 & (a.bs - 1))) * (uint32_t)a.H + (uint32_t)h0;
+    // flat-row offset of tile row rho from row0
+    auto ro = [&](int rho) __attribute__((always_inline)) {
+      return (uint32_t)((rho >> hp) * a.H + (rho & (HPC - 1)));
+    };
+    const int t = lane & 31;
+    const bool live = bok && t0 + (t >> hp) < tok_end;
+    const uint64_t live_mask = __ballot(live);
+    const uint32_t r_own = row0 + ro(t);
+    const uint8_t* kb = a.k_codes + (size_t)row0 * KS::RB;
+    const uint8_t* vb = a.v_codes + (size_t)row0 * VS::RB;
+#pragma unroll
+    for (int i = 0; i < S::NLK; ++i) {
+      const int p = 64 * i + lane;
+      const int row = p / CHK;
+      const int col = (p % CHK) ^ kswz<CHK>(row);
+      r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(kb + ro(row) * KS::RB + col * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < S::NLV; ++i) {
+      const int p = 64 * i + lane;
+      const int row = p / VS::CH;
+      const int col = (p % VS::CH) ^ vswz<VS::CH>(row);
+      r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(vb + ro(row) * VS::RB + col * 16));
+    }
+    {
+      const uint16_t* src;
+      if (lane < 32) src = FK == F_KIVI ? a.v_scales : a.k_scales + (r_own & ~1u);
+      else src = a.v_scales + ((size_t)r_own * VS::NG & ~(size_t)1);
+      r.s[0] = *reinterpret_cast<const uint32_t*>(src);
+      r.par = (uint32_t)__ballot(live && (r_own & 1u));
+    }
+#pragma unroll
+    for (int g = 1; g < S::NGD; ++g)
+      r.s[g] = *reinterpret_cast<const uint32_t*>(a.v_scales + (lane < 32 ? (size_t)r_own * VS::NG + 2 * g : 0));
+    if constexpr (FK == F_KIVI) {
+      using TR = TileRegs<FK, FV, D, HPC>;
+      constexpr int HALF = HPC * D / 8;
+      const size_t mrow = ((size_t)blk * a.H + h0) * D;
+#pragma unroll
+      for (int k = 0; k < TR::KM; ++k) {
+        const int c = 64 * k + lane;
+        const bool use = c < TR::MCH;
+        const uint16_t* src = (c < HALF ? a.k_scales : a.k_zeros) + (use ? mrow + 8 * (c < HALF ? c : c - HALF) : 0);
+        r.m[k] = *reinterpret_cast<const u4*>(src);
+      }
+    }
+    return live_mask;
+  }
   // row index of token `lane & 31`, or ~0 when masked; shared with shuffles
   bool live;
   const uint32_t r_own = tile_row(a, bid, lane & 31, t0, tok_end, h0, live);
@@ -443,7 +504,13 @@ __device__ __forceinline__ void seek(SeqCursor& c, const DecodeArgs& a, int x) {
 
 // Block id of the page of tile row lane % 32 of tile x of the cursor's
 // sequence (entry 0 of its row past the sequence's end; those rows are masked).
+// OP: every lane loads the page of the tile's first token (in the sequence).
+template <bool OP>
 __device__ __forceinline__ int load_ids(const DecodeArgs& a, const SeqCursor& c, int x) {
+  if constexpr (OP) {
+    const int tok0 = (TILE * (x - c.lo)) >> a.hp_log2;
+    return a.block_table[(size_t)c.b * a.max_blocks + (tok0 >> a.log2_bs)];
+  }
   const int tok = ((TILE * (x - c.lo)) >> a.hp_log2) + (((int)threadIdx.x & 31) >> a.hp_log2);
   const int pg = tok < c.lq ? tok >> a.log2_bs : 0;
   return a.block_table[(size_t)c.b * a.max_blocks + pg];
@@ -451,7 +518,8 @@ __device__ __forceinline__ int load_ids(const DecodeArgs& a, const SeqCursor& c,
 
 // HPC: KV heads per wave (a.hp_log2 == log2 HPC).  Lane (j, n) keeps only the
 // scores of its column's head: rows 16 u + 4 j + r with r = hn (mod HPC).
-template <int FK, int FV, int D, int HPC>
+// OP: every tile lies in one page (32 / HPC <= block_size), see load_tile.
+template <int FK, int FV, int D, int HPC, bool OP>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Stage<FK, FV, D>::WPE, Stage<FK, FV, D>::WPE)))
 void decode_split_kernel(DecodeArgs a) {
   using KS = KShape<FK, D>;
@@ -585,15 +653,15 @@ void decode_split_kernel(DecodeArgs a) {
   for (int i = 0; i < L; ++i) {
     const int y = min(x_begin + i, x_last);
     seek<FK>(cd, a, y);
-    ids[i] = load_ids(a, cd, y);
+    ids[i] = load_ids<OP>(a, cd, y);
   }
   auto load_group = [&](int y, int& ids_out, int ids_in, TileRegs<FK, FV, D, HPC>& r) __attribute__((always_inline)) {
     const int yi = min(y + L, x_last);
     seek<FK>(cd, a, yi);
-    ids_out = load_ids(a, cd, yi);
+    ids_out = load_ids<OP>(a, cd, yi);
     const int yc = min(y, x_last);
     seek<FK>(ci, a, yc);
-    return load_tile<FK, FV, D, HPC>(a, ids_in, (TILE * (yc - ci.lo)) >> a.hp_log2, ci.lq, h0, r);
+    return load_tile<FK, FV, D, HPC, OP>(a, ids_in, (TILE * (yc - ci.lo)) >> a.hp_log2, ci.lq, h0, r);
   };
 #pragma unroll
   for (int i = 0; i < P; ++i) live[i] = load_group(x_begin + i, ids[(i + L) % NS], ids[i], regs[i]);
@@ -1176,7 +1244,7 @@ namespace {
 // device: WPE per SIMD (4 WPE per compute unit), or the occupancy if lower.
 // Every wave gets the same work, so a SIMD holding more waves than the
 // others would hold the whole launch back.  Cached per device.
-template <int FK, int FV, int D, int HPC>
+template <int FK, int FV, int D, int HPC, bool OP>
 int resident_waves() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -1186,7 +1254,7 @@ int resident_waves() {
     if (c > 0) return c;
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D, HPC>, 64, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D, HPC, OP>, 64, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   const int w = std::min(per_cu, 4 * Stage<FK, FV, D>::WPE) * cus;
@@ -1194,11 +1262,11 @@ int resident_waves() {
   return w;
 }
 
-template <int FK, int FV, int D, int HPC>
+template <int FK, int FV, int D, int HPC, bool OP>
 hipError_t launch4(DecodeArgs a, hipStream_t st) {
   if (a.share_tiles <= 0) {
     // balanced: all waves the same length, all resident at once
-    const int w = resident_waves<FK, FV, D, HPC>();
+    const int w = resident_waves<FK, FV, D, HPC, OP>();
     if (w <= 0) return hipErrorInvalidDevice;
     a.num_shares = min(a.max_shares, max(1, w / (a.H >> a.hp_log2)));
   } else {
@@ -1214,7 +1282,7 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
   }
   // one wave per (share, group of HP KV heads); see decode_split_kernel for the order
   const uint32_t wgs = (((uint32_t)a.num_shares + 7) / 8) * 8 * (uint32_t)(a.H >> a.hp_log2);
-  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D, HPC>), dim3(wgs), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D, HPC, OP>), dim3(wgs), dim3(64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.B * a.Hq < 512)
@@ -1226,10 +1294,16 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
 
 template <int FK, int FV, int D>
 hipError_t launch3(const DecodeArgs& a, hipStream_t st) {
+  constexpr bool OP_PAYS = FV == F_INT4 || FK == F_KIVI;
   switch (a.hp_log2) {
-    case 0: return launch4<FK, FV, D, 1>(a, st);
-    case 1: return launch4<FK, FV, D, 2>(a, st);
-    case 2: return launch4<FK, FV, D, 4>(a, st);
+    // Tiles of 32 / HP tokens lie in one page when the page holds at least
+    // that many (always for HP = 4: block_size >= 8).  The one-page address
+    // path saves about a sixth of the VALU work per tile, which pays where
+    // that work bounds the kernel (4-bit values, KIVI keys); with 8-bit keys
+    // and values it measured 1-2% slower, so those keep the general path.
+    case 0: return OP_PAYS && a.bs >= 32 ? launch4<FK, FV, D, 1, OP_PAYS>(a, st) : launch4<FK, FV, D, 1, false>(a, st);
+    case 1: return OP_PAYS && a.bs >= 16 ? launch4<FK, FV, D, 2, OP_PAYS>(a, st) : launch4<FK, FV, D, 2, false>(a, st);
+    case 2: return launch4<FK, FV, D, 4, OP_PAYS>(a, st);
   }
   return hipErrorInvalidValue;
 }
