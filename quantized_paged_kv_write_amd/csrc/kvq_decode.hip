@@ -210,6 +210,33 @@ __device__ __forceinline__ float add_split(float cs, uint32_t hi, uint32_t lo) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, lo), one, cs, false);
 }
 
+// Lanes l and l ^ 16 (or l ^ 32) without a trip through LDS: swapping x with
+// itself by v_permlane16_swap (v_permlane32_swap) leaves, on every lane, the
+// pair's lower-row (lower-half) value in one register and its upper one in
+// the other.  Max and sum are symmetric, so the results equal those of a
+// lane exchange bit for bit.
+// (The results are copied out element by element before the bit cast: a bit
+// cast of a vector element reference reads element 0 with this compiler.)
+template <int X>
+__device__ __forceinline__ f2 xor_pair(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = X == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return f2{__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi)};
+}
+// reduction over the 4 lanes l ^ {0, 16, 32, 48}
+__device__ __forceinline__ float sum_j(float x) {
+  f2 p = xor_pair<16>(x);
+  p = xor_pair<32>(p.x + p.y);
+  return p.x + p.y;
+}
+__device__ __forceinline__ float max_j(float x) {
+  f2 p = xor_pair<16>(x);
+  p = xor_pair<32>(fmaxf(p.x, p.y));
+  return fmaxf(p.x, p.y);
+}
+
 // Tile row rho (0..31) is token t0 + rho / HP of the sequence, KV head
 // h0 + rho % HP (HP = 2^hp_log2 heads per wave).  Returns its flat row index
 // (slot * H + head) and whether it is live: in the context and on a page
@@ -678,8 +705,7 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int g = 0; g < NCS; ++g) {
         float cs = cs_run[g];
-        cs += __shfl_xor(cs, 16);
-        cs += __shfl_xor(cs, 32);
+        cs = sum_j(cs);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float csr = __shfl(cs, 4 * j + r);
@@ -696,8 +722,7 @@ void decode_split_kernel(DecodeArgs a) {
       }
     }
     float l = l_run;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = sum_j(l);
     const size_t stride = (size_t)D + 2;
     float* pbase = a.part + ((size_t)(share + b) * a.Hq + hq0) * stride;
     if (j == 0 && n < NC) {
@@ -837,11 +862,9 @@ void decode_split_kernel(DecodeArgs a) {
             qz = __builtin_fmaf((float)qop[kb][e], (float)z8[ch], qz);
           }
         }
-        qz += __shfl_xor(qz, 16);
-        qz += __shfl_xor(qz, 32);
+        qz = sum_j(qz);
         qz *= a.qscale;
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_j(mx);
         // mx < 2^ex; F = 2^(11 - ex), so 16 F mx < 2^15
         const int ex = mx > 0.f ? min(max(__builtin_amdgcn_frexp_expf(mx), -100), 100) : 0;
         const float f_odd = __builtin_ldexpf(1.f, 11 - ex), f_even = 16.f * f_odd;
@@ -905,8 +928,7 @@ void decode_split_kernel(DecodeArgs a) {
         tmax = fmaxf(tmax, v);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_j(tmax);
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     // Rescale only when some head's running max moved (rare after the first
