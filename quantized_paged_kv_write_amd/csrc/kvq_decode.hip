@@ -10,10 +10,12 @@
 // How (MI355X design, not the pages' Hopper kernels):
 //  * Work partition: the quantized 32-token tiles of all sequences are
 //    numbered sequence after sequence and cut into equal shares (a small plan
-//    kernel computes the cut on the device).  A share is read by one wave per
-//    KV head, which handles all G query heads reading that head.  By default
-//    there is one wave per SIMD, all resident at once with the same amount
-//    of work, so no wave waits for a later round.  A wave writes one partial
+//    kernel, or each wave itself, computes the cut on the device).  A share
+//    is read by one wave per group of HP = 1, 2 or 4 KV heads, which handles
+//    the G query heads of each; the waves of a share form one workgroup, so
+//    they run on one compute unit.  By default as many waves run as fit at
+//    once (two per SIMD up to head_dim 128), all with the same amount of
+//    work, so no wave waits for a later round.  A wave writes one partial
 //    softmax state per sequence piece it covers; a merge kernel combines them.
 //  * Data path: a tile's key and value rows, scales and block ids are loaded
 //    into registers several tiles ahead (the compiler tracks the loads, and
@@ -283,6 +285,9 @@ struct Stage {
   static constexpr int OFF_S = KT + VT;              // raw scale dwords (see load_tile)
   static constexpr int OFF_M = OFF_S + 4 * TILE * (1 + NGD);
   static constexpr int BYTES = OFF_M + KIVI_BYTES;
+  // one wave's LDS: the stage, then this tile's key scales (TILE fp32) and
+  // value scales (TILE NG fp32)
+  static constexpr int WAVE_LDS = (BYTES + 4 * TILE + 4 * TILE * VS::NG + 15) / 16 * 16;
   // Waves per SIMD and register slots for tiles.  Head dims up to 128 run
   // two waves per SIMD (each within 256 registers), so one wave's compute
   // hides the other's waits; a wave then holds NS = 2 tiles (one in flight
@@ -331,7 +336,7 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
   using KS = KShape<FK, D>;
   using VS = VShape<FV, D>;
   constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
-  const int lane = (int)threadIdx.x;
+  const int lane = (int)threadIdx.x & 63;
   if constexpr (OP) {
     constexpr int hp = HPC == 4 ? 2 : HPC == 2 ? 1 : 0;
     const int bu = __builtin_amdgcn_readfirstlane(bid);
@@ -446,7 +451,7 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
 template <int FK, int FV, int D, int HPC>
 __device__ __forceinline__ void store_tile(const TileRegs<FK, FV, D, HPC>& r, uint8_t* st) {
   using S = Stage<FK, FV, D>;
-  const int lane = (int)threadIdx.x;
+  const int lane = (int)threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < S::NLK; ++i) reinterpret_cast<u4*>(st + S::OFF_K)[64 * i + lane] = r.k[i];
 #pragma unroll
@@ -483,7 +488,7 @@ __device__ __forceinline__ int seq_tokens(const DecodeArgs& a, int b) {
 
 template <int FK>
 __device__ __forceinline__ void fill_window(SeqCursor& c, const DecodeArgs& a, int wb) {
-  const int lane = (int)threadIdx.x, sb = wb + lane;
+  const int lane = (int)threadIdx.x & 63, sb = wb + lane;
   c.wb = wb;
   c.win_hi = sb < a.B ? a.plan[2 + sb] : INT_MAX;
   c.win_lq = sb < a.B ? seq_tokens<FK>(a, sb) : 0;
@@ -546,8 +551,14 @@ __device__ __forceinline__ int load_ids(const DecodeArgs& a, const SeqCursor& c,
 // HPC: KV heads per wave (a.hp_log2 == log2 HPC).  Lane (j, n) keeps only the
 // scores of its column's head: rows 16 u + 4 j + r with r = hn (mod HPC).
 // OP: every tile lies in one page (32 / HPC <= block_size), see load_tile.
+//
+// A workgroup holds NW = blockDim.x / 64 waves of one share: KV-head groups
+// c NW .. c NW + NW - 1.  They run on one compute unit and read neighbouring
+// segments of the same token rows at about the same time; each has its own
+// LDS (dynamic, NW Stage::WAVE_LDS bytes) and they never synchronize.
 template <int FK, int FV, int D, int HPC, bool OP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Stage<FK, FV, D>::WPE, Stage<FK, FV, D>::WPE)))
+__global__ __launch_bounds__((256 * Stage<FK, FV, D>::WPE))
+__attribute__((amdgpu_waves_per_eu(Stage<FK, FV, D>::WPE, Stage<FK, FV, D>::WPE)))
 void decode_split_kernel(DecodeArgs a) {
   using KS = KShape<FK, D>;
   using VS = VShape<FV, D>;
@@ -560,20 +571,23 @@ void decode_split_kernel(DecodeArgs a) {
   // tiles x + 1 .. x + P are in flight
   constexpr int NS = ST::NS, P = NS - 1;
   constexpr int L = NS > 2 ? 2 : 1;  // block ids are loaded L tiles ahead of their tile
-  __shared__ __attribute__((aligned(16))) uint8_t s_st[ST::BYTES];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+  const uint32_t wv = threadIdx.x >> 6;  // wave of the workgroup
+  uint8_t* const s_st = s_dyn + wv * ST::WAVE_LDS;
   // this tile's scales as fp32: key scale x sm_scale x log2 e, value scales
-  __shared__ __attribute__((aligned(16))) float s_fk[TILE];
-  __shared__ __attribute__((aligned(16))) float s_fv[TILE * VS::NG];
+  float* const s_fk = reinterpret_cast<float*>(s_st + ST::BYTES);
+  float* const s_fv = s_fk + TILE;
 
-  // Wave (share, group of HP KV heads).  The head groups of one share are
-  // consecutive workgroups of one XCD (workgroups are dealt to the 8 XCDs
-  // round robin), so they read the same page-scale lines of its L2 at about
-  // the same time.
+  // Wave (share, group of HP KV heads).  The workgroups of one share (when
+  // a share needs more than one) are consecutive workgroups of one XCD
+  // (workgroups are dealt to the 8 XCDs round robin), so they read the same
+  // page-scale lines of its L2 at about the same time.
   const uint32_t wg = blockIdx.x;
   const uint32_t kk = wg >> 3;
-  const uint32_t groups = (uint32_t)(a.H >> a.hp_log2);
-  const int h0 = (int)(kk % groups) << a.hp_log2;  // first KV head of the wave
-  const int share = (int)((kk / groups) * 8 + (wg & 7));
+  const uint32_t nw = blockDim.x >> 6;
+  const uint32_t nwg = (uint32_t)(a.H >> a.hp_log2) / nw;  // workgroups per share
+  const int h0 = (int)((kk % nwg) * nw + wv) << a.hp_log2;  // first KV head of the wave
+  const int share = (int)((kk / nwg) * 8 + (wg & 7));
   if (share >= a.num_shares) return;
   SeqCursor cc;  // tile being computed
   int S, total;
@@ -583,7 +597,7 @@ void decode_split_kernel(DecodeArgs a) {
     total = wave_plan<FK>(a, lq, nt, excl);
     S = share_size(a, total);
     if (share * S >= total) return;
-    const int lane = (int)threadIdx.x;
+    const int lane = (int)threadIdx.x & 63;
     cc.wb = 0;
     cc.win_hi = lane < a.B ? excl + nt : INT_MAX;
     cc.win_lq = lq;
@@ -606,7 +620,7 @@ void decode_split_kernel(DecodeArgs a) {
   const int x_end = min(x_begin + S, total);
   SeqCursor ci = cc, cd = cc;  // tile being issued, block ids being fetched
 
-  const int lane = (int)threadIdx.x;
+  const int lane = (int)threadIdx.x & 63;
   const int j = lane >> 4, n = lane & 15;
   // MFMA column n (query operand, scores, output rows) is query head
   // hq0 + n: KV head h0 + n / G, for n < NC = HP G (at most 16).
@@ -1263,32 +1277,42 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(DecodeArgs a) {
 namespace {
 
 // Waves of decode_split_kernel<FK, FV, D> to run at once on the current
-// device: WPE per SIMD (4 WPE per compute unit), or the occupancy if lower.
-// Every wave gets the same work, so a SIMD holding more waves than the
-// others would hold the whole launch back.  Cached per device.
+// device in workgroups of nw waves: WPE per SIMD (4 WPE per compute unit),
+// or the occupancy if lower.  Every wave gets the same work, so a SIMD
+// holding more waves than the others would hold the whole launch back.
+// Cached per device and nw.
 template <int FK, int FV, int D, int HPC, bool OP>
-int resident_waves() {
-  static std::atomic<int> cache[64];
+int resident_waves(int nw) {
+  constexpr int MAXW = 4 * Stage<FK, FV, D>::WPE;
+  static std::atomic<int> cache[64][MAXW + 1];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipGetDevice(&dev) != hipSuccess || nw < 1 || nw > MAXW) return 0;
   if (dev >= 0 && dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
+    const int c = cache[dev][nw].load(std::memory_order_relaxed);
     if (c > 0) return c;
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D, HPC, OP>, 64, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D, HPC, OP>, 64 * nw,
+                                                   (size_t)nw * Stage<FK, FV, D>::WAVE_LDS) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  const int w = std::min(per_cu, 4 * Stage<FK, FV, D>::WPE) * cus;
-  if (dev >= 0 && dev < 64 && w > 0) cache[dev].store(w, std::memory_order_relaxed);
+  const int w = std::min(per_cu * nw, MAXW) * cus;
+  if (dev >= 0 && dev < 64 && w > 0) cache[dev][nw].store(w, std::memory_order_relaxed);
   return w;
 }
 
 template <int FK, int FV, int D, int HPC, bool OP>
 hipError_t launch4(DecodeArgs a, hipStream_t st) {
+  // Waves per workgroup: the largest divisor of the share's head groups that
+  // fits on one compute unit (4 WPE waves).  Putting a share's head groups
+  // on one compute unit measured 4.5% (FP8, 4 heads per wave) to 11% (INT8,
+  // 2 heads per wave) faster than one wave per workgroup.
+  const int groups = a.H >> a.hp_log2;
+  int nw = std::min(groups, 4 * Stage<FK, FV, D>::WPE);
+  while (groups % nw) --nw;
   if (a.share_tiles <= 0) {
     // balanced: all waves the same length, all resident at once
-    const int w = resident_waves<FK, FV, D, HPC, OP>();
+    const int w = resident_waves<FK, FV, D, HPC, OP>(nw);
     if (w <= 0) return hipErrorInvalidDevice;
     a.num_shares = min(a.max_shares, max(1, w / (a.H >> a.hp_log2)));
   } else {
@@ -1302,9 +1326,11 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // one wave per (share, group of HP KV heads); see decode_split_kernel for the order
-  const uint32_t wgs = (((uint32_t)a.num_shares + 7) / 8) * 8 * (uint32_t)(a.H >> a.hp_log2);
-  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D, HPC, OP>), dim3(wgs), dim3(64), 0, st, a);
+  // one wave per (share, group of HP KV heads), nw waves per workgroup; see
+  // decode_split_kernel for the order
+  const uint32_t wgs = (((uint32_t)a.num_shares + 7) / 8) * 8 * (uint32_t)(groups / nw);
+  const size_t lds = (size_t)nw * Stage<FK, FV, D>::WAVE_LDS;
+  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D, HPC, OP>), dim3(wgs), dim3(64 * nw), lds, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.B * a.Hq < 512)
