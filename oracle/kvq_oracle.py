@@ -26,6 +26,10 @@ Readings taken where the pages leave a step open (each is repeated at its use):
   * FP8 is the OCP E4M3FN encoding (max 448, no infinities, S.1111.111 = NaN),
     rounded to nearest-even and saturated at +-448.  [P1] section 2.3 prints
     +-240, which is the maximum of the FNUZ variant, not of E4M3FN;
+  * the E5M2 variant ([P1] section 2.3 table, +-57344) is the OCP E5M2
+    encoding (bias 15, infinities and NaN in exponent field 31), scaled per
+    token and head like E4M3FN with q_max 57344, rounded to nearest-even and
+    saturated at +-57344;
   * a group whose fp16 scale is 0 (all-zero input, or a scale that underflows
     fp16) stores scale 0 and all codes 0;
   * INT4 packs two codes per byte, the even channel in the low nibble;
@@ -52,14 +56,17 @@ INT8 = "int8"
 FP8_E4M3FN = "fp8_e4m3fn"
 INT4_G32 = "int4_g32"
 INT4_KIVI = "int4_kivi"
+FP8_E5M2 = "fp8_e5m2"
 
-SYM_FORMATS = (INT8, FP8_E4M3FN, INT4_G32)
+SYM_FORMATS = (INT8, FP8_E4M3FN, INT4_G32, FP8_E5M2)
+FP8_FORMATS = (FP8_E4M3FN, FP8_E5M2)
 K_FORMATS = SYM_FORMATS + (INT4_KIVI,)
 V_FORMATS = SYM_FORMATS
 
 # Largest representable magnitude of each symmetric target ([P1] section 2.1
-# table: signed INT8 127, signed INT4 7; OCP E4M3FN 448).
-QMAX = {INT8: 127.0, INT4_G32: 7.0, FP8_E4M3FN: 448.0}
+# table: signed INT8 127, signed INT4 7; OCP E4M3FN 448; [P1] section 2.3
+# table: E5M2 57344).
+QMAX = {INT8: 127.0, INT4_G32: 7.0, FP8_E4M3FN: 448.0, FP8_E5M2: 57344.0}
 
 # Channels per scale group along head_dim ([P2] section 5, "Where the scales
 # live": INT4 with group=32).  Per-token-per-head formats have one group = D.
@@ -129,6 +136,60 @@ def e4m3fn_encode(y) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# FP8 E5M2, from the OCP 8-bit floating point definition: 1 sign bit, 5
+# exponent bits with bias 15, 2 mantissa bits; exponent field 0 holds
+# subnormals m * 2^-16; exponent field 31 holds infinities (mantissa 0) and
+# NaN, so the largest finite magnitude is 1.75 * 2^15 = 57344 ([P1] section
+# 2.3 table: 5 exponent bits, 2 mantissa bits, +-57344; [P3] "Numerical
+# Formats": 1-5-2 split, 4 levels per power of two).
+# --------------------------------------------------------------------------
+
+E5M2_MAX_CODE = 0x7B  # 57344
+
+
+def e5m2_value(code) -> np.ndarray:
+    """Exact float64 value of each E5M2 byte (+-inf for S.11111.00, NaN for
+    the other codes of exponent field 31)."""
+    c = np.asarray(code, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = (c & 0x3).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -16, (1.0 + m / 4.0) * np.exp2(e.astype(np.float64) - 15.0))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def e5m2_encode(y) -> np.ndarray:
+    """Round float32 values to E5M2 bytes: nearest, ties to the even code,
+    saturating at +-57344 (never an infinity).  The sign of zero (and of
+    values that round to zero) is kept.  NaN and infinite inputs are outside
+    the contract."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y).astype(np.float64)  # exact
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -14
+    # subnormal range: the value is m * 2^-16; m = 4 is the smallest normal
+    # (code 0x04) by continuity of the encoding
+    code[sub] = np.rint(a[sub] * 2.0 ** 16).astype(np.int64)
+    nrm = ~sub
+    frac, exp = np.frexp(a[nrm])  # a = frac * 2^exp, frac in [0.5, 1)
+    e = exp.astype(np.int64) - 1  # a = (1 + f) * 2^e
+    mant = np.rint((2.0 * frac - 1.0) * 4.0).astype(np.int64)  # 0..4, ties even
+    code[nrm] = ((e + 15) << 2) + mant  # a carry into the exponent is the + above
+    code = np.minimum(code, E5M2_MAX_CODE)  # saturate at 57344
+    code |= np.where(np.signbit(y), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def fp8_value(code, fmt: str) -> np.ndarray:
+    return e4m3fn_value(code) if fmt == FP8_E4M3FN else e5m2_value(code)
+
+
+def fp8_encode(y, fmt: str) -> np.ndarray:
+    return e4m3fn_encode(y) if fmt == FP8_E4M3FN else e5m2_encode(y)
+
+
+# --------------------------------------------------------------------------
 # Symmetric quantization ([P1] section 2.1):
 #   s = max|x| / q_max;  x_q = clip(round(x / s), -q_max, q_max);  x_hat = x_q s
 # Granularity: per token per head ([P2] section 5 "Where the scales live":
@@ -156,8 +217,8 @@ def quantize_sym(x16: np.ndarray, fmt: str):
     safe = np.where(zero, np.float32(1.0), s)
     with np.errstate(over="ignore", invalid="ignore"):
         y = x / safe[..., None]  # IEEE binary32 quotient
-    if fmt == FP8_E4M3FN:
-        c = e4m3fn_encode(y)
+    if fmt in FP8_FORMATS:
+        c = fp8_encode(y, fmt)
         c[np.broadcast_to(zero[..., None], c.shape)] = 0
         codes = c.reshape(x16.shape)
     else:
@@ -172,8 +233,8 @@ def dequant_sym(codes: np.ndarray, scales16: np.ndarray, fmt: str) -> np.ndarray
     """x_hat = code * s in float64 ([P1] section 2.1, Exercise 1 step 4)."""
     D = codes.shape[-1]
     g = INT4_GROUP if fmt == INT4_G32 else D
-    if fmt == FP8_E4M3FN:
-        v = e4m3fn_value(codes)
+    if fmt in FP8_FORMATS:
+        v = fp8_value(codes, fmt)
     else:
         v = codes.astype(np.int8).astype(np.float64)
     v = v.reshape(codes.shape[:-1] + (D // g, g))
@@ -345,7 +406,7 @@ def _dequant_rows(cache: OracleCache, which: str, blk, off):
     raw = codes_buf[blk, off]
     if fmt == INT4_G32:
         codes = unpack_int4(raw, signed=True)
-    elif fmt == FP8_E4M3FN:
+    elif fmt in FP8_FORMATS:
         codes = raw
     else:
         codes = raw.view(np.int8)

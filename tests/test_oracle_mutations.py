@@ -79,6 +79,38 @@ def test_wrong_fp8_exponent_bias_fails():
     assert _fails(pins.check_fp8_bruteforce, lambda y: o.e4m3fn_encode(np.asarray(y, np.float32) * 2))
 
 
+def test_e5m2_no_saturation_fails(monkeypatch):
+    # Mistake: let large quotients reach the infinity code.
+    monkeypatch.setattr(o.kvq_oracle, "E5M2_MAX_CODE", 0x7C)
+    assert _fails(pins.check_e5m2_specials, o.kvq_oracle.e5m2_encode)
+
+
+def test_e5m2_wrong_exponent_bias_fails():
+    assert _fails(pins.check_e5m2_bruteforce, lambda y: o.e5m2_encode(np.asarray(y, np.float32) * 2))
+
+
+def test_e5m2_mantissa_bits_fail():
+    # Mistake: E4M3's mantissa width with E5M2's exponent (encode through the
+    # E4M3 rounding grid scaled into E5M2's range).
+    def wrong(y):
+        y = np.asarray(y, np.float32)
+        snapped = o.e4m3fn_value(o.e4m3fn_encode(y / np.float32(2 ** 7))) * 2.0 ** 7
+        return o.e5m2_encode(snapped.astype(np.float32))
+    assert _fails(pins.check_e5m2_bruteforce, wrong)
+
+
+def test_e5m2_as_e4m3_in_invariants_fails():
+    # Mistake: encode E5M2 rows with the E4M3FN encoder (wrong format table).
+    def quantize(x16, fmt):
+        codes, s16 = o.quantize_sym(x16, fmt)
+        if fmt == o.FP8_E5M2:
+            s = s16.astype(np.float32)
+            y = x16.astype(np.float32) / np.where(s == 0, 1, s)
+            codes = o.e4m3fn_encode(y)
+        return codes, s16
+    assert _fails(pins.check_sym_invariants, quantize, o.dequant_sym, (o.FP8_E5M2,))
+
+
 def test_swapped_nibbles_fail():
     assert _fails(pins.check_pack_order, lambda c: o.pack_int4(np.asarray(c)[..., ::-1]))
 

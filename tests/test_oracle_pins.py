@@ -83,17 +83,27 @@ def check_sym_invariants(quantize_sym=o.quantize_sym, dequant=o.dequant_sym, fmt
         topx = np.take_along_axis(x, idx[..., None], -1)[..., 0]
         ok = normal & (topx != 0)
         assert np.all(np.abs(top[ok] / s[ok]) == q), fmt
-        # 2. reconstruction error bound
+        # 2. reconstruction error bound, half a step of the target grid at the
+        #    quotient (FP8: 2^(e - m - 1) for a normal quotient in [2^e, 2^(e+1)),
+        #    m mantissa bits, and half the subnormal step below 2^emin)
         err = np.abs(x - xhat)
-        if fmt == o.FP8_E4M3FN:
-            y = np.abs(x) / np.where(s == 0, 1, s)[..., None]
-            e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
-            half_step = np.where(y < 2.0 ** -6, 2.0 ** -10, 2.0 ** (e - 4))
+        y = np.abs(x) / np.where(s == 0, 1, s)[..., None]
+        if fmt in o.FP8_FORMATS:
+            mbits, emin = (3, -6) if fmt == o.FP8_E4M3FN else (2, -14)
+            e = np.floor(np.log2(np.maximum(y, 2.0 ** emin)))
+            half_step = np.where(y < 2.0 ** emin, 2.0 ** (emin - mbits - 1), 2.0 ** (e - mbits - 1))
+            top_half = 2.0 ** (math.floor(math.log2(q)) - mbits - 1)
             bound = s[..., None] * half_step * (1 + 2.0 ** -20)
         else:
+            top_half = 0.5
             bound = s[..., None] * (0.5 + 2.0 ** -17)
         bound = np.broadcast_to(bound, x.shape)
-        nz = np.broadcast_to((s > 0)[..., None], x.shape)
+        # A quotient beyond q_max plus half a step saturates.  That happens
+        # only when s16 rounded well below s32, i.e. in the fp16 subnormal
+        # range; a normal s16 keeps every quotient within q_max (1 + 2^-11).
+        sat = (s > 0) & (np.max(y, axis=-1) > q + top_half)
+        assert not np.any(sat & normal), fmt
+        nz = np.broadcast_to(((s > 0) & ~sat)[..., None], x.shape)
         assert np.all(err[nz] <= bound[nz]), fmt
         # 3. codes in range and carrying the sign of x
         vals = xhat / np.where(s == 0, 1, s)[..., None]
@@ -126,6 +136,37 @@ def check_fp8_bruteforce(encode=o.e4m3fn_encode):
     expect = np.where(a > 448, 0x7E, expect) | np.where(np.signbit(y), 0x80, 0)
     got = encode(y)
     assert np.array_equal(got.astype(np.int64), expect.astype(np.int64))
+
+
+def check_e5m2_bruteforce(encode=o.e5m2_encode):
+    # All finite E5M2 magnitudes, by code (0x7C is +inf, 0x7D..0x7F NaN).
+    mags = o.e5m2_value(np.arange(0x7C))  # codes 0x00..0x7B
+    assert mags[-1] == 57344.0
+    h = np.arange(0x10000, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    y = h[np.isfinite(h)].astype(np.float32)
+    rnd = (np.random.default_rng(8).standard_normal(200000) *
+           np.exp2(np.random.default_rng(9).uniform(-20, 18, 200000))).astype(np.float32)
+    y = np.concatenate([y, rnd])
+    a = np.abs(y).astype(np.float64)
+    d = np.abs(a[:, None] - mags[None, :])
+    best = d.min(axis=1)
+    cand = d == best[:, None]
+    codes = np.arange(0x7C)
+    even_pick = np.where(cand & (codes[None, :] % 2 == 0), codes[None, :], 999).min(axis=1)
+    any_pick = np.where(cand, codes[None, :], 999).min(axis=1)
+    ties = cand.sum(axis=1) > 1
+    expect = np.where(ties, even_pick, any_pick)
+    expect = np.where(a > 57344, 0x7B, expect) | np.where(np.signbit(y), 0x80, 0)
+    got = encode(y)
+    assert np.array_equal(got.astype(np.int64), expect.astype(np.int64))
+
+
+def check_e5m2_specials(encode=o.e5m2_encode):
+    cases = [(57344.0, 0x7B), (61440.0, 0x7B), (65504.0, 0x7B), (1e9, 0x7B), (-1e9, 0xFB),
+             (2.0 ** -16, 0x01), (2.0 ** -17, 0x00), (3 * 2.0 ** -17, 0x02), (2.0 ** -14, 0x04),
+             (1.0, 0x3C), (1.125, 0x3C), (1.375, 0x3E), (-0.0, 0x80), (0.0, 0x00), (-1e-9, 0x80)]
+    for y, c in cases:
+        assert int(encode(np.array([y], np.float32))[0]) == c, (y, hex(c))
 
 
 def check_fp8_specials(encode=o.e4m3fn_encode):
@@ -183,6 +224,44 @@ def test_fp8_bruteforce():
 
 def test_fp8_specials():
     check_fp8_specials()
+
+
+def test_e5m2_bruteforce():
+    check_e5m2_bruteforce()
+
+
+def test_e5m2_specials():
+    check_e5m2_specials()
+
+
+def test_e5m2_decode_table():
+    vals = o.e5m2_value(np.arange(256))
+    fin = np.isfinite(vals)
+    assert fin.sum() == 248  # +-inf and six NaN codes in exponent field 31
+    assert vals[0x7C] == np.inf and vals[0xFC] == -np.inf and np.isnan(vals[0x7D])
+    g = read_golden("closed_forms.txt")
+    assert vals[0x7B] == g["e5m2_max"] and vals[0xFB] == -g["e5m2_max"] and vals[0x01] == 2.0 ** -16
+    octave = vals[(vals >= 1.0) & (vals < 2.0)]
+    assert len(octave) == g["e5m2_levels_per_octave"]
+    # E5M2 is the upper byte of an fp16 value: the same bits read as fp16
+    as16 = (np.arange(256, dtype=np.uint16) << 8).view(np.float16).astype(np.float64)
+    assert np.array_equal(as16[fin], vals[fin])
+    codes = np.arange(256)[fin]
+    assert np.array_equal(o.e5m2_encode(vals[fin].astype(np.float32)), codes.astype(np.uint8))
+
+
+def test_e5m2_matches_torch_cast():
+    # torch's CPU float8_e5m2 cast is an independent RNE implementation; it
+    # overflows to infinity from 61440 up instead of saturating, so compare
+    # below that.
+    rng = np.random.default_rng(12)
+    y = (rng.standard_normal(400000) * np.exp2(rng.uniform(-22, 16, 400000))).astype(np.float32)
+    y = y[np.abs(y) < 61440]
+    h = np.arange(0x10000, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    h = h[np.isfinite(h) & (np.abs(h) < 61440)]
+    y = np.concatenate([y, h])
+    ref = torch.from_numpy(y).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(o.e5m2_encode(y), ref)
 
 
 def test_fp8_decode_table():
@@ -337,7 +416,8 @@ def _make_seq_cache(kf, vf, L, bs, H, D, table, seed=0, seqs=1):
     return c, k, v
 
 
-@pytest.mark.parametrize("kf,vf", [(o.INT8, o.INT8), (o.FP8_E4M3FN, o.FP8_E4M3FN), (o.INT8, o.INT4_G32),
+@pytest.mark.parametrize("kf,vf", [(o.INT8, o.INT8), (o.FP8_E4M3FN, o.FP8_E4M3FN), (o.FP8_E5M2, o.FP8_E5M2),
+                                   (o.INT8, o.INT4_G32),
                                    (o.INT4_KIVI, o.INT4_G32)])
 def test_paged_gather_equals_direct_quantization(kf, vf):
     # Writing through a shuffled block table and reading back through it gives
