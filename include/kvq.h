@@ -72,21 +72,27 @@ typedef enum kvq_status {
  *                A page is quantized when its last row is written; until then
  *                its rows (keys AND values) are kept in fp16 in the
  *                sequence's tail.
+ * KVQ_FP8_E5M2   symmetric, one fp16 scale per (token, head); codes are OCP
+ *                E5M2 bytes (bias 15, max 57344; [P1] 2.3 table), q_max
+ *                57344, round-to-nearest-even, saturating (never an infinity
+ *                code).  The fp16 scale max|x|/57344 is an fp16 subnormal
+ *                below max|x| = 3.5 and 0 below about 1.7e-3 (codes 0).
  * Every quotient x/s is the IEEE binary32 quotient by the STORED fp16 scale;
  * an fp16 scale of 0 stores all-zero codes. */
 typedef enum kvq_dtype {
   KVQ_INT8 = 1,
   KVQ_FP8_E4M3FN = 2,
   KVQ_INT4_G32 = 3,
-  KVQ_INT4_KIVI = 4
+  KVQ_INT4_KIVI = 4,
+  KVQ_FP8_E5M2 = 5
 } kvq_dtype;
 
 /* A paged, quantized KV cache for one attention layer.  All buffers are
  * caller-allocated device memory, contiguous, in these layouts (nb =
  * num_blocks, bs = block_size, H = n_kv_heads, D = head_dim):
- *   k_codes / v_codes  uint8 (nb, bs, H, D)    INT8, FP8
+ *   k_codes / v_codes  uint8 (nb, bs, H, D)    INT8, FP8 (E4M3FN, E5M2)
  *                      uint8 (nb, bs, H, D/2)  INT4_G32, INT4_KIVI
- *   k_scales/v_scales  fp16  (nb, bs, H)       INT8, FP8
+ *   k_scales/v_scales  fp16  (nb, bs, H)       INT8, FP8 (E4M3FN, E5M2)
  *                      fp16  (nb, bs, H, D/32) INT4_G32
  *                      fp16  (nb, H, D)        INT4_KIVI (k only)
  *   k_zeros            fp16  (nb, H, D)        INT4_KIVI only, else NULL

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 KVQ_OK = 0
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_SHAPE",
           -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_NO_DEVICE", -6: "KVQ_ERR_HIP"}
-DTYPES = {"int8": 1, "fp8_e4m3fn": 2, "int4_g32": 3, "int4_kivi": 4}
+DTYPES = {"int8": 1, "fp8_e4m3fn": 2, "int4_g32": 3, "int4_kivi": 4, "fp8_e5m2": 5}
 
 # Functions declared in include/kvq.h (the symbol test checks this list
 # against the header).

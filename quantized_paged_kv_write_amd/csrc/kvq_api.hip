@@ -10,13 +10,15 @@ using namespace kvq;
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-bool sym_fmt(int32_t f) { return f == KVQ_INT8 || f == KVQ_FP8_E4M3FN || f == KVQ_INT4_G32; }
+bool sym_fmt(int32_t f) {
+  return f == KVQ_INT8 || f == KVQ_FP8_E4M3FN || f == KVQ_INT4_G32 || f == KVQ_FP8_E5M2;
+}
 
 int check_cache(const kvq_cache* c) {
   if (!c) return KVQ_ERR_INVALID_ARG;
   if (c->num_blocks <= 0 || c->block_size <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0)
     return KVQ_ERR_INVALID_ARG;
-  if (!(c->k_dtype >= KVQ_INT8 && c->k_dtype <= KVQ_INT4_KIVI)) return KVQ_ERR_INVALID_ARG;
+  if (!(c->k_dtype >= KVQ_INT8 && c->k_dtype <= KVQ_FP8_E5M2)) return KVQ_ERR_INVALID_ARG;
   if (!sym_fmt(c->v_dtype)) {
     return (c->v_dtype == KVQ_INT4_KIVI) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
   }

@@ -101,6 +101,13 @@ __device__ __forceinline__ void fp8_to_h4(uint32_t d, uint32_t& lo, uint32_t& hi
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true));
 }
 
+// E5M2 -> fp16: an E5M2 byte is the upper byte of the fp16 of the same value
+// (one v_perm per two codes).
+__device__ __forceinline__ void e5m2_to_h4(uint32_t d, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_amdgcn_perm(0u, d, 0x010C000Cu);  // [0, c0, 0, c1]
+  hi = __builtin_amdgcn_perm(0u, d, 0x030C020Cu);  // [0, c2, 0, c3]
+}
+
 template <int FK>
 __device__ __forceinline__ h8 key_operand(const uint32_t* w, int kb) {
   u4 r;
@@ -120,6 +127,9 @@ __device__ __forceinline__ h8 key_operand(const uint32_t* w, int kb) {
     if constexpr (FK == F_FP8) {
       fp8_to_h4(w[2 * kb], x0, x1);
       fp8_to_h4(w[2 * kb + 1], x2, x3);
+    } else if constexpr (FK == F_E5M2) {
+      e5m2_to_h4(w[2 * kb], x0, x1);
+      e5m2_to_h4(w[2 * kb + 1], x2, x3);
     } else {
       int8_to_h4(w[2 * kb], x0, x1);
       int8_to_h4(w[2 * kb + 1], x2, x3);
@@ -139,7 +149,7 @@ __device__ __forceinline__ int key_channel(int j, int kb, int e) {
 }
 
 // ---- value operands: 8 exact bf16 values, 8 tokens of one channel ----------
-// FP8: the exact value.  INT8 and INT4: the unsigned code u (c + 128, or
+// FP8 (E4M3FN, E5M2): the exact value.  INT8 and INT4: the unsigned code u (c + 128, or
 // c + 8 for INT4) as the bf16 bit pattern u, which is exactly u 2^-133 for
 // every u < 256 (subnormal below 128; from 128 on the smallest exponent
 // continues the same spacing).  The probability operand carries 2^60 so the
@@ -156,6 +166,12 @@ __device__ __forceinline__ b8 value_operand_8bit(i2 t) {
     r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
     r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
     r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
+  } else if constexpr (FV == F_E5M2) {
+    // FP8 E5M2 -> bf16, two codes per instruction (exact)
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, 1.0f, true));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, 1.0f, false));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, 1.0f, true));
   } else {
     // bytes c + 128 into zero-padded halves: [u0, 0, u1, 0] per dword
     const uint32_t e0 = d0 ^ 0x80808080u, e1 = d1 ^ 0x80808080u;
@@ -566,7 +582,8 @@ void decode_split_kernel(DecodeArgs a) {
   constexpr int CHK = KS::RB / 16 > 0 ? KS::RB / 16 : 1;
   constexpr int NCS = FV == F_INT4 ? VS::NG : 1;  // bias-correction sums kept per value group
   // value scales carry 2^60 for the INT8 / INT4 value operands (u 2^-133)
-  constexpr float VSC = FV == F_FP8 ? 1.f : 0x1p60f;
+  constexpr bool VFP8 = FV == F_FP8 || FV == F_E5M2;  // value operands hold the exact value
+  constexpr float VSC = VFP8 ? 1.f : 0x1p60f;
   // NS tiles held in registers: tile x is stored to LDS and computed while
   // tiles x + 1 .. x + P are in flight
   constexpr int NS = ST::NS, P = NS - 1;
@@ -715,7 +732,7 @@ void decode_split_kernel(DecodeArgs a) {
     // 2^73 acc - 2^-53 cs; INT4 (u = c + 8): even channels 2^73 acc - 2^-57 cs,
     // odd channels (16 u 2^-133) 2^69 acc - 2^-57 cs; cs = sum of the
     // probability operands of query head g
-    if constexpr (FV != F_FP8) {
+    if constexpr (!VFP8) {
 #pragma unroll
       for (int g = 0; g < NCS; ++g) {
         float cs = cs_run[g];
@@ -792,7 +809,7 @@ void decode_split_kernel(DecodeArgs a) {
     }
 
     // ---- scales -> fp32 (0 for masked tokens); FP8 codes of masked value
-    //      rows zeroed (a garbage byte may be a NaN code)
+    //      rows zeroed (a garbage byte may be a NaN or infinity code)
     {
       const uint32_t* sdw = reinterpret_cast<const uint32_t*>(cur + ST::OFF_S);
       const int t = lane & 31;
@@ -821,7 +838,7 @@ void decode_split_kernel(DecodeArgs a) {
           }
         }
       }
-      if constexpr (FV == F_FP8) {
+      if constexpr (VFP8) {
         if (live_mask != ~0ull) {
 #pragma unroll
           for (int i = 0; i < ST::NLV; ++i) {
@@ -1372,6 +1389,7 @@ hipError_t by_v(int fv, int D, const DecodeArgs& a, hipStream_t s) {
     case F_INT8: return by_dim<FK, F_INT8>(D, a, s);
     case F_FP8: return by_dim<FK, F_FP8>(D, a, s);
     case F_INT4: return by_dim<FK, F_INT4>(D, a, s);
+    case F_E5M2: return by_dim<FK, F_E5M2>(D, a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1418,6 +1436,7 @@ hipError_t launch_decode(const kvq_cache& c, const DecodeArgs& a, hipStream_t s)
     case F_INT8: return by_v<F_INT8>(c.v_dtype, c.head_dim, a, s);
     case F_FP8: return by_v<F_FP8>(c.v_dtype, c.head_dim, a, s);
     case F_KIVI: return by_v<F_KIVI>(c.v_dtype, c.head_dim, a, s);
+    case F_E5M2: return by_v<F_E5M2>(c.v_dtype, c.head_dim, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -10,7 +10,13 @@
 
 namespace kvq {
 
-enum Fmt : int { F_INT8 = KVQ_INT8, F_FP8 = KVQ_FP8_E4M3FN, F_INT4 = KVQ_INT4_G32, F_KIVI = KVQ_INT4_KIVI };
+enum Fmt : int {
+  F_INT8 = KVQ_INT8,
+  F_FP8 = KVQ_FP8_E4M3FN,
+  F_INT4 = KVQ_INT4_G32,
+  F_KIVI = KVQ_INT4_KIVI,
+  F_E5M2 = KVQ_FP8_E5M2
+};
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return __half2float(__ushort_as_half((unsigned short)bits16));
@@ -65,6 +71,12 @@ __device__ __forceinline__ uint32_t rne_low_bits(float y) {
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+// Four values (within +-57344) to OCP E5M2 bytes, nearest-even (v_cvt_pk_bf8_f32).
+__device__ __forceinline__ uint32_t bf8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
   return (uint32_t)w;
 }
 

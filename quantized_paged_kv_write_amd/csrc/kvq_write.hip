@@ -27,12 +27,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int FMT>
 __device__ __forceinline__ float qmax() {
-  return FMT == F_INT8 ? 127.0f : (FMT == F_FP8 ? 448.0f : 7.0f);
+  return FMT == F_INT8 ? 127.0f : FMT == F_FP8 ? 448.0f : FMT == F_E5M2 ? 57344.0f : 7.0f;
 }
 // RN(1 / q_max), rounded once at compile time
 template <int FMT>
 __device__ __forceinline__ float inv_qmax() {
-  constexpr float r = FMT == F_INT8 ? 1.0f / 127.0f : (FMT == F_FP8 ? 1.0f / 448.0f : 1.0f / 7.0f);
+  constexpr float r = FMT == F_INT8   ? 1.0f / 127.0f
+                      : FMT == F_FP8  ? 1.0f / 448.0f
+                      : FMT == F_E5M2 ? 1.0f / 57344.0f
+                                      : 1.0f / 7.0f;
   return r;
 }
 
@@ -55,6 +58,14 @@ __device__ __forceinline__ u32x2 encode8(const float (&y)[8]) {
     for (int j = 0; j < 8; ++j) c[j] = fminf(fmaxf(y[j], -448.0f), 448.0f);
     out.x = fp8x4(c[0], c[1], c[2], c[3]);
     out.y = fp8x4(c[4], c[5], c[6], c[7]);
+  } else if constexpr (FMT == F_E5M2) {
+    // saturate before the conversion, which would round past 57344 to the
+    // infinity code
+    float c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = fminf(fmaxf(y[j], -57344.0f), 57344.0f);
+    out.x = bf8x4(c[0], c[1], c[2], c[3]);
+    out.y = bf8x4(c[4], c[5], c[6], c[7]);
   } else if constexpr (FMT == F_INT8) {
     // clip, round half to even (rne_low_bits), low bytes gathered by v_perm
     uint32_t b[8];
@@ -376,6 +387,7 @@ hipError_t by_v(int fv, int D, const WriteArgs& a, hipStream_t s) {
     case F_INT8: return by_dim<FK, F_INT8>(D, a, s);
     case F_FP8: return by_dim<FK, F_FP8>(D, a, s);
     case F_INT4: return by_dim<FK, F_INT4>(D, a, s);
+    case F_E5M2: return by_dim<FK, F_E5M2>(D, a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -388,6 +400,7 @@ hipError_t launch_write(const kvq_cache& c, const WriteArgs& a, hipStream_t s) {
     case F_FP8: return by_v<F_FP8>(c.v_dtype, c.head_dim, a, s);
     case F_INT4: return by_v<F_INT4>(c.v_dtype, c.head_dim, a, s);
     case F_KIVI: return by_v<F_KIVI>(c.v_dtype, c.head_dim, a, s);
+    case F_E5M2: return by_v<F_E5M2>(c.v_dtype, c.head_dim, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -63,8 +63,12 @@ WORKLOADS = {
     # KIVI-style INT4 keys (per channel, 32-token groups) + INT4 g32 values.
     "llama3_8b_kivi_int4": Workload("llama3_8b_kivi_int4", 4, 32, 8, 128, 32, "int4_kivi", "int4_g32",
                                     ("fixed", 131072), 4, sink_tokens=4),
+    # The Llama-3-8B FP8 shape with the E5M2 variant for keys and values.
+    "llama3_8b_e5m2": Workload("llama3_8b_e5m2", 27, 32, 8, 128, 16, "fp8_e5m2", "fp8_e5m2",
+                               ("fixed", 32768), 4, sink_tokens=4),
 }
-ORDER = ["tiny_int8", "llama3_8b_fp8", "llama3_8b_int8k_int4v", "llama3_70b_int8", "llama3_8b_kivi_int4"]
+ORDER = ["tiny_int8", "llama3_8b_fp8", "llama3_8b_int8k_int4v", "llama3_70b_int8", "llama3_8b_kivi_int4",
+         "llama3_8b_e5m2"]
 
 
 def ctx_lengths(w: Workload, seed: int) -> list:

@@ -12,7 +12,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 COMBOS = [("int8", "int8"), ("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("fp8_e4m3fn", "int4_g32"),
-          ("int8", "fp8_e4m3fn"), ("int4_kivi", "int4_g32"), ("int4_kivi", "int8"), ("int4_kivi", "fp8_e4m3fn")]
+          ("int8", "fp8_e4m3fn"), ("int4_kivi", "int4_g32"), ("int4_kivi", "int8"), ("int4_kivi", "fp8_e4m3fn"),
+          ("fp8_e5m2", "fp8_e5m2"), ("fp8_e5m2", "int4_g32"), ("int8", "fp8_e5m2"), ("int4_kivi", "fp8_e5m2")]
 RAGGED = [0, 1, 15, 16, 17, 31, 32, 33, 100, 257]
 
 

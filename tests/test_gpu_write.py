@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 COMBOS = [("int8", "int8"), ("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("fp8_e4m3fn", "int4_g32"),
-          ("int8", "fp8_e4m3fn"), ("int4_kivi", "int4_g32"), ("int4_kivi", "int8"), ("int4_kivi", "fp8_e4m3fn")]
+          ("int8", "fp8_e4m3fn"), ("int4_kivi", "int4_g32"), ("int4_kivi", "int8"), ("int4_kivi", "fp8_e4m3fn"),
+          ("fp8_e5m2", "fp8_e5m2"), ("fp8_e5m2", "int4_g32"), ("int8", "fp8_e5m2"), ("int4_kivi", "fp8_e5m2")]
 
 
 def _small(kf, vf, D, bs, ctx, H=2, G=2, seed=0, outliers=2, sinks=2):
@@ -65,6 +66,8 @@ def _edge_rows(D, rng):
     rows.append(rng.standard_normal(D) * 1e-6)                   # scale underflows fp16
     r = np.zeros(D); r[0] = 7.9375; r[1:] = rng.integers(-254, 255, D - 1) * 0.03125; rows.append(r)  # ties
     r = np.zeros(D); r[0] = 448.0; r[1:] = rng.standard_normal(D - 1); rows.append(r)
+    r = np.zeros(D); r[0] = 57344.0; r[1:] = rng.standard_normal(D - 1) * 1e4; rows.append(r)  # E5M2 max
+    r = rng.standard_normal(D) * 2.0; r[0] = 3.5; rows.append(r)  # E5M2 scale at the fp16 normal edge
     r = np.zeros(D); r[5] = -1.0; rows.append(r)                 # one spike
     r = rng.standard_normal(D); r[::7] *= 300; rows.append(r)
     rows.append(np.linspace(-1, 1, D) * 3.5)
@@ -72,7 +75,8 @@ def _edge_rows(D, rng):
     return np.stack(rows).astype(np.float16)
 
 
-@pytest.mark.parametrize("kf,vf", [("int8", "int4_g32"), ("fp8_e4m3fn", "int8"), ("int8", "fp8_e4m3fn")])
+@pytest.mark.parametrize("kf,vf", [("int8", "int4_g32"), ("fp8_e4m3fn", "int8"), ("int8", "fp8_e4m3fn"),
+                                   ("fp8_e5m2", "int8"), ("int8", "fp8_e5m2")])
 def test_write_edge_values(kf, vf):
     D, H, bs = 128, 2, 16
     rng = np.random.default_rng(3)
