@@ -212,6 +212,14 @@ def quantize_sym(x16: np.ndarray, fmt: str):
     # FP16).  The quotient below divides by the stored value.
     s32 = amax / np.float32(QMAX[fmt])
     s16 = s32.astype(np.float16)
+    return _codes_for_scale(x, s16, fmt).reshape(x16.shape), s16
+
+
+def _codes_for_scale(x, s16, fmt):
+    """Codes of fp32 groups x (..., n_groups, g) for fp16 scales s16 (...,
+    n_groups): the IEEE binary32 quotient by the stored scale, then the
+    format's rounding with saturation at +-q_max ([P1] section 2.1 clip);
+    a zero scale gives zero codes."""
     s = s16.astype(np.float32)
     zero = s == 0
     safe = np.where(zero, np.float32(1.0), s)
@@ -220,13 +228,26 @@ def quantize_sym(x16: np.ndarray, fmt: str):
     if fmt in FP8_FORMATS:
         c = fp8_encode(y, fmt)
         c[np.broadcast_to(zero[..., None], c.shape)] = 0
-        codes = c.reshape(x16.shape)
-    else:
-        q = QMAX[fmt]
-        c = np.clip(np.rint(y), -q, q)  # rint: round half to even
-        c[np.broadcast_to(zero[..., None], c.shape)] = 0
-        codes = c.astype(np.int8).reshape(x16.shape)
-    return codes, s16
+        return c
+    q = QMAX[fmt]
+    c = np.clip(np.rint(y), -q, q)  # rint: round half to even
+    c[np.broadcast_to(zero[..., None], c.shape)] = 0
+    return c.astype(np.int8)
+
+
+def quantize_sym_static(x16: np.ndarray, fmt: str, s16: np.ndarray):
+    """Quantize fp16 rows (..., D) with given (calibrated) fp16 scales s16 of
+    shape (...,), one per row, instead of max|x| / q_max: the fixed scaling
+    factors computed ahead of deployment of [P3] 'Calibrate Scaling Factors'
+    and [P4] (static calibration).  Quotients beyond +-q_max saturate.  For
+    INT4 group-32 rows the row's scale serves every group.  Returns (codes,
+    scales) like quantize_sym, the scales being s16 repeated per group."""
+    assert x16.dtype == np.float16 and s16.dtype == np.float16
+    D = x16.shape[-1]
+    g = INT4_GROUP if fmt == INT4_G32 else D
+    x = x16.astype(np.float32).reshape(x16.shape[:-1] + (D // g, g))
+    sg = np.broadcast_to(s16[..., None], x.shape[:-1]).astype(np.float16)
+    return _codes_for_scale(x, sg, fmt).reshape(x16.shape), sg.copy()
 
 
 def dequant_sym(codes: np.ndarray, scales16: np.ndarray, fmt: str) -> np.ndarray:
@@ -338,9 +359,14 @@ class OracleCache:
         return out
 
 
-def _store_sym(codes_buf, scales_buf, fmt, x16_rows, slots, bs):
-    """Quantize (n, H, D) rows and scatter them to flat slots."""
-    codes, s16 = quantize_sym(x16_rows, fmt)
+def _store_sym(codes_buf, scales_buf, fmt, x16_rows, slots, bs, static_s16=None):
+    """Quantize (n, H, D) rows and scatter them to flat slots (with the given
+    per-head scales static_s16 (H,) when present)."""
+    if static_s16 is None:
+        codes, s16 = quantize_sym(x16_rows, fmt)
+    else:
+        rows_s16 = np.broadcast_to(np.asarray(static_s16, np.float16)[None, :], x16_rows.shape[:2])
+        codes, s16 = quantize_sym_static(x16_rows, fmt, rows_s16)
     if fmt == INT4_G32:
         stored = pack_int4(codes)
     else:
@@ -396,6 +422,19 @@ def write(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, se
         for off, t in offs.items():
             cache.k_tail[seq, off] = k16[t]
             cache.v_tail[seq, off] = v16[t]
+
+
+def write_static(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, k_scale16, v_scale16):
+    """Quantize-on-write with calibrated per-KV-head fp16 scales (H,) for K
+    and V instead of the per-token amax ([P3] 'Calibrate Scaling Factors';
+    [P4] static calibration).  Symmetric formats only; every written row
+    stores its head's scale in its scale slot, so reading is unchanged."""
+    assert cache.k_fmt in SYM_FORMATS and cache.k_fmt != INT4_G32 and cache.v_fmt in SYM_FORMATS
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    valid = np.nonzero(slots >= 0)[0]
+    bs = cache.bs
+    _store_sym(cache.k_codes, cache.k_scales, cache.k_fmt, k16[valid], slots[valid], bs, k_scale16)
+    _store_sym(cache.v_codes, cache.v_scales, cache.v_fmt, v16[valid], slots[valid], bs, v_scale16)
 
 
 def _dequant_rows(cache: OracleCache, which: str, blk, off):

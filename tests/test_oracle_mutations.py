@@ -145,3 +145,25 @@ def test_wrong_gqa_mapping_fails():
 def test_unplanted_oracle_passes(fmt):
     # Control: the real oracle passes the same checks.
     pins.check_sym_invariants(o.quantize_sym, o.dequant_sym, (fmt,))
+
+
+
+def test_static_ignoring_given_scale_fails():
+    # Mistake: the static path recomputes the per-row amax scale.
+    def wrong(x16, fmt, s16):
+        codes, s = o.quantize_sym(x16, fmt)
+        g = s.shape[-1]
+        return codes, np.broadcast_to(s16[..., None], s16.shape + (g,)).astype(np.float16)
+    assert _fails(pins.check_static_saturation_bruteforce, wrong)
+
+
+def test_static_without_saturation_fails():
+    # Mistake: no clip at +-q_max for the integer formats.
+    def wrong(x16, fmt, s16):
+        codes, sg = o.quantize_sym_static(x16, fmt, s16)
+        if fmt in (o.INT8, o.INT4_G32):
+            s = s16.astype(np.float32)[:, None]
+            y = x16.astype(np.float32) / np.where(s == 0, 1, s)
+            codes = np.where(s == 0, 0, np.rint(y)).astype(np.int64)
+        return codes, sg
+    assert _fails(pins.check_static_saturation_bruteforce, wrong)

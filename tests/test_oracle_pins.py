@@ -498,3 +498,93 @@ def test_quantized_attention_close_to_fp16_attention():
     a = o.decode_attn(c, q, table, [L])[0]
     ref = o.attention_fp64(q[0].astype(np.float64), k.astype(np.float64), v.astype(np.float64))
     assert np.max(np.abs(a - ref)) < 2e-2
+
+
+# --------------------------------------------------------------------------
+# Static (calibrated) scales
+# --------------------------------------------------------------------------
+
+
+def check_static_reduces_to_dynamic(quantize_static=o.quantize_sym_static):
+    # With the scale the dynamic path would store, the static path must give
+    # the dynamic codes (the dynamic path is pinned above).
+    for fmt in o.SYM_FORMATS:
+        x16 = _bulk_rows(fmt, n=3000, seed=21)
+        codes, s16 = o.quantize_sym(x16, fmt)
+        if fmt == o.INT4_G32:
+            continue  # one dynamic scale per group, the static path has one per row
+        c2, s2 = quantize_static(x16, fmt, s16[..., 0])
+        assert np.array_equal(np.asarray(c2).view(np.uint8), np.asarray(codes).view(np.uint8)), fmt
+        assert np.array_equal(s2.view(np.uint16), s16.view(np.uint16)), fmt
+
+
+def check_static_saturation_bruteforce(quantize_static=o.quantize_sym_static):
+    # Scales well below max|x| / q_max: every element goes to the nearest
+    # level of the format's grid times s, ties to the even code, and
+    # quotients beyond the grid saturate at +-q_max.  Integer formats by brute
+    # force over the levels; FP8 formats through the pinned encoders.
+    rng = np.random.default_rng(31)
+    x16 = (rng.standard_normal((400, 64)) * 3).astype(np.float16)
+    x16[0, :4] = [0.0, -0.0, 1.5, -2.5]
+    for fmt in o.SYM_FORMATS:
+        q = o.QMAX[fmt]
+        s16 = (np.abs(x16.astype(np.float32)).max(axis=-1) / np.float32(q) * np.float32(0.3)).astype(np.float16)
+        s16[0] = np.float16(1.0)  # exact half-way quotients in row 0
+        s16[1] = np.float16(0.0)  # a zero scale: all codes 0
+        codes, sg = quantize_static(x16, fmt, s16)
+        g = o.INT4_GROUP if fmt == o.INT4_G32 else 64
+        assert sg.shape == (400, 64 // g) and np.all(sg.view(np.uint16) == s16.view(np.uint16)[:, None])
+        s = s16.astype(np.float32)[:, None]
+        y = (x16.astype(np.float32) / np.where(s == 0, 1, s)).astype(np.float64)
+        if fmt in o.FP8_FORMATS:
+            expect = o.fp8_encode(y.astype(np.float32), fmt)
+            top = o.E4M3FN_MAX_CODE if fmt == o.FP8_E4M3FN else o.E5M2_MAX_CODE
+            big = np.abs(y) > q
+            assert np.all((expect[big] & 0x7F) == top)
+        else:
+            levels = np.arange(-int(q), int(q) + 1)
+            d = np.abs(y[..., None] - levels)
+            best = d.min(axis=-1, keepdims=True)
+            cand = d == best
+            even = np.where(cand & (levels % 2 == 0), levels, 999).min(axis=-1)
+            anyl = np.where(cand, levels, 999).min(axis=-1)
+            expect = np.where(cand.sum(axis=-1) > 1, even, anyl)
+        expect = np.asarray(expect).copy()
+        expect[1] = 0
+        got = np.asarray(codes)
+        if fmt in o.FP8_FORMATS:
+            assert np.array_equal(got.astype(np.uint8), expect.astype(np.uint8)), fmt
+        else:
+            assert np.array_equal(got.astype(np.int64), expect.astype(np.int64)), fmt
+            assert np.abs(got).max() == q  # saturation reached
+
+
+def test_static_reduces_to_dynamic():
+    check_static_reduces_to_dynamic()
+
+
+def test_static_saturation_bruteforce():
+    check_static_saturation_bruteforce()
+
+
+def test_static_write_layout():
+    # write_static stores each head's scale in every written row's slot and
+    # leaves skipped slots alone; reading it back uses the ordinary path.
+    rng = np.random.default_rng(41)
+    H, D, bs = 2, 64, 16
+    k16 = (rng.standard_normal((40, H, D)) * 2).astype(np.float16)
+    v16 = (rng.standard_normal((40, H, D))).astype(np.float16)
+    slots = rng.permutation(4 * bs)[:40].astype(np.int64)
+    slots[5] = -1
+    ks = np.array([0.02, 0.05], np.float16)
+    vs = np.array([0.5, 0.01], np.float16)
+    c = o.OracleCache(4, bs, H, D, o.INT8, o.INT4_G32)
+    o.write_static(c, k16, v16, slots, ks, vs)
+    blk, off = slots // bs, slots % bs
+    m = slots >= 0
+    assert np.all(c.k_scales[blk[m], off[m], :, 0].view(np.uint16) == ks.view(np.uint16))
+    assert np.all(c.v_scales[blk[m], off[m]].view(np.uint16) == vs.view(np.uint16)[:, None])
+    codes, _ = o.quantize_sym_static(k16[m], o.INT8, np.broadcast_to(ks, (m.sum(), H)).astype(np.float16))
+    assert np.array_equal(c.k_codes[blk[m], off[m]].view(np.int8), codes)
+    skipped = np.setdiff1d(np.arange(4 * bs), slots[m])
+    assert np.all(c.k_codes[skipped // bs, skipped % bs] == 0)
