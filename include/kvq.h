@@ -101,7 +101,8 @@ typedef enum kvq_dtype {
  *                      of its not-yet-quantized page at offset r.
  * Token slot s (= block * bs + offset) of a page lives at [s / bs, s % bs].
  * Shape rules: head_dim in {64, 128, 256}; INT4_KIVI only for keys, with
- * block_size 32 and max_seqs > 0; values use INT8, FP8_E4M3FN or INT4_G32. */
+ * block_size 32 and max_seqs > 0; values use INT8, FP8_E4M3FN, FP8_E5M2 or
+ * INT4_G32. */
 typedef struct kvq_cache {
   int32_t num_blocks;
   int32_t block_size;
@@ -134,6 +135,23 @@ typedef struct kvq_cache {
 int kvq_write(const kvq_cache* cache, const void* k, const void* v,
               const int64_t* slot_mapping, const int32_t* seq_idx,
               int64_t num_tokens, void* stream);
+
+/* Quantize-on-write with calibrated scales ([P3] "Calibrate Scaling
+ * Factors": static per-head scales computed before deployment; [P4] static
+ * calibration): like kvq_write, but row (token, head h) is quantized with
+ * the given scale instead of max|x| / q_max.
+ *   k_scale, v_scale  fp16 (n_kv_heads) device arrays, caller-owned, read
+ *                     only; a per-tensor scale is the same value H times.
+ *                     Each scale must be positive and finite, or 0 (codes 0).
+ * Quotients x / s beyond +-q_max saturate at +-q_max (the largest code of
+ * the format).  Every written row stores its head's scale in its ordinary
+ * scale slot (each group slot for INT4_G32), so kvq_decode_attn reads the
+ * cache unchanged.  Symmetric formats only: KVQ_INT4_KIVI keys return
+ * KVQ_ERR_UNSUPPORTED; NULL k_scale or v_scale returns KVQ_ERR_INVALID_ARG.
+ * Other arguments, errors and asynchrony as for kvq_write. */
+int kvq_write_static(const kvq_cache* cache, const void* k, const void* v,
+                     const int64_t* slot_mapping, int64_t num_tokens,
+                     const void* k_scale, const void* v_scale, void* stream);
 
 /* Bytes of device workspace kvq_decode_attn needs for these sizes and this
  * split_tokens (see below): the work partition and the partial softmax

@@ -5,4 +5,4 @@ paged cache and runs dequantizing paged decode attention; `binding` exposes
 its C ABI to torch tensors and `workloads` draws seeded synthetic inputs.
 """
 from .binding import (DTYPES, KvqError, PagedKVCache, decode_attn, decode_workspace_bytes, lib,  # noqa: F401
-                      status_string, write)
+                      status_string, write, write_static)

@@ -23,7 +23,7 @@ DTYPES = {"int8": 1, "fp8_e4m3fn": 2, "int4_g32": 3, "int4_kivi": 4, "fp8_e5m2":
 
 # Functions declared in include/kvq.h (the symbol test checks this list
 # against the header).
-EXPORTS = ("kvq_write", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_status_string")
+EXPORTS = ("kvq_write", "kvq_write_static", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_status_string")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         cp = ctypes.POINTER(KvqCacheStruct)
         L.kvq_write.argtypes = [cp, vp, vp, vp, vp, i64, vp]
         L.kvq_write.restype = ctypes.c_int
+        L.kvq_write_static.argtypes = [cp, vp, vp, vp, i64, vp, vp, vp]
+        L.kvq_write_static.restype = ctypes.c_int
         L.kvq_decode_workspace_bytes.argtypes = [cp, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.kvq_decode_workspace_bytes.restype = ctypes.c_int
         L.kvq_decode_attn.argtypes = [cp, vp, vp, i32, vp, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
@@ -153,6 +155,27 @@ def write(cache: PagedKVCache, k, v, slot_mapping, seq_idx=None, stream=None):
     rc = lib().kvq_write(ctypes.byref(c), _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(seq_idx), T, _stream(stream))
     if rc != KVQ_OK:
         raise KvqError(rc, "kvq_write")
+
+
+def write_static(cache: PagedKVCache, k, v, slot_mapping, k_scale, v_scale, stream=None):
+    """kvq_write_static: quantize fp16 k, v (T, H, D) with calibrated fp16
+    scales k_scale, v_scale (H,) per KV head."""
+    dev = cache.device
+    _check(k, torch.float16, "k", dev)
+    _check(v, torch.float16, "v", dev)
+    _check(slot_mapping, torch.int64, "slot_mapping", dev)
+    _check(k_scale, torch.float16, "k_scale", dev)
+    _check(v_scale, torch.float16, "v_scale", dev)
+    T = slot_mapping.numel()
+    if k.shape != (T, cache.n_kv_heads, cache.head_dim) or v.shape != k.shape:
+        raise ValueError(f"k/v must be ({T}, {cache.n_kv_heads}, {cache.head_dim})")
+    if k_scale.shape != (cache.n_kv_heads,) or v_scale.shape != (cache.n_kv_heads,):
+        raise ValueError(f"k_scale/v_scale must be ({cache.n_kv_heads},)")
+    c = cache.struct()
+    rc = lib().kvq_write_static(ctypes.byref(c), _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_scale),
+                                _ptr(v_scale), _stream(stream))
+    if rc != KVQ_OK:
+        raise KvqError(rc, "kvq_write_static")
 
 
 def decode_workspace_bytes(cache: PagedKVCache, batch, n_q_heads, max_blocks_per_seq, split_tokens=0) -> int:

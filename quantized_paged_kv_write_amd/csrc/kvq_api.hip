@@ -58,11 +58,17 @@ const char* kvq_status_string(int status) {
   return "unknown kvq status";
 }
 
-int kvq_write(const kvq_cache* cache, const void* k, const void* v, const int64_t* slot_mapping,
-              const int32_t* seq_idx, int64_t num_tokens, void* stream) {
+namespace {
+
+// kvq_write and kvq_write_static: k_static / v_static are NULL for the
+// dynamic per-token scale.
+int write_impl(const kvq_cache* cache, const void* k, const void* v, const int64_t* slot_mapping,
+               const int32_t* seq_idx, int64_t num_tokens, const void* k_static, const void* v_static,
+               void* stream) {
   int rc = check_cache(cache);
   if (rc != KVQ_OK) return rc;
   if (cache->k_dtype == KVQ_INT4_G32) return KVQ_ERR_UNSUPPORTED;  // INT4 keys: KIVI only
+  if (k_static && cache->k_dtype == KVQ_INT4_KIVI) return KVQ_ERR_UNSUPPORTED;  // KIVI keys are dynamic
   if (num_tokens < 0) return KVQ_ERR_INVALID_ARG;
   if (num_tokens == 0) return KVQ_OK;
   if (!k || !v || !slot_mapping) return KVQ_ERR_INVALID_ARG;
@@ -71,6 +77,8 @@ int kvq_write(const kvq_cache* cache, const void* k, const void* v, const int64_
   rc = device_present();
   if (rc != KVQ_OK) return rc;
   WriteArgs a{};
+  a.k_static = static_cast<const uint16_t*>(k_static);
+  a.v_static = static_cast<const uint16_t*>(v_static);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.slots = slot_mapping;
@@ -92,6 +100,19 @@ int kvq_write(const kvq_cache* cache, const void* k, const void* v, const int64_
   // per 32 tokens otherwise
   a.seal_chunk = num_tokens <= 2048 ? 1 : 32;
   return launch_write(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+int kvq_write(const kvq_cache* cache, const void* k, const void* v, const int64_t* slot_mapping,
+              const int32_t* seq_idx, int64_t num_tokens, void* stream) {
+  return write_impl(cache, k, v, slot_mapping, seq_idx, num_tokens, nullptr, nullptr, stream);
+}
+
+int kvq_write_static(const kvq_cache* cache, const void* k, const void* v, const int64_t* slot_mapping,
+                     int64_t num_tokens, const void* k_scale, const void* v_scale, void* stream) {
+  if (!k_scale || !v_scale) return KVQ_ERR_INVALID_ARG;
+  return write_impl(cache, k, v, slot_mapping, nullptr, num_tokens, k_scale, v_scale, stream);
 }
 
 int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t n_q_heads,

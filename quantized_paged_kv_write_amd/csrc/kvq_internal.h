@@ -47,6 +47,10 @@ struct WriteArgs {
   uint16_t* v_tail;
   int32_t max_seqs;
   int32_t seal_chunk;  // KIVI: call tokens per seal wave (32, or 1 for small calls)
+  // Calibrated scales, fp16 per KV head, used instead of max|x| / q_max
+  // (kvq_write_static); NULL for the dynamic per-token scale.
+  const uint16_t* k_static;
+  const uint16_t* v_static;
 };
 
 struct DecodeArgs {

@@ -92,9 +92,12 @@ __device__ __forceinline__ u32x2 encode8(const float (&y)[8]) {
   return out;
 }
 
+// stat: calibrated fp16 scale per KV head (uniform over the launch), or NULL
+// for the per-token max|x| / q_max.
 template <int FMT, int D, int ITER, bool TAIL>
 __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* __restrict__ src,
-                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                           const uint16_t* __restrict__ stat) {
   using S = WShape<FMT, D>;
   const int lir = threadIdx.x % S::LPR;
   const uint32_t nrows = (uint32_t)(a.T * a.H);
@@ -147,14 +150,19 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
     const bool valid = s >= 0 && s < a.capacity;
     float x[8];
     unpack8(uint4{xin[i].x, xin[i].y, xin[i].z, xin[i].w}, x);
-    float am = 0.0f;
+    const uint32_t h = r - tok[i] * (uint32_t)a.H;
+    uint32_t s16;
+    if (stat) {
+      s16 = stat[h];  // calibrated: quotients beyond q_max saturate in encode8
+    } else {
+      float am = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
-    am = group_max<S::LPG>(am);
-    // Scale: fp32 quotient, rounded once more to fp16 for storage; the codes
-    // divide by the stored value.
-    const float s32 = exact_div(am, qmax<FMT>(), inv_qmax<FMT>());
-    const uint32_t s16 = f2h_bits(s32);
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+      am = group_max<S::LPG>(am);
+      // Scale: fp32 quotient, rounded once more to fp16 for storage; the
+      // codes divide by the stored value.
+      s16 = f2h_bits(exact_div(am, qmax<FMT>(), inv_qmax<FMT>()));
+    }
     const float sc = h2f(s16);
     u32x2 enc = {0u, 0u};
     if (sc != 0.0f) {
@@ -165,7 +173,6 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
       enc = encode8<FMT>(y);
     }
     if (valid) {
-      const uint32_t h = r - tok[i] * (uint32_t)a.H;
       const size_t orow = (size_t)s * a.H + h;
       if constexpr (FMT == F_INT4) {
         reinterpret_cast<uint32_t*>(codes + orow * S::CB)[lir] = enc.x;
@@ -196,9 +203,9 @@ template <int FK, int FV, int D, int ITER>
 __global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0) {
   const int tensor = (int)blockIdx.y + tensor0;
   if (tensor == 0) {
-    if constexpr (FK != F_KIVI) write_rows<FK, D, ITER, false>(a, a.k, a.k_codes, a.k_scales);
+    if constexpr (FK != F_KIVI) write_rows<FK, D, ITER, false>(a, a.k, a.k_codes, a.k_scales, a.k_static);
   } else {
-    write_rows<FV, D, ITER, FK == F_KIVI>(a, a.v, a.v_codes, a.v_scales);
+    write_rows<FV, D, ITER, FK == F_KIVI>(a, a.v, a.v_codes, a.v_scales, a.v_static);
   }
 }
 

@@ -76,6 +76,25 @@ def test_write_argument_errors():
     assert L.kvq_write(ctypes.byref(_cache()), None, FAKE, FAKE, None, 4, None) == INVALID
     kc = _cache(k_dtype=4, block_size=32, max_seqs=2, k_zeros=FAKE, k_tail=FAKE, v_tail=FAKE)
     assert _write(kc, seq=None) == INVALID  # KIVI needs seq_idx
+    assert _write(_cache(k_dtype=6)) == INVALID
+    assert _write(_cache(k_dtype=5, v_dtype=5), T=0) == OK  # FP8 E5M2 keys and values
+
+
+def _write_static(c, T=4, ks=FAKE, vs=FAKE):
+    return kvq.lib().kvq_write_static(ctypes.byref(c), FAKE, FAKE, FAKE, T, ks, vs, None)
+
+
+def test_write_static_argument_errors():
+    L = kvq.lib()
+    assert L.kvq_write_static(None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == INVALID
+    assert _write_static(_cache(), ks=None) == INVALID
+    assert _write_static(_cache(), vs=None) == INVALID
+    kc = _cache(k_dtype=4, block_size=32, max_seqs=2, k_zeros=FAKE, k_tail=FAKE, v_tail=FAKE)
+    assert _write_static(kc) == UNSUPPORTED  # KIVI keys take no calibrated scale
+    assert _write_static(_cache(k_dtype=3)) == UNSUPPORTED
+    assert _write_static(_cache(v_dtype=9)) == INVALID
+    assert _write_static(_cache(), T=-1) == INVALID
+    assert _write_static(_cache(k_dtype=2, v_dtype=3), T=0) == OK  # no-op
 
 
 def test_workspace_query():

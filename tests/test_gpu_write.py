@@ -217,3 +217,34 @@ def test_write_full_size_sampled(name):
                 assert np.array_equal(cache.k_codes[pb, :, h].cpu().numpy(), o.pack_int4(c))
                 assert np.array_equal(cache.k_scales[pb, h].cpu().numpy().view(np.uint16), s16.view(np.uint16))
                 assert np.array_equal(cache.k_zeros[pb, h].cpu().numpy().view(np.uint16), z16.view(np.uint16))
+
+
+@pytest.mark.parametrize("kf,vf", [("int8", "int8"), ("fp8_e4m3fn", "fp8_e4m3fn"), ("fp8_e5m2", "int4_g32"),
+                                   ("int8", "fp8_e5m2")])
+@pytest.mark.parametrize("D", [64, 128])
+def test_write_static_scales(kf, vf, D):
+    """kvq_write_static: calibrated per-head scales at half the median
+    dynamic scale (about half the rows saturate), one key head with scale 0;
+    codes and stored scales bit-exact, and decode reads the cache as usual."""
+    import quantized_paged_kv_write_amd as kvq
+    from kvq_testlib import decode_both, decode_error
+    H, bs, ctx = 4, 16, [1, 31, 100]
+    inp = _small(kf, vf, D, bs, ctx, H=H, G=2, seed=D + 7)
+    k16, v16 = to_np16(inp.k), to_np16(inp.v)
+
+    def scales(x16, fmt, zero_head=None):
+        amax = np.abs(x16.astype(np.float32)).max(axis=-1)  # (T, H)
+        s = (np.median(amax, axis=0) / o.QMAX[fmt] * 0.5).astype(np.float16)
+        if zero_head is not None:
+            s[zero_head] = 0
+        return s
+
+    ks, vs = scales(k16, kf, zero_head=1), scales(v16, vf)
+    dev, orc = new_caches(inp.num_blocks, bs, H, D, kf, vf, len(ctx), DEV, seed=D + 8)
+    kvq.write_static(dev, inp.k.to(DEV), inp.v.to(DEV), inp.slot_mapping.to(DEV), torch.from_numpy(ks).to(DEV),
+                     torch.from_numpy(vs).to(DEV))
+    o.write_static(orc, k16, v16, inp.slot_mapping.numpy(), ks, vs)
+    torch.cuda.synchronize()
+    assert compare_buffers(dev, orc) == {}
+    got, ref = decode_both(inp, dev, orc, DEV)
+    assert decode_error(got, ref)[0] <= 2e-3
