@@ -248,3 +248,30 @@ def test_write_static_scales(kf, vf, D):
     assert compare_buffers(dev, orc) == {}
     got, ref = decode_both(inp, dev, orc, DEV)
     assert decode_error(got, ref)[0] <= 2e-3
+
+
+@pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "fp8_e5m2"), ("int8", "int4_g32")])
+def test_write_static_every_fp16_pattern(kf, vf):
+    """With a calibrated scale of 1 every quotient is the fp16 input itself,
+    so writing all finite fp16 bit patterns checks the hardware encoders
+    (v_cvt_pk_fp8_f32, v_cvt_pk_bf8_f32, the integer rounding and clip)
+    against the oracle over their whole fp16 domain, signed zeros and
+    saturation included."""
+    import quantized_paged_kv_write_amd as kvq
+    H, D, bs = 2, 128, 16
+    h = np.arange(0x10000, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    h = h[np.isfinite(h)]
+    n = -(-h.size // (H * D)) * H * D
+    vals = np.concatenate([h, np.zeros(n - h.size, np.float16)])
+    T = n // (H * D)
+    k = vals.reshape(T, H, D)
+    v = k[::-1].copy()
+    nb = -(-T // bs)
+    slots = np.arange(T, dtype=np.int64)
+    ones = np.ones(H, np.float16)
+    dev, orc = new_caches(nb, bs, H, D, kf, vf, 1, DEV, seed=12)
+    kvq.write_static(dev, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV), torch.from_numpy(slots).to(DEV),
+                     torch.from_numpy(ones).to(DEV), torch.from_numpy(ones).to(DEV))
+    o.write_static(orc, k, v, slots, ones, ones)
+    torch.cuda.synchronize()
+    assert compare_buffers(dev, orc) == {}
