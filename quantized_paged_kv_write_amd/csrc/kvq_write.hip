@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0
   }
 }
 
-// KIVI key pages.  Block (chunk of C call tokens, head h), one wave; C = 32
+// KIVI key pages.  Wave (chunk of C call tokens, head h); C = 32
 // for large calls (a chunk then holds about one page end) and 1 for small
 // ones (a decode step may complete a page in every sequence at once, and
 // each page gets its own wave).  Every token of the chunk that lands on the
@@ -223,21 +223,24 @@ __global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0
 // registers.  The rows are loaded from the call positions while the check
 // that they hold the page's tokens is in flight; rows that fail it are
 // reloaded from the tail.
+//
+// A workgroup holds NW = blockDim.x / 64 waves: heads c NW .. c NW + NW - 1
+// of one chunk, so the waves that read the neighbouring head segments of the
+// same token rows (and write neighbouring code rows) run on one compute
+// unit.  They never synchronize.
 template <int D>
-__global__ __launch_bounds__(64) void kivi_seal_kernel(WriteArgs a) {
+__global__ __launch_bounds__(512) void kivi_seal_kernel(WriteArgs a) {
   constexpr int PPL = D >= 256 ? D / 128 : 1;  // channel pairs per lane
   constexpr int LPR = D / 2 / PPL;             // lanes per row
   constexpr int RG = 64 / LPR;                 // row groups
   constexpr int RPL = 32 / RG;                 // rows per lane
-  // Workgroups are dealt to the 8 XCDs round robin in dispatch order (x
-  // fastest): workgroup (x, y) runs on XCD x % 8.  The H waves of one chunk
-  // (whose code rows share cache lines) are workgroups (8 h + c, y) of
-  // chunk 8 y + c: same XCD, same L2.
-  const int h = (int)(blockIdx.x >> 3);
-  const int64_t chunk = (int64_t)blockIdx.y * 8 + (blockIdx.x & 7);
+  const int nw = (int)(blockDim.x >> 6);
+  const int wgs_per_chunk = a.H / nw;
+  const int h = (int)(blockIdx.x % (uint32_t)wgs_per_chunk) * nw + (int)(threadIdx.x >> 6);
+  const int64_t chunk = (int64_t)(blockIdx.x / (uint32_t)wgs_per_chunk);
   const int C = a.seal_chunk;
   const int64_t t0 = chunk * C;
-  const int lane = (int)threadIdx.x;
+  const int lane = (int)threadIdx.x & 63;
   // slot and sequence of the chunk's token `lane` (lanes < C)
   int64_t my_slot = -1;
   int32_t my_seq = -1;
@@ -370,8 +373,12 @@ template <int FK, int FV, int D>
 hipError_t launch_all(const WriteArgs& a, hipStream_t s) {
   if constexpr (FK == F_KIVI) {
     const int64_t chunks = (a.T + a.seal_chunk - 1) / a.seal_chunk;
-    const int64_t groups = (chunks + 7) / 8;  // chunks padded to a multiple of 8 (extra waves find no token)
-    hipLaunchKernelGGL((kivi_seal_kernel<D>), dim3((unsigned)(8 * a.H), (unsigned)groups), dim3(64), 0, s, a);
+    // waves per workgroup: the largest divisor of H up to 8 (heads of one chunk)
+    int nw = a.H < 8 ? a.H : 8;
+    while (a.H % nw) --nw;
+    const int64_t wgs = chunks * (a.H / nw);
+    if (wgs >= (1ll << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((kivi_seal_kernel<D>), dim3((unsigned)wgs), dim3(64 * nw), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
