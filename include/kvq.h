@@ -9,7 +9,8 @@
  *   [P1] "Use Less Memory: Quantization and Offloading", section 2.1
  *        (symmetric quantization: s = max|x| / q_max, x_q = clip(round(x/s),
  *        -q_max, q_max), x_hat = x_q * s; q_max 127 for INT8, 7 for INT4),
- *        section 2.2 (per-token / per-head granularity), section 2.3 (FP8).
+ *        section 2.2 (per-token / per-head granularity), section 2.3 (FP8
+ *        E4M3 and E5M2 layouts and ranges).
  *   [P2] "12 KV Cache Quantization", section 5: "Where the scales live"
  *        (k_cache (num_blocks, block_size, n_kv_heads, head_dim) in
  *        FP8/INT8/INT4, k_scale (num_blocks, block_size, n_kv_heads) in FP16;
@@ -17,9 +18,10 @@
  *        V" (softmax(q.k^T/sqrt(d)), sum_i p_i v_i; per-channel K, per-token V),
  *        "The kernel side" (the attention kernel dequantizes while reading).
  *   [P3] "Quantized KV caches in production: FP8 vs INT8 vs INT4", Numerical
- *        Formats (E4M3 1-4-3 layout; KIVI per-channel keys / per-token values)
- *        and Kernel Backends (dequantization on load; paged block allocator
- *        keeping scale metadata beside the page tables).
+ *        Formats (E4M3 1-4-3 and E5M2 1-5-2 layouts; KIVI per-channel keys /
+ *        per-token values), Kernel Backends (dequantization on load; paged
+ *        block allocator keeping scale metadata beside the page tables) and
+ *        Implementation Best Practices (calibrated scaling factors).
  *   [P4] "KV Cache Quantization" glossary: asymmetric quantization (min and
  *        max onto the full integer range), PagedAttention, GQA.
  *
@@ -136,9 +138,9 @@ int kvq_write(const kvq_cache* cache, const void* k, const void* v,
               const int64_t* slot_mapping, const int32_t* seq_idx,
               int64_t num_tokens, void* stream);
 
-/* Quantize-on-write with calibrated scales ([P3] "Calibrate Scaling
- * Factors": static per-head scales computed before deployment; [P4] static
- * calibration): like kvq_write, but row (token, head h) is quantized with
+/* Quantize-on-write with calibrated scales ([P3] Implementation Best
+ * Practices: static per-head scaling factors computed before deployment;
+ * [P4] static calibration): like kvq_write, but row (token, head h) is quantized with
  * the given scale instead of max|x| / q_max.
  *   k_scale, v_scale  fp16 (n_kv_heads) device arrays, caller-owned, read
  *                     only; a per-tensor scale is the same value H times.

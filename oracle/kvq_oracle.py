@@ -238,8 +238,8 @@ def _codes_for_scale(x, s16, fmt):
 def quantize_sym_static(x16: np.ndarray, fmt: str, s16: np.ndarray):
     """Quantize fp16 rows (..., D) with given (calibrated) fp16 scales s16 of
     shape (...,), one per row, instead of max|x| / q_max: the fixed scaling
-    factors computed ahead of deployment of [P3] 'Calibrate Scaling Factors'
-    and [P4] (static calibration).  Quotients beyond +-q_max saturate.  For
+    factors computed ahead of deployment of [P3] Implementation Best Practices
+    (calibrated scaling factors) and [P4] (static calibration).  Quotients beyond +-q_max saturate.  For
     INT4 group-32 rows the row's scale serves every group.  Returns (codes,
     scales) like quantize_sym, the scales being s16 repeated per group."""
     assert x16.dtype == np.float16 and s16.dtype == np.float16
@@ -426,8 +426,8 @@ def write(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, se
 
 def write_static(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, k_scale16, v_scale16):
     """Quantize-on-write with calibrated per-KV-head fp16 scales (H,) for K
-    and V instead of the per-token amax ([P3] 'Calibrate Scaling Factors';
-    [P4] static calibration).  Symmetric formats only; every written row
+    and V instead of the per-token amax ([P3] Implementation Best Practices,
+    calibrated scaling factors; [P4] static calibration).  Symmetric formats only; every written row
     stores its head's scale in its scale slot, so reading is unchanged."""
     assert cache.k_fmt in SYM_FORMATS and cache.k_fmt != INT4_G32 and cache.v_fmt in SYM_FORMATS
     slots = np.asarray(slot_mapping, dtype=np.int64)
