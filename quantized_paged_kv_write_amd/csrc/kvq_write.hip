@@ -358,10 +358,16 @@ __global__ __launch_bounds__(512) void kivi_seal_kernel(WriteArgs a) {
 
 namespace {
 
-constexpr int kIter = 4;
+// Rows per lane of write_sym_kernel.  Measured in one process (prefill
+// writes of the large workloads): one row per lane, i.e. more and shorter
+// workgroups, 5.45 -> 5.88 TB/s for the symmetric formats against 4 rows
+// per lane; the KIVI value pass (with its tail lookups) is fastest at 2.
+template <int FK>
+constexpr int rows_per_lane() { return FK == F_KIVI ? 2 : 1; }
 
 template <int FK, int FV, int D>
 hipError_t launch_sym(const WriteArgs& a, hipStream_t s) {
+  constexpr int kIter = rows_per_lane<FK>();
   constexpr int RPP = 256 / (D / 8);
   const int64_t rows = a.T * a.H;
   const int64_t blocks = (rows + RPP * kIter - 1) / (RPP * kIter);
