@@ -123,6 +123,14 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
     const uint32_t r = row0 + i * S::RPP;
     if (r < nrows) xin[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)r * D) + lir);
   }
+  // calibrated scales: the row's head's scale, loaded beside the rows
+  uint32_t sst[ITER];
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const uint32_t r = row0 + i * S::RPP;
+    sst[i] = 0;
+    if (stat && r < nrows) sst[i] = stat[r - tok[i] * (uint32_t)a.H];
+  }
   // KIVI keys: whether the row's page is completed within this call (its
   // last row is at the matching call position).  The lookups are issued
   // while the rows are in flight and compared only when the row is stored.
@@ -153,7 +161,7 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
     const uint32_t h = r - tok[i] * (uint32_t)a.H;
     uint32_t s16;
     if (stat) {
-      s16 = stat[h];  // calibrated: quotients beyond q_max saturate in encode8
+      s16 = sst[i];  // calibrated: quotients beyond q_max saturate in encode8
     } else {
       float am = 0.0f;
 #pragma unroll
