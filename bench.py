@@ -14,7 +14,9 @@ value = decode KV-read bytes per step / step time (GB/s); the roofline entry
 is for the decode kernels (split-K attention + split merge), timed with HIP
 events on the stream they run on.  Bytes are algorithmic: what the method has
 to move (codes, scale metadata, block-table entries, q and out; for the write
-the fp16 K/V read, codes and metadata written, slot indices).
+the fp16 K/V read, codes and metadata written, slot indices).  For symmetric
+formats the same prefill is also timed through kvq_write_static with
+calibrated per-head scales (write_static_GBps).
 """
 
 from __future__ import annotations
