@@ -84,14 +84,15 @@ __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, 
 __device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
 // ---- key operands: 8 exact fp16 values of the k-block's 8 channels ----------
-// INT8: the unsigned code u = c + 128 as the fp16 bit pattern u, which is
-// exactly the subnormal u 2^-24 (one v_perm per two codes; the matrix cores
-// keep fp16 subnormal inputs).  The score is then 2^24 raw - 128 sum(q) per
-// query head (qcorr in decode_split_kernel), times the key scale.
+// INT8: (1024 + (c + 128)) - 1152 = c, exactly, in fp16.
 __device__ __forceinline__ void int8_to_h4(uint32_t d, uint32_t& lo, uint32_t& hi) {
   d ^= 0x80808080u;
-  lo = __builtin_amdgcn_perm(0u, d, 0x0C010C00u);  // [u0, 0, u1, 0]
-  hi = __builtin_amdgcn_perm(0u, d, 0x0C030C02u);  // [u2, 0, u3, 0]
+  // v_perm_b32: bytes [c0, 0x64, c1, 0x64] and [c2, 0x64, c3, 0x64]
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, d, 0x04010400u);
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, d, 0x04030402u);
+  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = h2_bits(as_h2(a) - bias);
+  hi = h2_bits(as_h2(b) - bias);
 }
 // FP8 E4M3FN -> fp16, two codes per instruction (exact: every E4M3FN value
 // is an fp16 value; the scale operand 1.0 leaves the values unchanged).
@@ -689,7 +690,6 @@ void decode_split_kernel(DecodeArgs a) {
   // KIVI: q * s of the current page (fp16 hi + lo) and q . z, column n's head
   h8 qhi[FK == F_KIVI ? KS::KB : 1], qlo[FK == F_KIVI ? KS::KB : 1];
   float qz = 0.f, kmul = 0.f;  // score = raw kmul + qz
-  float qcorr = 0.f;            // INT8 keys: 128 sum(q) of column n's query head
 
   // Value transpose reads: lane (j, i) points at row T_j[i / 2] of the value
   // tile, byte 8 (i % 2) of the chunk, where T_j[e] = 16 (e / 4) + 4 j + e % 4
@@ -804,14 +804,6 @@ void decode_split_kernel(DecodeArgs a) {
           const uint16_t bits = qrow[key_channel<FK, D>(j, kb, e)];
           qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < NC ? bits : 0));
         }
-      }
-      if constexpr (FK == F_INT8) {
-        float qs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KS::KB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qs += (float)qop[kb][e];
-        qcorr = 128.f * sum_j(qs);
       }
       piece_start = false;
     }
@@ -959,7 +951,6 @@ void decode_split_kernel(DecodeArgs a) {
         else raw = hn == 0 ? sc[u][0] : hn == 1 ? sc[u][1] : hn == 2 ? sc[u][2] : sc[u][3];
         float v;
         if constexpr (FK == F_KIVI) v = __builtin_fmaf(raw, kmul, qz);
-        else if constexpr (FK == F_INT8) v = __builtin_fmaf(raw, 0x1p24f, -qcorr) * s_fk[tr];
         else v = raw * s_fk[tr];
         // a masked row's key codes may be anything, and a row of another KV
         // head than column n's does not belong to it: select, don't multiply

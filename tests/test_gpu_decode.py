@@ -145,3 +145,17 @@ def test_decode_full_size_sampled(name):
         ref = oracle_head_attention(inp, b, h)
         worst = max(worst, float(np.max(np.abs(got[b, h * G:(h + 1) * G] - ref))))
     assert worst <= ATOL, worst
+
+
+@pytest.mark.parametrize("kf", ["int8", "fp8_e4m3fn", "fp8_e5m2", "int4_kivi"])
+@pytest.mark.parametrize("qmode", ["sharp_positive", "flat"])
+def test_decode_query_scales(kf, qmode):
+    """Queries far from N(0,1): all-positive and 8x larger (a sharp softmax,
+    and for INT8 keys a bias term 128 sum(q) much larger than the score), or
+    100x smaller (a nearly flat softmax over every token)."""
+    inp, dev, orc = _setup(kf, "int8", 128, [300, 1000, 33], seed=17)
+    q = inp.q.float()
+    inp.q = ((q.abs() * 8) if qmode == "sharp_positive" else (q * 0.01)).half()
+    got, ref = decode_both(inp, dev, orc, DEV)
+    err, err16 = decode_error(got, ref)
+    assert err <= ATOL, (err, err16)
