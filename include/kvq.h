@@ -29,13 +29,16 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates, frees or keeps them beyond the call.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *     Work is enqueued on it asynchronously; no entry point synchronizes.
+ *     Work is enqueued on it asynchronously; no entry point synchronizes
+ *     except the diagnostics call kvq_get_device_error.
  *   - Return value: KVQ_OK (0) or a negative kvq_status.  Arguments are
  *     validated on the host before anything is launched; on error nothing is
  *     enqueued.  No C++ exception crosses this interface.
  *   - Device-side ids are bounds-checked by the kernels: a slot outside
  *     [0, num_blocks * block_size) is skipped by kvq_write, and a page whose
  *     block id is outside [0, num_blocks) contributes nothing to attention.
+ *     Such ids (other than the negative slots that mean "skip") are also
+ *     recorded in a per-device error word that kvq_get_device_error reads.
  */
 #ifndef KVQ_H_
 #define KVQ_H_
@@ -56,6 +59,21 @@ typedef enum kvq_status {
   KVQ_ERR_NO_DEVICE = -5,    /* no HIP device visible                       */
   KVQ_ERR_HIP = -6           /* a HIP runtime call or launch failed         */
 } kvq_status;
+
+/* Device-side data errors: bits of the word kvq_get_device_error returns.
+ * The kernels still finish normally; the offending id is handled as stated. */
+typedef enum kvq_device_error {
+  KVQ_DEVERR_SLOT = 1,  /* kvq_write / kvq_write_static: a slot at or past
+                           num_blocks * block_size (the token is skipped)   */
+  KVQ_DEVERR_SEQ = 2,   /* kvq_write, KIVI keys: a seq_idx outside
+                           [0, max_seqs) for a token with a valid slot (its
+                           key is dropped: no tail row, no page completed)  */
+  KVQ_DEVERR_BLOCK = 4, /* kvq_decode_attn: a block id outside
+                           [0, num_blocks) on a page within the context (the
+                           page contributes nothing)                        */
+  KVQ_DEVERR_CTX = 8    /* kvq_decode_attn: a ctx_len below 0 or above
+                           max_blocks_per_seq * block_size (clamped)        */
+} kvq_device_error;
 
 /* Storage formats of a cache tensor.
  * KVQ_INT8       symmetric, one fp16 scale per (token, head), q_max 127
@@ -205,6 +223,16 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q,
 
 /* Static description of a status code (never NULL). */
 const char* kvq_status_string(int status);
+
+/* Diagnostics (the failure-detection side of the boundary): returns the
+ * kvq_device_error bits recorded on the current device since the previous
+ * call (0 if none), and clears them.  The read is ordered after the work
+ * already enqueued on `stream` (NULL = the default stream), and this call
+ * synchronizes that stream: it is meant for tests and debugging, not for the
+ * hot loop.  Kernels on other streams record into the same per-device word;
+ * calls that overlap with them may report their bits here or in the next
+ * call.  Negative kvq_status on failure (KVQ_ERR_NO_DEVICE, KVQ_ERR_HIP). */
+int kvq_get_device_error(void* stream);
 
 #ifdef __cplusplus
 }

@@ -380,8 +380,10 @@ def write(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, se
     """Quantize-on-write of k, v (T, H, D) fp16 into the paged cache.
 
     Token t goes to flat slot slot_mapping[t] = block * block_size + offset;
-    a negative slot means "skip".  Symmetric formats quantize each (token,
-    head) row on its own ([P2] section 5: per-token, per-head scaling).
+    a negative slot means "skip", and so does a slot past the last block
+    (num_blocks * block_size or more: there is no page to hold it).
+    Symmetric formats quantize each (token, head) row on its own ([P2]
+    section 5: per-token, per-head scaling).
 
     KIVI keys: the rows of one page form one 32-token group.  A page is
     quantized when its last row (offset block_size - 1) is written; its other
@@ -390,9 +392,12 @@ def write(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, se
     call are stored, K and V in fp16, in the tail of their sequence
     (seq_idx[t]) at their page offset.  Completion reads the tail as it was
     before this call.  V is quantized per token into its page in every case.
+    A token whose seq_idx names no tail row (outside [0, max_seqs)) keeps its
+    value but its key goes nowhere: it neither completes a page nor enters a
+    tail.
     """
     slots = np.asarray(slot_mapping, dtype=np.int64)
-    valid = np.nonzero(slots >= 0)[0]
+    valid = np.nonzero(slot_in_range(cache, slots))[0]
     bs = cache.bs
     _store_sym(cache.v_codes, cache.v_scales, cache.v_fmt, v16[valid], slots[valid], bs)
     if cache.k_fmt != INT4_KIVI:
@@ -402,6 +407,8 @@ def write(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, se
     seq_idx = np.asarray(seq_idx, dtype=np.int64)
     pages = {}  # (seq, block) -> {offset: token index}
     for t in valid:
+        if not 0 <= seq_idx[t] < cache.max_seqs:
+            continue  # no tail row to keep the key in: the key is dropped
         key = (int(seq_idx[t]), int(slots[t] // bs))
         off = int(slots[t] % bs)
         assert off not in pages.setdefault(key, {}), "a slot written twice in one call"
@@ -424,6 +431,13 @@ def write(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, se
             cache.v_tail[seq, off] = v16[t]
 
 
+def slot_in_range(cache: OracleCache, slots) -> np.ndarray:
+    """Whether each flat slot addresses a row of the cache: 0 <= slot <
+    num_blocks * block_size."""
+    slots = np.asarray(slots, dtype=np.int64)
+    return (slots >= 0) & (slots < cache.nb * cache.bs)
+
+
 def write_static(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, k_scale16, v_scale16):
     """Quantize-on-write with calibrated per-KV-head fp16 scales (H,) for K
     and V instead of the per-token amax ([P3] Implementation Best Practices,
@@ -431,7 +445,7 @@ def write_static(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapp
     stores its head's scale in its scale slot, so reading is unchanged."""
     assert cache.k_fmt in SYM_FORMATS and cache.k_fmt != INT4_G32 and cache.v_fmt in SYM_FORMATS
     slots = np.asarray(slot_mapping, dtype=np.int64)
-    valid = np.nonzero(slots >= 0)[0]
+    valid = np.nonzero(slot_in_range(cache, slots))[0]
     bs = cache.bs
     _store_sym(cache.k_codes, cache.k_scales, cache.k_fmt, k16[valid], slots[valid], bs, k_scale16)
     _store_sym(cache.v_codes, cache.v_scales, cache.v_fmt, v16[valid], slots[valid], bs, v_scale16)
@@ -452,14 +466,31 @@ def _dequant_rows(cache: OracleCache, which: str, blk, off):
     return dequant_sym(codes, scales_buf[blk, off], fmt)
 
 
+def token_live(cache: OracleCache, block_table_row, L: int) -> np.ndarray:
+    """Which of a sequence's first L tokens take part in attention: those on
+    a page whose block id lies in [0, num_blocks).  A page with any other id
+    has no storage behind it and contributes nothing.  For KIVI keys the last
+    L mod 32 tokens live in the sequence's fp16 tail and always take part."""
+    bs = cache.bs
+    t = np.arange(L)
+    blk = np.asarray(block_table_row, dtype=np.int64)[t // bs]
+    live = (blk >= 0) & (blk < cache.nb)
+    if cache.k_fmt == INT4_KIVI:
+        live[(L // bs) * bs:] = True
+    return live
+
+
 def gather_dequant(cache: OracleCache, block_table_row, L: int, seq: int):
     """Dequantized K_hat, V_hat (L, H, D) float64 of one sequence, gathered
     through its block-table row: token t lives at block
     block_table_row[t // block_size], offset t % block_size.  For KIVI keys
-    the last L mod 32 tokens are read from the sequence's fp16 tail."""
+    the last L mod 32 tokens are read from the sequence's fp16 tail.  Tokens
+    on a page whose block id is out of range (see token_live) read block 0 in
+    its place; the caller leaves them out."""
     bs = cache.bs
     t = np.arange(L)
     blk = np.asarray(block_table_row, dtype=np.int64)[t // bs]
+    blk = np.where((blk >= 0) & (blk < cache.nb), blk, 0)
     off = t % bs
     V = _dequant_rows(cache, "v", blk, off)
     if cache.k_fmt != INT4_KIVI:
@@ -499,15 +530,19 @@ def dequantized_sequence(k16: np.ndarray, v16: np.ndarray, k_fmt: str, v_fmt: st
     return K, V
 
 
-def attention_fp64(q, K, V, sm_scale=None):
+def attention_fp64(q, K, V, sm_scale=None, live=None):
     """One decode query per head against L cached tokens, float64:
     o = softmax(q k^T * sm_scale) V  ([P2] section 5 "K is more sensitive than
     V": softmax(q.k^T / sqrt(d)) and sum_i p_i v_i), with grouped-query
     attention: query head hq reads KV head hq // G ([P4] GQA: groups of query
     heads share one key/value head).
-    q: (Hq, D); K, V: (L, H, D).  Returns (Hq, D); zeros when L == 0."""
+    q: (Hq, D); K, V: (L, H, D); live: optional bool (L,), tokens to attend
+    (all by default).  Returns (Hq, D); zeros when no token is attended."""
     q = np.asarray(q, dtype=np.float64)
     Hq, D = q.shape
+    if live is not None:
+        live = np.asarray(live, dtype=bool)
+        K, V = K[live], V[live]
     L, H, _ = K.shape
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
@@ -525,15 +560,19 @@ def attention_fp64(q, K, V, sm_scale=None):
 
 def decode_attn(cache: OracleCache, q, block_table, ctx_lens, sm_scale=None, seqs=None):
     """Decode attention over the quantized paged cache, float64 (B, Hq, D).
-    For KIVI keys, batch row b reads tail row b.  `seqs` restricts the work to
-    a subset of batch rows (others are left zero)."""
+    Sequence b attends to its first ctx_lens[b] tokens, the count taken into
+    [0, pages in its block-table row * block_size]; tokens on pages whose
+    block id is out of range are left out (token_live).  For KIVI keys, batch
+    row b reads tail row b.  `seqs` restricts the work to a subset of batch
+    rows (others are left zero)."""
     q = np.asarray(q)
+    block_table = np.asarray(block_table)
     B = q.shape[0]
     out = np.zeros(q.shape, np.float64)
     for b in (range(B) if seqs is None else seqs):
-        L = int(ctx_lens[b])
+        L = min(max(int(ctx_lens[b]), 0), block_table.shape[1] * cache.bs)
         K, V = gather_dequant(cache, block_table[b], L, b)
-        out[b] = attention_fp64(q[b], K, V, sm_scale)
+        out[b] = attention_fp64(q[b], K, V, sm_scale, live=token_live(cache, block_table[b], L))
     return out
 
 

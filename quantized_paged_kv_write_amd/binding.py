@@ -23,7 +23,10 @@ DTYPES = {"int8": 1, "fp8_e4m3fn": 2, "int4_g32": 3, "int4_kivi": 4, "fp8_e5m2":
 
 # Functions declared in include/kvq.h (the symbol test checks this list
 # against the header).
-EXPORTS = ("kvq_write", "kvq_write_static", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_status_string")
+EXPORTS = ("kvq_write", "kvq_write_static", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_status_string",
+           "kvq_get_device_error")
+# Bits of kvq_get_device_error (kvq_device_error in include/kvq.h).
+DEVERR = {"slot": 1, "seq": 2, "block": 4, "ctx": 8}
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -67,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]
         L.kvq_status_string.restype = ctypes.c_char_p
+        L.kvq_get_device_error.argtypes = [vp]
+        L.kvq_get_device_error.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -178,6 +183,16 @@ def write_static(cache: PagedKVCache, k, v, slot_mapping, k_scale, v_scale, stre
         raise KvqError(rc, "kvq_write_static")
 
 
+def get_device_error(stream=None) -> int:
+    """kvq_get_device_error: the kvq_device_error bits recorded on the current
+    device since the previous call (DEVERR), cleared by the read.  Orders
+    after the work on `stream` and synchronizes it."""
+    rc = lib().kvq_get_device_error(_stream(stream))
+    if rc < 0:
+        raise KvqError(rc, "kvq_get_device_error")
+    return rc
+
+
 def decode_workspace_bytes(cache: PagedKVCache, batch, n_q_heads, max_blocks_per_seq, split_tokens=0) -> int:
     out = ctypes.c_size_t(0)
     c = cache.struct()
@@ -201,9 +216,12 @@ def decode_attn(cache: PagedKVCache, q, block_table, ctx_lens, sm_scale=0.0, spl
     if out is None:
         out = torch.empty_like(q)
     _check(out, torch.float16, "out", dev)
+    if out.shape != q.shape:
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
     need = decode_workspace_bytes(cache, B, Hq, block_table.shape[1], split_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, torch.uint8, "workspace", dev)
     c = cache.struct()
     rc = lib().kvq_decode_attn(ctypes.byref(c), _ptr(q), _ptr(block_table), block_table.shape[1], _ptr(ctx_lens),
                                B, Hq, float(sm_scale), split_tokens, _ptr(out), _ptr(workspace),

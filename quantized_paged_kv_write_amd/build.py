@@ -25,10 +25,14 @@ SOURCES = {
     "kvq_api.hip": [],
     "kvq_write.hip": ["-ffp-contract=off"],
     "kvq_decode.hip": [],
+    "kvq_decode_kint8.hip": [],
+    "kvq_decode_kfp8.hip": [],
+    "kvq_decode_kkivi.hip": [],
+    "kvq_decode_ke5m2.hip": [],
 }
 
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(HERE, "..", "include"),

@@ -1,12 +1,53 @@
 // C-ABI entry points: host-side validation, then launches on the caller's
-// stream.  Nothing here allocates device memory or synchronizes.
+// stream.  Nothing here allocates device memory, and only the diagnostics
+// call synchronizes.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kvq_internal.h"
+
+// Per-device error word (kvq_device_error bits; [0] accumulates, [1] receives
+// the value taken by kvq_get_device_error).  Each device holds its own copy;
+// host code uses the address hipGetSymbolAddress returns on that device.
+__device__ __align__(16) uint32_t kvq_error_word[2];
 
 namespace {
 
 using namespace kvq;
+
+// Device addresses of this library's file-scope device symbols, looked up
+// once per device with that device current.
+constexpr int kMaxDevices = 64;
+struct DeviceSymbols {
+  uint32_t* err = nullptr;
+};
+std::atomic<bool> g_sym_ready[kMaxDevices];
+DeviceSymbols g_sym[kMaxDevices];
+std::mutex g_sym_mutex;
+
+int device_symbols(DeviceSymbols* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KVQ_ERR_NO_DEVICE;
+  if (dev >= kMaxDevices) return KVQ_ERR_UNSUPPORTED;
+  if (!g_sym_ready[dev].load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> lock(g_sym_mutex);
+    if (!g_sym_ready[dev].load(std::memory_order_relaxed)) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(kvq_error_word)) != hipSuccess || !p) return KVQ_ERR_HIP;
+      g_sym[dev].err = static_cast<uint32_t*>(p);
+      g_sym_ready[dev].store(true, std::memory_order_release);
+    }
+  }
+  *out = g_sym[dev];
+  return KVQ_OK;
+}
+
+// w[1] = the accumulated bits, w[0] = 0, in one atomic exchange.
+__global__ void take_errors_kernel(uint32_t* w) {
+  if (threadIdx.x == 0) w[1] = __hip_atomic_exchange(&w[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -76,7 +117,11 @@ int write_impl(const kvq_cache* cache, const void* k, const void* v, const int64
   if (num_tokens * (int64_t)cache->n_kv_heads >= (1ll << 31)) return KVQ_ERR_SHAPE;
   rc = device_present();
   if (rc != KVQ_OK) return rc;
+  DeviceSymbols sym;
+  rc = device_symbols(&sym);
+  if (rc != KVQ_OK) return rc;
   WriteArgs a{};
+  a.err = sym.err;
   a.k_static = static_cast<const uint16_t*>(k_static);
   a.v_static = static_cast<const uint16_t*>(v_static);
   a.k = static_cast<const uint16_t*>(k);
@@ -147,7 +192,11 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_
   if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return KVQ_ERR_WORKSPACE;
   rc = device_present();
   if (rc != KVQ_OK) return rc;
+  DeviceSymbols sym;
+  rc = device_symbols(&sym);
+  if (rc != KVQ_OK) return rc;
   DecodeArgs a{};
+  a.err = sym.err;
   a.q = static_cast<const uint16_t*>(q);
   a.block_table = block_table;
   a.ctx_lens = ctx_lens;
@@ -178,6 +227,21 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_
   a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.plan_bytes);
   a.out = static_cast<uint16_t*>(out);
   return launch_decode(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_get_device_error(void* stream) {
+  int rc = device_present();
+  if (rc != KVQ_OK) return rc;
+  DeviceSymbols sym;
+  rc = device_symbols(&sym);
+  if (rc != KVQ_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(take_errors_kernel, dim3(1), dim3(64), 0, st, sym.err);
+  if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+  uint32_t bits = 0;
+  if (hipMemcpyAsync(&bits, sym.err + 1, sizeof(bits), hipMemcpyDeviceToHost, st) != hipSuccess) return KVQ_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return KVQ_ERR_HIP;
+  return (int)(bits & 0x7FFFFFFFu);
 }
 
 }  // extern "C"

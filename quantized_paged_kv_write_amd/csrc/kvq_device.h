@@ -102,4 +102,12 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Record a device-side data error: the lowest lane of the wave whose `bad`
+// is set ORs `bit` into the error word (one vector atomic per wave at most).
+__device__ __forceinline__ void report_error(uint32_t* err, bool bad, uint32_t bit) {
+  const uint64_t m = __ballot(bad);
+  if (m != 0 && (threadIdx.x & 63u) == (uint32_t)(__ffsll((unsigned long long)m) - 1))
+    __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace kvq

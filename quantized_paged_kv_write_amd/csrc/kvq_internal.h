@@ -5,25 +5,11 @@
 #include <stdint.h>
 
 #include "../../include/kvq.h"
+#include "kvq_fastdiv.h"
 
 namespace kvq {
 
-// Unsigned division by a run-time constant d >= 1 with a precomputed
-// multiplier (round-up method of Granlund and Montgomery, "Division by
-// Invariant Integers using Multiplication", 1994): for n < 2^32,
-// n / d == (umulhi(n, m) + n) >> s with s = ceil(log2 d) and
-// m = floor(2^32 (2^s - d) / d) + 1.
-struct FastDiv {
-  uint32_t d, m, s;
-};
-
-inline FastDiv make_fastdiv(uint32_t d) {
-  uint32_t s = 0;
-  while ((1ull << s) < d) ++s;
-  uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
-  return FastDiv{d, (uint32_t)m, s};
-}
-
+// n / f.d on the device (see kvq_fastdiv.h)
 __device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
   return (uint32_t)(((uint64_t)__umulhi(n, f.m) + n) >> f.s);
 }
@@ -51,6 +37,7 @@ struct WriteArgs {
   // (kvq_write_static); NULL for the dynamic per-token scale.
   const uint16_t* k_static;
   const uint16_t* v_static;
+  uint32_t* err;  // per-device kvq_device_error word
 };
 
 struct DecodeArgs {
@@ -87,6 +74,7 @@ struct DecodeArgs {
   // Records: share i's piece of sequence b -> i + b.
   float* part;
   uint16_t* out;  // fp16 (B, Hq, D)
+  uint32_t* err;  // per-device kvq_device_error word (checked by the merge kernel)
 };
 
 // Workspace layout of one decode call (host side, no device needed).
@@ -107,6 +95,11 @@ int32_t heads_per_wave_log2(const kvq_cache& c, int32_t G);
 // Launchers (return hipError_t of the launch).
 hipError_t launch_write(const kvq_cache& c, const WriteArgs& a, hipStream_t s);
 hipError_t launch_decode(const kvq_cache& c, const DecodeArgs& a, hipStream_t s);
+// Per key format (kvq_decode_k*.hip): fv value format, D head dim.
+hipError_t decode_keys_int8(int fv, int D, const DecodeArgs& a, hipStream_t s);
+hipError_t decode_keys_fp8(int fv, int D, const DecodeArgs& a, hipStream_t s);
+hipError_t decode_keys_kivi(int fv, int D, const DecodeArgs& a, hipStream_t s);
+hipError_t decode_keys_e5m2(int fv, int D, const DecodeArgs& a, hipStream_t s);
 
 
 }  // namespace kvq

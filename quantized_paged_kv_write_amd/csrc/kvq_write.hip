@@ -156,6 +156,7 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
     if (r >= nrows) continue;  // uniform over the lanes of a row
     const int64_t s = slot[i];
     const bool valid = s >= 0 && s < a.capacity;
+    report_error(a.err, s >= a.capacity, KVQ_DEVERR_SLOT);
     float x[8];
     unpack8(uint4{xin[i].x, xin[i].y, xin[i].z, xin[i].w}, x);
     const uint32_t h = r - tok[i] * (uint32_t)a.H;
@@ -197,7 +198,9 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
         const int off = (int)(s % a.bs);
         const int32_t seq = tseq[i];
         const bool sealed = te_[i] < a.T && tseq_e[i] == seq && tslot_e[i] == s + (a.bs - 1 - off);
-        if (!sealed && seq >= 0 && seq < a.max_seqs) {
+        const bool seq_ok = seq >= 0 && seq < a.max_seqs;
+        report_error(a.err, !seq_ok, KVQ_DEVERR_SEQ);
+        if (!sealed && seq_ok) {
           const size_t trow = ((size_t)seq * a.bs + off) * a.H + h;
           reinterpret_cast<u32x4*>(a.v_tail + trow * D)[lir] = xin[i];
           reinterpret_cast<u32x4*>(a.k_tail + trow * D)[lir] =

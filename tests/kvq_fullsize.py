@@ -1,0 +1,62 @@
+"""Oracle side of the full-size parity tests, run in worker processes.
+
+Each piece is one sequence and a slice of its KV heads.  The worker
+quantizes that piece's fp16 keys and values with the oracle (into an oracle
+cache whose pages are the sequence's pages in order), compares every byte of
+those pages with the GPU cache's pages of the same sequence, and compares the
+GPU decode output of the piece's query heads with the oracle's float64
+attention.  Imports only NumPy and the oracle, so it runs in fresh processes
+that never touch the GPU."""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as o
+
+
+def check_piece(p: dict) -> dict:
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        return _check_piece(p)
+
+
+def _check_piece(p: dict) -> dict:
+    kf, vf, bs, D = p["k_fmt"], p["v_fmt"], p["block_size"], p["head_dim"]
+    k16, v16 = p["k16"], p["v16"]  # (L, Hs, D) fp16, positions 0..L-1
+    L, Hs = k16.shape[0], k16.shape[1]
+    npg = -(-L // bs)
+    c = o.OracleCache(max(npg, 1), bs, Hs, D, kf, vf, max_seqs=1)
+    pos = np.arange(L)
+    o.write(c, k16, v16, pos, np.zeros(L, np.int32))  # page j of the sequence is oracle block j
+    mism = {}
+    for name, got in p["pages"].items():
+        ref = getattr(c, name)
+        if name in ("k_tail", "v_tail"):
+            ref = ref[0]
+        else:
+            ref = ref[:npg]
+        a = got.view(np.uint16) if got.dtype == np.float16 else got
+        b = ref.view(np.uint16) if ref.dtype == np.float16 else ref
+        if a.shape != b.shape:
+            mism[name] = f"shape {a.shape} vs {b.shape}"
+        else:
+            n = int(np.count_nonzero(a != b))
+            if n:
+                mism[name] = n
+    res = {"b": p["b"], "h0": p["h0"], "mismatch": mism, "bytes": int(sum(x.nbytes for x in p["pages"].values()))}
+    if p.get("q") is not None:
+        K, V = o.gather_dequant(c, np.arange(npg), L, 0)
+        ref = o.attention_fp64(p["q"].astype(np.float64), K, V)
+        got = p["out"].astype(np.float64)
+        res["err"] = float(np.max(np.abs(got - ref))) if got.size else 0.0
+        res["err16"] = float(np.max(np.abs(got - ref.astype(np.float16).astype(np.float64)))) if got.size else 0.0
+        res["rows"] = int(got.shape[0])
+        if p.get("quality"):
+            # unquantized fp16 keys and values: the quality statistic
+            ref0 = o.attention_fp64(p["q"].astype(np.float64), k16.astype(np.float64), v16.astype(np.float64))
+            res["q_maxabs"] = float(np.max(np.abs(got - ref0)))
+            res["q_l2_num"] = float(np.sum((got - ref0) ** 2))
+            res["q_l2_den"] = float(np.sum(ref0 ** 2))
+    return res

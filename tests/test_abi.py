@@ -147,17 +147,47 @@ def test_valid_call_without_device_reports_no_device():
     assert _write(_cache()) == NO_DEVICE
 
 
-def test_fastdiv_constants_match_integer_division():
+def test_fastdiv_constants_match_integer_division(tmp_path):
     # The write kernel divides row indices by n_kv_heads with the round-up
-    # multiplier method; recompute its constants here and check exhaustively
-    # over the ranges the kernel sees (rows < 2^31).
-    import random
-    for d in list(range(1, 70)) + [96, 128, 255, 1000, 65535]:
-        s = 0
-        while (1 << s) < d:
-            s += 1
-        m = ((1 << 32) * ((1 << s) - d)) // d + 1
-        rnd = random.Random(d)
-        for n in [0, 1, d - 1, d, d + 1, 2 ** 31 - 1, 2 ** 31 - d] + [rnd.randrange(2 ** 31) for _ in range(2000)]:
-            q = ((n * m >> 32) + n) >> s
-            assert q == n // d, (d, n)
+    # multiplier method.  Build the library's own constants (make_fastdiv in
+    # csrc/kvq_fastdiv.h) with the host compiler and check the quotient the
+    # kernel forms from them against integer division, exhaustively near the
+    # multiples of d and on random rows below 2^31.
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    src = tmp_path / "fastdiv_check.cc"
+    src.write_text(r"""
+#include <cstdio>
+#include <random>
+#include "kvq_fastdiv.h"
+int main() {
+  unsigned ds[] = {96, 128, 255, 1000, 65535, 65536, 1u << 20, 2147483647u};
+  std::mt19937 rng(7);
+  long bad = 0, checked = 0;
+  auto check = [&](unsigned d) {
+    const kvq::FastDiv f = kvq::make_fastdiv(d);
+    auto one = [&](unsigned n) { ++checked; if (kvq::fastdiv_host(n, f) != n / d) ++bad; };
+    for (unsigned n = 0; n < 4096; ++n) one(n);
+    for (unsigned k = 1; k < 2000; ++k) {
+      const unsigned long long base = (unsigned long long)k * d;
+      if (base >= (1ull << 31)) break;
+      one((unsigned)base - 1); one((unsigned)base); one((unsigned)base + 1);
+    }
+    one(2147483647u); one(2147483647u - d);
+    for (int i = 0; i < 20000; ++i) one(rng() & 0x7FFFFFFFu);
+  };
+  for (unsigned d = 1; d < 70; ++d) check(d);
+  for (unsigned d : ds) check(d);
+  printf("%ld %ld\n", checked, bad);
+  return bad != 0;
+}
+""")
+    exe = tmp_path / "fastdiv_check"
+    inc = os.path.join(ROOT, "quantized_paged_kv_write_amd", "csrc")
+    subprocess.run([cxx, "-O2", "-std=c++17", "-I", inc, str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    checked, bad = map(int, r.stdout.split())
+    assert r.returncode == 0 and bad == 0 and checked > 1_000_000, r.stdout

@@ -1,0 +1,132 @@
+"""Full-size parity of the large workloads, in the launch configuration the
+benchmark times: a prefill write of every token but the last of each
+sequence (one call), a write of the last token of every sequence (one call),
+then one decode step with the automatic partition.  Every byte of the cache
+(codes, scales, zero points, KIVI tails) is compared with the oracle, and so
+is every (sequence, query head) row of the decode output (within 2e-3).
+
+The oracle runs per sequence and slice of KV heads, in a pool of fresh
+worker processes (NumPy only; they never touch the GPU)."""
+
+import concurrent.futures as cf
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_paged_kv_write_amd as kvq
+from kvq_testlib import ATOL
+from quantized_paged_kv_write_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+WORKERS = max(1, min(8, (os.cpu_count() or 2) - 1))
+
+# name -> (workload, context lengths or None for the workload's own)
+CASES = {
+    "llama3_8b_fp8": ("llama3_8b_fp8", None),
+    "llama3_8b_int8k_int4v": ("llama3_8b_int8k_int4v", None),
+    "llama3_70b_int8": ("llama3_70b_int8", None),
+    "llama3_8b_kivi_int4": ("llama3_8b_kivi_int4", None),
+    # the KIVI shape with fp16 tails of 31, 1 and 15 tokens (and none)
+    "llama3_8b_kivi_int4_tails": ("llama3_8b_kivi_int4", [131072, 131071, 131041, 131055]),
+    "llama3_8b_e5m2": ("llama3_8b_e5m2", None),
+}
+
+
+@pytest.fixture(scope="module")
+def pool():
+    ex = cf.ProcessPoolExecutor(max_workers=WORKERS, mp_context=mp.get_context("spawn"))
+    yield ex
+    ex.shutdown()
+
+
+def _run_workload(name):
+    wname, ctx = CASES[name]
+    w = wl.WORKLOADS[wname]
+    seed = wl.ORDER.index(wname) + 1
+    inp = wl.make_inputs(w, seed, DEV, ctx_lens=ctx)
+    B = w.batch
+    cache = kvq.PagedKVCache(inp.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, w.k_dtype, w.v_dtype,
+                             max_seqs=B, device=DEV)
+    last = torch.tensor([inp.seq_start[b] + inp.ctx_lens[b] - 1 for b in range(B)])
+    mask = torch.ones(inp.k.shape[0], dtype=torch.bool)
+    mask[last] = False
+    pre = torch.nonzero(mask)[:, 0]
+    slots, seqs = inp.slot_mapping, inp.seq_idx
+    kvq.write(cache, inp.k[pre.to(DEV)], inp.v[pre.to(DEV)], slots[pre].to(DEV), seqs[pre].to(DEV))
+    kvq.write(cache, inp.k[last.to(DEV)].contiguous(), inp.v[last.to(DEV)].contiguous(), slots[last].to(DEV),
+              seqs[last].to(DEV))
+    ctx_d = torch.tensor(inp.ctx_lens, dtype=torch.int32, device=DEV)
+    out = kvq.decode_attn(cache, inp.q, inp.block_table.to(DEV), ctx_d)
+    torch.cuda.synchronize()
+    assert kvq.get_device_error() == 0
+    return w, inp, cache, out
+
+
+def _pieces(w, inp, cache, out):
+    """Per (sequence, KV-head slice): the host data a worker needs."""
+    H, D, bs = w.n_kv_heads, w.head_dim, w.block_size
+    G = w.n_q_heads // H
+    bufs = cache.buffers()
+    k_host = inp.k.cpu().numpy()
+    v_host = inp.v.cpu().numpy()
+    q_host = inp.q.cpu().numpy()
+    out_host = out.cpu().numpy()
+    for b in range(w.batch):
+        L = inp.ctx_lens[b]
+        st = inp.seq_start[b]
+        npg = -(-L // bs)
+        blocks = inp.block_table[b, :npg].to(DEV).long()
+        # slices of about 2^17 token-heads each
+        hs = max(1, min(H, (1 << 17) // max(L, 1)))
+        while H % hs:
+            hs -= 1
+        gathered = {}
+        for name, t in bufs.items():
+            if name in ("k_tail", "v_tail"):
+                gathered[name] = t[b].cpu().numpy()
+            else:
+                gathered[name] = t[blocks].cpu().numpy()
+        for h0 in range(0, H, hs):
+            pages = {}
+            for name, a in gathered.items():
+                if (name in ("k_scales", "k_zeros") and w.k_dtype == "int4_kivi") or name in ("k_tail", "v_tail"):
+                    pages[name] = a[:, h0:h0 + hs]  # (pages, H, D) or the tail (bs, H, D)
+                else:
+                    pages[name] = a[:, :, h0:h0 + hs]  # (pages or 32, bs, H, ...)
+            yield {
+                "b": b, "h0": h0, "k_fmt": w.k_dtype, "v_fmt": w.v_dtype, "block_size": bs, "head_dim": D,
+                "k16": k_host[st:st + L, h0:h0 + hs], "v16": v_host[st:st + L, h0:h0 + hs], "pages": pages,
+                "q": q_host[b, h0 * G:(h0 + hs) * G], "out": out_host[b, h0 * G:(h0 + hs) * G],
+            }
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_full_size_whole_cache_and_every_row(name, pool):
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import kvq_fullsize
+    t0 = time.time()
+    w, inp, cache, out = _run_workload(name)
+    print(f"[fullsize] {name}: GPU write + decode done in {time.time() - t0:.1f} s; oracle in {WORKERS} workers",
+          flush=True)
+    futs = [pool.submit(kvq_fullsize.check_piece, p) for p in _pieces(w, inp, cache, out)]
+    del cache
+    bad, worst, worst16, rows, nbytes = [], 0.0, 0.0, 0, 0
+    for f in cf.as_completed(futs):
+        r = f.result()
+        if r["mismatch"]:
+            bad.append((r["b"], r["h0"], r["mismatch"]))
+        worst = max(worst, r["err"])
+        worst16 = max(worst16, r["err16"])
+        rows += r["rows"]
+        nbytes += r["bytes"]
+    print(f"[fullsize] {name}: {nbytes} cache bytes compared, {rows} output rows, max|err| {worst:.3e} "
+          f"(vs fp16-rounded oracle {worst16:.3e}), {time.time() - t0:.1f} s", flush=True)
+    assert not bad, bad[:5]
+    assert rows == w.batch * w.n_q_heads
+    assert worst <= ATOL, (worst, worst16)

@@ -167,3 +167,34 @@ def test_static_without_saturation_fails():
             codes = np.where(s == 0, 0, np.rint(y)).astype(np.int64)
         return codes, sg
     assert _fails(pins.check_static_saturation_bruteforce, wrong)
+
+def _decode_tail_row_0(cache, q, block_table, ctx_lens, sm_scale=None):
+    # Mistake: every batch row reads tail row 0.
+    out = np.zeros(np.asarray(q).shape)
+    for b in range(len(ctx_lens)):
+        L = int(ctx_lens[b])
+        K, V = o.gather_dequant(cache, block_table[b], L, 0)
+        out[b] = o.attention_fp64(q[b], K, V, sm_scale, live=o.token_live(cache, block_table[b], L))
+    return out
+
+
+def _decode_table_row_0(cache, q, block_table, ctx_lens, sm_scale=None):
+    # Mistake: every batch row reads the pages of block-table row 0.
+    out = np.zeros(np.asarray(q).shape)
+    for b in range(len(ctx_lens)):
+        L = int(ctx_lens[b])
+        K, V = o.gather_dequant(cache, block_table[0], L, b)
+        out[b] = o.attention_fp64(q[b], K, V, sm_scale, live=o.token_live(cache, block_table[0], L))
+    return out
+
+
+def _write_ignoring_seq_idx(cache, k16, v16, slot_mapping, seq_idx=None):
+    # Mistake: every token's tail row is row 0.
+    return o.write(cache, k16, v16, slot_mapping, None if seq_idx is None else np.zeros_like(seq_idx))
+
+
+def test_routing_mistakes_fail():
+    assert _fails(pins.check_multi_sequence_routing, o.write, _decode_tail_row_0)
+    assert _fails(pins.check_multi_sequence_routing, o.write, _decode_table_row_0)
+    assert _fails(pins.check_multi_sequence_routing, _write_ignoring_seq_idx, o.decode_attn)
+    pins.check_multi_sequence_routing()

@@ -588,3 +588,139 @@ def test_static_write_layout():
     assert np.array_equal(c.k_codes[blk[m], off[m]].view(np.int8), codes)
     skipped = np.setdiff1d(np.arange(4 * bs), slots[m])
     assert np.all(c.k_codes[skipped // bs, skipped % bs] == 0)
+
+
+# --------------------------------------------------------------------------
+# Several sequences in one cache: routing of tokens to pages and tails, and of
+# batch rows to block-table rows, context lengths and tails
+# --------------------------------------------------------------------------
+
+
+def _three_sequences(kf, vf, ctx, bs, H=2, D=32, seed=40):
+    """fp16 K/V of len(ctx) sequences, a shuffled block table over a pool
+    with spare blocks, and per-token slots and sequence indices."""
+    rng = np.random.default_rng(seed)
+    pages = [-(-L // bs) for L in ctx]
+    nb = sum(pages) + 3
+    perm = rng.permutation(nb)
+    table = np.zeros((len(ctx), max(pages)), np.int64)
+    o_ = 0
+    for b, n in enumerate(pages):
+        table[b, :n] = perm[o_:o_ + n]
+        o_ += n
+    ks = [(rng.standard_normal((L, H, D)) * (1 + b)).astype(np.float16) for b, L in enumerate(ctx)]
+    vs = [rng.standard_normal((L, H, D)).astype(np.float16) for L in ctx]
+    slots = [table[b, np.arange(L) // bs] * bs + np.arange(L) % bs for b, L in enumerate(ctx)]
+    return nb, table, ks, vs, slots
+
+
+def check_multi_sequence_routing(write=o.write, decode=o.decode_attn):
+    # Three sequences written interleaved (a prefill chunk holding part of
+    # every sequence, then one token per sequence per call, as decoding does)
+    # and decoded in one batch must give, row by row, the attention of each
+    # sequence quantized on its own.  KIVI tails of lengths 0, 1 and 31.
+    for kf, vf in ((o.INT4_KIVI, o.INT4_G32), (o.INT8, o.INT4_G32), (o.FP8_E4M3FN, o.INT8)):
+        bs = 32 if kf == o.INT4_KIVI else 16
+        ctx = [64, 33, 95]
+        H, D, Hq = 2, 32, 4
+        nb, table, ks, vs, slots = _three_sequences(kf, vf, ctx, bs, H, D)
+        c = o.OracleCache(nb, bs, H, D, kf, vf, max_seqs=len(ctx))
+        pre = [20, 9, 40]
+        cat = lambda parts: np.concatenate(parts)  # noqa: E731
+        write(c, cat([k[:p] for k, p in zip(ks, pre)]), cat([v[:p] for v, p in zip(vs, pre)]),
+              cat([s[:p] for s, p in zip(slots, pre)]), cat([np.full(p, b, np.int32) for b, p in enumerate(pre)]))
+        for t in range(min(pre), max(ctx)):
+            bb = [b for b in range(len(ctx)) if pre[b] <= t < ctx[b]]
+            if bb:
+                write(c, np.stack([ks[b][t] for b in bb]), np.stack([vs[b][t] for b in bb]),
+                      np.array([slots[b][t] for b in bb]), np.array(bb, np.int32))
+        q = np.random.default_rng(41).standard_normal((len(ctx), Hq, D)).astype(np.float16)
+        got = decode(c, q, table, ctx)
+        for b in range(len(ctx)):
+            K, V = o.dequantized_sequence(ks[b], vs[b], kf, vf)
+            ref = o.attention_fp64(q[b].astype(np.float64), K, V)
+            assert np.max(np.abs(got[b] - ref)) <= 1e-12, (kf, vf, b)
+
+
+def test_multi_sequence_routing():
+    check_multi_sequence_routing()
+
+
+def test_out_of_range_slots_are_skipped():
+    # A slot at or past num_blocks * block_size addresses no row: the write
+    # equals the write of the other tokens alone (and raises nothing).
+    rng = np.random.default_rng(42)
+    k = rng.standard_normal((6, 2, 32)).astype(np.float16)
+    slots = np.array([3, 64, 17, 1000, -2, 63])
+    a = o.OracleCache(4, 16, 2, 32, o.INT8, o.INT4_G32)
+    b = o.OracleCache(4, 16, 2, 32, o.INT8, o.INT4_G32)
+    o.write(a, k, k, slots)
+    keep = np.array([0, 2, 5])
+    o.write(b, k[keep], k[keep], slots[keep])
+    for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
+        assert np.array_equal(getattr(a, name), getattr(b, name))
+    assert np.array_equal(o.slot_in_range(a, slots), [True, False, True, False, False, True])
+
+
+def test_kivi_token_without_tail_row_keeps_only_its_value():
+    # seq_idx outside [0, max_seqs): the value is written, the key goes
+    # nowhere (it can neither wait in a tail nor complete a page).
+    rng = np.random.default_rng(43)
+    k = rng.standard_normal((32, 2, 32)).astype(np.float16)
+    c = o.OracleCache(2, 32, 2, 32, o.INT4_KIVI, o.INT8, max_seqs=1)
+    o.write(c, k, k, np.arange(32) + 32, np.full(32, 1, np.int32))
+    assert not np.any(c.k_codes) and not np.any(c.k_scales) and not np.any(c.k_tail)
+    codes, s = o.quantize_sym(k, o.INT8)
+    assert np.array_equal(c.v_codes[1].view(np.int8), codes) and np.array_equal(c.v_scales[1], s)
+
+
+@pytest.mark.parametrize("kf,vf", [(o.INT8, o.INT8), (o.INT4_KIVI, o.INT4_G32)])
+def test_pages_with_out_of_range_block_ids_contribute_nothing(kf, vf):
+    # Corrupt some block-table entries (negative, or >= num_blocks): decode
+    # equals attention over the tokens of the remaining pages, computed from
+    # the sequence quantized on its own; KIVI tail tokens always count.
+    bs = 32 if kf == o.INT4_KIVI else 16
+    ctx = [150, 97]
+    H, D, Hq = 2, 32, 4
+    nb, table, ks, vs, slots = _three_sequences(kf, vf, ctx, bs, H, D, seed=44)
+    c = o.OracleCache(nb, bs, H, D, kf, vf, max_seqs=len(ctx))
+    o.write(c, np.concatenate(ks), np.concatenate(vs), np.concatenate(slots),
+            np.concatenate([np.full(L, b, np.int32) for b, L in enumerate(ctx)]))
+    bad = table.copy()
+    bad[0, 1] = -1
+    bad[0, 3] = nb
+    bad[1, 0] = nb + 1000
+    q = np.random.default_rng(45).standard_normal((len(ctx), Hq, D)).astype(np.float16)
+    got = o.decode_attn(c, q, bad, ctx)
+    for b, L in enumerate(ctx):
+        K, V = o.dequantized_sequence(ks[b], vs[b], kf, vf)
+        page = np.arange(L) // bs
+        keep = ~np.isin(page, [p for p in range(bad.shape[1]) if not 0 <= bad[b, p] < nb])
+        if kf == o.INT4_KIVI:
+            keep[(L // bs) * bs:] = True
+        ref = o.attention_fp64(q[b].astype(np.float64), K[keep], V[keep])
+        assert np.max(np.abs(got[b] - ref)) <= 1e-12, b
+    # every page of a sequence out of range: nothing attended, zeros (INT8);
+    # for KIVI the tail alone
+    allbad = np.full_like(table, -5)
+    got = o.decode_attn(c, q, allbad, ctx)
+    for b, L in enumerate(ctx):
+        if kf == o.INT4_KIVI:
+            nf = (L // bs) * bs
+            ref = o.attention_fp64(q[b].astype(np.float64), ks[b][nf:].astype(np.float64),
+                                   vs[b][nf:].astype(np.float64))
+            assert np.max(np.abs(got[b] - ref)) <= 1e-12
+        else:
+            assert not np.any(got[b])
+
+
+def test_context_length_is_clamped_to_the_block_table():
+    # ctx_lens beyond the tokens a block-table row addresses read that many;
+    # a negative ctx_len attends to nothing.
+    bs, H, D, L = 16, 2, 32, 64
+    nb, table, ks, vs, slots = _three_sequences(o.INT8, o.INT8, [L], bs, H, D, seed=46)
+    c = o.OracleCache(nb, bs, H, D, o.INT8, o.INT8, max_seqs=1)
+    o.write(c, ks[0], vs[0], slots[0])
+    q = np.random.default_rng(47).standard_normal((1, 4, D)).astype(np.float16)
+    assert np.array_equal(o.decode_attn(c, q, table, [L + 1000]), o.decode_attn(c, q, table, [L]))
+    assert not np.any(o.decode_attn(c, q, table, [-3]))
