@@ -1,8 +1,9 @@
 """Oracle side of the full-size parity tests, run in worker processes.
 
 Each piece is one sequence and a slice of its KV heads.  The worker
-quantizes that piece's fp16 keys and values with the oracle (into an oracle
-cache whose pages are the sequence's pages in order), compares every byte of
+quantizes that piece's fp16 keys and values with the oracle in the GPU
+side's two calls (into an oracle cache whose pages are the sequence's pages
+in order), compares every byte of
 those pages with the GPU cache's pages of the same sequence, and compares the
 GPU decode output of the piece's query heads with the oracle's float64
 attention.  Imports only NumPy and the oracle, so it runs in fresh processes
@@ -29,7 +30,12 @@ def _check_piece(p: dict) -> dict:
     npg = -(-L // bs)
     c = o.OracleCache(max(npg, 1), bs, Hs, D, kf, vf, max_seqs=1)
     pos = np.arange(L)
-    o.write(c, k16, v16, pos, np.zeros(L, np.int32))  # page j of the sequence is oracle block j
+    seq = np.zeros(L, np.int32)
+    # page j of the sequence is oracle block j; the same two calls as the GPU
+    # side: every token but the last, then the last (a KIVI page completed by
+    # the last token keeps its earlier rows in the tail as well)
+    o.write(c, k16[:L - 1], v16[:L - 1], pos[:L - 1], seq[:L - 1])
+    o.write(c, k16[L - 1:], v16[L - 1:], pos[L - 1:], seq[L - 1:])
     mism = {}
     for name, got in p["pages"].items():
         ref = getattr(c, name)
