@@ -221,6 +221,27 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q,
                     float sm_scale, int32_t split_tokens, void* out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode attention with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * kvq_decode_attn without `workspace` / `workspace_bytes`: the workspace is a
+ * fixed per-device array of KVQ_NOALLOC_WORKSPACE_BYTES inside the library,
+ * which every GPU the library runs on holds from the library's load until the
+ * process ends.  This call allocates and frees nothing.
+ * KVQ_ERR_WORKSPACE if kvq_decode_workspace_bytes() for these arguments
+ * exceeds KVQ_NOALLOC_WORKSPACE_BYTES (use a larger split_tokens, or
+ * kvq_decode_attn).  The array is shared by every call on the device and
+ * keeps the last call's contents (which the kernels never read before they
+ * write them): calls that overlap on one GPU, on different streams or from
+ * different threads, race and must not be issued. */
+#define KVQ_NOALLOC_WORKSPACE_BYTES (64u << 20)
+int kvq_decode_attn_noalloc(const kvq_cache* cache, const void* q,
+                            const int32_t* block_table,
+                            int32_t max_blocks_per_seq,
+                            const int32_t* ctx_lens, int32_t batch,
+                            int32_t n_q_heads, float sm_scale,
+                            int32_t split_tokens, void* out, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* kvq_status_string(int status);
 

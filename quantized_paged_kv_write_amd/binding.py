@@ -24,7 +24,8 @@ DTYPES = {"int8": 1, "fp8_e4m3fn": 2, "int4_g32": 3, "int4_kivi": 4, "fp8_e5m2":
 # Functions declared in include/kvq.h (the symbol test checks this list
 # against the header).
 EXPORTS = ("kvq_write", "kvq_write_static", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_status_string",
-           "kvq_get_device_error")
+           "kvq_get_device_error", "kvq_decode_attn_noalloc")
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # KVQ_NOALLOC_WORKSPACE_BYTES
 # Bits of kvq_get_device_error (kvq_device_error in include/kvq.h).
 DEVERR = {"slot": 1, "seq": 2, "block": 4, "ctx": 8}
 
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]
         L.kvq_status_string.restype = ctypes.c_char_p
+        L.kvq_decode_attn_noalloc.argtypes = [cp, vp, vp, i32, vp, i32, i32, ctypes.c_float, i32, vp, vp]
+        L.kvq_decode_attn_noalloc.restype = ctypes.c_int
         L.kvq_get_device_error.argtypes = [vp]
         L.kvq_get_device_error.restype = ctypes.c_int
         _lib = L
@@ -228,4 +231,27 @@ def decode_attn(cache: PagedKVCache, q, block_table, ctx_lens, sm_scale=0.0, spl
                                workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != KVQ_OK:
         raise KvqError(rc, "kvq_decode_attn")
+    return out
+
+
+def decode_attn_noalloc(cache: PagedKVCache, q, block_table, ctx_lens, out, sm_scale=0.0, split_tokens=0,
+                        stream=None):
+    """kvq_decode_attn_noalloc: decode into the caller's `out` (B, Hq, D) fp16
+    with the library's fixed per-device workspace (nothing is allocated)."""
+    dev = cache.device
+    _check(q, torch.float16, "q", dev)
+    _check(block_table, torch.int32, "block_table", dev)
+    _check(ctx_lens, torch.int32, "ctx_lens", dev)
+    _check(out, torch.float16, "out", dev)
+    B, Hq, D = q.shape
+    if D != cache.head_dim or block_table.dim() != 2 or block_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("shape mismatch between q, block_table and ctx_lens")
+    if out.shape != q.shape:
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    c = cache.struct()
+    rc = lib().kvq_decode_attn_noalloc(ctypes.byref(c), _ptr(q), _ptr(block_table), block_table.shape[1],
+                                       _ptr(ctx_lens), B, Hq, float(sm_scale), split_tokens, _ptr(out),
+                                       _stream(stream))
+    if rc != KVQ_OK:
+        raise KvqError(rc, "kvq_decode_attn_noalloc")
     return out

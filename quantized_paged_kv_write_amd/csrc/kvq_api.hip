@@ -13,6 +13,12 @@
 // host code uses the address hipGetSymbolAddress returns on that device.
 __device__ __align__(16) uint32_t kvq_error_word[2];
 
+// Decode workspace of kvq_decode_attn_noalloc: one fixed array per device,
+// held from the library's load until the process ends.  Host code must not
+// pass this name to a kernel (on the host it is only a stand-in): it uses the
+// device address looked up per device below.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_WORKSPACE_BYTES];
+
 namespace {
 
 using namespace kvq;
@@ -22,6 +28,7 @@ using namespace kvq;
 constexpr int kMaxDevices = 64;
 struct DeviceSymbols {
   uint32_t* err = nullptr;
+  uint8_t* scratch = nullptr;
 };
 std::atomic<bool> g_sym_ready[kMaxDevices];
 DeviceSymbols g_sym[kMaxDevices];
@@ -36,7 +43,10 @@ int device_symbols(DeviceSymbols* out) {
     if (!g_sym_ready[dev].load(std::memory_order_relaxed)) {
       void* p = nullptr;
       if (hipGetSymbolAddress(&p, HIP_SYMBOL(kvq_error_word)) != hipSuccess || !p) return KVQ_ERR_HIP;
+      void* ps = nullptr;
+      if (hipGetSymbolAddress(&ps, HIP_SYMBOL(scratch)) != hipSuccess || !ps) return KVQ_ERR_HIP;
       g_sym[dev].err = static_cast<uint32_t*>(p);
+      g_sym[dev].scratch = static_cast<uint8_t*>(ps);
       g_sym_ready[dev].store(true, std::memory_order_release);
     }
   }
@@ -172,9 +182,13 @@ int kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t n_
   return KVQ_OK;
 }
 
-int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
-                    const int32_t* ctx_lens, int32_t batch, int32_t n_q_heads, float sm_scale,
-                    int32_t split_tokens, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// kvq_decode_attn and kvq_decode_attn_noalloc; for the latter `workspace` is
+// NULL and the per-device scratch array serves as the workspace.
+int decode_impl(const kvq_cache* cache, const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
+                const int32_t* ctx_lens, int32_t batch, int32_t n_q_heads, float sm_scale, int32_t split_tokens,
+                void* out, void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
   int rc = check_cache(cache);
   if (rc != KVQ_OK) return rc;
   if (cache->k_dtype == KVQ_INT4_G32) return KVQ_ERR_UNSUPPORTED;
@@ -188,13 +202,18 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_
   if (!q || !block_table || !ctx_lens || !out) return KVQ_ERR_INVALID_ARG;
   DecodePlan p;
   if (!plan_decode(*cache, batch, n_q_heads, max_blocks_per_seq, split_tokens, &p)) return KVQ_ERR_SHAPE;
-  if (!workspace || workspace_bytes < p.bytes) return KVQ_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return KVQ_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (p.bytes > KVQ_NOALLOC_WORKSPACE_BYTES) return KVQ_ERR_WORKSPACE;
+  } else {
+    if (!workspace || workspace_bytes < p.bytes) return KVQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return KVQ_ERR_WORKSPACE;
+  }
   rc = device_present();
   if (rc != KVQ_OK) return rc;
   DeviceSymbols sym;
   rc = device_symbols(&sym);
   if (rc != KVQ_OK) return rc;
+  if (use_scratch) workspace = sym.scratch;  // this device's copy of the array
   DecodeArgs a{};
   a.err = sym.err;
   a.q = static_cast<const uint16_t*>(q);
@@ -227,6 +246,22 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_
   a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.plan_bytes);
   a.out = static_cast<uint16_t*>(out);
   return launch_decode(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+int kvq_decode_attn(const kvq_cache* cache, const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* ctx_lens, int32_t batch, int32_t n_q_heads, float sm_scale,
+                    int32_t split_tokens, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(cache, q, block_table, max_blocks_per_seq, ctx_lens, batch, n_q_heads, sm_scale, split_tokens,
+                     out, workspace, workspace_bytes, false, stream);
+}
+
+int kvq_decode_attn_noalloc(const kvq_cache* cache, const void* q, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* ctx_lens, int32_t batch, int32_t n_q_heads,
+                            float sm_scale, int32_t split_tokens, void* out, void* stream) {
+  return decode_impl(cache, q, block_table, max_blocks_per_seq, ctx_lens, batch, n_q_heads, sm_scale, split_tokens,
+                     out, nullptr, 0, true, stream);
 }
 
 int kvq_get_device_error(void* stream) {
