@@ -1,6 +1,7 @@
 """Benchmark: quantized paged decode on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra A,B,...|none]
+                    [--no-cpu-baseline] [--no-probes]
 
 One step is one decode step of the workload's batch: quantize-on-write of the
 new token of every sequence into the paged cache (kvq_write), then decode
@@ -17,6 +18,14 @@ to move (codes, scale metadata, block-table entries, q and out; for the write
 the fp16 K/V read, codes and metadata written, slot indices).  For symmetric
 formats the same prefill is also timed through kvq_write_static with
 calibrated per-head scales (write_static_GBps).
+
+The headline workload (--workload, default the Llama-3-8B FP8 layer) gives
+`value`, the roofline and the CPU baseline; every other large workload
+(--extra) is measured the same way afterwards and reported, with the headline
+one, under "workloads" (decode call and step GB/s, % of peak, write GB/s, and
+the quality statistic: the decode output against float64 attention over the
+unquantized fp16 K/V).  "stream_probes" are plain streaming rates of this GPU
+with the same 16-byte non-temporal accesses (libkvq_probe.so).
 """
 
 from __future__ import annotations
@@ -33,14 +42,18 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD specification
 QMAX = {"int8": 127.0, "fp8_e4m3fn": 448.0, "fp8_e5m2": 57344.0, "int4_g32": 7.0}  # symmetric formats
-DECODE_SRC = os.path.join(ROOT, "quantized_paged_kv_write_amd", "csrc", "kvq_decode.hip")
+# sources of the decode kernels (their hash tags the committed counter summaries)
+DECODE_SRC = [os.path.join(ROOT, "quantized_paged_kv_write_amd", "csrc", f) for f in ("kvq_decode.h", "kvq_decode.hip")]
 CAL_ELEMS = 1 << 28  # calibration kernel: negate 1 GiB of fp32 (reads 1 GiB, writes 1 GiB)
 
 
 def decode_source_hash() -> str:
     import hashlib
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in DECODE_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_profile_path(workload: str) -> str:
@@ -134,6 +147,20 @@ def write_bytes(w, T: int) -> int:
     return int(T * (per + 8 + (4 if w.k_dtype == "int4_kivi" else 0)))
 
 
+def host_info() -> dict:
+    """Logical CPUs and CPU model of the host the CPU baseline ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_logical_cpus": os.cpu_count(), "host_cpu_model": model}
+
+
 def cpu_baseline(w, inp, budget_s: float):
     """The CPU oracle, single-threaded, on whole sequences of the same
     workload until about budget_s seconds of decode work have been timed."""
@@ -168,52 +195,103 @@ def cpu_baseline(w, inp, budget_s: float):
             seqs += 1
             if dec_t + wr_t >= budget_s:
                 break
-    return {
+    res = {
         "value": round(dec_b / dec_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": f"{seqs} of {w.batch} sequences (ctx {inp.ctx_lens[0]}), decode step over their cache; "
                   f"oracle write of the same sequences {wr_b / wr_t / 1e9:.4f} GB/s",
         "decode_s": round(dec_t, 3), "write_s": round(wr_t, 3),
     }
+    res.update(host_info())
+    return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama3_8b_fp8")
-    ap.add_argument("--prefill-reps", type=int, default=5)
-    ap.add_argument("--settle", type=float, default=0.5,
-                    help="seconds of untimed decode calls after the cache fill, before any timing")
-    ap.add_argument("--caches", type=int, default=2, choices=(1, 2),
-                    help="identical caches the timed decode steps alternate between, so that no call reads "
-                         "data the previous call left in the memory-side cache")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="reduce two rocprofv3 counter CSVs to profiles/decode_<workload>_hbm_traffic.json")
-    ap.add_argument("--pmc-command", default="", help="the command that produced the counter CSVs")
-    args = ap.parse_args()
-    if args.pmc_summary:
-        d = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.pmc_command)
-        os.makedirs(os.path.dirname(traffic_profile_path(args.workload)), exist_ok=True)
-        with open(traffic_profile_path(args.workload), "w") as f:
-            json.dump(d, f, indent=1)
-        print(json.dumps(d, indent=1))
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode and write kernels shard "
-              "by sequence or KV head with no communication, so run one process per GPU instead.", file=sys.stderr)
-        sys.exit(2)
+def quality(w, inp, out, sm_scale=None, sample=3):
+    """Quality statistic (reported, not gated): the decode output against
+    float64 attention over the ORIGINAL fp16 keys and values (no
+    quantization), on `sample` sequences (first, middle, last) and all their
+    query heads: max |out - ref| and ||out - ref||_2 / ||ref||_2.  Plain
+    torch float64 on the GPU."""
+    import torch
+    B, H, D = w.batch, w.n_kv_heads, w.head_dim
+    G = w.n_q_heads // H
+    scale = sm_scale if sm_scale else 1.0 / math.sqrt(D)
+    bs = sorted({0, B // 2, B - 1})[:sample]
+    num = den = 0.0
+    mx = 0.0
+    for b in bs:
+        L = inp.ctx_lens[b]
+        st = inp.seq_start[b]
+        if L == 0:
+            continue
+        K = inp.k[st:st + L].double()
+        V = inp.v[st:st + L].double()
+        for h in range(H):
+            qh = inp.q[b, h * G:(h + 1) * G].double()  # (G, D)
+            s = torch.matmul(K[:, h, :].contiguous(), qh.t().contiguous()) * scale  # (L, G)
+            p = torch.softmax(s, dim=0)
+            ref = torch.matmul(p.t().contiguous(), V[:, h, :].contiguous())  # (G, D)
+            got = out[b, h * G:(h + 1) * G].double()
+            d = got - ref
+            mx = max(mx, float(d.abs().max()))
+            num += float((d * d).sum())
+            den += float((ref * ref).sum())
+    return {"max_abs": mx, "rel_l2": math.sqrt(num / den) if den > 0 else 0.0,
+            "sample": f"sequences {bs}, all {w.n_q_heads} query heads; reference = float64 attention over the "
+                      "unquantized fp16 K/V"}
 
+
+def stream_probes(dev):
+    """Plain HBM streaming rates with the same 16-byte non-temporal loads and
+    stores the cache kernels use (libkvq_probe.so): read only, copy, and the
+    2:1 read/write mix of the write path.  GB/s of bytes moved."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "quantized_paged_kv_write_amd", "libkvq_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.kvq_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.kvq_probe_stream.restype = ctypes.c_int
+    nbytes = 4 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    res = {}
+    for mode, name, moved in ((0, "read_GBps", nbytes), (1, "copy_GBps", 2 * nbytes),
+                              (2, "read2_write1_GBps", nbytes + nbytes // 2)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        run = lambda: L.kvq_probe_stream(mode, ctypes.c_void_p(src.data_ptr()),  # noqa: E731
+                                         ctypes.c_void_p(dst.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                         0, sp)
+        for _ in range(2):
+            if run() != 0:
+                return None
+        ev[0].record(stream)
+        for _ in range(10):
+            run()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(moved * 10 / (ev[0].elapsed_time(ev[1]) * 1e6), 1)
+    del src, dst
+    return res
+
+
+def measure(w, args, steps, warmup, dev="cuda", want_inputs=False):
+    """Fill two identical caches with the workload's prefill, time the
+    prefill write, then time `steps` decode steps (write of the new token of
+    every sequence + decode over the whole cache).  Returns a result dict (and
+    the inputs, for the CPU baseline)."""
     import torch
 
     import quantized_paged_kv_write_amd as kvq
     from quantized_paged_kv_write_amd import workloads as wl
 
-    dev = "cuda"
-    w = wl.WORKLOADS[args.workload]
-    seed = wl.ORDER.index(args.workload) + 1
+    seed = wl.ORDER.index(w.name) + 1
     print(f"[bench] workload {w.name}: B={w.batch} Hq={w.n_q_heads} H={w.n_kv_heads} D={w.head_dim} "
           f"bs={w.block_size} K={w.k_dtype} V={w.v_dtype}", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, seed, dev)
@@ -246,6 +324,7 @@ def main():
     for c in caches:
         kvq.write(c, k_pre, v_pre, s_pre, q_pre)
     torch.cuda.synchronize()
+
     # Settle: after idle time or a different heavy kernel, decode calls run
     # at a varying, slower rate for tens of milliseconds (clock and power
     # management adjusting), so untimed decode calls run for a fixed time
@@ -289,19 +368,6 @@ def main():
         print(f"[bench] prefill write with calibrated scales: {static_ms:.3f} ms, "
               f"{wbytes / static_ms / 1e6:.1f} GB/s", file=sys.stderr, flush=True)
 
-    # ---- plain device copy: the achievable HBM ceiling ---------------------
-    nbytes = 2 << 30
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    ev[0].record(stream)
-    for _ in range(5):
-        dst.copy_(src)
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * nbytes * 5 / (ev[0].elapsed_time(ev[1]) * 1e6)
-    del src, dst
     # known-size kernel for calibrating the FETCH_SIZE / WRITE_SIZE counters
     cal = torch.ones(CAL_ELEMS, dtype=torch.float32, device=dev)
     cal = cal.neg()
@@ -325,23 +391,115 @@ def main():
             evs[2].record(stream)
 
     settle()
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    stepw_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
-
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    stepw_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    ms_per_step = wall * 1e3 / steps
     dbytes = decode_bytes(w, ctx)
+    res = {
+        "workload": w.name, "batch": B,
+        "ctx_lens": "fixed %d" % ctx[0] if len(set(ctx)) == 1
+        else f"ragged {min(ctx)}..{max(ctx)} (mean {sum(ctx) / len(ctx):.0f})",
+        "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+        "block_size": w.block_size, "k_format": w.k_dtype, "v_format": w.v_dtype,
+        "decode_bytes_per_step": dbytes,
+        "ms_per_step": round(ms_per_step, 4),
+        "step_GBps": round(dbytes / (ms_per_step * 1e6), 2),
+        "decode_call_ms": round(dec_ms, 4),
+        "decode_call_GBps": round(dbytes / (dec_ms * 1e6), 2),
+        "decode_call_pct_hbm_peak": round(100 * dbytes / (dec_ms * 1e6) / HBM_PEAK_GBPS, 2),
+        "decode_step_write_ms": round(stepw_ms, 4),
+        "decode_tok_s": round(B / (ms_per_step * 1e-3), 1),
+        "decode_tok_s_attention_only_all_layers": round(B / (ms_per_step * 1e-3 * w.n_layers), 1),
+        "write_GBps": round(wbytes / (write_ms * 1e6), 2),
+        "write_pct_hbm_peak": round(100 * wbytes / (write_ms * 1e6) / HBM_PEAK_GBPS, 2),
+        "write_ms": round(write_ms, 4),
+        "write_tokens": int(pre_idx.numel()),
+        "write_static_GBps": None if static_ms is None else round(wbytes / (static_ms * 1e6), 2),
+    }
+    res["quality"] = quality(w, inp, out)
+    print(f"[bench] {w.name}: decode call {dec_ms:.4f} ms = {res['decode_call_GBps']:.0f} GB/s "
+          f"({res['decode_call_pct_hbm_peak']:.1f}% of peak), quality max|err| {res['quality']['max_abs']:.3e} "
+          f"rel L2 {res['quality']['rel_l2']:.3e}", file=sys.stderr, flush=True)
+    del caches, cache, ws
+    if want_inputs:
+        return res, inp
+    del inp
+    return res, None
+
+
+EXTRA_DEFAULT = "llama3_8b_int8k_int4v,llama3_70b_int8,llama3_8b_kivi_int4"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_fp8", help="the headline workload (value, roofline)")
+    ap.add_argument("--extra", default=EXTRA_DEFAULT,
+                    help="comma-separated workloads measured after the headline one, each reported in "
+                         "'workloads' ('none' for none)")
+    ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed decode calls after the cache fill, before any timing")
+    ap.add_argument("--caches", type=int, default=2, choices=(1, 2),
+                    help="identical caches the timed decode steps alternate between, so that no call reads "
+                         "data the previous call left in the memory-side cache")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="reduce two rocprofv3 counter CSVs to profiles/decode_<workload>_hbm_traffic.json")
+    ap.add_argument("--pmc-command", default="", help="the command that produced the counter CSVs")
+    args = ap.parse_args()
+    if args.pmc_summary:
+        d = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.pmc_command)
+        os.makedirs(os.path.dirname(traffic_profile_path(args.workload)), exist_ok=True)
+        with open(traffic_profile_path(args.workload), "w") as f:
+            json.dump(d, f, indent=1)
+        print(json.dumps(d, indent=1))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode and write kernels shard "
+              "by sequence or KV head with no communication, so run one process per GPU instead.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_paged_kv_write_amd import workloads as wl
+
+    dev = "cuda"
+    w = wl.WORKLOADS[args.workload]
+    head, inp = measure(w, args, args.steps, args.warmup, dev, want_inputs=not args.no_cpu_baseline)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, inp, args.cpu_budget)
+    del inp
+    torch.cuda.empty_cache()
+    workloads = {w.name: head}
+    extras = [] if args.extra in ("", "none") else [x for x in args.extra.split(",") if x and x != w.name]
+    for name in extras:
+        r, _ = measure(wl.WORKLOADS[name], args, args.extra_steps, args.warmup, dev)
+        workloads[name] = r
+        torch.cuda.empty_cache()
+    probes = None if args.no_probes else stream_probes(dev)
+
+    ms_per_step = head["ms_per_step"]
+    dbytes = head["decode_bytes_per_step"]
     value = dbytes / (ms_per_step * 1e6)
-    achieved = dbytes / (dec_ms * 1e6)
+    achieved = dbytes / (head["decode_call_ms"] * 1e6)
     res = {
         "metric": "quantized paged-decode KV-read GB/s (% HBM peak) + decode tok/s; write GB/s",
         "value": round(value, 2),
@@ -350,37 +508,36 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_s": args.settle,
-        "timed_caches": len(caches),
+        "timed_caches": args.caches,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp8_e4m3fn": "fp8_e4m3fn", "int8": "int8"}.get(w.k_dtype, w.k_dtype) + "+" + w.v_dtype
-                 + " codes, fp32 accumulate",
+        "dtype": w.k_dtype + "+" + w.v_dtype + " codes, fp32 accumulate",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "ctx_lens": "fixed %d" % ctx[0] if len(set(ctx)) == 1
-                   else f"ragged {min(ctx)}..{max(ctx)} (mean {sum(ctx) / len(ctx):.0f})",
-                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
-                   "block_size": w.block_size, "k_format": w.k_dtype, "v_format": w.v_dtype},
+        "config": {"workload": w.name, "batch": w.batch, "ctx_lens": head["ctx_lens"], "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "k_format": w.k_dtype, "v_format": w.v_dtype},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "decode_kernels_ms": round(dec_ms, 4),
-        "decode_step_write_ms": round(stepw_ms, 4),
+        "decode_kernels_ms": head["decode_call_ms"],
+        "decode_step_write_ms": head["decode_step_write_ms"],
         "decode_bytes_per_step": dbytes,
-        "decode_tok_s": round(B / (ms_per_step * 1e-3), 1),
-        "decode_tok_s_attention_only_all_layers": round(B / (ms_per_step * 1e-3 * w.n_layers), 1),
-        "write_GBps": round(wbytes / (write_ms * 1e6), 2),
-        "write_pct_hbm_peak": round(100 * wbytes / (write_ms * 1e6) / HBM_PEAK_GBPS, 2),
-        "write_ms": round(write_ms, 4),
-        "write_tokens": int(pre_idx.numel()),
-        "write_static_GBps": None if static_ms is None else round(wbytes / (static_ms * 1e6), 2),
-        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "decode_tok_s": head["decode_tok_s"],
+        "decode_tok_s_attention_only_all_layers": head["decode_tok_s_attention_only_all_layers"],
+        "write_GBps": head["write_GBps"],
+        "write_pct_hbm_peak": head["write_pct_hbm_peak"],
+        "write_ms": head["write_ms"],
+        "write_tokens": head["write_tokens"],
+        "write_static_GBps": head["write_static_GBps"],
+        "quality": head["quality"],
+        "stream_probes": probes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w.name),
                      "kernel": "plan_kernel + decode_split_kernel + merge_kernel (one kvq_decode_attn call)"},
+        "workloads": workloads,
     }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

@@ -46,11 +46,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libkvq.so)")
 
 
+PROBE_SRC = "kvq_probe.hip"  # benchmark reference points, its own library
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     procs = []
     objs = []
+    probe_obj = os.path.join(BUILD, PROBE_SRC.replace(".hip", ".o"))
+    procs.append((PROBE_SRC, subprocess.Popen([cc, *COMMON, "-c", os.path.join(CSRC, PROBE_SRC), "-o", probe_obj],
+                                              stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
     for src, extra in SOURCES.items():
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
@@ -76,6 +83,9 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", probe_obj, "-o", tmp], check=True)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

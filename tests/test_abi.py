@@ -191,3 +191,32 @@ int main() {
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     checked, bad = map(int, r.stdout.split())
     assert r.returncode == 0 and bad == 0 and checked > 1_000_000, r.stdout
+
+
+def test_bench_quality_statistic_matches_the_oracle_attention():
+    # bench.py's quality statistic (float64 attention over the unquantized
+    # fp16 K/V, in torch) against the oracle's float64 attention over the
+    # same K/V, on CPU tensors.
+    import sys
+
+    import numpy as np
+    import torch
+
+    import oracle as o
+    from quantized_paged_kv_write_amd import workloads as wl
+    sys.path.insert(0, ROOT)
+    import bench
+    w = wl.Workload("small", 3, 8, 2, 64, 16, "int8", "int8", ("fixed", 0), 2, sink_tokens=4)
+    inp = wl.make_inputs(w, 5, "cpu", ctx_lens=[40, 0, 75])
+    out = torch.randn(inp.q.shape, generator=torch.Generator().manual_seed(1)).half()
+    got = bench.quality(w, inp, out)
+    num = den = mx = 0.0
+    for b in (0, 2):
+        st, L = inp.seq_start[b], inp.ctx_lens[b]
+        ref = o.attention_fp64(inp.q[b].numpy(), inp.k[st:st + L].numpy().astype(np.float64),
+                               inp.v[st:st + L].numpy().astype(np.float64))
+        d = out[b].double().numpy() - ref
+        mx = max(mx, float(np.abs(d).max()))
+        num += float((d * d).sum())
+        den += float((ref * ref).sum())
+    assert abs(got["max_abs"] - mx) <= 1e-12 and abs(got["rel_l2"] - (num / den) ** 0.5) <= 1e-12
