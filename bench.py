@@ -437,6 +437,158 @@ def measure(w, args, steps, warmup, dev="cuda", want_inputs=False):
     return res, None
 
 
+def offload_measure(args, dev="cuda"):
+    """Offloaded pages with double-buffered prefetch ("Use Less Memory",
+    section 4): the headline FP8 layer (27 x 32k) whose first --offload-pages
+    pages of every sequence live in a pool in pinned host memory.  Each step
+    decodes over the cache with those pages read from staging set t % 2,
+    while the prefetch of step t + 1 (kvq_copy_blocks, host -> device, on a
+    second stream) fills set (t + 1) % 2.  Reports the copy rate, the decode
+    time with and without the concurrent prefetch, the overlapped and the
+    serial step time, and whether every step's output equals the decode of
+    the pages that never left the device (bitwise)."""
+    import torch
+
+    import quantized_paged_kv_write_amd as kvq
+    from quantized_paged_kv_write_amd import workloads as wl
+
+    w = wl.WORKLOADS["llama3_8b_fp8"]
+    P = args.offload_pages
+    B = w.batch
+    n_off = B * P
+    inp = wl.make_inputs(w, wl.ORDER.index(w.name) + 1, dev)
+    print(f"[bench] offload: {w.name}, {P} pages of every sequence ({n_off} pages) prefetched per step",
+          file=sys.stderr, flush=True)
+    # the two staging sets are contiguous runs of blocks after the workload's
+    # own, so one prefetch is one DMA copy per buffer (a page is 16 KB of
+    # codes; page-by-page copies would go to small blit kernels instead)
+    nb0 = inp.num_blocks
+    cache = kvq.PagedKVCache(nb0 + 2 * n_off, w.block_size, w.n_kv_heads, w.head_dim, w.k_dtype, w.v_dtype,
+                             max_seqs=B, device=dev)
+    kvq.write(cache, inp.k, inp.v, inp.slot_mapping.to(dev), inp.seq_idx.to(dev))
+    q = inp.q.clone()
+    ctx_d = torch.tensor(inp.ctx_lens, dtype=torch.int32, device=dev)
+    table = inp.block_table
+    del inp
+    torch.cuda.empty_cache()
+    pool = kvq.PagedKVCache(n_off, w.block_size, w.n_kv_heads, w.head_dim, w.k_dtype, w.v_dtype, device="cpu",
+                            pin_memory=True)
+    import numpy as np
+    offl = np.array([int(table[b, p]) for b in range(B) for p in range(P)], np.int32)
+    host_ids = np.arange(n_off, dtype=np.int32)
+    kvq.copy_blocks(cache, pool, offl, host_ids)  # offload
+    sets = [np.arange(nb0, nb0 + n_off, dtype=np.int32), np.arange(nb0 + n_off, nb0 + 2 * n_off, dtype=np.int32)]
+    tables = []
+    for st in sets:
+        t2 = table.clone()
+        for i, d in enumerate(st):
+            t2[i // P, i % P] = d
+        tables.append(t2.to(dev))
+    base_table = table.to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(kvq.decode_workspace_bytes(cache, B, w.n_q_heads, table.shape[1]), dtype=torch.uint8,
+                     device=dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ref = kvq.decode_attn(cache, q, base_table, ctx_d).clone()
+    torch.cuda.synchronize()
+    page_bytes = 2 * w.block_size * w.n_kv_heads * (w.head_dim + 2)  # FP8 K and V codes + scales
+    nbytes = n_off * page_bytes
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    reps = args.offload_steps
+
+    # prefetch alone
+    kvq.copy_blocks(pool, cache, host_ids, sets[0])
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record(main)
+    for r in range(reps):
+        kvq.copy_blocks(pool, cache, host_ids, sets[r % 2])
+    e1.record(main)
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / reps
+    # decode alone (over the staging sets)
+    for r in range(3):
+        kvq.decode_attn(cache, q, tables[r % 2], ctx_d, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0.record(main)
+    for r in range(reps):
+        kvq.decode_attn(cache, q, tables[r % 2], ctx_d, out=out, workspace=ws)
+    e1.record(main)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / reps
+    equal = bool(torch.equal(out, ref))
+    # serial: prefetch, then decode, on one stream
+    e0.record(main)
+    for r in range(reps):
+        kvq.copy_blocks(pool, cache, host_ids, sets[r % 2])
+        kvq.decode_attn(cache, q, tables[r % 2], ctx_d, out=out, workspace=ws)
+    e1.record(main)
+    torch.cuda.synchronize()
+    serial_ms = e0.elapsed_time(e1) / reps
+    equal = equal and bool(torch.equal(out, ref))
+    # overlapped: decode t on the main stream while set (t + 1) % 2 is filled
+    # on the side stream; decode t + 1 waits for that prefetch (event), and
+    # the prefetch into a set waits for the decode that last read it
+    ready = [torch.cuda.Event() for _ in range(2)]
+    freed = [torch.cuda.Event() for _ in range(2)]
+    dev_ev = [(ev(), ev()) for _ in range(reps)]
+    outs = [torch.empty_like(out) for _ in range(reps // 8)]
+    t_start, t_end = ev(), ev()
+
+    def pipeline(timed):
+        with torch.cuda.stream(side):
+            kvq.copy_blocks(pool, cache, host_ids, sets[0], stream=side)
+            ready[0].record(side)
+        if timed:
+            t_start.record(main)
+        for r in range(reps):
+            cur = r % 2
+            main.wait_event(ready[cur])
+            if r + 1 < reps:
+                if r >= 1:
+                    side.wait_event(freed[1 - cur])  # decode r - 1 read set 1 - cur
+                kvq.copy_blocks(pool, cache, host_ids, sets[1 - cur], stream=side)
+                ready[1 - cur].record(side)
+            if timed:
+                dev_ev[r][0].record(main)
+            kvq.decode_attn(cache, q, tables[cur], ctx_d, out=out, workspace=ws)
+            if timed:
+                dev_ev[r][1].record(main)
+            freed[cur].record(main)
+            if timed and r % 8 == 7:
+                outs[r // 8].copy_(out)
+        if timed:
+            t_end.record(main)
+
+    pipeline(False)
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    pipeline(True)
+    enqueue_ms = (time.perf_counter() - c0) * 1e3 / reps
+    torch.cuda.synchronize()
+    overlap_ms = t_start.elapsed_time(t_end) / reps
+    dec_conc_ms = sum(a.elapsed_time(b) for a, b in dev_ev[1:]) / max(reps - 1, 1)
+    equal = equal and all(bool(torch.equal(x, ref)) for x in outs)
+    del cache, pool, ws
+    torch.cuda.empty_cache()
+    res = {
+        "workload": w.name, "pages_per_step": n_off, "bytes_per_step": nbytes,
+        "prefetch_ms": round(copy_ms, 4), "prefetch_GBps_h2d": round(nbytes / (copy_ms * 1e6), 2),
+        "decode_ms_alone": round(dec_ms, 4), "decode_ms_with_concurrent_prefetch": round(dec_conc_ms, 4),
+        "step_ms_serial": round(serial_ms, 4), "step_ms_overlapped": round(overlap_ms, 4),
+        "host_enqueue_ms_per_step": round(enqueue_ms, 4),
+        "bitwise_equal_to_resident_decode": equal,
+        "note": "a step is decode over the whole cache with the prefetched pages read from the staging set; "
+                "overlapped = max(prefetch, decode) when hidden, serial = prefetch + decode; step times from "
+                "HIP events on the decode stream",
+    }
+    print(f"[bench] offload: prefetch {copy_ms:.3f} ms ({res['prefetch_GBps_h2d']:.1f} GB/s), decode {dec_ms:.3f} ms "
+          f"alone / {dec_conc_ms:.3f} ms with prefetch, step serial {serial_ms:.3f} / overlapped {overlap_ms:.3f} ms, "
+          f"bitwise equal {equal}", file=sys.stderr, flush=True)
+    return res
+
+
 EXTRA_DEFAULT = "llama3_8b_int8k_int4v,llama3_70b_int8,llama3_8b_kivi_int4"
 
 
@@ -459,6 +611,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
+    ap.add_argument("--no-offload", action="store_true")
+    ap.add_argument("--offload-pages", type=int, default=10, help="pages of every sequence prefetched per step")
+    ap.add_argument("--offload-steps", type=int, default=40)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="reduce two rocprofv3 counter CSVs to profiles/decode_<workload>_hbm_traffic.json")
     ap.add_argument("--pmc-command", default="", help="the command that produced the counter CSVs")
@@ -494,6 +649,7 @@ def main():
         r, _ = measure(wl.WORKLOADS[name], args, args.extra_steps, args.warmup, dev)
         workloads[name] = r
         torch.cuda.empty_cache()
+    offload = None if args.no_offload else offload_measure(args, dev)
     probes = None if args.no_probes else stream_probes(dev)
 
     ms_per_step = head["ms_per_step"]
@@ -531,6 +687,7 @@ def main():
         "write_static_GBps": head["write_static_GBps"],
         "quality": head["quality"],
         "stream_probes": probes,
+        "offload": offload,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w.name),
                      "kernel": "plan_kernel + decode_split_kernel + merge_kernel (one kvq_decode_attn call)"},

@@ -242,6 +242,31 @@ int kvq_decode_attn_noalloc(const kvq_cache* cache, const void* q,
                             int32_t n_q_heads, float sm_scale,
                             int32_t split_tokens, void* out, void* stream);
 
+/* Copy whole pages between two caches of the same geometry and formats
+ * (block_size, n_kv_heads, head_dim, k_dtype, v_dtype; num_blocks may
+ * differ): page dst_blocks[i] of `dst` becomes a byte copy of page
+ * src_blocks[i] of `src`, for i < n ("Use Less Memory: Quantization and
+ * Offloading", section 4: quantized blocks offloaded to CPU RAM and
+ * prefetched into a second set of GPU buffers for the next step while the
+ * current one computes).  Either cache may live in device memory or in
+ * pinned host memory (hipHostMalloc; the per-page layout is the same), so
+ * the call offloads (device -> host), prefetches (host -> device) or moves
+ * pages on the device.  A page is its codes, scales and (KIVI keys) zero
+ * points; the per-sequence KIVI tails are not paged and are not copied.
+ *   src_blocks, dst_blocks  int32 HOST arrays of n block ids, read during the
+ *                           call only; ids outside [0, num_blocks) of their
+ *                           cache give KVQ_ERR_INVALID_ARG before any copy.
+ * The copies are enqueued on `stream` (hipMemcpyAsync, so the DMA engines
+ * carry them and kernels on other streams keep running); runs of consecutive
+ * source and destination ids become one copy per buffer.  With pageable
+ * instead of pinned host memory the copies are correct but not asynchronous.
+ * Destination pages listed twice, or pages that are both read and written by
+ * the call, give an unspecified result.  KVQ_ERR_SHAPE if the geometries or
+ * formats differ; KVQ_ERR_INVALID_ARG for a NULL buffer the formats need. */
+int kvq_copy_blocks(const kvq_cache* src, const kvq_cache* dst,
+                    const int32_t* src_blocks, const int32_t* dst_blocks,
+                    int32_t n, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* kvq_status_string(int status);
 

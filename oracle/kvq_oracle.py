@@ -577,6 +577,32 @@ def decode_attn(cache: OracleCache, q, block_table, ctx_lens, sm_scale=None, seq
 
 
 # --------------------------------------------------------------------------
+# Offloading whole pages ([P1] section 4 "Pipelining and Latency Overlap":
+# quantized blocks move between GPU memory and CPU RAM unchanged; [P1] key
+# insight: quantization and offloading compose, the offloaded blocks keep
+# their quantized format).
+# --------------------------------------------------------------------------
+
+
+def paged_buffer_names(cache: OracleCache):
+    """The buffers that hold one entry per page (the KIVI tails are per
+    sequence, not per page)."""
+    names = ["k_codes", "v_codes", "k_scales", "v_scales"]
+    if cache.k_fmt == INT4_KIVI:
+        names.append("k_zeros")
+    return names
+
+
+def copy_blocks(src: OracleCache, dst: OracleCache, src_blocks, dst_blocks):
+    """Page dst_blocks[i] of dst becomes page src_blocks[i] of src: every
+    paged buffer's entry copied byte for byte, in list order."""
+    assert (src.bs, src.H, src.D, src.k_fmt, src.v_fmt) == (dst.bs, dst.H, dst.D, dst.k_fmt, dst.v_fmt)
+    for s_id, d_id in zip(np.asarray(src_blocks).ravel(), np.asarray(dst_blocks).ravel()):
+        for name in paged_buffer_names(src):
+            getattr(dst, name)[int(d_id)] = getattr(src, name)[int(s_id)]
+
+
+# --------------------------------------------------------------------------
 # Closed forms ([P1] Exercise 3 and [P3] "The Mathematics of KV Cache
 # Growth": bytes per token = 2 * layers * kv_heads * head_dim * bytes/element;
 # [P2] section 5 scale overheads).

@@ -24,7 +24,7 @@ DTYPES = {"int8": 1, "fp8_e4m3fn": 2, "int4_g32": 3, "int4_kivi": 4, "fp8_e5m2":
 # Functions declared in include/kvq.h (the symbol test checks this list
 # against the header).
 EXPORTS = ("kvq_write", "kvq_write_static", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_status_string",
-           "kvq_get_device_error", "kvq_decode_attn_noalloc")
+           "kvq_get_device_error", "kvq_decode_attn_noalloc", "kvq_copy_blocks")
 NOALLOC_WORKSPACE_BYTES = 64 << 20  # KVQ_NOALLOC_WORKSPACE_BYTES
 # Bits of kvq_get_device_error (kvq_device_error in include/kvq.h).
 DEVERR = {"slot": 1, "seq": 2, "block": 4, "ctx": 8}
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_decode_attn_noalloc.argtypes = [cp, vp, vp, i32, vp, i32, i32, ctypes.c_float, i32, vp, vp]
         L.kvq_decode_attn_noalloc.restype = ctypes.c_int
+        L.kvq_copy_blocks.argtypes = [cp, cp, vp, vp, i32, vp]
+        L.kvq_copy_blocks.restype = ctypes.c_int
         L.kvq_get_device_error.argtypes = [vp]
         L.kvq_get_device_error.restype = ctypes.c_int
         _lib = L
@@ -109,7 +111,7 @@ class PagedKVCache:
     the layouts of include/kvq.h (codes uint8, scales/zeros/tails fp16)."""
 
     def __init__(self, num_blocks, block_size, n_kv_heads, head_dim, k_dtype, v_dtype, max_seqs=0,
-                 device="cuda"):
+                 device="cuda", pin_memory=False):
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
         self.n_kv_heads, self.head_dim = int(n_kv_heads), int(head_dim)
         self.k_dtype, self.v_dtype, self.max_seqs = k_dtype, v_dtype, int(max_seqs)
@@ -118,7 +120,10 @@ class PagedKVCache:
             dev = torch.device("cuda", torch.cuda.current_device())
         self.device = dev
         nb, bs, H, D = self.num_blocks, self.block_size, self.n_kv_heads, self.head_dim
-        z = lambda *shape, dt: torch.zeros(shape, dtype=dt, device=self.device)  # noqa: E731
+        # device="cpu", pin_memory=True: a pool of pages in pinned host memory
+        # (for kvq_copy_blocks), laid out like the device cache
+        self.pinned = bool(pin_memory)
+        z = lambda *shape, dt: torch.zeros(shape, dtype=dt, device=self.device, pin_memory=self.pinned)  # noqa: E731
         half_row = lambda f: D // 2 if f in ("int4_g32", "int4_kivi") else D  # noqa: E731
         groups = lambda f: D // 32 if f == "int4_g32" else 1  # noqa: E731
         self.k_codes = z(nb, bs, H, half_row(k_dtype), dt=torch.uint8)
@@ -184,6 +189,22 @@ def write_static(cache: PagedKVCache, k, v, slot_mapping, k_scale, v_scale, stre
                                 _ptr(v_scale), _stream(stream))
     if rc != KVQ_OK:
         raise KvqError(rc, "kvq_write_static")
+
+
+def copy_blocks(src: PagedKVCache, dst: PagedKVCache, src_blocks, dst_blocks, stream=None):
+    """kvq_copy_blocks: page dst_blocks[i] of `dst` becomes a copy of page
+    src_blocks[i] of `src` (either cache on the device or in pinned host
+    memory), enqueued on the stream.  The id lists are host sequences."""
+    import numpy as np
+    s_ids = np.ascontiguousarray(np.asarray(src_blocks, dtype=np.int32).ravel())
+    d_ids = np.ascontiguousarray(np.asarray(dst_blocks, dtype=np.int32).ravel())
+    if s_ids.size != d_ids.size:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    cs, cd = src.struct(), dst.struct()
+    rc = lib().kvq_copy_blocks(ctypes.byref(cs), ctypes.byref(cd), s_ids.ctypes.data_as(ctypes.c_void_p),
+                               d_ids.ctypes.data_as(ctypes.c_void_p), int(s_ids.size), _stream(stream))
+    if rc != KVQ_OK:
+        raise KvqError(rc, "kvq_copy_blocks")
 
 
 def get_device_error(stream=None) -> int:

@@ -29,6 +29,7 @@ SOURCES = {
     "kvq_decode_kfp8.hip": [],
     "kvq_decode_kkivi.hip": [],
     "kvq_decode_ke5m2.hip": [],
+    "kvq_offload.hip": [],
 }
 
 COMMON = [

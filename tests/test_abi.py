@@ -220,3 +220,22 @@ def test_bench_quality_statistic_matches_the_oracle_attention():
         num += float((d * d).sum())
         den += float((ref * ref).sum())
     assert abs(got["max_abs"] - mx) <= 1e-12 and abs(got["rel_l2"] - (num / den) ** 0.5) <= 1e-12
+
+
+def test_copy_blocks_argument_errors():
+    L = kvq.lib()
+    a, b = _cache(), _cache(num_blocks=4)
+    ids = (ctypes.c_int32 * 2)(0, 3)
+    bad = (ctypes.c_int32 * 2)(0, 4)  # 4 is past b's 4 blocks
+
+    def cp(s, d, si=ids, di=ids, n=2):
+        return L.kvq_copy_blocks(ctypes.byref(s), ctypes.byref(d), si, di, n, None)
+
+    assert L.kvq_copy_blocks(None, ctypes.byref(b), ids, ids, 2, None) == INVALID
+    assert cp(a, _cache(head_dim=64)) == SHAPE          # geometries differ
+    assert cp(a, _cache(v_dtype=2)) == SHAPE            # formats differ
+    assert cp(a, b, di=bad) == INVALID                  # id out of range, nothing copied
+    assert cp(a, b, n=-1) == INVALID
+    assert cp(a, b, n=0) == OK                          # nothing to do
+    assert cp(a, _cache(num_blocks=4, v_scales=None)) == INVALID
+    assert L.kvq_copy_blocks(ctypes.byref(a), ctypes.byref(b), None, ids, 2, None) == INVALID

@@ -724,3 +724,35 @@ def test_context_length_is_clamped_to_the_block_table():
     q = np.random.default_rng(47).standard_normal((1, 4, D)).astype(np.float16)
     assert np.array_equal(o.decode_attn(c, q, table, [L + 1000]), o.decode_attn(c, q, table, [L]))
     assert not np.any(o.decode_attn(c, q, table, [-3]))
+
+
+# --------------------------------------------------------------------------
+# Offloaded pages
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("kf,vf", [(o.FP8_E4M3FN, o.FP8_E4M3FN), (o.INT4_KIVI, o.INT4_G32)])
+def test_offload_round_trip_leaves_attention_unchanged(kf, vf):
+    # Pages offloaded to a pool and prefetched back into other blocks, with
+    # the block table pointing at the new blocks: every paged byte equal and
+    # decode bitwise unchanged (the copy is the identity on page contents).
+    bs = 32 if kf == o.INT4_KIVI else 16
+    ctx = [150, 97]
+    H, D, Hq = 2, 32, 4
+    nb, table, ks, vs, slots = _three_sequences(kf, vf, ctx, bs, H, D, seed=50)
+    c = o.OracleCache(nb + 8, bs, H, D, kf, vf, max_seqs=2)
+    o.write(c, np.concatenate(ks), np.concatenate(vs), np.concatenate(slots),
+            np.concatenate([np.full(L, b, np.int32) for b, L in enumerate(ctx)]))
+    q = np.random.default_rng(51).standard_normal((2, Hq, D)).astype(np.float16)
+    before = o.decode_attn(c, q, table, ctx)
+    pool = o.OracleCache(16, bs, H, D, kf, vf, max_seqs=1)
+    moved = [int(table[0, 0]), int(table[0, 2]), int(table[1, 1]), int(table[1, 0])]
+    o.copy_blocks(c, pool, moved, [3, 4, 5, 9])
+    for name in o.paged_buffer_names(c):
+        for s_id, d_id in zip(moved, [3, 4, 5, 9]):
+            assert np.array_equal(getattr(pool, name)[d_id], getattr(c, name)[s_id])
+    new = [nb + 1, nb + 2, nb + 3, nb + 7]  # free blocks of the cache
+    o.copy_blocks(pool, c, [3, 4, 5, 9], new)
+    t2 = table.copy()
+    t2[0, 0], t2[0, 2], t2[1, 1], t2[1, 0] = new
+    assert np.array_equal(o.decode_attn(c, q, t2, ctx), before)
