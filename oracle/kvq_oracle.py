@@ -199,10 +199,11 @@ def fp8_encode(y, fmt: str) -> np.ndarray:
 
 
 def quantize_sym(x16: np.ndarray, fmt: str):
-    """Quantize fp16 rows (..., D).  Returns (codes, scales):
+    """Quantize fp16 rows (..., D) -- or the fp32 rows of a rotated cache
+    (rotate_rows) -- the same way.  Returns (codes, scales):
     codes int8 (INT8/INT4, values in [-q_max, q_max]) or uint8 (FP8 bytes),
     shape (..., D); scales float16 of shape (..., D // group)."""
-    assert x16.dtype == np.float16
+    assert x16.dtype in (np.float16, np.float32)
     D = x16.shape[-1]
     g = INT4_GROUP if fmt == INT4_G32 else D
     x = x16.astype(np.float32).reshape(x16.shape[:-1] + (D // g, g))
@@ -241,8 +242,9 @@ def quantize_sym_static(x16: np.ndarray, fmt: str, s16: np.ndarray):
     factors computed ahead of deployment of [P3] Implementation Best Practices
     (calibrated scaling factors) and [P4] (static calibration).  Quotients beyond +-q_max saturate.  For
     INT4 group-32 rows the row's scale serves every group.  Returns (codes,
-    scales) like quantize_sym, the scales being s16 repeated per group."""
-    assert x16.dtype == np.float16 and s16.dtype == np.float16
+    scales) like quantize_sym, the scales being s16 repeated per group.  Rows
+    may be the fp32 rows of a rotated cache."""
+    assert x16.dtype in (np.float16, np.float32) and s16.dtype == np.float16
     D = x16.shape[-1]
     g = INT4_GROUP if fmt == INT4_G32 else D
     x = x16.astype(np.float32).reshape(x16.shape[:-1] + (D // g, g))
@@ -317,6 +319,67 @@ def kivi_dequant(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndar
 
 
 # --------------------------------------------------------------------------
+# Walsh-Hadamard rotation ([P3] "Numerical Formats": QuaRot applies randomized
+# orthogonal Walsh-Hadamard transforms that spread outlier peaks over all
+# channels before uniform 4-bit quantization; "Accuracy, Latency, and
+# Serving Economics": INT4 with Hadamard rotations keeps baseline quality).
+# Reading: the rotation of a head_dim row x is R x with R = H diag(sigma) /
+# sqrt(D), H the Sylvester Hadamard matrix (entries +-1) and sigma a vector
+# of random signs drawn by the caller ("randomized").  The cache stores the
+# unnormalised rotation y = H (sigma * x): each entry of y is a sum of +-x_c,
+# computed exactly and rounded once to fp32, and y is quantized like any row
+# (its per-row scale absorbs the factor sqrt(D)).  The inverse of a stored
+# row is x = sigma * (H y) / D.  Scores need no inverse on the keys side:
+# q . x_hat = q' . y_hat with q' = H (sigma * q) / D.
+# --------------------------------------------------------------------------
+
+
+def hadamard(D: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order D (a power of two), int64 +-1:
+    H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]."""
+    H = np.ones((1, 1), np.int64)
+    while H.shape[0] < D:
+        H = np.block([[H, H], [H, -H]])
+    assert H.shape[0] == D
+    return H
+
+
+def sign_vector(sign_bits, D: int) -> np.ndarray:
+    """sigma (D,) float64 of +-1 from a bit array: bit c (bit c % 32 of word
+    c // 32) set means sigma_c = -1."""
+    w = np.asarray(sign_bits, dtype=np.uint64)
+    c = np.arange(D)
+    bit = (w[c // 32] >> (c % 32).astype(np.uint64)) & np.uint64(1)
+    return np.where(bit == 1, -1.0, 1.0)
+
+
+def rotate_rows(x16: np.ndarray, sign_bits) -> np.ndarray:
+    """fp16 rows (..., D) -> fp32 rows y = H (sigma * x), each entry rounded
+    once to fp32.  The float64 sums are exact: every term is an fp16 value
+    (a multiple of 2^-24 below 2^16), so any partial sum of at most 256
+    terms needs fewer than 53 significant bits."""
+    D = x16.shape[-1]
+    x = x16.astype(np.float64) * sign_vector(sign_bits, D)
+    y = x @ hadamard(D).T.astype(np.float64)
+    return y.astype(np.float32)
+
+
+def unrotate_rows(y, sign_bits) -> np.ndarray:
+    """float64 rows x = sigma * (H y) / D (the inverse of the rotation, since
+    H H = D I)."""
+    y = np.asarray(y, dtype=np.float64)
+    D = y.shape[-1]
+    return (y @ hadamard(D).T.astype(np.float64)) * sign_vector(sign_bits, D) / D
+
+
+def rotate_query(q16: np.ndarray, sign_bits) -> np.ndarray:
+    """float64 q' = H (sigma * q) / D: q . x_hat = q' . y_hat for the stored
+    (rotated) rows y_hat of a key."""
+    D = q16.shape[-1]
+    return (q16.astype(np.float64) * sign_vector(sign_bits, D)) @ hadamard(D).T.astype(np.float64) / D
+
+
+# --------------------------------------------------------------------------
 # Paged cache ([P2] section 5: k_cache (num_blocks, block_size, n_kv_heads,
 # head_dim) with k_scale (num_blocks, block_size, n_kv_heads) in FP16; [P4]
 # PagedAttention: fixed-size, non-contiguous physical blocks).
@@ -332,10 +395,15 @@ class OracleCache:
       k_tail, v_tail fp16 (max_seqs, block_size, H, D)   KIVI keys only
     """
 
-    def __init__(self, num_blocks, block_size, n_kv_heads, head_dim, k_fmt, v_fmt, max_seqs=0):
+    def __init__(self, num_blocks, block_size, n_kv_heads, head_dim, k_fmt, v_fmt, max_seqs=0, rot_k=None,
+                 rot_v=None):
+        """rot_k / rot_v: sign bits of the keys' / values' rotation (see
+        rotate_rows), or None for unrotated rows.  KIVI keys are not
+        rotated."""
         assert k_fmt in K_FORMATS and v_fmt in V_FORMATS
         if k_fmt == INT4_KIVI:
-            assert block_size == KIVI_GROUP
+            assert block_size == KIVI_GROUP and rot_k is None
+        self.rot_k, self.rot_v = rot_k, rot_v
         self.nb, self.bs, self.H, self.D = num_blocks, block_size, n_kv_heads, head_dim
         self.k_fmt, self.v_fmt, self.max_seqs = k_fmt, v_fmt, max_seqs
         nb, bs, H, D = num_blocks, block_size, n_kv_heads, head_dim
@@ -359,9 +427,12 @@ class OracleCache:
         return out
 
 
-def _store_sym(codes_buf, scales_buf, fmt, x16_rows, slots, bs, static_s16=None):
+def _store_sym(codes_buf, scales_buf, fmt, x16_rows, slots, bs, static_s16=None, rot=None):
     """Quantize (n, H, D) rows and scatter them to flat slots (with the given
-    per-head scales static_s16 (H,) when present)."""
+    per-head scales static_s16 (H,) when present; rotated first when rot
+    holds sign bits)."""
+    if rot is not None:
+        x16_rows = rotate_rows(x16_rows, rot)
     if static_s16 is None:
         codes, s16 = quantize_sym(x16_rows, fmt)
     else:
@@ -399,9 +470,9 @@ def write(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapping, se
     slots = np.asarray(slot_mapping, dtype=np.int64)
     valid = np.nonzero(slot_in_range(cache, slots))[0]
     bs = cache.bs
-    _store_sym(cache.v_codes, cache.v_scales, cache.v_fmt, v16[valid], slots[valid], bs)
+    _store_sym(cache.v_codes, cache.v_scales, cache.v_fmt, v16[valid], slots[valid], bs, rot=cache.rot_v)
     if cache.k_fmt != INT4_KIVI:
-        _store_sym(cache.k_codes, cache.k_scales, cache.k_fmt, k16[valid], slots[valid], bs)
+        _store_sym(cache.k_codes, cache.k_scales, cache.k_fmt, k16[valid], slots[valid], bs, rot=cache.rot_k)
         return
     assert seq_idx is not None
     seq_idx = np.asarray(seq_idx, dtype=np.int64)
@@ -447,8 +518,8 @@ def write_static(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapp
     slots = np.asarray(slot_mapping, dtype=np.int64)
     valid = np.nonzero(slot_in_range(cache, slots))[0]
     bs = cache.bs
-    _store_sym(cache.k_codes, cache.k_scales, cache.k_fmt, k16[valid], slots[valid], bs, k_scale16)
-    _store_sym(cache.v_codes, cache.v_scales, cache.v_fmt, v16[valid], slots[valid], bs, v_scale16)
+    _store_sym(cache.k_codes, cache.k_scales, cache.k_fmt, k16[valid], slots[valid], bs, k_scale16, rot=cache.rot_k)
+    _store_sym(cache.v_codes, cache.v_scales, cache.v_fmt, v16[valid], slots[valid], bs, v_scale16, rot=cache.rot_v)
 
 
 def _dequant_rows(cache: OracleCache, which: str, blk, off):
@@ -463,7 +534,9 @@ def _dequant_rows(cache: OracleCache, which: str, blk, off):
         codes = raw
     else:
         codes = raw.view(np.int8)
-    return dequant_sym(codes, scales_buf[blk, off], fmt)
+    rows = dequant_sym(codes, scales_buf[blk, off], fmt)
+    rot = cache.rot_k if which == "k" else cache.rot_v
+    return rows if rot is None else unrotate_rows(rows, rot)
 
 
 def token_live(cache: OracleCache, block_table_row, L: int) -> np.ndarray:
@@ -507,17 +580,25 @@ def gather_dequant(cache: OracleCache, block_table_row, L: int, seq: int):
     return K, V
 
 
-def dequantized_sequence(k16: np.ndarray, v16: np.ndarray, k_fmt: str, v_fmt: str, block_size: int = 32):
+def dequantized_sequence(k16: np.ndarray, v16: np.ndarray, k_fmt: str, v_fmt: str, block_size: int = 32,
+                         rot_k=None, rot_v=None):
     """K_hat, V_hat (L, H, D) float64 of one sequence written whole, without
     paging: what gather_dequant returns for a sequence written in position
     order.  KIVI keys: complete 32-token groups quantized per channel, the
-    last L mod 32 tokens (keys and values) kept in fp16."""
+    last L mod 32 tokens (keys and values) kept in fp16.  rot_k / rot_v:
+    rotated rows (quantized after rotate_rows, returned unrotated)."""
     L = k16.shape[0]
-    codes, s = quantize_sym(v16, v_fmt)
-    V = dequant_sym(codes, s, v_fmt)
+
+    def sym(x16, fmt, rot):
+        x = x16 if rot is None else rotate_rows(x16, rot)
+        codes, s = quantize_sym(x, fmt)
+        r = dequant_sym(codes, s, fmt)
+        return r if rot is None else unrotate_rows(r, rot)
+
+    V = sym(v16, v_fmt, rot_v)
     if k_fmt != INT4_KIVI:
-        codes, s = quantize_sym(k16, k_fmt)
-        return dequant_sym(codes, s, k_fmt), V
+        return sym(k16, k_fmt, rot_k), V
+    assert rot_k is None
     nfull = (L // KIVI_GROUP) * KIVI_GROUP
     K = np.empty(k16.shape, np.float64)
     for p in range(nfull // KIVI_GROUP):

@@ -198,3 +198,30 @@ def test_routing_mistakes_fail():
     assert _fails(pins.check_multi_sequence_routing, o.write, _decode_table_row_0)
     assert _fails(pins.check_multi_sequence_routing, _write_ignoring_seq_idx, o.decode_attn)
     pins.check_multi_sequence_routing()
+
+
+def test_rotation_mistakes_fail():
+    # Walsh-Hadamard rotation: signs dropped, the 1/D of the inverse dropped,
+    # the query's signs applied after H instead of before, a non-Sylvester
+    # block order.
+    def rot_no_signs(x16, bits):
+        D = x16.shape[-1]
+        return (x16.astype(np.float64) @ o.hadamard(D).T.astype(np.float64)).astype(np.float32)
+
+    def unrot_no_div(y, bits):
+        return o.unrotate_rows(y, bits) * y.shape[-1]
+
+    def rotq_signs_after(q16, bits):
+        D = q16.shape[-1]
+        return (q16.astype(np.float64) @ o.hadamard(D).T.astype(np.float64)) * o.sign_vector(bits, D) / D
+
+    def hadamard_wrong(D):
+        H = np.ones((1, 1), np.int64)
+        while H.shape[0] < D:
+            H = np.block([[H, H], [-H, H]])
+        return H
+
+    assert _fails(pins.check_rotation_exact, rot_no_signs)
+    assert _fails(pins.check_rotation_round_trip, o.rotate_rows, unrot_no_div)
+    assert _fails(pins.check_rotated_cache_attention, rotq_signs_after)
+    assert _fails(pins.check_hadamard, hadamard_wrong)

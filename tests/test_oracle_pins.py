@@ -756,3 +756,150 @@ def test_offload_round_trip_leaves_attention_unchanged(kf, vf):
     t2 = table.copy()
     t2[0, 0], t2[0, 2], t2[1, 1], t2[1, 0] = new
     assert np.array_equal(o.decode_attn(c, q, t2, ctx), before)
+
+
+# --------------------------------------------------------------------------
+# Walsh-Hadamard rotation
+# --------------------------------------------------------------------------
+
+
+def _signs(D, seed):
+    rng = np.random.default_rng(seed)
+    bits = np.zeros(8, np.uint32)
+    for c in np.nonzero(rng.integers(0, 2, D))[0]:
+        bits[c // 32] |= np.uint32(1) << np.uint32(c % 32)
+    return bits
+
+
+def check_hadamard(hadamard=o.hadamard):
+    import scipy.linalg
+    for D in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        H = hadamard(D)
+        assert np.array_equal(H, scipy.linalg.hadamard(D))  # the library's Sylvester matrix
+        assert np.array_equal(H @ H.T, D * np.eye(D, dtype=np.int64))
+    # entry (i, j) is (-1)^popcount(i & j)
+    H = hadamard(64)
+    i, j = np.meshgrid(np.arange(64), np.arange(64), indexing="ij")
+    pc = np.vectorize(lambda x: bin(int(x)).count("1"))(i & j)
+    assert np.array_equal(H, np.where(pc % 2 == 1, -1, 1))
+
+
+def test_hadamard():
+    check_hadamard()
+
+
+def check_rotation_exact(rotate_rows=o.rotate_rows):
+    # y = H (sigma * x) rounded once to fp32, against exact rational
+    # arithmetic on the fp16 inputs (spread over the whole fp16 range, so an
+    # fp32 running sum would round).
+    from fractions import Fraction
+    rng = np.random.default_rng(60)
+    D = 32
+    bits = _signs(D, 61)
+    sig = o.sign_vector(bits, D)
+    x = (rng.standard_normal((6, D)) * np.exp2(rng.integers(-20, 15, (6, D)))).astype(np.float16)
+    x[0, :3] = [65504, -6e-8, 1e-7]
+    y = rotate_rows(x, bits)
+    assert y.dtype == np.float32
+    H = scipy_hadamard(D)
+    for r in range(x.shape[0]):
+        for i in range(D):
+            exact = sum(Fraction(float(x[r, c])) * int(sig[c]) * int(H[i, c]) for c in range(D))
+            assert y[r, i] == np.float32(float(exact)), (r, i)
+
+
+def scipy_hadamard(D):
+    import scipy.linalg
+    return scipy.linalg.hadamard(D)
+
+
+def test_rotation_exact():
+    check_rotation_exact()
+
+
+def check_rotation_round_trip(rotate_rows=o.rotate_rows, unrotate_rows=o.unrotate_rows):
+    # Rotating back gives the row (the fp32 rounding of y aside), and the
+    # quantization error of a rotated INT8/INT4 row, measured after the
+    # inverse rotation, obeys the closed form ||x - x_hat||_2 <= sqrt(sum_g
+    # n_g (s_g/2)^2) / sqrt(D) (the rotation is orthogonal up to sqrt(D)).
+    rng = np.random.default_rng(62)
+    for D in (64, 128, 256):
+        bits = _signs(D, D)
+        x = rng.standard_normal((500, D)).astype(np.float16)
+        x[:, :4] *= 20
+        back = unrotate_rows(rotate_rows(x, bits), bits)
+        assert np.max(np.abs(back - x.astype(np.float64))) <= 1e-4 * np.max(np.abs(x.astype(np.float64)))
+        for fmt in (o.INT8, o.INT4_G32):
+            y = rotate_rows(x, bits)
+            codes, s16 = o.quantize_sym(y, fmt)
+            xh = unrotate_rows(o.dequant_sym(codes, s16, fmt), bits)
+            g = 32 if fmt == o.INT4_G32 else D
+            bound = np.sqrt(np.sum(g * (s16.astype(np.float64) / 2) ** 2, axis=-1)) / np.sqrt(D)
+            err = np.sqrt(np.sum((xh - x.astype(np.float64)) ** 2, axis=-1))
+            # + the fp32 rounding of y, carried back through the rotation
+            assert np.all(err <= bound * (1 + 1e-6) + 1e-5 * np.max(np.abs(x.astype(np.float64)))), fmt
+
+
+def test_rotation_round_trip():
+    check_rotation_round_trip()
+
+
+def test_rotation_spreads_outlier_channels():
+    # The reason for the rotation: rows with a few large channels quantize
+    # to INT4 with a much smaller error once rotated (the largest element
+    # shrinks relative to the row's norm).
+    rng = np.random.default_rng(63)
+    D = 128
+    bits = _signs(D, 64)
+    x = rng.standard_normal((2000, D)).astype(np.float32)
+    x[:, [3, 40, 77, 101]] *= 20
+    x16 = x.astype(np.float16)
+    c, s = o.quantize_sym(x16, o.INT4_G32)
+    plain = np.mean((o.dequant_sym(c, s, o.INT4_G32) - x16.astype(np.float64)) ** 2)
+    y = o.rotate_rows(x16, bits)
+    c, s = o.quantize_sym(y, o.INT4_G32)
+    rot = np.mean((o.unrotate_rows(o.dequant_sym(c, s, o.INT4_G32), bits) - x16.astype(np.float64)) ** 2)
+    assert rot < 0.5 * plain, (rot, plain)
+
+
+def check_rotated_cache_attention(rotate_query=o.rotate_query):
+    # A cache written with rotated keys and values: decode equals fp64
+    # attention over the stored rows brought back with the library Hadamard
+    # matrix (x_hat = sigma * (H y_hat) / D), and also equals attention of the
+    # rotated query q' = H (sigma * q) / D against the stored keys directly,
+    # with the values brought back after the weighted sum.
+    for kf, vf in ((o.INT8, o.INT4_G32), (o.FP8_E4M3FN, o.FP8_E5M2)):
+        bs, H, D, Hq = 16, 2, 64, 4
+        ctx = [70, 33]
+        nb, table, ks, vs, slots = _three_sequences(kf, vf, ctx, bs, H, D, seed=65)
+        rk, rv = _signs(D, 66), _signs(D, 67)
+        c = o.OracleCache(nb, bs, H, D, kf, vf, max_seqs=2, rot_k=rk, rot_v=rv)
+        o.write(c, np.concatenate(ks), np.concatenate(vs), np.concatenate(slots))
+        q = np.random.default_rng(68).standard_normal((2, Hq, D)).astype(np.float16)
+        got = o.decode_attn(c, q, table, ctx)
+        Hm = scipy_hadamard(D).astype(np.float64)
+        sk, sv = o.sign_vector(rk, D), o.sign_vector(rv, D)
+        for b, L in enumerate(ctx):
+            t = np.arange(L)
+            blk, off = table[b, t // bs], t % bs
+            def raw(which):
+                fmt = kf if which == "k" else vf
+                buf = c.k_codes if which == "k" else c.v_codes
+                sc = c.k_scales if which == "k" else c.v_scales
+                r = buf[blk, off]
+                cd = o.unpack_int4(r, True) if fmt == o.INT4_G32 else (r if fmt in o.FP8_FORMATS else r.view(np.int8))
+                return o.dequant_sym(cd, sc[blk, off], fmt)
+            Yk, Yv = raw("k"), raw("v")
+            K = (Yk @ Hm.T) * sk / D
+            V = (Yv @ Hm.T) * sv / D
+            ref = o.attention_fp64(q[b].astype(np.float64), K, V)
+            assert np.max(np.abs(got[b] - ref)) <= 1e-10
+            # rotated-query form: scores against the stored keys, values rotated back at the end
+            qr = rotate_query(q[b], rk)
+            acc = o.attention_fp64(qr, Yk, Yv)
+            ref2 = (acc @ Hm.T) * sv / D
+            assert np.max(np.abs(got[b] - ref2)) <= 1e-10
+
+
+def test_rotated_cache_attention():
+    check_rotated_cache_attention()
