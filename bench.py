@@ -291,14 +291,16 @@ def measure(w, args, steps, warmup, dev="cuda", want_inputs=False):
     import quantized_paged_kv_write_amd as kvq
     from quantized_paged_kv_write_amd import workloads as wl
 
-    seed = wl.ORDER.index(w.name) + 1
+    seed = wl.seed_of(w)
     print(f"[bench] workload {w.name}: B={w.batch} Hq={w.n_q_heads} H={w.n_kv_heads} D={w.head_dim} "
           f"bs={w.block_size} K={w.k_dtype} V={w.v_dtype}", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, seed, dev)
     ctx = inp.ctx_lens
     B = w.batch
+    signs = wl.rotation_signs(w.head_dim, seed) if (w.rotate_k or w.rotate_v) else None
     caches = [kvq.PagedKVCache(inp.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, w.k_dtype, w.v_dtype,
-                               max_seqs=B, device=dev) for _ in range(args.caches)]
+                               max_seqs=B, device=dev, rotate_k=w.rotate_k, rotate_v=w.rotate_v, rot_signs=signs)
+              for _ in range(args.caches)]
     cache = caches[0]
     pos = inp.positions
     last = torch.tensor([inp.seq_start[b] + ctx[b] - 1 for b in range(B)])
@@ -411,6 +413,7 @@ def measure(w, args, steps, warmup, dev="cuda", want_inputs=False):
         else f"ragged {min(ctx)}..{max(ctx)} (mean {sum(ctx) / len(ctx):.0f})",
         "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
         "block_size": w.block_size, "k_format": w.k_dtype, "v_format": w.v_dtype,
+        "rotated": {"k": w.rotate_k, "v": w.rotate_v},
         "decode_bytes_per_step": dbytes,
         "ms_per_step": round(ms_per_step, 4),
         "step_GBps": round(dbytes / (ms_per_step * 1e6), 2),
@@ -456,7 +459,7 @@ def offload_measure(args, dev="cuda"):
     P = args.offload_pages
     B = w.batch
     n_off = B * P
-    inp = wl.make_inputs(w, wl.ORDER.index(w.name) + 1, dev)
+    inp = wl.make_inputs(w, wl.seed_of(w), dev)
     print(f"[bench] offload: {w.name}, {P} pages of every sequence ({n_off} pages) prefetched per step",
           file=sys.stderr, flush=True)
     # the two staging sets are contiguous runs of blocks after the workload's
@@ -589,7 +592,7 @@ def offload_measure(args, dev="cuda"):
     return res
 
 
-EXTRA_DEFAULT = "llama3_8b_int8k_int4v,llama3_70b_int8,llama3_8b_kivi_int4"
+EXTRA_DEFAULT = "llama3_8b_int8k_int4v,llama3_70b_int8,llama3_8b_kivi_int4,llama3_70b_int8_rot"
 
 
 def main():

@@ -131,7 +131,7 @@ typedef struct kvq_cache {
   int32_t k_dtype; /* kvq_dtype */
   int32_t v_dtype; /* kvq_dtype */
   int32_t max_seqs;
-  int32_t reserved;
+  uint32_t flags;  /* kvq_cache_flags */
   void* k_codes;
   void* v_codes;
   void* k_scales;
@@ -139,7 +139,29 @@ typedef struct kvq_cache {
   void* k_zeros;
   void* k_tail;
   void* v_tail;
+  /* Random signs of the Walsh-Hadamard rotation (KVQ_ROTATE_K / _V): bit c
+   * (bit c % 32 of word c / 32) set means channel c is negated.  The same
+   * signs serve keys and values; unused without a rotation flag. */
+  uint32_t rot_signs[8];
 } kvq_cache;
+
+/* kvq_cache.flags.  Walsh-Hadamard rotation ([P3] Numerical Formats: QuaRot's
+ * randomized orthogonal Walsh-Hadamard transforms spread outlier channels
+ * before 4-bit quantization; Accuracy, Latency, and Serving Economics: INT4
+ * with Hadamard rotations keeps baseline quality).  A rotated tensor stores,
+ * for each (token, head) row x, the row y = H (sigma * x) -- H the Sylvester
+ * Hadamard matrix of order head_dim (entries +-1), sigma the signs of
+ * rot_signs -- with every entry computed exactly and rounded once to fp32,
+ * then quantized like an ordinary row (its scale absorbs the factor
+ * sqrt(head_dim)).  Decode attends to x_hat = sigma * (H y_hat) / head_dim:
+ * for rotated keys it scores the rotated query H (sigma * q) / head_dim
+ * against the stored rows; for rotated values it rotates the weighted sum
+ * back.  Symmetric formats only (KIVI keys: KVQ_ERR_UNSUPPORTED); KIVI fp16
+ * tails keep the original rows. */
+typedef enum kvq_cache_flags {
+  KVQ_ROTATE_K = 1,
+  KVQ_ROTATE_V = 2
+} kvq_cache_flags;
 
 /* Quantize-on-write ([P1] 2.1-2.2, [P2] 5 "Where the scales live").
  *   k, v          fp16 (num_tokens, H, D), row-major; read only.

@@ -35,11 +35,15 @@ class KvqCacheStruct(ctypes.Structure):
         ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
         ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("k_dtype", ctypes.c_int32), ("v_dtype", ctypes.c_int32),
-        ("max_seqs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("max_seqs", ctypes.c_int32), ("flags", ctypes.c_uint32),
         ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
         ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
         ("k_zeros", ctypes.c_void_p), ("k_tail", ctypes.c_void_p), ("v_tail", ctypes.c_void_p),
+        ("rot_signs", ctypes.c_uint32 * 8),
     ]
+
+
+ROTATE_K, ROTATE_V = 1, 2  # kvq_cache_flags
 
 
 class KvqError(RuntimeError):
@@ -111,10 +115,17 @@ class PagedKVCache:
     the layouts of include/kvq.h (codes uint8, scales/zeros/tails fp16)."""
 
     def __init__(self, num_blocks, block_size, n_kv_heads, head_dim, k_dtype, v_dtype, max_seqs=0,
-                 device="cuda", pin_memory=False):
+                 device="cuda", pin_memory=False, rotate_k=False, rotate_v=False, rot_signs=None):
+        """rotate_k / rotate_v: Walsh-Hadamard rotation of keys / values with
+        the signs rot_signs (8 uint32 words: bit c set negates channel c)."""
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
         self.n_kv_heads, self.head_dim = int(n_kv_heads), int(head_dim)
         self.k_dtype, self.v_dtype, self.max_seqs = k_dtype, v_dtype, int(max_seqs)
+        self.flags = (ROTATE_K if rotate_k else 0) | (ROTATE_V if rotate_v else 0)
+        words = [0] * 8 if rot_signs is None else [int(x) & 0xFFFFFFFF for x in rot_signs]
+        if len(words) != 8:
+            raise ValueError("rot_signs must hold 8 uint32 words")
+        self.rot_signs = words
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
             dev = torch.device("cuda", torch.cuda.current_device())
@@ -141,9 +152,9 @@ class PagedKVCache:
     def struct(self) -> KvqCacheStruct:
         return KvqCacheStruct(
             self.num_blocks, self.block_size, self.n_kv_heads, self.head_dim,
-            DTYPES[self.k_dtype], DTYPES[self.v_dtype], self.max_seqs, 0,
+            DTYPES[self.k_dtype], DTYPES[self.v_dtype], self.max_seqs, self.flags,
             _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scales), _ptr(self.v_scales),
-            _ptr(self.k_zeros), _ptr(self.k_tail), _ptr(self.v_tail))
+            _ptr(self.k_zeros), _ptr(self.k_tail), _ptr(self.v_tail), (ctypes.c_uint32 * 8)(*self.rot_signs))
 
     def buffers(self) -> dict:
         out = {"k_codes": self.k_codes, "v_codes": self.v_codes, "k_scales": self.k_scales,

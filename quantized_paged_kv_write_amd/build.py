@@ -29,6 +29,9 @@ SOURCES = {
     "kvq_decode_kfp8.hip": [],
     "kvq_decode_kkivi.hip": [],
     "kvq_decode_ke5m2.hip": [],
+    "kvq_decode_kint8_rot.hip": [],
+    "kvq_decode_kfp8_rot.hip": [],
+    "kvq_decode_ke5m2_rot.hip": [],
     "kvq_offload.hip": [],
 }
 

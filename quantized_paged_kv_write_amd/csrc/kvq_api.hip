@@ -82,6 +82,8 @@ int check_cache(const kvq_cache* c) {
     if (c->max_seqs <= 0) return KVQ_ERR_SHAPE;
     if (!c->k_zeros || !c->k_tail || !c->v_tail) return KVQ_ERR_INVALID_ARG;
   }
+  if (c->flags & ~(uint32_t)(KVQ_ROTATE_K | KVQ_ROTATE_V)) return KVQ_ERR_INVALID_ARG;
+  if ((c->flags & KVQ_ROTATE_K) && c->k_dtype == KVQ_INT4_KIVI) return KVQ_ERR_UNSUPPORTED;  // per-channel keys
   return KVQ_OK;
 }
 
@@ -154,6 +156,9 @@ int write_impl(const kvq_cache* cache, const void* k, const void* v, const int64
   // KIVI seal waves: one per call token for small calls (decode steps), one
   // per 32 tokens otherwise
   a.seal_chunk = num_tokens <= 2048 ? 1 : 32;
+  a.rot_k = (cache->flags & KVQ_ROTATE_K) ? 1 : 0;
+  a.rot_v = (cache->flags & KVQ_ROTATE_V) ? 1 : 0;
+  for (int i = 0; i < 8; ++i) a.rot_signs[i] = cache->rot_signs[i];
   return launch_write(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
@@ -245,6 +250,10 @@ int decode_impl(const kvq_cache* cache, const void* q, const int32_t* block_tabl
   a.plan = static_cast<int32_t*>(workspace);
   a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.plan_bytes);
   a.out = static_cast<uint16_t*>(out);
+  a.rot_k = (cache->flags & KVQ_ROTATE_K) ? 1 : 0;
+  a.rot_v = (cache->flags & KVQ_ROTATE_V) ? 1 : 0;
+  for (int i = 0; i < 8; ++i) a.rot_signs[i] = cache->rot_signs[i];
+  a.qrot = a.rot_k ? reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + p.qrot_offset) : nullptr;
   return launch_decode(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

@@ -574,7 +574,12 @@ __device__ __forceinline__ int load_ids(const DecodeArgs& a, const SeqCursor& c,
 // c NW .. c NW + NW - 1.  They run on one compute unit and read neighbouring
 // segments of the same token rows at about the same time; each has its own
 // LDS (dynamic, NW Stage::WAVE_LDS bytes) and they never synchronize.
-template <int FK, int FV, int D, int HPC, bool OP>
+//
+// ROTQ (keys stored Walsh-Hadamard rotated): the query operand is the rotated
+// query q' = H (sigma q) / D, which is not an fp16 value: it is read as fp16
+// hi + lo (a pre-pass writes both to the workspace) and every key k-block
+// takes two MFMAs, so the products stay exact and q' keeps fp32 accuracy.
+template <int FK, int FV, int D, int HPC, bool OP, bool ROTQ>
 __global__ __launch_bounds__((256 * Stage<FK, FV, D>::WPE))
 __attribute__((amdgpu_waves_per_eu(Stage<FK, FV, D>::WPE, Stage<FK, FV, D>::WPE)))
 void decode_split_kernel(DecodeArgs a) {
@@ -688,6 +693,7 @@ void decode_split_kernel(DecodeArgs a) {
   // piece: lane (j, n) holds query head n's channels of k-slots 8j..8j+7 in
   // the key operand's channel order.
   h8 qop[KS::KB];
+  h8 qlo_r[ROTQ ? KS::KB : 1];  // rotated keys: the low half of the rotated query
   bool piece_start = true;
   // KIVI: q * s of the current page (fp16 hi + lo) and q . z, column n's head
   h8 qhi[FK == F_KIVI ? KS::KB : 1], qlo[FK == F_KIVI ? KS::KB : 1];
@@ -798,13 +804,24 @@ void decode_split_kernel(DecodeArgs a) {
     // ---- first tile of a sequence's piece: its query operand ---------------
     const bool new_piece = piece_start;
     if (piece_start) {
-      const uint16_t* qrow = a.q + ((size_t)cc.b * a.Hq + hq0 + (n < NC ? n : 0)) * D;
+      const uint16_t* qrow = (ROTQ ? a.qrot : a.q) + ((size_t)cc.b * a.Hq + hq0 + (n < NC ? n : 0)) * D;
 #pragma unroll
       for (int kb = 0; kb < KS::KB; ++kb) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint16_t bits = qrow[key_channel<FK, D>(j, kb, e)];
           qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < NC ? bits : 0));
+        }
+      }
+      if constexpr (ROTQ) {
+        const uint16_t* qlo = qrow + (size_t)a.B * a.Hq * D;
+#pragma unroll
+        for (int kb = 0; kb < KS::KB; ++kb) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t bits = qlo[key_channel<FK, D>(j, kb, e)];
+            qlo_r[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < NC ? bits : 0));
+          }
         }
       }
       piece_start = false;
@@ -928,6 +945,9 @@ void decode_split_kernel(DecodeArgs a) {
         if constexpr (FK == F_KIVI) {
           sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qhi[kb], sc[u], 0, 0, 0);
           sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qlo[kb], sc[u], 0, 0, 0);
+        } else if constexpr (ROTQ) {
+          sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kb], sc[u], 0, 0, 0);
+          sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qlo_r[kb], sc[u], 0, 0, 0);
         } else {
           sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kb], sc[u], 0, 0, 0);
         }
@@ -1188,6 +1208,9 @@ __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
     __syncthreads();
     tm = s_tail[0];
   }
+  float tailv[CPL];  // rotated values: the KIVI tail's weighted values (wave 0)
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) tailv[c] = 0.f;
   float M = tm;
   for (int i = tid; i < nrec; i += MERGE_WAVES * 64) M = fmaxf(M, rec(i)[0]);
 #pragma unroll
@@ -1213,8 +1236,14 @@ __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
     if (KIVI && w == 0 && tm != -INFINITY) {
       const float wgt = exp2f(tm - M);
       l = __builtin_fmaf(s_tail[1], wgt, l);
+      // the tail holds the original (unrotated) values: with rotated values
+      // it joins after the pages' sum is rotated back
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(s_tail[2 + lane * CPL + c], wgt, accv[c]);
+      for (int c = 0; c < CPL; ++c) {
+        const float t = s_tail[2 + lane * CPL + c] * wgt;
+        if (a.rot_v) tailv[c] = t;
+        else accv[c] += t;
+      }
     }
   }
 #pragma unroll
@@ -1227,13 +1256,46 @@ __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   for (int i = 0; i < MERGE_WAVES; ++i) lt += s_acc[i][D];
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   uint16_t* o = a.out + (size_t)bh * D;
+  float v[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    float v = 0.f;
+    v[c] = 0.f;
 #pragma unroll
-    for (int i = 0; i < MERGE_WAVES; ++i) v += s_acc[i][lane * CPL + c];
-    o[lane * CPL + c] = (uint16_t)f2h_bits(v * inv);
+    for (int i = 0; i < MERGE_WAVES; ++i) v[c] += s_acc[i][lane * CPL + c];
   }
+  if (a.rot_v) {
+    // values stored rotated (y = H (sigma x)): the weighted sum of the stored
+    // rows is rotated back, x = sigma (H y) / D, in fp32.  Channel c = lane
+    // CPL + i: its low bits are inside the lane, the lane bits above them.
+#pragma unroll
+    for (int s = 1; s < CPL; s <<= 1) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        if (i & s) continue;
+        const float x0 = v[i], x1 = v[i + s];
+        v[i] = x0 + x1;
+        v[i + s] = x0 - x1;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const float p = __shfl_xor(v[i], m);
+        v[i] = (lane & m) ? p - v[i] : v[i] + p;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane * CPL + i;
+      uint32_t wd = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) wd = (c >> 5) == k ? a.rot_signs[k] : wd;
+      v[i] = (((wd >> (c & 31)) & 1) ? -v[i] : v[i]) * (1.0f / D) + tailv[i];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) o[lane * CPL + c] = (uint16_t)f2h_bits(v[c] * inv);
 }
 
 // The partition of one call: tiles per sequence, their prefix sums, the
@@ -1316,7 +1378,7 @@ namespace {
 // or the occupancy if lower.  Every wave gets the same work, so a SIMD
 // holding more waves than the others would hold the whole launch back.
 // Cached per device and nw.
-template <int FK, int FV, int D, int HPC, bool OP>
+template <int FK, int FV, int D, int HPC, bool OP, bool ROTQ>
 int resident_waves(int nw) {
   constexpr int MAXW = 4 * Stage<FK, FV, D>::WPE;
   static std::atomic<int> cache[64][MAXW + 1];
@@ -1327,7 +1389,7 @@ int resident_waves(int nw) {
     if (c > 0) return c;
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D, HPC, OP>, 64 * nw,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<FK, FV, D, HPC, OP, ROTQ>, 64 * nw,
                                                    (size_t)nw * Stage<FK, FV, D>::WAVE_LDS) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
@@ -1336,7 +1398,7 @@ int resident_waves(int nw) {
   return w;
 }
 
-template <int FK, int FV, int D, int HPC, bool OP>
+template <int FK, int FV, int D, int HPC, bool OP, bool ROTQ>
 hipError_t launch4(DecodeArgs a, hipStream_t st) {
   // Waves per workgroup: the largest divisor of the share's head groups that
   // fits on one compute unit (4 WPE waves).  Putting a share's head groups
@@ -1347,7 +1409,7 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
   while (groups % nw) --nw;
   if (a.share_tiles <= 0) {
     // balanced: all waves the same length, all resident at once
-    const int w = resident_waves<FK, FV, D, HPC, OP>(nw);
+    const int w = resident_waves<FK, FV, D, HPC, OP, ROTQ>(nw);
     if (w <= 0) return hipErrorInvalidDevice;
     a.num_shares = min(a.max_shares, max(1, w / (a.H >> a.hp_log2)));
   } else {
@@ -1365,7 +1427,7 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
   // decode_split_kernel for the order
   const uint32_t wgs = (((uint32_t)a.num_shares + 7) / 8) * 8 * (uint32_t)(groups / nw);
   const size_t lds = (size_t)nw * Stage<FK, FV, D>::WAVE_LDS;
-  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D, HPC, OP>), dim3(wgs), dim3(64 * nw), lds, st, a);
+  hipLaunchKernelGGL((decode_split_kernel<FK, FV, D, HPC, OP, ROTQ>), dim3(wgs), dim3(64 * nw), lds, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.B * a.Hq < 512)
@@ -1375,7 +1437,7 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int FK, int FV, int D>
+template <int FK, int FV, int D, bool ROTQ>
 hipError_t launch3(const DecodeArgs& a, hipStream_t st) {
   constexpr bool OP_PAYS = FV == F_INT4 || FK == F_KIVI;
   switch (a.hp_log2) {
@@ -1384,32 +1446,36 @@ hipError_t launch3(const DecodeArgs& a, hipStream_t st) {
     // path saves about a sixth of the VALU work per tile, which pays where
     // that work bounds the kernel (4-bit values, KIVI keys); with 8-bit keys
     // and values it measured 1-2% slower, so those keep the general path.
-    case 0: return OP_PAYS && a.bs >= 32 ? launch4<FK, FV, D, 1, OP_PAYS>(a, st) : launch4<FK, FV, D, 1, false>(a, st);
-    case 1: return OP_PAYS && a.bs >= 16 ? launch4<FK, FV, D, 2, OP_PAYS>(a, st) : launch4<FK, FV, D, 2, false>(a, st);
-    case 2: return launch4<FK, FV, D, 4, OP_PAYS>(a, st);
+    case 0:
+      return OP_PAYS && a.bs >= 32 ? launch4<FK, FV, D, 1, OP_PAYS, ROTQ>(a, st)
+                                   : launch4<FK, FV, D, 1, false, ROTQ>(a, st);
+    case 1:
+      return OP_PAYS && a.bs >= 16 ? launch4<FK, FV, D, 2, OP_PAYS, ROTQ>(a, st)
+                                   : launch4<FK, FV, D, 2, false, ROTQ>(a, st);
+    case 2: return launch4<FK, FV, D, 4, OP_PAYS, ROTQ>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <int FK, int FV>
+template <int FK, int FV, bool ROTQ>
 hipError_t by_dim(int D, const DecodeArgs& a, hipStream_t s) {
   switch (D) {
-    case 64: return launch3<FK, FV, 64>(a, s);
-    case 128: return launch3<FK, FV, 128>(a, s);
-    case 256: return launch3<FK, FV, 256>(a, s);
+    case 64: return launch3<FK, FV, 64, ROTQ>(a, s);
+    case 128: return launch3<FK, FV, 128, ROTQ>(a, s);
+    case 256: return launch3<FK, FV, 256, ROTQ>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 // Decode launch for key format FK and any value format (one instantiation
 // per translation unit kvq_decode_k*.hip).
-template <int FK>
+template <int FK, bool ROTQ>
 hipError_t decode_for_keys(int fv, int D, const DecodeArgs& a, hipStream_t s) {
   switch (fv) {
-    case F_INT8: return by_dim<FK, F_INT8>(D, a, s);
-    case F_FP8: return by_dim<FK, F_FP8>(D, a, s);
-    case F_INT4: return by_dim<FK, F_INT4>(D, a, s);
-    case F_E5M2: return by_dim<FK, F_E5M2>(D, a, s);
+    case F_INT8: return by_dim<FK, F_INT8, ROTQ>(D, a, s);
+    case F_FP8: return by_dim<FK, F_FP8, ROTQ>(D, a, s);
+    case F_INT4: return by_dim<FK, F_INT4, ROTQ>(D, a, s);
+    case F_E5M2: return by_dim<FK, F_E5M2, ROTQ>(D, a, s);
   }
   return hipErrorInvalidValue;
 }

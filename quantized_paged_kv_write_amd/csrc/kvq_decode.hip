@@ -39,11 +39,92 @@ bool plan_decode(const kvq_cache& c, int32_t batch, int32_t n_q_heads, int32_t m
   const size_t ints = 2 + (size_t)batch + (size_t)shares;
   p->plan_bytes = (ints * sizeof(int32_t) + 255) / 256 * 256;
   p->records = (size_t)shares + batch;
-  p->bytes = p->plan_bytes + p->records * n_q_heads * ((size_t)c.head_dim + 2) * sizeof(float);
+  const size_t end = p->plan_bytes + p->records * n_q_heads * ((size_t)c.head_dim + 2) * sizeof(float);
+  p->qrot_offset = (end + 255) / 256 * 256;
+  // rotated keys: the rotated query, fp16 hi and lo (B, Hq, D) each
+  p->bytes = (c.flags & KVQ_ROTATE_K) ? p->qrot_offset + 2 * (size_t)batch * n_q_heads * c.head_dim * 2 : end;
   return true;
 }
 
+namespace {
+
+// The rotated query of rotated keys ("Quantized KV caches in production",
+// Numerical Formats: Walsh-Hadamard rotation): q' = H (sigma q) / D for every
+// (sequence, query head), written as fp16 hi = RN(q') and lo = RN(q' - hi).
+// One wave per row; lane l holds channels l CPL .. l CPL + CPL - 1.  The
+// transform runs in float64 and is exact (sums of at most 256 fp16 values);
+// 1/D is a power of two.
+template <int D>
+__global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
+  constexpr int CPL = D / 64;
+  const int lane = (int)threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t rows = (size_t)a.B * a.Hq;
+  if (row >= rows) return;  // uniform over the wave
+  const uint16_t* qr = a.q + row * D;
+  double y[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane * CPL + i;
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w = (c >> 5) == k ? a.rot_signs[k] : w;
+    const double x = (double)h2f(qr[c]);
+    y[i] = ((w >> (c & 31)) & 1) ? -x : x;
+  }
+#pragma unroll
+  for (int s = 1; s < CPL; s <<= 1) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      if (i & s) continue;
+      const double u = y[i], v = y[i + s];
+      y[i] = u + v;
+      y[i + s] = u - v;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const double p = __shfl_xor(y[i], m);
+      y[i] = (lane & m) ? p - y[i] : y[i] + p;
+    }
+  }
+  uint16_t* hi = a.qrot + row * D;
+  uint16_t* lo = a.qrot + rows * D + row * D;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const double qp = y[i] * (1.0 / D);
+    const uint32_t h = f2h_bits((float)qp);
+    hi[lane * CPL + i] = (uint16_t)h;
+    lo[lane * CPL + i] = (uint16_t)f2h_bits((float)(qp - (double)h2f(h)));
+  }
+}
+
+hipError_t rotate_query(const kvq_cache& c, const DecodeArgs& a, hipStream_t s) {
+  const unsigned blocks = (unsigned)(((size_t)a.B * a.Hq + 3) / 4);
+  switch (c.head_dim) {
+    case 64: hipLaunchKernelGGL(rotate_q_kernel<64>, dim3(blocks), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(rotate_q_kernel<128>, dim3(blocks), dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(rotate_q_kernel<256>, dim3(blocks), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_decode(const kvq_cache& c, const DecodeArgs& a, hipStream_t s) {
+  if (a.rot_k) {
+    const hipError_t e = rotate_query(c, a, s);
+    if (e != hipSuccess) return e;
+    switch (c.k_dtype) {
+      case F_INT8: return decode_keys_int8_rot(c.v_dtype, c.head_dim, a, s);
+      case F_FP8: return decode_keys_fp8_rot(c.v_dtype, c.head_dim, a, s);
+      case F_E5M2: return decode_keys_e5m2_rot(c.v_dtype, c.head_dim, a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (c.k_dtype) {
     case F_INT8: return decode_keys_int8(c.v_dtype, c.head_dim, a, s);
     case F_FP8: return decode_keys_fp8(c.v_dtype, c.head_dim, a, s);

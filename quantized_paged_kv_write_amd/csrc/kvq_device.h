@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/kvq.h"
 
 namespace kvq {
@@ -24,6 +26,19 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
 // fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 in the default mode).
 __device__ __forceinline__ uint32_t f2h_bits(float x) {
   return (uint32_t)__half_as_ushort(__float2half_rn(x));
+}
+
+// fp16 bits of an fp32 value computed just before, rounded twice as the
+// format requires: first to fp32 (the computation's own rounding), then to
+// fp16.  The empty asm pins the fp32 result in a register; without it the
+// compiler fuses a final FMA and the conversion into one mixed-precision FMA
+// with an fp16 result (v_fma_mixlo_f16), which rounds the exact value once,
+// straight to fp16 -- a different result whenever the fp32 value is an exact
+// fp16 tie (it happens for quotients of fp32 numerators, such as the rows of
+// a rotated cache).
+__device__ __forceinline__ uint32_t f2h_bits_of_f32(float x) {
+  asm volatile("" : "+v"(x));
+  return f2h_bits(x);
 }
 
 // Eight fp16 values packed in a uint4 -> fp32.
@@ -100,6 +115,53 @@ __device__ __forceinline__ float group_max(float v) {
 #pragma unroll
   for (int m = 16; m < N; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
+}
+
+// Exchange of a double with lane ^ M (M < 32) through ds_swizzle (bitmask
+// mode: and_mask 0x1F, xor_mask M).
+template <int M>
+__device__ __forceinline__ double swz_xor(double v) {
+  constexpr int pat = (M << 10) | 0x1F;
+  const int lo = __builtin_amdgcn_ds_swizzle(__double2loint(v), pat);
+  const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(v), pat);
+  return __hiloint2double(hi, lo);
+}
+
+// Walsh-Hadamard transform y = H (sigma * x) of one row spread over LPR
+// consecutive lanes (aligned, LPR <= 32), 8 channels per lane: lane l of the
+// row holds channels 8 l .. 8 l + 7.  H is the Sylvester matrix: for each
+// index bit, the pair (i, i + 2^k) with bit k of i clear becomes (x_i + x_j,
+// x_i - x_j).  Bits 0-2 of the channel are inside the lane, bits 3.. are the
+// lane bits.  Every partial sum is a sum of at most 256 fp16 values, exact in
+// float64, so the result is the exact transform; sbits: the lane's 8 sign
+// bits (bit j set negates channel 8 l + j).
+template <int LPR>
+__device__ __forceinline__ void fwht_row8(const float (&x)[8], uint32_t sbits, int lir, double (&y)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = (double)((sbits >> j) & 1 ? -x[j] : x[j]);
+#pragma unroll
+  for (int s = 1; s < 8; s <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j & s) continue;
+      const double a = y[j], b = y[j + s];
+      y[j] = a + b;
+      y[j + s] = a - b;
+    }
+  }
+  // lane bits: the lower lane of a pair keeps own + partner, the upper one
+  // partner - own
+  auto stage = [&](auto mconst) __attribute__((always_inline)) {
+    constexpr int M = decltype(mconst)::value;
+    const double sg = (lir & M) ? -1.0 : 1.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = __builtin_fma(y[j], sg, swz_xor<M>(y[j]));
+  };
+  if constexpr (LPR >= 2) stage(std::integral_constant<int, 1>{});
+  if constexpr (LPR >= 4) stage(std::integral_constant<int, 2>{});
+  if constexpr (LPR >= 8) stage(std::integral_constant<int, 4>{});
+  if constexpr (LPR >= 16) stage(std::integral_constant<int, 8>{});
+  if constexpr (LPR >= 32) stage(std::integral_constant<int, 16>{});
 }
 
 // Record a device-side data error: the lowest lane of the wave whose `bad`

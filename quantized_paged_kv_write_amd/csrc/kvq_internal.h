@@ -38,6 +38,9 @@ struct WriteArgs {
   const uint16_t* k_static;
   const uint16_t* v_static;
   uint32_t* err;  // per-device kvq_device_error word
+  // Walsh-Hadamard rotation of keys / values (kvq_cache_flags) and its signs
+  int32_t rot_k, rot_v;
+  uint32_t rot_signs[8];
 };
 
 struct DecodeArgs {
@@ -75,6 +78,13 @@ struct DecodeArgs {
   float* part;
   uint16_t* out;  // fp16 (B, Hq, D)
   uint32_t* err;  // per-device kvq_device_error word (checked by the merge kernel)
+  // Walsh-Hadamard rotation (kvq_cache_flags): rotated keys are scored
+  // against the rotated query q' = H (sigma q) / D, held in the workspace as
+  // fp16 hi (B, Hq, D) then lo (B, Hq, D) with hi + lo = q' (to fp32
+  // accuracy); rotated values are rotated back by the merge.
+  int32_t rot_k, rot_v;
+  uint32_t rot_signs[8];
+  uint16_t* qrot;
 };
 
 // Workspace layout of one decode call (host side, no device needed).
@@ -83,6 +93,7 @@ struct DecodePlan {
   int32_t max_shares;    // upper bound on the shares any launch of this call uses
   size_t plan_bytes;     // plan ints, rounded up to 256 bytes
   size_t records;        // partial records
+  size_t qrot_offset;    // rotated query (rotated keys only), 256-byte aligned
   size_t bytes;          // total workspace
 };
 // Returns false if the sizes overflow the ranges the kernels index with.
@@ -100,6 +111,10 @@ hipError_t decode_keys_int8(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_fp8(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_kivi(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_e5m2(int fv, int D, const DecodeArgs& a, hipStream_t s);
+// rotated keys (the query operand is the rotated query, fp16 hi + lo)
+hipError_t decode_keys_int8_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
+hipError_t decode_keys_fp8_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
+hipError_t decode_keys_e5m2_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
 
 
 }  // namespace kvq

@@ -93,13 +93,23 @@ __device__ __forceinline__ u32x2 encode8(const float (&y)[8]) {
 }
 
 // stat: calibrated fp16 scale per KV head (uniform over the launch), or NULL
-// for the per-token max|x| / q_max.
-template <int FMT, int D, int ITER, bool TAIL>
+// for the per-token max|x| / q_max.  ROT: the rows are Walsh-Hadamard rotated
+// first (y = H (sigma x), exact, then rounded once to fp32), and y is
+// quantized in their place.
+template <int FMT, int D, int ITER, bool TAIL, bool ROT>
 __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* __restrict__ src,
                                            uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
                                            const uint16_t* __restrict__ stat) {
   using S = WShape<FMT, D>;
   const int lir = threadIdx.x % S::LPR;
+  // the lane's 8 rotation signs: bits 8 lir .. 8 lir + 7 of rot_signs
+  uint32_t sbits = 0;
+  if constexpr (ROT) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w = (lir >> 2) == i ? a.rot_signs[i] : w;
+    sbits = (w >> (8 * (lir & 3))) & 0xFFu;
+  }
   const uint32_t nrows = (uint32_t)(a.T * a.H);
   const uint32_t row0 = blockIdx.x * (uint32_t)(S::RPP * ITER) + threadIdx.x / S::LPR;
   u32x4 xin[ITER];
@@ -159,6 +169,12 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
     report_error(a.err, s >= a.capacity, KVQ_DEVERR_SLOT);
     float x[8];
     unpack8(uint4{xin[i].x, xin[i].y, xin[i].z, xin[i].w}, x);
+    if constexpr (ROT) {
+      double y[8];
+      fwht_row8<S::LPR>(x, sbits, lir, y);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = (float)y[j];  // one rounding, to nearest even
+    }
     const uint32_t h = r - tok[i] * (uint32_t)a.H;
     uint32_t s16;
     if (stat) {
@@ -170,7 +186,10 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
       am = group_max<S::LPG>(am);
       // Scale: fp32 quotient, rounded once more to fp16 for storage; the
       // codes divide by the stored value.
-      s16 = f2h_bits(exact_div(am, qmax<FMT>(), inv_qmax<FMT>()));
+      s16 = f2h_bits_of_f32(exact_div(am, qmax<FMT>(), inv_qmax<FMT>()));
+      // beyond fp16 (rotated rows only: their entries reach D x 65504): the
+      // largest finite fp16 value, the quotients then saturate
+      if constexpr (ROT) s16 = s16 < 0x7BFFu ? s16 : 0x7BFFu;
     }
     const float sc = h2f(s16);
     u32x2 enc = {0u, 0u};
@@ -213,13 +232,13 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
 
 // grid.y: 0 = keys, 1 = values (keys are skipped for KIVI: grid.y = 1 and
 // tensor0 = 1).
-template <int FK, int FV, int D, int ITER>
+template <int FK, int FV, int D, int ITER, bool ROTK, bool ROTV>
 __global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0) {
   const int tensor = (int)blockIdx.y + tensor0;
   if (tensor == 0) {
-    if constexpr (FK != F_KIVI) write_rows<FK, D, ITER, false>(a, a.k, a.k_codes, a.k_scales, a.k_static);
+    if constexpr (FK != F_KIVI) write_rows<FK, D, ITER, false, ROTK>(a, a.k, a.k_codes, a.k_scales, a.k_static);
   } else {
-    write_rows<FV, D, ITER, FK == F_KIVI>(a, a.v, a.v_codes, a.v_scales, a.v_static);
+    write_rows<FV, D, ITER, FK == F_KIVI, ROTV>(a, a.v, a.v_codes, a.v_scales, a.v_static);
   }
 }
 
@@ -331,7 +350,7 @@ __global__ __launch_bounds__(512) void kivi_seal_kernel(WriteArgs a) {
 #pragma unroll
     for (int c = 0; c < 2 * PPL; ++c) {
       const float range = mx[c] - mn[c];  // fl32(max - min)
-      s16[c] = f2h_bits(range / 15.0f);
+      s16[c] = f2h_bits_of_f32(range / 15.0f);
       z16[c] = f2h_bits(mn[c]);  // exact: mn is an fp16 value
       sc[c] = h2f(s16[c]);
       rc[c] = sc[c] != 0.0f ? recip_fp16(sc[c]) : 0.0f;
@@ -384,8 +403,15 @@ hipError_t launch_sym(const WriteArgs& a, hipStream_t s) {
   const int64_t blocks = (rows + RPP * kIter - 1) / (RPP * kIter);
   const int tensors = FK == F_KIVI ? 1 : 2;
   const int tensor0 = FK == F_KIVI ? 1 : 0;
-  hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIter>), dim3((unsigned)blocks, tensors), dim3(256), 0, s, a,
-                     tensor0);
+  const dim3 grid((unsigned)blocks, tensors);
+  if (a.rot_k && a.rot_v)
+    hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIter, FK != F_KIVI, true>), grid, dim3(256), 0, s, a, tensor0);
+  else if (a.rot_k)
+    hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIter, FK != F_KIVI, false>), grid, dim3(256), 0, s, a, tensor0);
+  else if (a.rot_v)
+    hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIter, false, true>), grid, dim3(256), 0, s, a, tensor0);
+  else
+    hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIter, false, false>), grid, dim3(256), 0, s, a, tensor0);
   return hipGetLastError();
 }
 

@@ -42,6 +42,9 @@ class Workload:
     sink_tokens: int = 0
     sink_mult: float = 10.0
     n_layers: int = 32  # for the attention-only tokens/s projection
+    rotate_k: bool = False  # Walsh-Hadamard rotation of the stored keys / values
+    rotate_v: bool = False
+    base: str = ""  # draw the inputs of this workload (same seed), if set
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -67,8 +70,30 @@ WORKLOADS = {
     "llama3_8b_e5m2": Workload("llama3_8b_e5m2", 27, 32, 8, 128, 16, "fp8_e5m2", "fp8_e5m2",
                                ("fixed", 32768), 4, sink_tokens=4),
 }
+# The Llama-3-70B INT8 layer with Walsh-Hadamard rotated keys and values
+# (per-token INT8 keys with channel outliers are where the rotation helps).
+WORKLOADS["llama3_70b_int8_rot"] = WORKLOADS["llama3_70b_int8"].with_(name="llama3_70b_int8_rot", rotate_k=True,
+                                                                       rotate_v=True, base="llama3_70b_int8")
 ORDER = ["tiny_int8", "llama3_8b_fp8", "llama3_8b_int8k_int4v", "llama3_70b_int8", "llama3_8b_kivi_int4",
-         "llama3_8b_e5m2"]
+         "llama3_8b_e5m2", "llama3_70b_int8_rot"]
+
+
+def seed_of(w: Workload) -> int:
+    """Seed of a workload's inputs: its position in ORDER plus one (a variant
+    with `base` set uses its base's seed, so both see the same inputs)."""
+    return ORDER.index(w.base or w.name) + 1
+
+
+def rotation_signs(head_dim: int, seed: int) -> list:
+    """Random signs of a Walsh-Hadamard rotation drawn from a seeded CPU
+    generator: 8 uint32 words, bit c set = channel c negated."""
+    g = torch.Generator().manual_seed(seed)
+    bits = torch.randint(0, 2, (head_dim,), generator=g)
+    words = [0] * 8
+    for c in range(head_dim):
+        if int(bits[c]):
+            words[c // 32] |= 1 << (c % 32)
+    return words
 
 
 def ctx_lengths(w: Workload, seed: int) -> list:

@@ -28,7 +28,7 @@ def _check_piece(p: dict) -> dict:
     k16, v16 = p["k16"], p["v16"]  # (L, Hs, D) fp16, positions 0..L-1
     L, Hs = k16.shape[0], k16.shape[1]
     npg = -(-L // bs)
-    c = o.OracleCache(max(npg, 1), bs, Hs, D, kf, vf, max_seqs=1)
+    c = o.OracleCache(max(npg, 1), bs, Hs, D, kf, vf, max_seqs=1, rot_k=p.get("rot_k"), rot_v=p.get("rot_v"))
     pos = np.arange(L)
     seq = np.zeros(L, np.int32)
     # page j of the sequence is oracle block j; the same two calls as the GPU

@@ -22,11 +22,26 @@ def garbage_like(shape, dtype, seed):
     return raw.view(dtype).reshape(shape)
 
 
-def new_caches(num_blocks, bs, H, D, kf, vf, max_seqs, device, seed=99, garbage=True):
-    """(device PagedKVCache, OracleCache) holding identical initial bytes."""
+def sign_bits(D, seed):
+    """Seeded random signs of a Walsh-Hadamard rotation: 8 uint32 words, bit c
+    set = channel c negated (about half the channels)."""
+    g = np.random.default_rng(seed)
+    words = np.zeros(8, np.uint32)
+    for c in np.nonzero(g.integers(0, 2, D))[0]:
+        words[c // 32] |= np.uint32(1) << np.uint32(c % 32)
+    return words
+
+
+def new_caches(num_blocks, bs, H, D, kf, vf, max_seqs, device, seed=99, garbage=True, rot_k=None, rot_v=None):
+    """(device PagedKVCache, OracleCache) holding identical initial bytes;
+    rot_k / rot_v: sign words of a Walsh-Hadamard rotation of keys / values
+    (one set of signs serves both, so they must be equal when both given)."""
     from quantized_paged_kv_write_amd import PagedKVCache
-    dev = PagedKVCache(num_blocks, bs, H, D, kf, vf, max_seqs=max_seqs, device=device)
-    orc = o.OracleCache(num_blocks, bs, H, D, kf, vf, max_seqs=max(max_seqs, 1))
+    signs = rot_k if rot_k is not None else rot_v
+    assert rot_k is None or rot_v is None or np.array_equal(rot_k, rot_v)
+    dev = PagedKVCache(num_blocks, bs, H, D, kf, vf, max_seqs=max_seqs, device=device, rotate_k=rot_k is not None,
+                       rotate_v=rot_v is not None, rot_signs=None if signs is None else [int(x) for x in signs])
+    orc = o.OracleCache(num_blocks, bs, H, D, kf, vf, max_seqs=max(max_seqs, 1), rot_k=rot_k, rot_v=rot_v)
     if garbage:
         for i, (name, t) in enumerate(dev.buffers().items()):
             init = garbage_like(tuple(t.shape), t.dtype, seed + i)

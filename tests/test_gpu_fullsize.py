@@ -35,6 +35,8 @@ CASES = {
     # the KIVI shape with fp16 tails of 31, 1 and 15 tokens (and none)
     "llama3_8b_kivi_int4_tails": ("llama3_8b_kivi_int4", [131072, 131071, 131041, 131055]),
     "llama3_8b_e5m2": ("llama3_8b_e5m2", None),
+    # Walsh-Hadamard rotated keys and values
+    "llama3_70b_int8_rot": ("llama3_70b_int8_rot", None),
 }
 
 
@@ -48,11 +50,12 @@ def pool():
 def _run_workload(name):
     wname, ctx = CASES[name]
     w = wl.WORKLOADS[wname]
-    seed = wl.ORDER.index(wname) + 1
+    seed = wl.seed_of(w)
     inp = wl.make_inputs(w, seed, DEV, ctx_lens=ctx)
     B = w.batch
+    signs = wl.rotation_signs(w.head_dim, seed) if (w.rotate_k or w.rotate_v) else None
     cache = kvq.PagedKVCache(inp.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, w.k_dtype, w.v_dtype,
-                             max_seqs=B, device=DEV)
+                             max_seqs=B, device=DEV, rotate_k=w.rotate_k, rotate_v=w.rotate_v, rot_signs=signs)
     last = torch.tensor([inp.seq_start[b] + inp.ctx_lens[b] - 1 for b in range(B)])
     mask = torch.ones(inp.k.shape[0], dtype=torch.bool)
     mask[last] = False
@@ -72,6 +75,9 @@ def _pieces(w, inp, cache, out):
     """Per (sequence, KV-head slice): the host data a worker needs."""
     H, D, bs = w.n_kv_heads, w.head_dim, w.block_size
     G = w.n_q_heads // H
+    signs = None
+    if w.rotate_k or w.rotate_v:
+        signs = np.array(wl.rotation_signs(D, wl.seed_of(w)), np.uint32)
     bufs = cache.buffers()
     k_host = inp.k.cpu().numpy()
     v_host = inp.v.cpu().numpy()
@@ -103,6 +109,7 @@ def _pieces(w, inp, cache, out):
                 "b": b, "h0": h0, "k_fmt": w.k_dtype, "v_fmt": w.v_dtype, "block_size": bs, "head_dim": D,
                 "k16": k_host[st:st + L, h0:h0 + hs], "v16": v_host[st:st + L, h0:h0 + hs], "pages": pages,
                 "q": q_host[b, h0 * G:(h0 + hs) * G], "out": out_host[b, h0 * G:(h0 + hs) * G],
+                "rot_k": signs if w.rotate_k else None, "rot_v": signs if w.rotate_v else None,
             }
 
 

@@ -903,3 +903,26 @@ def check_rotated_cache_attention(rotate_query=o.rotate_query):
 
 def test_rotated_cache_attention():
     check_rotated_cache_attention()
+
+
+def test_rotated_scale_saturates_at_the_fp16_maximum():
+    # Rotated rows reach D x 65504; a scale beyond the fp16 range is stored
+    # as 65504 and the quotients saturate at +-q_max (brute force).
+    D = 128
+    bits = _signs(D, 70)
+    x = np.full((3, D), -65504.0, np.float16)
+    x[0] = (65504.0 * o.sign_vector(bits, D)).astype(np.float16)  # sigma * x = 65504: y_0 = 65504 D
+    x[1, ::2] = 65504.0
+    x[2] = 1.0
+    y = o.rotate_rows(x, bits)
+    for fmt in (o.INT8, o.INT4_G32):
+        codes, s16 = o.quantize_sym(y, fmt)
+        assert np.all(np.isfinite(s16))
+        g = 32 if fmt == o.INT4_G32 else D
+        yy = y.reshape(3, D // g, g).astype(np.float64)
+        over = np.max(np.abs(yy), axis=-1) / o.QMAX[fmt] > 65519.0
+        assert np.any(over) and np.all(s16[over] == np.float16(65504.0))
+        q = o.QMAX[fmt]
+        want = np.clip(np.rint(yy / 65504.0), -q, q)
+        got = codes.reshape(3, D // g, g).astype(np.float64)
+        assert np.array_equal(got[over], want[over])
