@@ -212,7 +212,12 @@ def quantize_sym(x16: np.ndarray, fmt: str):
     # keeps s in FP32; [P1] Exercise 1 step 2 and [P2] section 5 store it as
     # FP16).  The quotient below divides by the stored value.
     s32 = amax / np.float32(QMAX[fmt])
-    s16 = s32.astype(np.float16)
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)
+    # A scale beyond the fp16 range (possible only for the fp32 rows of a
+    # rotated cache, whose entries reach D times the largest fp16 value) is
+    # stored as the largest finite fp16 value; the quotients then saturate.
+    s16 = np.minimum(s16, np.float16(65504.0))
     return _codes_for_scale(x, s16, fmt).reshape(x16.shape), s16
 
 
