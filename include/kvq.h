@@ -278,16 +278,24 @@ int kvq_decode_attn_noalloc(const kvq_cache* cache, const void* q,
  *   src_blocks, dst_blocks  int32 HOST arrays of n block ids, read during the
  *                           call only; ids outside [0, num_blocks) of their
  *                           cache give KVQ_ERR_INVALID_ARG before any copy.
- * The copies are enqueued on `stream` (hipMemcpyAsync, so the DMA engines
- * carry them and kernels on other streams keep running); runs of consecutive
- * source and destination ids become one copy per buffer.  With pageable
- * instead of pinned host memory the copies are correct but not asynchronous.
+ * The copies are enqueued on `stream` by the chosen engine (below); runs of
+ * consecutive source and destination ids are merged.  The copy kernel needs
+ * pinned (device-mapped) host memory and 16-byte aligned buffers
+ * (KVQ_ERR_INVALID_ARG otherwise); with DMA, pageable host memory is
+ * correct but not asynchronous.
  * Destination pages listed twice, or pages that are both read and written by
  * the call, give an unspecified result.  KVQ_ERR_SHAPE if the geometries or
  * formats differ; KVQ_ERR_INVALID_ARG for a NULL buffer the formats need. */
+typedef enum kvq_copy_engine {
+  KVQ_COPY_KERNEL = 0, /* one copy-kernel launch for the whole list (pinned
+                          host memory through its device mapping); its
+                          waves are small enough to run beside a decode */
+  KVQ_COPY_DMA = 1     /* hipMemcpyAsync per run of consecutive ids and
+                          buffer: no compute units, more host time per call */
+} kvq_copy_engine;
 int kvq_copy_blocks(const kvq_cache* src, const kvq_cache* dst,
                     const int32_t* src_blocks, const int32_t* dst_blocks,
-                    int32_t n, void* stream);
+                    int32_t n, int32_t engine, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* kvq_status_string(int status);

@@ -44,6 +44,7 @@ class KvqCacheStruct(ctypes.Structure):
 
 
 ROTATE_K, ROTATE_V = 1, 2  # kvq_cache_flags
+COPY_ENGINES = {"kernel": 0, "dma": 1}  # kvq_copy_engine
 
 
 class KvqError(RuntimeError):
@@ -77,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_decode_attn_noalloc.argtypes = [cp, vp, vp, i32, vp, i32, i32, ctypes.c_float, i32, vp, vp]
         L.kvq_decode_attn_noalloc.restype = ctypes.c_int
-        L.kvq_copy_blocks.argtypes = [cp, cp, vp, vp, i32, vp]
+        L.kvq_copy_blocks.argtypes = [cp, cp, vp, vp, i32, i32, vp]
         L.kvq_copy_blocks.restype = ctypes.c_int
         L.kvq_get_device_error.argtypes = [vp]
         L.kvq_get_device_error.restype = ctypes.c_int
@@ -202,10 +203,11 @@ def write_static(cache: PagedKVCache, k, v, slot_mapping, k_scale, v_scale, stre
         raise KvqError(rc, "kvq_write_static")
 
 
-def copy_blocks(src: PagedKVCache, dst: PagedKVCache, src_blocks, dst_blocks, stream=None):
+def copy_blocks(src: PagedKVCache, dst: PagedKVCache, src_blocks, dst_blocks, stream=None, engine="kernel"):
     """kvq_copy_blocks: page dst_blocks[i] of `dst` becomes a copy of page
     src_blocks[i] of `src` (either cache on the device or in pinned host
-    memory), enqueued on the stream.  The id lists are host sequences."""
+    memory), enqueued on the stream by the copy kernel or the DMA engines.
+    The id lists are host sequences."""
     import numpy as np
     s_ids = np.ascontiguousarray(np.asarray(src_blocks, dtype=np.int32).ravel())
     d_ids = np.ascontiguousarray(np.asarray(dst_blocks, dtype=np.int32).ravel())
@@ -213,7 +215,8 @@ def copy_blocks(src: PagedKVCache, dst: PagedKVCache, src_blocks, dst_blocks, st
         raise ValueError("src_blocks and dst_blocks differ in length")
     cs, cd = src.struct(), dst.struct()
     rc = lib().kvq_copy_blocks(ctypes.byref(cs), ctypes.byref(cd), s_ids.ctypes.data_as(ctypes.c_void_p),
-                               d_ids.ctypes.data_as(ctypes.c_void_p), int(s_ids.size), _stream(stream))
+                               d_ids.ctypes.data_as(ctypes.c_void_p), int(s_ids.size), COPY_ENGINES[engine],
+                               _stream(stream))
     if rc != KVQ_OK:
         raise KvqError(rc, "kvq_copy_blocks")
 
@@ -287,3 +290,44 @@ def decode_attn_noalloc(cache: PagedKVCache, q, block_table, ctx_lens, out, sm_s
     if rc != KVQ_OK:
         raise KvqError(rc, "kvq_decode_attn_noalloc")
     return out
+
+
+class DecodeCall:
+    """kvq_decode_attn with its arguments checked and marshalled once, for
+    loops that issue the same decode step many times (serving loops, double-
+    buffered pipelines): calling it only calls into the library.  The tensors
+    must stay alive and keep their storage while the object is used."""
+
+    def __init__(self, cache: PagedKVCache, q, block_table, ctx_lens, out, workspace, sm_scale=0.0, split_tokens=0):
+        decode_attn(cache, q, block_table, ctx_lens, sm_scale=sm_scale, split_tokens=split_tokens, out=out,
+                    workspace=workspace)  # validates every argument (and runs once)
+        self._c = cache.struct()
+        self._args = (ctypes.byref(self._c), _ptr(q), _ptr(block_table), block_table.shape[1], _ptr(ctx_lens),
+                      q.shape[0], q.shape[1], float(sm_scale), split_tokens, _ptr(out), _ptr(workspace),
+                      workspace.numel() * workspace.element_size())
+        self._refs = (cache, q, block_table, ctx_lens, out, workspace)
+
+    def __call__(self, stream=None):
+        rc = lib().kvq_decode_attn(*self._args, _stream(stream))
+        if rc != KVQ_OK:
+            raise KvqError(rc, "kvq_decode_attn")
+
+
+class CopyCall:
+    """kvq_copy_blocks with its arguments marshalled once (see DecodeCall)."""
+
+    def __init__(self, src: PagedKVCache, dst: PagedKVCache, src_blocks, dst_blocks, engine="kernel"):
+        import numpy as np
+        self._s = np.ascontiguousarray(np.asarray(src_blocks, dtype=np.int32).ravel())
+        self._d = np.ascontiguousarray(np.asarray(dst_blocks, dtype=np.int32).ravel())
+        if self._s.size != self._d.size:
+            raise ValueError("src_blocks and dst_blocks differ in length")
+        self._cs, self._cd = src.struct(), dst.struct()
+        self._args = (ctypes.byref(self._cs), ctypes.byref(self._cd), self._s.ctypes.data_as(ctypes.c_void_p),
+                      self._d.ctypes.data_as(ctypes.c_void_p), int(self._s.size), COPY_ENGINES[engine])
+        self._refs = (src, dst)
+
+    def __call__(self, stream=None):
+        rc = lib().kvq_copy_blocks(*self._args, _stream(stream))
+        if rc != KVQ_OK:
+            raise KvqError(rc, "kvq_copy_blocks")

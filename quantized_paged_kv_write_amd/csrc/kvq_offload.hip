@@ -6,10 +6,11 @@
 // current step computes).
 //
 // A page of a cache is one contiguous run of bytes in each of its paged
-// buffers (codes, scales, KIVI zero points), so a batch of pages becomes a
-// few hipMemcpyAsync calls: runs of consecutive source and destination ids
-// are merged into one copy per buffer.  The copies go to the DMA engines,
-// so they overlap kernels on other streams without taking compute units.
+// buffers (codes, scales, KIVI zero points).  Two engines move them: a copy
+// kernel (one launch for the whole list, reading and writing pinned host
+// memory through its device mapping), or the DMA engines (one hipMemcpyAsync
+// per run of consecutive ids and buffer; no compute units, but each call
+// costs host time in the runtime).
 #include <algorithm>
 #include <vector>
 
@@ -58,10 +59,54 @@ int paged_buffers(const kvq_cache* s, const kvq_cache* d, std::vector<PagedBuffe
   return KVQ_OK;
 }
 
+// The copy kernel: one workgroup per page of the batch, each lane moving
+// 16-byte chunks of every paged buffer of that page, four in flight.  Pinned
+// host memory is read and written directly through its device mapping, so
+// one launch serves any list of pages; the kernel holds few registers and no
+// LDS, so its waves fit beside a decode launch on the same compute units.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMaxRuns = 160;
+struct CopyRun {
+  int32_t src, dst, count;
+};
+struct CopyArgs {
+  const u32x4* src[5];
+  u32x4* dst[5];
+  uint32_t chunks[5];  // 16-byte chunks per page of each buffer
+  int32_t nbuf, nruns;
+  int32_t run_start[kMaxRuns + 1];  // first page (of the batch) of each run
+  CopyRun runs[kMaxRuns];
+};
+
+__global__ __launch_bounds__(256) void copy_pages_kernel(CopyArgs a) {
+  const int p = (int)blockIdx.x;  // page of the batch
+  int r = 0;
+  while (r + 1 < a.nruns && a.run_start[r + 1] <= p) ++r;  // uniform scan over at most kMaxRuns runs
+  const int k = p - a.run_start[r];
+  const size_t sp = (size_t)(a.runs[r].src + k), dp = (size_t)(a.runs[r].dst + k);
+  for (int b = 0; b < a.nbuf; ++b) {
+    const uint32_t c = a.chunks[b];
+    const u32x4* s = a.src[b] + sp * c;
+    u32x4* d = a.dst[b] + dp * c;
+    uint32_t i = threadIdx.x;
+    for (; i + 768 < c; i += 1024) {
+      const u32x4 v0 = __builtin_nontemporal_load(s + i);
+      const u32x4 v1 = __builtin_nontemporal_load(s + i + 256);
+      const u32x4 v2 = __builtin_nontemporal_load(s + i + 512);
+      const u32x4 v3 = __builtin_nontemporal_load(s + i + 768);
+      __builtin_nontemporal_store(v0, d + i);
+      __builtin_nontemporal_store(v1, d + i + 256);
+      __builtin_nontemporal_store(v2, d + i + 512);
+      __builtin_nontemporal_store(v3, d + i + 768);
+    }
+    for (; i < c; i += 256) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
+  }
+}
+
 }  // namespace
 
 extern "C" int kvq_copy_blocks(const kvq_cache* src, const kvq_cache* dst, const int32_t* src_blocks,
-                               const int32_t* dst_blocks, int32_t n, void* stream) {
+                               const int32_t* dst_blocks, int32_t n, int32_t engine, void* stream) {
   std::vector<PagedBuffer> bufs;
   int rc = paged_buffers(src, dst, &bufs);
   if (rc != KVQ_OK) return rc;
@@ -71,9 +116,41 @@ extern "C" int kvq_copy_blocks(const kvq_cache* src, const kvq_cache* dst, const
   for (int32_t i = 0; i < n; ++i)
     if (src_blocks[i] < 0 || src_blocks[i] >= src->num_blocks || dst_blocks[i] < 0 || dst_blocks[i] >= dst->num_blocks)
       return KVQ_ERR_INVALID_ARG;
+  if (engine != KVQ_COPY_KERNEL && engine != KVQ_COPY_DMA) return KVQ_ERR_INVALID_ARG;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return KVQ_ERR_NO_DEVICE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (engine == KVQ_COPY_KERNEL) {
+    for (const PagedBuffer& b : bufs)
+      if ((b.page_bytes & 15) || (reinterpret_cast<uintptr_t>(b.src) & 15) || (reinterpret_cast<uintptr_t>(b.dst) & 15))
+        return KVQ_ERR_INVALID_ARG;
+    CopyArgs a{};
+    a.nbuf = (int32_t)bufs.size();
+    for (int b = 0; b < a.nbuf; ++b) {
+      a.src[b] = reinterpret_cast<const u32x4*>(bufs[b].src);
+      a.dst[b] = reinterpret_cast<u32x4*>(bufs[b].dst);
+      a.chunks[b] = (uint32_t)(bufs[b].page_bytes / 16);
+    }
+    // runs of consecutive ids, launched kMaxRuns at a time
+    int32_t i = 0;
+    while (i < n) {
+      a.nruns = 0;
+      int32_t pages = 0;
+      while (i < n && a.nruns < kMaxRuns) {
+        int32_t j = i + 1;
+        while (j < n && src_blocks[j] == src_blocks[j - 1] + 1 && dst_blocks[j] == dst_blocks[j - 1] + 1) ++j;
+        a.run_start[a.nruns] = pages;
+        a.runs[a.nruns] = CopyRun{src_blocks[i], dst_blocks[i], j - i};
+        ++a.nruns;
+        pages += j - i;
+        i = j;
+      }
+      a.run_start[a.nruns] = pages;
+      hipLaunchKernelGGL(copy_pages_kernel, dim3((unsigned)pages), dim3(256), 0, st, a);
+      if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+    }
+    return KVQ_OK;
+  }
   // runs [i, j) with consecutive source and destination ids, in list order.
   // (One hipMemcpyAsync per run and buffer: the batched copy call is newer
   // than the HIP runtime that PyTorch-ROCm processes load.)

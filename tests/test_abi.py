@@ -228,14 +228,15 @@ def test_copy_blocks_argument_errors():
     ids = (ctypes.c_int32 * 2)(0, 3)
     bad = (ctypes.c_int32 * 2)(0, 4)  # 4 is past b's 4 blocks
 
-    def cp(s, d, si=ids, di=ids, n=2):
-        return L.kvq_copy_blocks(ctypes.byref(s), ctypes.byref(d), si, di, n, None)
+    def cp(s, d, si=ids, di=ids, n=2, engine=0):
+        return L.kvq_copy_blocks(ctypes.byref(s), ctypes.byref(d), si, di, n, engine, None)
 
-    assert L.kvq_copy_blocks(None, ctypes.byref(b), ids, ids, 2, None) == INVALID
+    assert L.kvq_copy_blocks(None, ctypes.byref(b), ids, ids, 2, 0, None) == INVALID
+    assert cp(a, b, engine=2) == INVALID                # unknown engine
     assert cp(a, _cache(head_dim=64)) == SHAPE          # geometries differ
     assert cp(a, _cache(v_dtype=2)) == SHAPE            # formats differ
     assert cp(a, b, di=bad) == INVALID                  # id out of range, nothing copied
     assert cp(a, b, n=-1) == INVALID
     assert cp(a, b, n=0) == OK                          # nothing to do
     assert cp(a, _cache(num_blocks=4, v_scales=None)) == INVALID
-    assert L.kvq_copy_blocks(ctypes.byref(a), ctypes.byref(b), None, ids, 2, None) == INVALID
+    assert L.kvq_copy_blocks(ctypes.byref(a), ctypes.byref(b), None, ids, 2, 1, None) == INVALID

@@ -33,9 +33,10 @@ def _host_pool(dev, orc, n):
     return pool, opool
 
 
+@pytest.mark.parametrize("engine", ["kernel", "dma"])
 @pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("int4_kivi", "int4_g32"),
                                    ("fp8_e5m2", "int8")])
-def test_offload_and_prefetch_round_trip(kf, vf):
+def test_offload_and_prefetch_round_trip(kf, vf, engine):
     ctx = [300, 77, 1000]
     spare = 40
     inp, dev, orc = _setup(kf, vf, ctx, spare, seed=11)
@@ -51,7 +52,7 @@ def test_offload_and_prefetch_round_trip(kf, vf):
     src = [int(t[b, p]) for b, p in pages]
     host = list(range(10, 10 + len(pages)))
     pool, opool = _host_pool(dev, orc, 32)
-    kvq.copy_blocks(dev, pool, src, host)
+    kvq.copy_blocks(dev, pool, src, host, engine=engine)
     o.copy_blocks(orc, opool, src, host)
     torch.cuda.synchronize()
     assert compare_buffers(pool, opool, names=o.paged_buffer_names(opool)) == {}
@@ -60,7 +61,7 @@ def test_offload_and_prefetch_round_trip(kf, vf):
     dst = free[:6] + [free[20], free[13]]
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
-        kvq.copy_blocks(pool, dev, host, dst)
+        kvq.copy_blocks(pool, dev, host, dst, engine=engine)
     o.copy_blocks(opool, orc, host, dst)
     torch.cuda.synchronize()
     assert compare_buffers(dev, orc) == {}
@@ -73,7 +74,8 @@ def test_offload_and_prefetch_round_trip(kf, vf):
     assert np.array_equal(ref1, ref0)
 
 
-def test_prefetch_overlaps_decode_on_another_stream():
+@pytest.mark.parametrize("engine", ["kernel", "dma"])
+def test_prefetch_overlaps_decode_on_another_stream(engine):
     # Double buffering: while decode t reads staging set t % 2, the prefetch
     # of step t + 1 fills set (t + 1) % 2 on a second stream; decode t + 1
     # waits for it through an event.  Every step's output equals the decode
@@ -102,7 +104,7 @@ def test_prefetch_overlaps_decode_on_another_stream():
     main, side = torch.cuda.current_stream(), torch.cuda.Stream()
     ready = [torch.cuda.Event() for _ in range(2)]
     with torch.cuda.stream(side):
-        kvq.copy_blocks(pool, dev, list(range(3 * n_off)), sets[0])
+        kvq.copy_blocks(pool, dev, list(range(3 * n_off)), sets[0], engine=engine)
         ready[0].record(side)
     outs = []
     for step in range(6):
@@ -111,9 +113,49 @@ def test_prefetch_overlaps_decode_on_another_stream():
         if step + 1 < 6:
             side.wait_stream(main)  # the set being refilled is not read by an earlier step still in flight
             with torch.cuda.stream(side):
-                kvq.copy_blocks(pool, dev, list(range(3 * n_off)), sets[1 - cur])
+                kvq.copy_blocks(pool, dev, list(range(3 * n_off)), sets[1 - cur], engine=engine)
                 ready[1 - cur].record(side)
         outs.append(kvq.decode_attn(dev, q, tables[cur], ctx_d).clone())
     torch.cuda.synchronize()
     for out in outs:
         assert torch.equal(out, base)
+
+
+def test_prepared_calls_match_the_plain_calls():
+    # DecodeCall / CopyCall marshal their arguments once; results are the
+    # same as the plain binding calls.
+    ctx = [300, 77]
+    inp, dev, orc = _setup("int8", "int4_g32", ctx, 16, seed=31)
+    ctx_d = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    q, table = inp.q.to(DEV), inp.block_table.to(DEV)
+    ref = kvq.decode_attn(dev, q, table, ctx_d)
+    out = torch.empty_like(q)
+    ws = torch.empty(kvq.decode_workspace_bytes(dev, 2, q.shape[1], table.shape[1]), dtype=torch.uint8, device=DEV)
+    call = kvq.DecodeCall(dev, q, table, ctx_d, out, ws)
+    out.zero_()
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    pool, opool = _host_pool(dev, orc, 8)
+    src = [int(x) for x in inp.block_table[0, :4]]
+    kvq.CopyCall(dev, pool, src, [4, 5, 6, 7])()
+    o.copy_blocks(orc, opool, src, [4, 5, 6, 7])
+    torch.cuda.synchronize()
+    assert compare_buffers(pool, opool, names=o.paged_buffer_names(opool)) == {}
+
+
+def test_copy_kernel_with_many_scattered_runs():
+    # more runs than one launch holds (the kernel takes 160 runs per launch),
+    # device to device and back, against the oracle's copy
+    ctx = [2000, 1500]
+    inp, dev, orc = _setup("int8", "fp8_e4m3fn", ctx, 400, seed=41)
+    t = inp.block_table.numpy()
+    used = sorted(int(x) for b, L in enumerate(ctx) for x in t[b, :-(-L // dev.block_size)])
+    free = [x for x in range(inp.num_blocks) if x not in set(used)]
+    rng = np.random.default_rng(3)
+    src = [int(x) for x in rng.choice(used, 200, replace=False)]
+    dst = [int(x) for x in rng.choice(free, 200, replace=False)]
+    kvq.copy_blocks(dev, dev, src, dst, engine="kernel")
+    o.copy_blocks(orc, orc, src, dst)
+    torch.cuda.synchronize()
+    assert compare_buffers(dev, orc) == {}
