@@ -5,9 +5,9 @@ tables, slot mappings).  It contains none of the quantization or attention
 arithmetic, so the GPU path and the CPU oracle can both be fed from it.
 
 Value structure follows the pages' description of real KV tensors:
-  * keys have a few channel-consistent outlier channels per head ("K's
-    outliers are channel-consistent", 12 KV Cache Quantization, section 5
-    "K is more sensitive than V"; KIVI in "Quantized KV caches in production",
+  * keys have a few outlier channels per head, and the same channels stay
+    large across tokens (12 KV Cache Quantization, section 5 on why keys are
+    more sensitive than values; KIVI in "Quantized KV caches in production",
     Numerical Formats);
   * the first few tokens of a sequence (attention sinks) carry large keys
     ("Use Less Memory: Quantization and Offloading", section 2.2);

@@ -77,7 +77,7 @@ def check_sym_invariants(quantize_sym=o.quantize_sym, dequant=o.dequant_sym, fmt
         q = o.QMAX[fmt]
         normal = s >= 2.0 ** -14  # s16 is a normal fp16 number
         # 1. the largest-magnitude element lands on +-q_max ('Use Less Memory',
-        #    Exercise 1 step 3: "hits q_max exactly")
+        #    Exercise 1 step 3: the absmax element maps to the top code)
         idx = np.argmax(np.abs(x), axis=-1)
         top = np.take_along_axis(xhat, idx[..., None], -1)[..., 0]
         topx = np.take_along_axis(x, idx[..., None], -1)[..., 0]
