@@ -1,5 +1,6 @@
-"""CPU oracle for quantize-on-write into a paged KV cache and for dequantizing
-paged decode attention.
+"""CPU oracle for quantize-on-write into a paged KV cache, for dequantizing
+paged decode attention and for causal chunked-prefill attention over the
+cache.
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
 and the benchmark's CPU-baseline leg may import this module.  It is a plain,
@@ -35,7 +36,10 @@ Readings taken where the pages leave a step open (each is repeated at its use):
   * INT4 packs two codes per byte, the even channel in the low nibble;
   * KIVI-style keys: one fp16 scale and one fp16 zero point (= the group
     minimum) per channel per 32-token group, unsigned codes 0..15; the rows of a
-    page wait in a per-sequence fp16 tail until the page's last row arrives.
+    page wait in a per-sequence fp16 tail until the page's last row arrives;
+  * chunked prefill: a sequence's chunk of n queries are its last n
+    positions (their keys and values already in the cache), and query i
+    attends causally to tokens 0 .. L - n + i.
 
 Parity unpinned: nothing here.  Every function below is pinned by a test in
 tests/test_oracle_*.py against the pages' worked example, closed forms,
@@ -659,6 +663,63 @@ def decode_attn(cache: OracleCache, q, block_table, ctx_lens, sm_scale=None, seq
         L = min(max(int(ctx_lens[b]), 0), block_table.shape[1] * cache.bs)
         K, V = gather_dequant(cache, block_table[b], L, b)
         out[b] = attention_fp64(q[b], K, V, sm_scale, live=token_live(cache, block_table[b], L))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Chunked prefill over the cache ([P1] "What Comes Next": a long prompt is
+# processed in scheduled pieces; [P2] "Interaction with prefix caching":
+# quantized blocks stay shareable, so a new piece of a prompt attends to a
+# prefix already in the cache).
+# Reading: the n queries of a sequence's chunk are its last n positions, and
+# their keys and values were written into the cache before the call; query i
+# of the chunk sits at position p = L - n + i, where L is the sequence's
+# context length taken into range as decode_attn takes it, and attends to
+# tokens 0..p (causal decoder attention; tokens on pages with an
+# out-of-range block id are left out as in decode).  A query at p < 0 (a chunk
+# longer than the context) attends to nothing and gets zeros.
+# --------------------------------------------------------------------------
+
+
+def causal_attention_fp64(q, K, V, positions, sm_scale=None, live=None):
+    """Queries q (n, Hq, D) at the given positions (n,) against K, V
+    (L, H, D), float64: query i attends to the live tokens t <= positions[i]
+    (attention_fp64 per query).  Returns (n, Hq, D)."""
+    q = np.asarray(q, dtype=np.float64)
+    L = K.shape[0]
+    out = np.zeros(q.shape, np.float64)
+    t = np.arange(L)
+    for i, p in enumerate(np.asarray(positions, dtype=np.int64)):
+        m = t <= p
+        if live is not None:
+            m = m & np.asarray(live, dtype=bool)
+        out[i] = attention_fp64(q[i], K, V, sm_scale, live=m)
+    return out
+
+
+def prefill_attn(cache: OracleCache, q, q_start, block_table, ctx_lens, sm_scale=None, seqs=None, rows=None):
+    """Chunked-prefill attention over the quantized paged cache, float64
+    (Tq, Hq, D).  q (Tq, Hq, D) holds the chunks of all sequences one after
+    the other: sequence b's queries are rows q_start[b] .. q_start[b+1] - 1.
+    `seqs` restricts the work to a subset of sequences and `rows` to a subset
+    of query rows (others are left zero).  For KIVI keys, sequence b reads
+    tail row b."""
+    q = np.asarray(q)
+    q_start = np.asarray(q_start, dtype=np.int64)
+    block_table = np.asarray(block_table)
+    out = np.zeros(q.shape, np.float64)
+    want = None if rows is None else set(int(r) for r in rows)
+    for b in (range(len(q_start) - 1) if seqs is None else seqs):
+        r0, r1 = int(q_start[b]), int(q_start[b + 1])
+        n = r1 - r0
+        idx = [r for r in range(r0, r1) if want is None or r in want]
+        if not idx:
+            continue
+        L = min(max(int(ctx_lens[b]), 0), block_table.shape[1] * cache.bs)
+        K, V = gather_dequant(cache, block_table[b], L, b)
+        live = token_live(cache, block_table[b], L)
+        pos = [L - n + (r - r0) for r in idx]
+        out[idx] = causal_attention_fp64(q[idx], K, V, pos, sm_scale, live)
     return out
 
 

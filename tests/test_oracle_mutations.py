@@ -225,3 +225,48 @@ def test_rotation_mistakes_fail():
     assert _fails(pins.check_rotation_round_trip, o.rotate_rows, unrot_no_div)
     assert _fails(pins.check_rotated_cache_attention, rotq_signs_after)
     assert _fails(pins.check_hadamard, hadamard_wrong)
+
+
+def _causal_strict(q, K, V, positions, sm_scale=None, live=None):
+    # Mistake: a query does not see its own position (t < p).
+    return o.kvq_oracle._causal_ok(q, K, V, [p - 1 for p in positions], sm_scale, live)
+
+
+def _causal_none(q, K, V, positions, sm_scale=None, live=None):
+    # Mistake: no causal mask inside the chunk.
+    return o.kvq_oracle._causal_ok(q, K, V, [K.shape[0] - 1] * len(positions), sm_scale, live)
+
+
+def _prefill_positions_from_zero(cache, q, q_start, block_table, ctx_lens, sm_scale=None, seqs=None, rows=None):
+    # Mistake: chunk row i sits at position i instead of L - n + i.
+    q = np.asarray(q)
+    out = np.zeros(q.shape)
+    for b in range(len(q_start) - 1):
+        r0, r1 = int(q_start[b]), int(q_start[b + 1])
+        L = min(max(int(ctx_lens[b]), 0), np.asarray(block_table).shape[1] * cache.bs)
+        K, V = o.gather_dequant(cache, block_table[b], L, b)
+        live = o.token_live(cache, block_table[b], L)
+        out[r0:r1] = o.causal_attention_fp64(q[r0:r1], K, V, list(range(r1 - r0)), sm_scale, live)
+    return out
+
+
+def _prefill_head_major(cache, q, q_start, block_table, ctx_lens, sm_scale=None, seqs=None, rows=None):
+    # Mistake: the query tensor read as (Hq, Tq, D) memory.
+    q = np.asarray(q)
+    qq = np.ascontiguousarray(q).reshape(q.shape[1], q.shape[0], q.shape[2]).transpose(1, 0, 2)
+    return o.prefill_attn(cache, qq, q_start, block_table, ctx_lens, sm_scale, seqs, rows)
+
+
+def test_prefill_mistakes_fail(monkeypatch):
+    checks = (pins.check_prefill_bruteforce, pins.check_prefill_rows_are_decodes, pins.check_prefill_split_chunks,
+              pins.check_prefill_special_cases, pins.check_prefill_causality)
+    monkeypatch.setattr(o.kvq_oracle, "_causal_ok", o.kvq_oracle.causal_attention_fp64, raising=False)
+    for wrong in (_causal_strict, _causal_none):
+        with monkeypatch.context() as m:
+            m.setattr(o.kvq_oracle, "causal_attention_fp64", wrong)
+            failed = [c.__name__ for c in checks if _fails(c)]
+            assert failed, wrong.__name__
+    for wrong in (_prefill_positions_from_zero, _prefill_head_major):
+        assert any(_fails(c, wrong) for c in checks), wrong.__name__
+    for c in checks:
+        c()

@@ -926,3 +926,147 @@ def test_rotated_scale_saturates_at_the_fp16_maximum():
         want = np.clip(np.rint(yy / 65504.0), -q, q)
         got = codes.reshape(3, D // g, g).astype(np.float64)
         assert np.array_equal(got[over], want[over])
+
+
+# --------------------------------------------------------------------------
+# Chunked prefill: a chunk of queries at the last positions of each sequence,
+# causal over the cached tokens
+# --------------------------------------------------------------------------
+
+# (key format, value format, context lengths, chunk lengths): chunks shorter
+# than the context (a cached prefix), equal to it (a whole prompt) and longer
+# than it (queries at negative positions)
+PREFILL_CASES = [
+    (o.INT8, o.INT4_G32, [11, 7, 2], [5, 7, 3]),
+    (o.FP8_E4M3FN, o.FP8_E5M2, [40, 17], [1, 17]),
+    (o.INT4_KIVI, o.INT4_G32, [70, 33, 64], [40, 33, 9]),
+]
+
+
+def _prefill_setup(kf, vf, ctx, qlen, H=2, D=32, Hq=4, seed=80):
+    bs = 32 if kf == o.INT4_KIVI else 4
+    nb, table, ks, vs, slots = _three_sequences(kf, vf, ctx, bs, H, D, seed=seed)
+    c = o.OracleCache(nb, bs, H, D, kf, vf, max_seqs=len(ctx))
+    seq = np.concatenate([np.full(L, b, np.int32) for b, L in enumerate(ctx)])
+    o.write(c, np.concatenate(ks), np.concatenate(vs), np.concatenate(slots), seq)
+    q_start = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int64)
+    q = (np.random.default_rng(seed + 1).standard_normal((int(q_start[-1]), Hq, D)) * 2).astype(np.float16)
+    return c, table, ks, vs, q, q_start
+
+
+def check_prefill_bruteforce(prefill=o.prefill_attn):
+    # Explicit loops over query rows, heads and visible tokens with math.exp,
+    # against the dequantized rows of each sequence quantized on its own
+    # (KIVI: complete 32-token groups quantized, the last L mod 32 tokens fp16).
+    for kf, vf, ctx, qlen in PREFILL_CASES:
+        c, table, ks, vs, q, q_start = _prefill_setup(kf, vf, ctx, qlen)
+        got = prefill(c, q, q_start, table, ctx)
+        Hq, D = q.shape[1], q.shape[2]
+        G = Hq // c.H
+        for b, (L, n) in enumerate(zip(ctx, qlen)):
+            K, V = o.dequantized_sequence(ks[b], vs[b], kf, vf)
+            for i in range(n):
+                r = int(q_start[b]) + i
+                pos = L - n + i
+                for hq in range(Hq):
+                    h = hq // G
+                    if pos < 0:
+                        assert not np.any(got[r, hq]), (kf, b, i)
+                        continue
+                    sc = [sum(float(q[r, hq, d]) * K[t, h, d] for d in range(D)) / math.sqrt(D)
+                          for t in range(pos + 1)]
+                    mx = max(sc)
+                    w = [math.exp(x - mx) for x in sc]
+                    ref = [sum(w[t] * V[t, h, d] for t in range(pos + 1)) / sum(w) for d in range(D)]
+                    assert np.max(np.abs(got[r, hq] - np.array(ref))) <= 1e-12, (kf, b, i, hq)
+
+
+def check_prefill_rows_are_decodes(prefill=o.prefill_attn):
+    # Symmetric formats: every chunk row equals decode attention of that query
+    # with the context cut at its position (ctx = p + 1), and chunks of one
+    # query equal decode.
+    for kf, vf, ctx, qlen in PREFILL_CASES[:2]:
+        c, table, ks, vs, q, q_start = _prefill_setup(kf, vf, ctx, qlen, seed=82)
+        got = prefill(c, q, q_start, table, ctx)
+        for b, (L, n) in enumerate(zip(ctx, qlen)):
+            for i in range(n):
+                r, pos = int(q_start[b]) + i, L - n + i
+                ref = o.decode_attn(c, q[r][None], table[b:b + 1], [pos + 1])[0]
+                assert np.array_equal(got[r], ref), (kf, b, i)
+        ones = np.arange(len(ctx) + 1)
+        last = q[[int(q_start[b + 1]) - 1 for b in range(len(ctx))]]
+        assert np.array_equal(prefill(c, last, ones, table, ctx), o.decode_attn(c, last, table, ctx))
+
+
+def check_prefill_split_chunks(prefill=o.prefill_attn):
+    # A chunk computed in two pieces, the first while the context ended where
+    # the second piece starts, equals the chunk in one call.
+    for kf, vf, ctx, qlen in PREFILL_CASES[:2]:
+        c, table, ks, vs, q, q_start = _prefill_setup(kf, vf, ctx, qlen, seed=84)
+        whole = prefill(c, q, q_start, table, ctx)
+        for b, (L, n) in enumerate(zip(ctx, qlen)):
+            r0 = int(q_start[b])
+            for m in range(1, n):
+                first = prefill(c, q[r0:r0 + m], [0, m], table[b:b + 1], [L - (n - m)])
+                second = prefill(c, q[r0 + m:r0 + n], [0, n - m], table[b:b + 1], [L])
+                assert np.array_equal(np.concatenate([first, second]), whole[r0:r0 + n]), (kf, b, m)
+
+
+def check_prefill_special_cases(prefill=o.prefill_attn):
+    # A whole prompt: the query at position 0 returns v_hat_0 of its head; a
+    # zero query returns the mean of v_hat over tokens 0..p.
+    kf, vf, ctx, qlen = o.INT8, o.INT8, [13], [13]
+    c, table, ks, vs, q, q_start = _prefill_setup(kf, vf, ctx, qlen, seed=86)
+    K, V = o.dequantized_sequence(ks[0], vs[0], kf, vf)
+    G = q.shape[1] // c.H
+    got = prefill(c, q, q_start, table, ctx)
+    assert np.array_equal(got[0], V[0][np.arange(q.shape[1]) // G])
+    got = prefill(c, np.zeros_like(q), q_start, table, ctx)
+    for p in range(13):
+        assert np.max(np.abs(got[p] - V[:p + 1].mean(axis=0)[np.arange(q.shape[1]) // G])) <= 1e-14
+
+
+def check_prefill_causality(prefill=o.prefill_attn):
+    # Rewriting the key and value of token t changes exactly the rows at
+    # positions >= t.
+    kf, vf, ctx, qlen = o.INT8, o.INT4_G32, [24], [24]
+    c, table, ks, vs, q, q_start = _prefill_setup(kf, vf, ctx, qlen, seed=88)
+    before = prefill(c, q, q_start, table, ctx)
+    t = 9
+    slot = np.array([table[0, t // c.bs] * c.bs + t % c.bs])
+    rng = np.random.default_rng(89)
+    o.write(c, (rng.standard_normal((1, c.H, c.D)) * 3).astype(np.float16),
+            rng.standard_normal((1, c.H, c.D)).astype(np.float16), slot)
+    after = prefill(c, q, q_start, table, ctx)
+    assert np.array_equal(after[:t], before[:t])
+    assert np.all(np.any(after[t:] != before[t:], axis=(1, 2)))
+
+
+def test_prefill_bruteforce():
+    check_prefill_bruteforce()
+
+
+def test_prefill_rows_are_decodes():
+    check_prefill_rows_are_decodes()
+
+
+def test_prefill_split_chunks():
+    check_prefill_split_chunks()
+
+
+def test_prefill_special_cases():
+    check_prefill_special_cases()
+
+
+def test_prefill_causality():
+    check_prefill_causality()
+
+
+def test_prefill_row_subset():
+    kf, vf, ctx, qlen = PREFILL_CASES[0]
+    c, table, ks, vs, q, q_start = _prefill_setup(kf, vf, ctx, qlen)
+    full = o.prefill_attn(c, q, q_start, table, ctx)
+    rows = [0, 4, 6, 13]
+    part = o.prefill_attn(c, q, q_start, table, ctx, rows=rows)
+    assert np.array_equal(part[rows], full[rows])
+    assert not np.any(np.delete(part, rows, axis=0))
