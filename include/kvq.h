@@ -4,8 +4,8 @@
  *
  * The library stores keys and values of a transformer's KV cache as low-bit
  * codes plus fp16 scales in fixed-size pages, and runs single-query (decode)
- * attention that reads those pages through a block table and dequantizes them
- * in registers.  Sources, cited by page title and section:
+ * attention and causal chunked-prefill attention that read those pages
+ * through a block table and dequantize them in registers.  Sources, cited by page title and section:
  *   [P1] "Use Less Memory: Quantization and Offloading", section 2.1
  *        (symmetric quantization: s = max|x| / q_max, x_q = clip(round(x/s),
  *        -q_max, q_max), x_hat = x_q * s; q_max 127 for INT8, 7 for INT4),
@@ -71,8 +71,13 @@ typedef enum kvq_device_error {
   KVQ_DEVERR_BLOCK = 4, /* kvq_decode_attn: a block id outside
                            [0, num_blocks) on a page within the context (the
                            page contributes nothing)                        */
-  KVQ_DEVERR_CTX = 8    /* kvq_decode_attn: a ctx_len below 0 or above
-                           max_blocks_per_seq * block_size (clamped)        */
+  KVQ_DEVERR_CTX = 8,   /* kvq_decode_attn / kvq_prefill_attn: a ctx_len
+                           below 0 or above max_blocks_per_seq * block_size
+                           (clamped)                                        */
+  KVQ_DEVERR_QLEN = 16  /* kvq_prefill_attn: a chunk with q_start[b] < 0,
+                           q_start[b + 1] > total_q, or a length below 0 or
+                           above max_q_len (the sequence is skipped: its
+                           output rows are not written)                     */
 } kvq_device_error;
 
 /* Storage formats of a cache tensor.
@@ -263,6 +268,48 @@ int kvq_decode_attn_noalloc(const kvq_cache* cache, const void* q,
                             const int32_t* ctx_lens, int32_t batch,
                             int32_t n_q_heads, float sm_scale,
                             int32_t split_tokens, void* out, void* stream);
+
+/* Workspace bytes of kvq_prefill_attn for a chunk batch of total_q query
+ * rows: 0 unless the cache stores rotated keys (KVQ_ROTATE_K), which need the
+ * rotated queries, 2 x total_q x n_q_heads x head_dim fp16 values. */
+int kvq_prefill_workspace_bytes(const kvq_cache* cache, int64_t total_q,
+                                int32_t n_q_heads, size_t* bytes);
+
+/* Causal chunked-prefill attention over the quantized pages ("Use Less
+ * Memory: Quantization and Offloading", What Comes Next: a long prompt is
+ * processed in scheduled pieces; "12 KV Cache Quantization", Interaction
+ * with prefix caching: the pieces attend to quantized blocks already cached).
+ * Each sequence b brings a chunk of n_b = q_start[b + 1] - q_start[b]
+ * queries, its last n_b positions: their keys and values must already be in
+ * the cache (kvq_write before this call).  Query i of the chunk sits at
+ * position p = L_b - n_b + i and attends to tokens 0..p,
+ * o = softmax(q k_hat^T * sm_scale) V_hat, where L_b is ctx_lens[b] taken
+ * into [0, max_blocks_per_seq * block_size].  A query at p < 0 (a chunk
+ * longer than the context) gets an all-zero row.
+ *   q            fp16 (total_q, n_q_heads, D): the chunks one after another
+ *   q_start      int32 (batch + 1), non-decreasing, q_start[0] >= 0,
+ *                q_start[batch] <= total_q
+ *   block_table, max_blocks_per_seq, ctx_lens, sm_scale: as kvq_decode_attn
+ *                (KVQ_INT4_KIVI keys: sequence b's last L_b % 32 tokens are
+ *                read from tail row b)
+ *   max_q_len    an upper bound on every n_b (it sizes the grid); a longer
+ *                chunk is skipped and recorded as KVQ_DEVERR_QLEN
+ *   out          fp16 (total_q, n_q_heads, D), 16-byte aligned: rows of the
+ *                chunks are written, other rows are left as they are
+ *   workspace    at least kvq_prefill_workspace_bytes() (may be NULL when
+ *                that is 0), 16-byte aligned
+ * Query head hq reads KV head hq / (n_q_heads / n_kv_heads) ([P4] GQA).
+ * Scores and the softmax are accumulated in fp32 and the result is rounded
+ * to fp16 once; a given call gives bitwise the same result every time.
+ * KVQ_ERR_SHAPE when total_q x n_q_heads x head_dim reaches 2^31 or
+ * max_q_len x n_q_heads / n_kv_heads reaches 2^30; KVQ_ERR_UNSUPPORTED for
+ * KVQ_INT4_G32 keys. */
+int kvq_prefill_attn(const kvq_cache* cache, const void* q,
+                     const int32_t* q_start, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, const int32_t* ctx_lens,
+                     int32_t batch, int64_t total_q, int32_t n_q_heads,
+                     int32_t max_q_len, float sm_scale, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Copy whole pages between two caches of the same geometry and formats
  * (block_size, n_kv_heads, head_dim, k_dtype, v_dtype; num_blocks may

@@ -24,10 +24,11 @@ DTYPES = {"int8": 1, "fp8_e4m3fn": 2, "int4_g32": 3, "int4_kivi": 4, "fp8_e5m2":
 # Functions declared in include/kvq.h (the symbol test checks this list
 # against the header).
 EXPORTS = ("kvq_write", "kvq_write_static", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_status_string",
-           "kvq_get_device_error", "kvq_decode_attn_noalloc", "kvq_copy_blocks")
+           "kvq_get_device_error", "kvq_decode_attn_noalloc", "kvq_copy_blocks", "kvq_prefill_workspace_bytes",
+           "kvq_prefill_attn")
 NOALLOC_WORKSPACE_BYTES = 64 << 20  # KVQ_NOALLOC_WORKSPACE_BYTES
 # Bits of kvq_get_device_error (kvq_device_error in include/kvq.h).
-DEVERR = {"slot": 1, "seq": 2, "block": 4, "ctx": 8}
+DEVERR = {"slot": 1, "seq": 2, "block": 4, "ctx": 8, "qlen": 16}
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -80,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn_noalloc.restype = ctypes.c_int
         L.kvq_copy_blocks.argtypes = [cp, cp, vp, vp, i32, i32, vp]
         L.kvq_copy_blocks.restype = ctypes.c_int
+        L.kvq_prefill_workspace_bytes.argtypes = [cp, i64, i32, ctypes.POINTER(sz)]
+        L.kvq_prefill_workspace_bytes.restype = ctypes.c_int
+        L.kvq_prefill_attn.argtypes = [cp, vp, vp, vp, i32, vp, i32, i64, i32, i32, ctypes.c_float, vp, vp, sz, vp]
+        L.kvq_prefill_attn.restype = ctypes.c_int
         L.kvq_get_device_error.argtypes = [vp]
         L.kvq_get_device_error.restype = ctypes.c_int
         _lib = L
@@ -289,6 +294,51 @@ def decode_attn_noalloc(cache: PagedKVCache, q, block_table, ctx_lens, out, sm_s
                                        _stream(stream))
     if rc != KVQ_OK:
         raise KvqError(rc, "kvq_decode_attn_noalloc")
+    return out
+
+
+def prefill_workspace_bytes(cache: PagedKVCache, total_q, n_q_heads) -> int:
+    """kvq_prefill_workspace_bytes (0 unless the cache stores rotated keys)."""
+    n = ctypes.c_size_t(0)
+    c = cache.struct()
+    rc = lib().kvq_prefill_workspace_bytes(ctypes.byref(c), int(total_q), int(n_q_heads), ctypes.byref(n))
+    if rc != KVQ_OK:
+        raise KvqError(rc, "kvq_prefill_workspace_bytes")
+    return n.value
+
+
+def prefill_attn(cache: PagedKVCache, q, q_start, block_table, ctx_lens, max_q_len, sm_scale=0.0, out=None,
+                 workspace=None, stream=None):
+    """kvq_prefill_attn: causal attention of the chunks q (total_q, Hq, D)
+    fp16, sequence b's rows q_start[b] .. q_start[b + 1] - 1 (int32, B + 1),
+    over the cache; returns out (total_q, Hq, D) fp16."""
+    dev = cache.device
+    _check(q, torch.float16, "q", dev)
+    _check(q_start, torch.int32, "q_start", dev)
+    _check(block_table, torch.int32, "block_table", dev)
+    _check(ctx_lens, torch.int32, "ctx_lens", dev)
+    Tq, Hq, D = q.shape
+    B = ctx_lens.shape[0]
+    if (D != cache.head_dim or block_table.dim() != 2 or block_table.shape[0] != B or ctx_lens.dim() != 1
+            or q_start.shape != (B + 1,)):
+        raise ValueError("shape mismatch between q, q_start, block_table and ctx_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, torch.float16, "out", dev)
+    if out.shape != q.shape:
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    need = prefill_workspace_bytes(cache, Tq, Hq)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check(workspace, torch.uint8, "workspace", dev)
+    c = cache.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    rc = lib().kvq_prefill_attn(ctypes.byref(c), _ptr(q), _ptr(q_start), _ptr(block_table), block_table.shape[1],
+                                _ptr(ctx_lens), B, Tq, Hq, int(max_q_len), float(sm_scale), _ptr(out),
+                                _ptr(workspace), ws_bytes, _stream(stream))
+    if rc != KVQ_OK:
+        raise KvqError(rc, "kvq_prefill_attn")
     return out
 
 

@@ -33,6 +33,11 @@ SOURCES = {
     "kvq_decode_kfp8_rot.hip": [],
     "kvq_decode_ke5m2_rot.hip": [],
     "kvq_offload.hip": [],
+    "kvq_prefill.hip": [],
+    "kvq_prefill_kint8.hip": [],
+    "kvq_prefill_kfp8.hip": [],
+    "kvq_prefill_kkivi.hip": [],
+    "kvq_prefill_ke5m2.hip": [],
 }
 
 COMMON = [

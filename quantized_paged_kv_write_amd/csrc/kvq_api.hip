@@ -273,6 +273,87 @@ int kvq_decode_attn_noalloc(const kvq_cache* cache, const void* q, const int32_t
                      out, nullptr, 0, true, stream);
 }
 
+int kvq_prefill_workspace_bytes(const kvq_cache* cache, int64_t total_q, int32_t n_q_heads, size_t* bytes) {
+  int rc = check_cache(cache);
+  if (rc != KVQ_OK) return rc;
+  if (!bytes || total_q < 0 || n_q_heads <= 0) return KVQ_ERR_INVALID_ARG;
+  if (total_q * n_q_heads * (int64_t)cache->head_dim >= (1ll << 31)) return KVQ_ERR_SHAPE;
+  *bytes = (cache->flags & KVQ_ROTATE_K) ? 2 * (size_t)total_q * n_q_heads * cache->head_dim * 2 : 0;
+  return KVQ_OK;
+}
+
+int kvq_prefill_attn(const kvq_cache* cache, const void* q, const int32_t* q_start, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, const int32_t* ctx_lens, int32_t batch, int64_t total_q,
+                     int32_t n_q_heads, int32_t max_q_len, float sm_scale, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != KVQ_OK) return rc;
+  if (cache->k_dtype == KVQ_INT4_G32) return KVQ_ERR_UNSUPPORTED;
+  if (batch < 0 || total_q < 0 || n_q_heads <= 0 || max_blocks_per_seq <= 0 || max_q_len < 0)
+    return KVQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return KVQ_ERR_SHAPE;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return KVQ_ERR_INVALID_ARG;
+  const int32_t G = n_q_heads / cache->n_kv_heads;
+  if (total_q * n_q_heads * (int64_t)cache->head_dim >= (1ll << 31)) return KVQ_ERR_SHAPE;
+  if ((int64_t)max_q_len * G >= (1ll << 30)) return KVQ_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * cache->block_size >= (1ll << 30)) return KVQ_ERR_SHAPE;
+  if (batch == 0 || total_q == 0 || max_q_len == 0) return KVQ_OK;
+  if (cache->k_dtype == KVQ_INT4_KIVI && batch > cache->max_seqs) return KVQ_ERR_SHAPE;  // tail row per sequence
+  if (!q || !q_start || !block_table || !ctx_lens || !out) return KVQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(out) & 15) != 0 || (reinterpret_cast<uintptr_t>(q) & 15) != 0)
+    return KVQ_ERR_INVALID_ARG;
+  size_t need = 0;
+  rc = kvq_prefill_workspace_bytes(cache, total_q, n_q_heads, &need);
+  if (rc != KVQ_OK) return rc;
+  if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0))
+    return KVQ_ERR_WORKSPACE;
+  // query tiles of one (sequence, KV head): rows of 128 (head_dim <= 128) or 64
+  const int32_t rows_per_tile = cache->head_dim <= 128 ? 128 : 64;
+  const int64_t n_qtiles = ((int64_t)max_q_len * G + rows_per_tile - 1) / rows_per_tile;
+  const int64_t n_wg = (int64_t)batch * cache->n_kv_heads * n_qtiles;
+  if (n_wg >= (1ll << 31) - 8) return KVQ_ERR_SHAPE;
+  rc = device_present();
+  if (rc != KVQ_OK) return rc;
+  DeviceSymbols sym;
+  rc = device_symbols(&sym);
+  if (rc != KVQ_OK) return rc;
+  PrefillArgs a{};
+  a.err = sym.err;
+  a.q = static_cast<const uint16_t*>(q);
+  a.qrot = need > 0 ? static_cast<const uint16_t*>(workspace) : nullptr;
+  a.q_start = q_start;
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.Tq = total_q;
+  a.max_blocks = max_blocks_per_seq;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.H = cache->n_kv_heads;
+  a.G = G;
+  a.bs = cache->block_size;
+  a.log2_bs = 0;
+  while ((1 << a.log2_bs) < cache->block_size) ++a.log2_bs;
+  a.nb = cache->num_blocks;
+  a.max_q_len = max_q_len;
+  a.n_qtiles = (int32_t)n_qtiles;
+  a.n_wg = (int32_t)n_wg;
+  const float scale = sm_scale == 0.0f ? 1.0f / sqrtf((float)cache->head_dim) : sm_scale;
+  a.qscale = scale * 1.4426950408889634f;  // log2(e): the softmax runs on exp2
+  a.k_codes = static_cast<const uint8_t*>(cache->k_codes);
+  a.k_scales = static_cast<const uint16_t*>(cache->k_scales);
+  a.k_zeros = static_cast<const uint16_t*>(cache->k_zeros);
+  a.v_codes = static_cast<const uint8_t*>(cache->v_codes);
+  a.v_scales = static_cast<const uint16_t*>(cache->v_scales);
+  a.k_tail = static_cast<const uint16_t*>(cache->k_tail);
+  a.v_tail = static_cast<const uint16_t*>(cache->v_tail);
+  a.max_seqs = cache->max_seqs;
+  a.out = static_cast<uint16_t*>(out);
+  a.rot_k = (cache->flags & KVQ_ROTATE_K) ? 1 : 0;
+  a.rot_v = (cache->flags & KVQ_ROTATE_V) ? 1 : 0;
+  for (int i = 0; i < 8; ++i) a.rot_signs[i] = cache->rot_signs[i];
+  return launch_prefill(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
 int kvq_get_device_error(void* stream) {
   int rc = device_present();
   if (rc != KVQ_OK) return rc;

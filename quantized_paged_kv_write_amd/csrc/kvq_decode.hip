@@ -50,17 +50,23 @@ namespace {
 
 // The rotated query of rotated keys ("Quantized KV caches in production",
 // Numerical Formats: Walsh-Hadamard rotation): q' = H (sigma q) / D for every
-// (sequence, query head), written as fp16 hi = RN(q') and lo = RN(q' - hi).
-// One wave per row; lane l holds channels l CPL .. l CPL + CPL - 1.  The
-// transform runs in float64 and is exact (sums of at most 256 fp16 values);
-// 1/D is a power of two.
+// row (a query head of a sequence or of a chunk position), written as fp16
+// hi = RN(q') and lo = RN(q' - hi).  One wave per row; lane l holds channels
+// l CPL .. l CPL + CPL - 1.  The transform runs in float64 and is exact (sums
+// of at most 256 fp16 values); 1/D is a power of two.
+struct RotQArgs {
+  const uint16_t* q;
+  uint16_t* qrot;
+  size_t rows;
+  uint32_t signs[8];
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void rotate_q_kernel(RotQArgs a) {
   constexpr int CPL = D / 64;
   const int lane = (int)threadIdx.x & 63;
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const size_t rows = (size_t)a.B * a.Hq;
-  if (row >= rows) return;  // uniform over the wave
+  if (row >= a.rows) return;  // uniform over the wave
   const uint16_t* qr = a.q + row * D;
   double y[CPL];
 #pragma unroll
@@ -68,7 +74,7 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
     const int c = lane * CPL + i;
     uint32_t w = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w = (c >> 5) == k ? a.rot_signs[k] : w;
+    for (int k = 0; k < 8; ++k) w = (c >> 5) == k ? a.signs[k] : w;
     const double x = (double)h2f(qr[c]);
     y[i] = ((w >> (c & 31)) & 1) ? -x : x;
   }
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
     }
   }
   uint16_t* hi = a.qrot + row * D;
-  uint16_t* lo = a.qrot + rows * D + row * D;
+  uint16_t* lo = a.qrot + a.rows * D + row * D;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const double qp = y[i] * (1.0 / D);
@@ -101,9 +107,15 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t rotate_query(const kvq_cache& c, const DecodeArgs& a, hipStream_t s) {
-  const unsigned blocks = (unsigned)(((size_t)a.B * a.Hq + 3) / 4);
-  switch (c.head_dim) {
+}  // namespace
+
+hipError_t launch_rotate_query(const uint16_t* q, uint16_t* qrot, size_t rows, int D, const uint32_t* signs,
+                               hipStream_t s) {
+  RotQArgs a{q, qrot, rows, {}};
+  for (int i = 0; i < 8; ++i) a.signs[i] = signs[i];
+  if (rows == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  switch (D) {
     case 64: hipLaunchKernelGGL(rotate_q_kernel<64>, dim3(blocks), dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(rotate_q_kernel<128>, dim3(blocks), dim3(256), 0, s, a); break;
     case 256: hipLaunchKernelGGL(rotate_q_kernel<256>, dim3(blocks), dim3(256), 0, s, a); break;
@@ -112,11 +124,9 @@ hipError_t rotate_query(const kvq_cache& c, const DecodeArgs& a, hipStream_t s) 
   return hipGetLastError();
 }
 
-}  // namespace
-
 hipError_t launch_decode(const kvq_cache& c, const DecodeArgs& a, hipStream_t s) {
   if (a.rot_k) {
-    const hipError_t e = rotate_query(c, a, s);
+    const hipError_t e = launch_rotate_query(a.q, a.qrot, (size_t)a.B * a.Hq, c.head_dim, a.rot_signs, s);
     if (e != hipSuccess) return e;
     switch (c.k_dtype) {
       case F_INT8: return decode_keys_int8_rot(c.v_dtype, c.head_dim, a, s);

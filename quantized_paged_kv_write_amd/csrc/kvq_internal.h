@@ -87,6 +87,33 @@ struct DecodeArgs {
   uint16_t* qrot;
 };
 
+struct PrefillArgs {
+  const uint16_t* q;        // fp16 (Tq, Hq, D): the chunks of all sequences
+  const uint16_t* qrot;     // rotated keys: q' as fp16 hi (Tq, Hq, D) then lo
+  const int32_t* q_start;   // (B + 1): sequence b's queries are rows q_start[b] .. q_start[b + 1] - 1
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  int64_t Tq;               // rows of q and out
+  int32_t max_blocks;
+  int32_t B, Hq, H, G, bs, log2_bs, nb;
+  int32_t max_q_len;        // largest chunk the grid covers
+  int32_t n_qtiles;         // query tiles per (sequence, KV head)
+  int32_t n_wg;             // workgroups with work: B H n_qtiles
+  float qscale;             // sm_scale * log2(e)
+  const uint8_t* k_codes;
+  const uint16_t* k_scales;
+  const uint16_t* k_zeros;
+  const uint8_t* v_codes;
+  const uint16_t* v_scales;
+  const uint16_t* k_tail;
+  const uint16_t* v_tail;
+  int32_t max_seqs;
+  uint16_t* out;            // fp16 (Tq, Hq, D)
+  uint32_t* err;            // per-device kvq_device_error word
+  int32_t rot_k, rot_v;
+  uint32_t rot_signs[8];
+};
+
 // Workspace layout of one decode call (host side, no device needed).
 struct DecodePlan {
   int32_t share_tiles;   // requested S (0 = balanced)
@@ -115,6 +142,18 @@ hipError_t decode_keys_e5m2(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_int8_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_fp8_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_e5m2_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
+
+// The rotated query q' = H (sigma q) / D of `rows` fp16 rows of head_dim D,
+// written as fp16 hi (rows, D) at qrot and lo (rows, D) right after it.
+hipError_t launch_rotate_query(const uint16_t* q, uint16_t* qrot, size_t rows, int D, const uint32_t* signs,
+                               hipStream_t s);
+
+// Chunked-prefill attention (kvq_prefill*.hip).
+hipError_t launch_prefill(const kvq_cache& c, const PrefillArgs& a, hipStream_t s);
+hipError_t prefill_keys_int8(int fv, int D, bool rot, const PrefillArgs& a, hipStream_t s);
+hipError_t prefill_keys_fp8(int fv, int D, bool rot, const PrefillArgs& a, hipStream_t s);
+hipError_t prefill_keys_kivi(int fv, int D, bool rot, const PrefillArgs& a, hipStream_t s);
+hipError_t prefill_keys_e5m2(int fv, int D, bool rot, const PrefillArgs& a, hipStream_t s);
 
 
 }  // namespace kvq

@@ -177,3 +177,28 @@ def make_inputs(w: Workload, seed: int, device="cpu", ctx_lens=None, extra_block
     return Inputs(w=w, ctx_lens=ctx_lens, q=q.to(torch.float16), k=k.to(torch.float16), v=v.to(torch.float16),
                   seq_start=seq_start, num_blocks=num_blocks, block_table=block_table,
                   slot_mapping=slot_mapping, seq_idx=seq_idx, positions=positions, outlier_channels=outl)
+
+
+@dataclass
+class Chunks:
+    """Queries of a chunked-prefill step: sequence b brings q_lens[b] queries
+    (its last q_lens[b] positions), stored one sequence after another."""
+    q: torch.Tensor        # (Tq, Hq, D) fp16
+    q_start: torch.Tensor  # (B + 1,) int32
+    q_lens: list
+    max_q_len: int
+
+
+def chunk_queries(w: Workload, q_lens, seed: int, device="cpu") -> Chunks:
+    """Draw the chunk queries of one prefill step: N(0, 1) in fp32 from a
+    generator on `device` seeded with `seed` + 7919, rounded to fp16 (the
+    value distribution of the decode queries)."""
+    q_lens = [int(x) for x in q_lens]
+    Tq = sum(q_lens)
+    gen = torch.Generator(device=torch.device(device)).manual_seed(seed + 7919)
+    q = torch.randn((Tq, w.n_q_heads, w.head_dim), generator=gen, device=device, dtype=torch.float32)
+    starts = [0]
+    for n in q_lens:
+        starts.append(starts[-1] + n)
+    return Chunks(q=q.to(torch.float16), q_start=torch.tensor(starts, dtype=torch.int32), q_lens=q_lens,
+                  max_q_len=max(q_lens + [0]))
