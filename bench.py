@@ -26,6 +26,13 @@ one, under "workloads" (decode call and step GB/s, % of peak, write GB/s, and
 the quality statistic: the decode output against float64 attention over the
 unquantized fp16 K/V).  "stream_probes" are plain streaming rates of this GPU
 with the same 16-byte non-temporal accesses (libkvq_probe.so).
+
+Chunked prefill (--prefill A:n,B:m): over the filled cache of workload A, one
+kvq_prefill_attn call whose chunks are the last n positions of every
+sequence (their keys and values are already in the cache), timed with HIP
+events; reported under that workload's "prefill" entry as algorithmic
+TFLOP/s (4 D flops per visible (query head, token) pair: q.k and p v) against
+the 2.5 PFLOP/s dense fp16 peak, and chunk tokens per second.
 """
 
 from __future__ import annotations
@@ -41,6 +48,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD specification
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, AMD specification
 QMAX = {"int8": 127.0, "fp8_e4m3fn": 448.0, "fp8_e5m2": 57344.0, "int4_g32": 7.0}  # symmetric formats
 # sources of the decode kernels (their hash tags the committed counter summaries)
 DECODE_SRC = [os.path.join(ROOT, "quantized_paged_kv_write_amd", "csrc", f) for f in ("kvq_decode.h", "kvq_decode.hip")]
@@ -281,6 +289,57 @@ def stream_probes(dev):
     return res
 
 
+def prefill_flops(w, ctx_lens, q_lens) -> int:
+    """Algorithmic flops of one chunked-prefill call: query i of a chunk of n
+    over a context of L sees L - n + i + 1 tokens, each costing q.k and p v
+    (2 D flops each) per query head."""
+    tot = 0
+    for L, n in zip(ctx_lens, q_lens):
+        n = min(n, L)
+        tot += n * (L - n) + n * (n + 1) // 2
+    return 4 * w.head_dim * w.n_q_heads * tot
+
+
+def prefill_measure(w, inp, cache, chunk, reps, dev="cuda"):
+    """One chunked-prefill call over the filled cache (chunks = the last
+    `chunk` positions of every sequence), timed over `reps` calls."""
+    import torch
+
+    import quantized_paged_kv_write_amd as kvq
+    from quantized_paged_kv_write_amd import workloads as wl
+
+    qlen = [min(chunk, L) for L in inp.ctx_lens]
+    ch = wl.chunk_queries(w, qlen, wl.seed_of(w), dev)
+    q_start = ch.q_start.to(dev)
+    table = inp.block_table.to(dev)
+    ctx_d = torch.tensor(inp.ctx_lens, dtype=torch.int32, device=dev)
+    out = torch.empty_like(ch.q)
+    need = kvq.prefill_workspace_bytes(cache, ch.q.shape[0], w.n_q_heads)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        kvq.prefill_attn(cache, ch.q, q_start, table, ctx_d, ch.max_q_len, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        kvq.prefill_attn(cache, ch.q, q_start, table, ctx_d, ch.max_q_len, out=out, workspace=ws)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    ms = times[len(times) // 2]
+    flops = prefill_flops(w, inp.ctx_lens, qlen)
+    tf = flops / (ms * 1e9)
+    res = {"chunk": chunk, "query_rows": int(ch.q.shape[0]), "flops": flops, "call_ms_median": round(ms, 4),
+           "call_ms_min": round(times[0], 4), "TFLOPs": round(tf, 2),
+           "pct_mfma_peak_fp16": round(100 * tf / MFMA_PEAK_TFLOPS, 2),
+           "chunk_tokens_per_s": round(ch.q.shape[0] / (ms * 1e-3), 1),
+           "kernel": "prefill_kernel (one kvq_prefill_attn call)"}
+    print(f"[bench] {w.name}: prefill chunk {chunk} x {w.batch}: {ms:.3f} ms = {tf:.1f} TFLOP/s "
+          f"({res['pct_mfma_peak_fp16']:.1f}% of the fp16 MFMA peak)", file=sys.stderr, flush=True)
+    return res
+
+
 def measure(w, args, steps, warmup, dev="cuda", want_inputs=False):
     """Fill two identical caches with the workload's prefill, time the
     prefill write, then time `steps` decode steps (write of the new token of
@@ -430,6 +489,8 @@ def measure(w, args, steps, warmup, dev="cuda", want_inputs=False):
         "write_static_GBps": None if static_ms is None else round(wbytes / (static_ms * 1e6), 2),
     }
     res["quality"] = quality(w, inp, out)
+    if w.name in args.prefill_chunks:
+        res["prefill"] = prefill_measure(w, inp, caches[0], args.prefill_chunks[w.name], args.prefill_calls, dev)
     print(f"[bench] {w.name}: decode call {dec_ms:.4f} ms = {res['decode_call_GBps']:.0f} GB/s "
           f"({res['decode_call_pct_hbm_peak']:.1f}% of peak), quality max|err| {res['quality']['max_abs']:.3e} "
           f"rel L2 {res['quality']['rel_l2']:.3e}", file=sys.stderr, flush=True)
@@ -601,6 +662,7 @@ def offload_measure(args, dev="cuda", engine="kernel"):
 
 
 EXTRA_DEFAULT = "llama3_8b_int8k_int4v,llama3_70b_int8,llama3_8b_kivi_int4,llama3_70b_int8_rot"
+PREFILL_DEFAULT = "llama3_70b_int8:2048,llama3_8b_kivi_int4:2048,llama3_8b_fp8:512"
 
 
 def main():
@@ -625,10 +687,15 @@ def main():
     ap.add_argument("--no-offload", action="store_true")
     ap.add_argument("--offload-pages", type=int, default=10, help="pages of every sequence prefetched per step")
     ap.add_argument("--offload-steps", type=int, default=40)
+    ap.add_argument("--prefill", default=PREFILL_DEFAULT,
+                    help="workload:chunk pairs measured with one chunked-prefill call each ('none' for none)")
+    ap.add_argument("--prefill-calls", type=int, default=5)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="reduce two rocprofv3 counter CSVs to profiles/decode_<workload>_hbm_traffic.json")
     ap.add_argument("--pmc-command", default="", help="the command that produced the counter CSVs")
     args = ap.parse_args()
+    args.prefill_chunks = {} if args.prefill in ("", "none") else \
+        {x.split(":")[0]: int(x.split(":")[1]) for x in args.prefill.split(",") if x}
     if args.pmc_summary:
         d = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.pmc_command)
         os.makedirs(os.path.dirname(traffic_profile_path(args.workload)), exist_ok=True)
@@ -703,6 +770,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w.name),
                      "kernel": "plan_kernel + decode_split_kernel + merge_kernel (one kvq_decode_attn call)"},
         "workloads": workloads,
+        "prefill": {k: v["prefill"] for k, v in workloads.items() if "prefill" in v},
     }
     if cpu is not None:
         res["cpu_baseline"] = cpu

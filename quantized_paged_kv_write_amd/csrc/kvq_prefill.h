@@ -13,10 +13,13 @@
 //    rows).  Query rows are (position, query head) pairs, position-major, so
 //    the G heads of a position share every key and value the tile reads.
 //    Each wave holds NQB blocks of 16 rows: the 16 columns of its MFMAs.
-//  * Keys and values are read once per workgroup in tiles of 32 tokens:
-//    the 256 threads load tile x + 1 into registers while the waves compute
-//    tile x from LDS (two LDS buffers, one barrier per tile).  Block ids are
-//    fetched two tiles ahead.
+//  * Keys and values are read once per workgroup in tiles of 32 tokens: the
+//    256 threads load tile x + 2 into registers while the waves compute from
+//    LDS, and store it at the end of the step (three LDS buffers, one barrier
+//    per tile).  In the step of tile x each wave issues the score MFMAs of
+//    tile x + 1 before the softmax and P V of tile x, so matrix and vector
+//    work of one wave overlap.  Key codes are converted to fp16 once, when
+//    stored.  Block ids are fetched two tiles ahead of their loads.
 //  * Workgroup order: the grid is dealt to the 8 XCDs round robin; the
 //    workgroups an XCD receives are consecutive (sequence, KV head, tile)
 //    triples, so the ~64 workgroups resident on one XCD read the same
@@ -50,10 +53,11 @@ struct PLayout {
   static constexpr int NWAVE = 4;
   static constexpr int THREADS = 64 * NWAVE;
   static constexpr int ROWS = NWAVE * 16 * NQB;  // query rows per workgroup
-  // LDS: two buffers of [keys | values | key scales fp32 | value scales fp32]
-  // (KIVI keys: fp16 hi plane then lo plane), then (KIVI) the tail's values
-  // transposed, fp16 [D][32].
-  static constexpr int KRB = KIVI ? 2 * D : D;  // key row bytes in LDS (per plane)
+  // LDS: three buffers of [keys fp16 | value codes | key scales fp32 | value
+  // scales fp32] (KIVI keys: fp16 hi plane then lo plane), then (KIVI) the
+  // tail's values transposed, fp16 [D][32].  Value scales of INT4 groups are
+  // stored group-major, [group][token].
+  static constexpr int KRB = 2 * D;             // key row bytes in LDS: fp16 (KIVI: per plane)
   static constexpr int KCH = KRB / 16;          // 16-byte chunks per key row
   static constexpr int KPLANE = TILE * KRB;
   static constexpr int OFF_K = 0;
@@ -61,8 +65,9 @@ struct PLayout {
   static constexpr int OFF_FK = OFF_V + TILE * VS::RB;
   static constexpr int OFF_FV = OFF_FK + 4 * TILE;
   static constexpr int BUF = (OFF_FV + 4 * TILE * VS::NG + 15) / 16 * 16;
-  static constexpr int OFF_VT = 2 * BUF;
-  static constexpr int LDS = 2 * BUF + (KIVI ? D * TILE * 2 : 0);
+  static constexpr int NBUF = 3;  // tiles x (softmax, P V), x + 1 (scores), x + 2 (being stored)
+  static constexpr int OFF_VT = NBUF * BUF;
+  static constexpr int LDS = NBUF * BUF + (KIVI ? D * TILE * 2 : 0);
   // a tile's 16-byte chunks of key codes (8-bit formats) and value codes
   static constexpr int NK = TILE * (D / 16);
   static constexpr int NLK = (NK + THREADS - 1) / THREADS;
@@ -100,9 +105,24 @@ struct PRegs {
   u4 ks[PL::KIVI ? PL::KM : 1];  // KIVI: scales of the thread's channels (tail tile: the key row)
   u4 kz[PL::KIVI ? PL::KM : 1];  // KIVI: zero points (tail tile: the value row)
   u4 v[PL::NLV];
-  uint32_t fk;                   // wave 0, lanes < 32: fp16 key scale of token lane
+  uint16_t fk;                   // wave 0, lanes < 32: fp16 key scale of token lane
   u4 fv;                         // wave 0, lanes >= 32: fp16 value scales of token lane - 32
 };
+
+// Value operand of 8-bit codes (as value_operand_8bit) whose INT8 codes were
+// stored already biased to c + 128: the bf16 bit patterns u (u 2^-133) are
+// placed by two byte permutes per dword pair, no xor.
+template <int FV>
+__device__ __forceinline__ b8 value_operand_biased(i2 t) {
+  if constexpr (FV != F_INT8) {
+    return value_operand_8bit<FV>(t);
+  } else {
+    const uint32_t d0 = (uint32_t)t.x, d1 = (uint32_t)t.y;
+    const u4 r = {__builtin_amdgcn_perm(0u, d0, 0x0C010C00u), __builtin_amdgcn_perm(0u, d0, 0x0C030C02u),
+                  __builtin_amdgcn_perm(0u, d1, 0x0C010C00u), __builtin_amdgcn_perm(0u, d1, 0x0C030C02u)};
+    return __builtin_bit_cast(b8, r);
+  }
+}
 
 // fp16 pair -> bf16 hi (truncated) and lo = x - hi; both exact (an fp16
 // value has 11 significant bits, hi keeps 8)
@@ -129,7 +149,6 @@ __attribute__((amdgpu_waves_per_eu(prefill_wpe<FK, FV, D, ROTQ>(), prefill_wpe<F
 void prefill_kernel(PrefillArgs a) {
   using PL = PLayout<FK, FV, D>;
   using VS = VShape<FV, D>;
-  using KS = KShape<FK == F_KIVI ? F_INT8 : FK, D>;  // 8-bit key row geometry
   constexpr int NQB = PL::NQB, KB = D / 32;
   constexpr bool KIVI = FK == F_KIVI;
   constexpr bool VFP8 = FV == F_FP8 || FV == F_E5M2;
@@ -145,9 +164,11 @@ void prefill_kernel(PrefillArgs a) {
   const int bh = logical / a.n_qtiles;
   const int qt = a.n_qtiles - 1 - (logical - bh * a.n_qtiles);
   const int b = bh / a.H, h = bh - b * a.H;
-  const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = (int)threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave of the workgroup (uniform)
   const int j = lane >> 4, n = lane & 15;
-  const int r0q = a.q_start[b], r1q = a.q_start[b + 1];
+  const int r0q = __builtin_amdgcn_readfirstlane(a.q_start[b]);
+  const int r1q = __builtin_amdgcn_readfirstlane(a.q_start[b + 1]);
   const int nq = r1q - r0q;
   if (r0q < 0 || (int64_t)r1q > a.Tq || nq < 0 || nq > a.max_q_len) {
     // a malformed chunk: the sequence is skipped
@@ -158,7 +179,7 @@ void prefill_kernel(PrefillArgs a) {
   const int R0 = qt * PL::ROWS;
   if (R0 >= rows) return;
   const int cap = a.max_blocks << a.log2_bs;
-  const int rawL = a.ctx_lens[b];
+  const int rawL = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
   const int L = min(max(rawL, 0), cap);
   if (qt == 0 && h == 0 && wv == 0) report_error(a.err, lane == 0 && (rawL < 0 || rawL > cap), KVQ_DEVERR_CTX);
   const int pos0 = L - nq;  // position of the chunk's first query
@@ -193,14 +214,14 @@ void prefill_kernel(PrefillArgs a) {
     }
   }
   // positions of the wave's first and last live rows (uniform)
-  const int pos_lo = Rw < rows ? pos0 + Rw / a.G : INT_MAX;
-  const int pos_hi = Rw < rows ? pos0 + (min(Rw + 16 * NQB, rows) - 1) / a.G : -1;
+  const int pos_lo = __builtin_amdgcn_readfirstlane(Rw < rows ? pos0 + Rw / a.G : INT_MAX);
+  const int pos_hi = __builtin_amdgcn_readfirstlane(Rw < rows ? pos0 + (min(Rw + 16 * NQB, rows) - 1) / a.G : -1);
 
   // ---- tiles ---------------------------------------------------------------
   const int pos_max = pos0 + (min(R0 + PL::ROWS, rows) - 1) / a.G;  // last position of the workgroup
   const int Lq = KIVI ? (L & ~31) : L;                               // tokens in quantized pages
   const int nt = pos_max >= 0 ? pos_max / TILE + 1 : 0;              // tiles with visible tokens
-  const int ntm = min(nt, (Lq + TILE - 1) / TILE);                   // of those, read from pages
+  const int ntm = __builtin_amdgcn_readfirstlane(min(nt, (Lq + TILE - 1) / TILE));  // of those, read from pages
   const bool tail = KIVI && nt > ntm;                                // KIVI: the fp16 tail is visible
 
   f4 acc[NQB][VS::NPV];
@@ -215,10 +236,15 @@ void prefill_kernel(PrefillArgs a) {
     for (int g = 0; g < NCS; ++g) cs_run[cb][g] = 0.f;
   }
 
-  // block id of token 32 x + lane % 32 (-1 past the quantized tokens)
+  // Block-table entry of the page of token 32 x + lane % 32, clamped to the
+  // sequence's last quantized page (tokens past Lq are masked where the id
+  // is used).  Always issued and never copied before its use a tile later,
+  // so the wait for it never covers the tile loads issued after it.
+  const int last_page = Lq > 0 ? (Lq - 1) >> a.log2_bs : 0;
+  const int* bt_row = a.block_table + (size_t)b * a.max_blocks;
   auto load_id = [&](int x) __attribute__((always_inline)) {
     const int tok = TILE * x + (lane & 31);
-    return (x < ntm && tok < Lq) ? a.block_table[(size_t)b * a.max_blocks + (tok >> a.log2_bs)] : -1;
+    return bt_row[min(tok >> a.log2_bs, last_page)];
   };
 
   // Issue the loads of page tile x (block id `id` of token lane % 32);
@@ -237,8 +263,7 @@ void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < PL::NLK; ++i) {
         const int p = tid + PL::THREADS * i;
         if (PL::NK % PL::THREADS == 0 || p < PL::NK) {
-          const int row = p / CHK;
-          const int col = (p % CHK) ^ kswz<CHK>(row);
+          const int row = p / CHK, col = p % CHK;
           const uint32_t fr = (uint32_t)__shfl((int)flat, row);
           r.k[i] = *reinterpret_cast<const u4*>(a.k_codes + (size_t)fr * D + col * 16);
         }
@@ -268,11 +293,10 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
     if (wv == 0) {
-      if (lane < 32) {
-        if constexpr (!KIVI) r.fk = (uint32_t)a.k_scales[flat];
-      } else {
-        r.fv = load_n<2 * VS::NG>(a.v_scales + (size_t)flat * VS::NG);
-      }
+      // every lane loads both (lanes < 32 keep the key scale, the others
+      // the value scales), so no branch waits on a load
+      if constexpr (!KIVI) r.fk = a.k_scales[flat];
+      r.fv = load_n<2 * VS::NG>(a.v_scales + (size_t)flat * VS::NG);
     }
     return live;
   };
@@ -284,8 +308,22 @@ void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < PL::NLK; ++i) {
         const int p = tid + PL::THREADS * i;
         if (PL::NK % PL::THREADS == 0 || p < PL::NK) {
-          const bool lv = (live >> (p / CHK)) & 1u;
-          reinterpret_cast<u4*>(buf + PL::OFF_K)[p] = lv ? r.k[i] : u4{0u, 0u, 0u, 0u};
+          // 16 codes of row p / CHK, channels 16 (p % CHK) ..: exact fp16
+          // values, 16-byte chunks 2 (p % CHK) and 2 (p % CHK) + 1 of the row
+          const int row = p / CHK, col = p % CHK;
+          const bool lv = (live >> row) & 1u;
+          const u4 c = lv ? r.k[i] : u4{0u, 0u, 0u, 0u};
+          const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+          uint32_t hw[8];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            if constexpr (FK == F_FP8) fp8_to_h4(cw[w], hw[2 * w], hw[2 * w + 1]);
+            else if constexpr (FK == F_E5M2) e5m2_to_h4(cw[w], hw[2 * w], hw[2 * w + 1]);
+            else int8_to_h4(cw[w], hw[2 * w], hw[2 * w + 1]);
+          }
+          u4* kr = reinterpret_cast<u4*>(buf + PL::OFF_K);
+          kr[row * PL::KCH + ((2 * col) ^ kswz<PL::KCH>(row))] = u4{hw[0], hw[1], hw[2], hw[3]};
+          kr[row * PL::KCH + ((2 * col + 1) ^ kswz<PL::KCH>(row))] = u4{hw[4], hw[5], hw[6], hw[7]};
         }
       }
     } else {
@@ -324,7 +362,9 @@ void prefill_kernel(PrefillArgs a) {
       const int p = tid + PL::THREADS * i;
       if (PL::NV % PL::THREADS == 0 || p < PL::NV) {
         const bool lv = (live >> (p / VS::CH)) & 1u;
-        reinterpret_cast<u4*>(buf + PL::OFF_V)[p] = lv ? r.v[i] : u4{0u, 0u, 0u, 0u};
+        u4 v = lv ? r.v[i] : u4{0u, 0u, 0u, 0u};
+        if constexpr (FV == F_INT8) v ^= 0x80808080u;  // codes c + 128 (unsigned), see value_operand_biased
+        reinterpret_cast<u4*>(buf + PL::OFF_V)[p] = v;
       }
     }
     if (wv == 0) {
@@ -337,7 +377,7 @@ void prefill_kernel(PrefillArgs a) {
       } else {
 #pragma unroll
         for (int g = 0; g < VS::NG; ++g)
-          fv[t * VS::NG + g] = lv ? h2f(u4_word(r.fv, g / 2) >> (16 * (g & 1))) * VSC : 0.f;
+          fv[g * TILE + t] = lv ? h2f(u4_word(r.fv, g / 2) >> (16 * (g & 1))) * VSC : 0.f;
       }
     }
   };
@@ -348,73 +388,80 @@ void prefill_kernel(PrefillArgs a) {
   const int tbase = PL::OFF_V + trow * VS::RB + 8 * (n & 1);
   const int tswz = vswz<VS::CH>(trow);
 
-  // Scores, online softmax and P V of one tile held in LDS buffer `buf`.
-  // TAILT: the KIVI tail tile (fp16 keys in the hi plane, lo plane unused;
-  // fp16 values transposed at OFF_VT; valid tokens t < ntail).
-  auto compute = [&](const uint8_t* buf, int x, uint32_t live, int ntail, auto tailc) __attribute__((always_inline)) {
+  // Raw scores S^T = K Q^T of tile x (held in LDS buffer `buf`) on the matrix
+  // cores.  TAILT: the KIVI tail tile (fp16 keys in the hi plane only).
+  auto scores = [&](const uint8_t* buf, int x, f4 (&sc)[NQB][2], auto tailc) __attribute__((always_inline)) {
     constexpr bool TAILT = decltype(tailc)::value;
-    const int t0 = TILE * x;
-    if (pos_hi < t0) return;  // every query of the wave precedes the tile
-    const bool full = !TAILT && live == 0xFFFFFFFFu && t0 + TILE - 1 <= pos_lo;
-    // ---- scores S^T on the matrix cores ----
-    f4 sc[NQB][2];
+    if (pos_hi < TILE * x) return;  // every query of the wave precedes the tile
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int row = 16 * u + n;
 #pragma unroll
       for (int cb = 0; cb < NQB; ++cb) sc[cb][u] = f4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (!KIVI) {
-        uint32_t kw[KS::NW];
 #pragma unroll
-        for (int q = 0; q < KS::LB / 16; ++q) {
-          const int col = (j * KS::LB / 16 + q) ^ kswz<CHK>(row);
-          const u4 v = *reinterpret_cast<const u4*>(buf + PL::OFF_K + (row * CHK + col) * 16);
-          kw[4 * q] = v.x; kw[4 * q + 1] = v.y; kw[4 * q + 2] = v.z; kw[4 * q + 3] = v.w;
+      for (int kb = 0; kb < KB; ++kb) {
+        const int c = j * (D / 32) + kb;
+        const int off = PL::OFF_K + (row * PL::KCH + (c ^ kswz<PL::KCH>(row))) * 16;
+        const h8 kh = *reinterpret_cast<const h8*>(buf + off);
+#pragma unroll
+        for (int cb = 0; cb < NQB; ++cb) {
+          sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qop[cb][kb], sc[cb][u], 0, 0, 0);
+          if constexpr (ROTQ) sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qlo[cb][kb], sc[cb][u], 0, 0, 0);
         }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const h8 kop = key_operand<FK>(kw, kb);
-#pragma unroll
-          for (int cb = 0; cb < NQB; ++cb) {
-            sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[cb][kb], sc[cb][u], 0, 0, 0);
-            if constexpr (ROTQ) sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qlo[cb][kb], sc[cb][u], 0, 0, 0);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int c = j * (D / 32) + kb;
-          const int off = PL::OFF_K + (row * PL::KCH + (c ^ kswz<PL::KCH>(row))) * 16;
-          const h8 kh = *reinterpret_cast<const h8*>(buf + off);
+        if constexpr (KIVI && !TAILT) {
+          const h8 kl = *reinterpret_cast<const h8*>(buf + off + PL::KPLANE);
 #pragma unroll
           for (int cb = 0; cb < NQB; ++cb)
-            sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qop[cb][kb], sc[cb][u], 0, 0, 0);
-          if constexpr (!TAILT) {
-            const h8 kl = *reinterpret_cast<const h8*>(buf + off + PL::KPLANE);
-#pragma unroll
-            for (int cb = 0; cb < NQB; ++cb)
-              sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl, qop[cb][kb], sc[cb][u], 0, 0, 0);
-          }
+            sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl, qop[cb][kb], sc[cb][u], 0, 0, 0);
         }
       }
     }
+  };
+
+  // Online softmax and P V of tile x (held in LDS buffer `buf`) from its raw
+  // scores.  TAILT: the KIVI tail tile (fp16 values transposed at OFF_VT;
+  // valid tokens t < ntail).
+  auto softmax_pv = [&](const uint8_t* buf, int x, uint32_t live, int ntail, const f4 (&sc)[NQB][2], auto tailc)
+                        __attribute__((always_inline)) {
+    constexpr bool TAILT = decltype(tailc)::value;
+    const int t0 = TILE * x;
+    if (pos_hi < t0) return;  // every query of the wave precedes the tile
+    const bool full = !TAILT && live == 0xFFFFFFFFu && t0 + TILE - 1 <= pos_lo;
     const float* fk = reinterpret_cast<const float*>(buf + PL::OFF_FK);
     const float* fv = reinterpret_cast<const float*>(buf + PL::OFF_FV);
+    // key scales of the lane's 8 tokens 16 u + 4 j + r (fp32, x sm_scale log2 e)
+    f4 fk4[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if constexpr (KIVI) fk4[u] = f4{a.qscale, a.qscale, a.qscale, a.qscale};
+      else fk4[u] = *reinterpret_cast<const f4*>(fk + 16 * u + 4 * j);
+    }
+    // tokens of the lane (bit 4 u + r: token 16 u + 4 j + r) that are live
+    // (in the tail tile: below ntail)
+    uint32_t lvm = 0xFFu;
+    if (!full) {
+      const uint32_t lv = TAILT ? (ntail >= 32 ? 0xFFFFFFFFu : (1u << ntail) - 1u) : live;
+      lvm = ((lv >> (4 * j)) & 0xFu) | (((lv >> (16 + 4 * j)) & 0xFu) << 4);
+    }
     float p[NQB][2][4];
 #pragma unroll
     for (int cb = 0; cb < NQB; ++cb) {
       float s[2][4];
       float tmax = -INFINITY;
+      // visible: live and at or before the column's position: tokens
+      // 16 u + 4 j + r <= lim (with lim = pos - t0 - 4 j), r < 4
+      uint32_t vm = 0xFFu;
+      if (!full) {
+        const int lim = pos_c[cb] - t0 - 4 * j;
+        const int n0 = min(max(lim + 1, 0), 4), n1 = min(max(lim - 15, 0), 4);
+        vm = lvm & (((1u << n0) - 1u) | (((1u << n1) - 1u) << 4));
+      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 16 * u + 4 * j + r;
-          float v = KIVI ? sc[cb][u][r] * a.qscale : sc[cb][u][r] * fk[t];
-          if (!full) {
-            const bool lv = TAILT ? t < ntail : ((live >> t) & 1u) != 0u;
-            v = (lv && t0 + t <= pos_c[cb]) ? v : -INFINITY;
-          }
+          float v = sc[cb][u][r] * fk4[u][r];
+          if (!full) v = ((vm >> (4 * u + r)) & 1u) ? v : -INFINITY;
           s[u][r] = v;
           tmax = fmaxf(tmax, v);
         }
@@ -491,7 +538,7 @@ void prefill_kernel(PrefillArgs a) {
           for (int q = 0; q < 4; ++q) {
             const int u = q >> 1, r0 = q & 1;
             const int ta = 16 * u + 4 * j + r0;
-            split_bf16x2(f2{p[cb][u][r0] * fv[ta * VS::NG + grp], p[cb][u][r0 + 2] * fv[(ta + 2) * VS::NG + grp]},
+            split_bf16x2(f2{p[cb][u][r0] * fv[grp * TILE + ta], p[cb][u][r0 + 2] * fv[grp * TILE + ta + 2]},
                          ah[q], al[q]);
             cs_run[cb][grp] = add_split(cs_run[cb][grp], ah[q], al[q]);
           }
@@ -528,7 +575,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int m = 0; m < VS::NPV; ++m) {
         const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(buf + tbase + ((m ^ tswz) << 4)));
-        const b8 vop = value_operand_8bit<FV>(raw);
+        const b8 vop = value_operand_biased<FV>(raw);
 #pragma unroll
         for (int cb = 0; cb < NQB; ++cb) {
           acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph[cb], acc[cb][m], 0, 0, 0);
@@ -538,24 +585,48 @@ void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- page tiles: load x + 1 while x is computed ----------------------------
+  // ---- page tiles, software-pipelined over three LDS buffers: in the step
+  //      of tile x the waves issue the scores of tile x + 1, then run the
+  //      softmax and P V of tile x (so the matrix cores work on x + 1 while
+  //      the vector units work on x), while the loads of tile x + 2 are in
+  //      flight; tile x + 2 is stored at the end of the step. -------------------
+  auto lbuf = [&](int i) __attribute__((always_inline)) { return s_lds + i * PL::BUF; };
   if (ntm > 0) {
     PRegs<FK, FV, D> regs;
-    int id_next = load_id(1), id_next2 = load_id(2);
-    uint32_t live_cur = load_tile(0, load_id(0), regs);
-    store_tile(regs, live_cur, s_lds);
+    const int id0 = load_id(0), id1 = load_id(min(1, ntm - 1));
+    int id2 = load_id(min(2, ntm - 1)), id3 = load_id(min(3, ntm - 1));
+    const uint32_t live0 = load_tile(0, id0, regs);
+    store_tile(regs, live0, lbuf(0));
+    const uint32_t live1 = load_tile(min(1, ntm - 1), id1, regs);
+    store_tile(regs, live1, lbuf(1));
     __syncthreads();
+    f4 sc_next[NQB][2];
+#pragma unroll
+    for (int cb = 0; cb < NQB; ++cb) sc_next[cb][0] = sc_next[cb][1] = f4{0.f, 0.f, 0.f, 0.f};
+    scores(lbuf(0), 0, sc_next, std::false_type{});
+    uint32_t live_cur = live0, live_nx = live1;
+    int bx = 0;  // buffer of tile x (x mod 3)
     for (int x = 0; x < ntm; ++x) {
-      uint32_t live_next = 0;
-      if (x + 1 < ntm) {
-        live_next = load_tile(x + 1, id_next, regs);
-        id_next = id_next2;
-        id_next2 = load_id(x + 3);
+      const int b1 = bx == 2 ? 0 : bx + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+      // tile x + 2 (the last tile again past the end: loaded and stored into
+      // the free buffer, never read), then the ids of tile x + 4
+      const int x2 = min(x + 2, ntm - 1);
+      const uint32_t live_n2 = load_tile(x2, id2, regs);
+      id2 = id3;
+      id3 = load_id(min(x + 4, ntm - 1));
+      f4 sc_cur[NQB][2];
+#pragma unroll
+      for (int cb = 0; cb < NQB; ++cb) {
+        sc_cur[cb][0] = sc_next[cb][0];
+        sc_cur[cb][1] = sc_next[cb][1];
       }
-      compute(s_lds + (x & 1) * PL::BUF, x, live_cur, 0, std::false_type{});
-      if (x + 1 < ntm) store_tile(regs, live_next, s_lds + ((x + 1) & 1) * PL::BUF);
+      if (x + 1 < ntm) scores(lbuf(b1), x + 1, sc_next, std::false_type{});
+      softmax_pv(lbuf(bx), x, live_cur, 0, sc_cur, std::false_type{});
+      store_tile(regs, live_n2, lbuf(b2));
       __syncthreads();
-      live_cur = live_next;
+      live_cur = live_nx;
+      live_nx = live_n2;
+      bx = b1;
     }
   }
 
@@ -665,7 +736,11 @@ void prefill_kernel(PrefillArgs a) {
       vt[(cg * PL::KE + e) * TILE + t] = (uint16_t)(w >> (16 * (e & 1)));
     }
     __syncthreads();
-    compute(buf, Lq / TILE, 0u, ntail, std::true_type{});
+    f4 sc[NQB][2];
+#pragma unroll
+    for (int cb = 0; cb < NQB; ++cb) sc[cb][0] = sc[cb][1] = f4{0.f, 0.f, 0.f, 0.f};
+    scores(buf, Lq / TILE, sc, std::true_type{});
+    softmax_pv(buf, Lq / TILE, 0u, ntail, sc, std::true_type{});
   }
 
   // ---- out = acc / l, fp16 -------------------------------------------------

@@ -65,4 +65,12 @@ def _check_piece(p: dict) -> dict:
             res["q_maxabs"] = float(np.max(np.abs(got - ref0)))
             res["q_l2_num"] = float(np.sum((got - ref0) ** 2))
             res["q_l2_den"] = float(np.sum(ref0 ** 2))
+    if p.get("pf_q") is not None:
+        # sampled rows of a chunked-prefill call over the same pages: causal
+        # attention of the query at each sampled position
+        K, V = o.gather_dequant(c, np.arange(npg), L, 0)
+        ref = o.causal_attention_fp64(p["pf_q"], K, V, p["pf_pos"])
+        got = p["pf_out"].astype(np.float64)
+        res["pf_err"] = float(np.max(np.abs(got - ref))) if got.size else 0.0
+        res["pf_rows"] = int(got.shape[0] * got.shape[1])
     return res

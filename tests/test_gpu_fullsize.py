@@ -4,6 +4,9 @@ sequence (one call), a write of the last token of every sequence (one call),
 then one decode step with the automatic partition.  Every byte of the cache
 (codes, scales, zero points, KIVI tails) is compared with the oracle, and so
 is every (sequence, query head) row of the decode output (within 2e-3).
+Then one chunked-prefill call over the same cache (a chunk of the last
+positions of every sequence) is checked on sampled positions: every query
+head of each sampled position, against the oracle's causal attention.
 
 The oracle runs per sequence and slice of KV heads, in a pool of fresh
 worker processes (NumPy only; they never touch the GPU)."""
@@ -26,18 +29,19 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 WORKERS = max(1, min(8, (os.cpu_count() or 2) - 1))
 
-# name -> (workload, context lengths or None for the workload's own)
+# name -> (workload, context lengths or None for the workload's own, prefill chunk)
 CASES = {
-    "llama3_8b_fp8": ("llama3_8b_fp8", None),
-    "llama3_8b_int8k_int4v": ("llama3_8b_int8k_int4v", None),
-    "llama3_70b_int8": ("llama3_70b_int8", None),
-    "llama3_8b_kivi_int4": ("llama3_8b_kivi_int4", None),
+    "llama3_8b_fp8": ("llama3_8b_fp8", None, 512),
+    "llama3_8b_int8k_int4v": ("llama3_8b_int8k_int4v", None, 1000),
+    "llama3_70b_int8": ("llama3_70b_int8", None, 2048),
+    "llama3_8b_kivi_int4": ("llama3_8b_kivi_int4", None, 2048),
     # the KIVI shape with fp16 tails of 31, 1 and 15 tokens (and none)
-    "llama3_8b_kivi_int4_tails": ("llama3_8b_kivi_int4", [131072, 131071, 131041, 131055]),
-    "llama3_8b_e5m2": ("llama3_8b_e5m2", None),
+    "llama3_8b_kivi_int4_tails": ("llama3_8b_kivi_int4", [131072, 131071, 131041, 131055], 2048),
+    "llama3_8b_e5m2": ("llama3_8b_e5m2", None, 512),
     # Walsh-Hadamard rotated keys and values
-    "llama3_70b_int8_rot": ("llama3_70b_int8_rot", None),
+    "llama3_70b_int8_rot": ("llama3_70b_int8_rot", None, 2048),
 }
+PF_SAMPLES = 24  # sampled positions per sequence
 
 
 @pytest.fixture(scope="module")
@@ -48,7 +52,7 @@ def pool():
 
 
 def _run_workload(name):
-    wname, ctx = CASES[name]
+    wname, ctx, chunk = CASES[name]
     w = wl.WORKLOADS[wname]
     seed = wl.seed_of(w)
     inp = wl.make_inputs(w, seed, DEV, ctx_lens=ctx)
@@ -66,12 +70,16 @@ def _run_workload(name):
               seqs[last].to(DEV))
     ctx_d = torch.tensor(inp.ctx_lens, dtype=torch.int32, device=DEV)
     out = kvq.decode_attn(cache, inp.q, inp.block_table.to(DEV), ctx_d)
+    # chunked prefill over the same cache: the last `chunk` positions of every sequence
+    qlen = [min(chunk, L) for L in inp.ctx_lens]
+    ch = wl.chunk_queries(w, qlen, seed, DEV)
+    pf = kvq.prefill_attn(cache, ch.q, ch.q_start.to(DEV), inp.block_table.to(DEV), ctx_d, ch.max_q_len)
     torch.cuda.synchronize()
     assert kvq.get_device_error() == 0
-    return w, inp, cache, out
+    return w, inp, cache, out, (ch, pf)
 
 
-def _pieces(w, inp, cache, out):
+def _pieces(w, inp, cache, out, prefill):
     """Per (sequence, KV-head slice): the host data a worker needs."""
     H, D, bs = w.n_kv_heads, w.head_dim, w.block_size
     G = w.n_q_heads // H
@@ -83,6 +91,9 @@ def _pieces(w, inp, cache, out):
     v_host = inp.v.cpu().numpy()
     q_host = inp.q.cpu().numpy()
     out_host = out.cpu().numpy()
+    ch, pf = prefill
+    pf_q, pf_out = ch.q.cpu().numpy(), pf.cpu().numpy()
+    rng = np.random.default_rng(wl.seed_of(w) + 100)
     for b in range(w.batch):
         L = inp.ctx_lens[b]
         st = inp.seq_start[b]
@@ -98,6 +109,10 @@ def _pieces(w, inp, cache, out):
                 gathered[name] = t[b].cpu().numpy()
             else:
                 gathered[name] = t[blocks].cpu().numpy()
+        n = ch.q_lens[b]
+        pick = np.unique(np.concatenate([[0, 1, n - 2, n - 1], rng.integers(0, n, PF_SAMPLES - 4)]))
+        pick = pick[(pick >= 0) & (pick < n)]
+        rows = int(ch.q_start[b]) + pick
         for h0 in range(0, H, hs):
             pages = {}
             for name, a in gathered.items():
@@ -110,6 +125,8 @@ def _pieces(w, inp, cache, out):
                 "k16": k_host[st:st + L, h0:h0 + hs], "v16": v_host[st:st + L, h0:h0 + hs], "pages": pages,
                 "q": q_host[b, h0 * G:(h0 + hs) * G], "out": out_host[b, h0 * G:(h0 + hs) * G],
                 "rot_k": signs if w.rotate_k else None, "rot_v": signs if w.rotate_v else None,
+                "pf_q": pf_q[rows, h0 * G:(h0 + hs) * G], "pf_out": pf_out[rows, h0 * G:(h0 + hs) * G],
+                "pf_pos": L - n + pick,
             }
 
 
@@ -118,12 +135,13 @@ def test_full_size_whole_cache_and_every_row(name, pool):
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import kvq_fullsize
     t0 = time.time()
-    w, inp, cache, out = _run_workload(name)
+    w, inp, cache, out, prefill = _run_workload(name)
     print(f"[fullsize] {name}: GPU write + decode done in {time.time() - t0:.1f} s; oracle in {WORKERS} workers",
           flush=True)
-    futs = [pool.submit(kvq_fullsize.check_piece, p) for p in _pieces(w, inp, cache, out)]
+    futs = [pool.submit(kvq_fullsize.check_piece, p) for p in _pieces(w, inp, cache, out, prefill)]
     del cache
     bad, worst, worst16, rows, nbytes = [], 0.0, 0.0, 0, 0
+    pf_worst, pf_rows = 0.0, 0
     for f in cf.as_completed(futs):
         r = f.result()
         if r["mismatch"]:
@@ -132,8 +150,12 @@ def test_full_size_whole_cache_and_every_row(name, pool):
         worst16 = max(worst16, r["err16"])
         rows += r["rows"]
         nbytes += r["bytes"]
+        pf_worst = max(pf_worst, r["pf_err"])
+        pf_rows += r["pf_rows"]
     print(f"[fullsize] {name}: {nbytes} cache bytes compared, {rows} output rows, max|err| {worst:.3e} "
-          f"(vs fp16-rounded oracle {worst16:.3e}), {time.time() - t0:.1f} s", flush=True)
+          f"(vs fp16-rounded oracle {worst16:.3e}); prefill: {pf_rows} sampled rows, max|err| {pf_worst:.3e}; "
+          f"{time.time() - t0:.1f} s", flush=True)
     assert not bad, bad[:5]
     assert rows == w.batch * w.n_q_heads
     assert worst <= ATOL, (worst, worst16)
+    assert pf_rows > 0 and pf_worst <= ATOL, pf_worst
