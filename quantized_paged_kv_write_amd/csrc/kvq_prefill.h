@@ -373,7 +373,11 @@ void prefill_kernel(PrefillArgs a) {
       const int t = lane & 31;
       const bool lv = (live >> t) & 1u;
       if (lane < 32) {
-        if constexpr (!KIVI) fk[t] = lv ? h2f(r.fk) * a.qscale : 0.f;
+        // A zero key scale comes with zero codes (the writer stores all-zero
+        // codes when the scale is 0), so such a row scores 0 with any factor;
+        // dead rows and zero scales store factor 1, so that a masked (-inf)
+        // raw score stays -inf when scaled.
+        if constexpr (!KIVI) fk[t] = (lv && (r.fk & 0x7FFFu) != 0u) ? h2f(r.fk) * a.qscale : 1.f;
       } else {
 #pragma unroll
         for (int g = 0; g < VS::NG; ++g)
@@ -421,12 +425,32 @@ void prefill_kernel(PrefillArgs a) {
   // Online softmax and P V of tile x (held in LDS buffer `buf`) from its raw
   // scores.  TAILT: the KIVI tail tile (fp16 values transposed at OFF_VT;
   // valid tokens t < ntail).
-  auto softmax_pv = [&](const uint8_t* buf, int x, uint32_t live, int ntail, const f4 (&sc)[NQB][2], auto tailc)
-                        __attribute__((always_inline)) {
-    constexpr bool TAILT = decltype(tailc)::value;
+  // Masks of a tile that is not fully visible: raw scores of tokens that are
+  // dead (or, in the tail tile, at or past ntail) or after the column's
+  // position become -inf (key scale factors are never 0, see store_tile, so
+  // the scaled score stays -inf).
+  auto mask_scores = [&](int x, uint32_t live, f4 (&sc)[NQB][2]) __attribute__((always_inline)) {
     const int t0 = TILE * x;
-    if (pos_hi < t0) return;  // every query of the wave precedes the tile
-    const bool full = !TAILT && live == 0xFFFFFFFFu && t0 + TILE - 1 <= pos_lo;
+    // bit 4 u + r: token 16 u + 4 j + r of the lane is live
+    const uint32_t lvm = ((live >> (4 * j)) & 0xFu) | (((live >> (16 + 4 * j)) & 0xFu) << 4);
+#pragma unroll
+    for (int cb = 0; cb < NQB; ++cb) {
+      // visible: live and 16 u + 4 j + r <= pos - t0 - 4 j =: lim
+      const int lim = pos_c[cb] - t0 - 4 * j;
+      const int n0 = min(max(lim + 1, 0), 4), n1 = min(max(lim - 15, 0), 4);
+      const uint32_t vm = lvm & (((1u << n0) - 1u) | (((1u << n1) - 1u) << 4));
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[cb][u][r] = ((vm >> (4 * u + r)) & 1u) ? sc[cb][u][r] : -INFINITY;
+    }
+  };
+
+  // Online softmax and P V of tile x (held in LDS buffer `buf`) from its
+  // masked raw scores.  TAILT: the KIVI tail tile (fp16 values transposed at
+  // OFF_VT).
+  auto softmax_pv = [&](const uint8_t* buf, const f4 (&sc)[NQB][2], auto tailc) __attribute__((always_inline)) {
+    constexpr bool TAILT = decltype(tailc)::value;
     const float* fk = reinterpret_cast<const float*>(buf + PL::OFF_FK);
     const float* fv = reinterpret_cast<const float*>(buf + PL::OFF_FV);
     // key scales of the lane's 8 tokens 16 u + 4 j + r (fp32, x sm_scale log2 e)
@@ -436,34 +460,17 @@ void prefill_kernel(PrefillArgs a) {
       if constexpr (KIVI) fk4[u] = f4{a.qscale, a.qscale, a.qscale, a.qscale};
       else fk4[u] = *reinterpret_cast<const f4*>(fk + 16 * u + 4 * j);
     }
-    // tokens of the lane (bit 4 u + r: token 16 u + 4 j + r) that are live
-    // (in the tail tile: below ntail)
-    uint32_t lvm = 0xFFu;
-    if (!full) {
-      const uint32_t lv = TAILT ? (ntail >= 32 ? 0xFFFFFFFFu : (1u << ntail) - 1u) : live;
-      lvm = ((lv >> (4 * j)) & 0xFu) | (((lv >> (16 + 4 * j)) & 0xFu) << 4);
-    }
     float p[NQB][2][4];
 #pragma unroll
     for (int cb = 0; cb < NQB; ++cb) {
       float s[2][4];
       float tmax = -INFINITY;
-      // visible: live and at or before the column's position: tokens
-      // 16 u + 4 j + r <= lim (with lim = pos - t0 - 4 j), r < 4
-      uint32_t vm = 0xFFu;
-      if (!full) {
-        const int lim = pos_c[cb] - t0 - 4 * j;
-        const int n0 = min(max(lim + 1, 0), 4), n1 = min(max(lim - 15, 0), 4);
-        vm = lvm & (((1u << n0) - 1u) | (((1u << n1) - 1u) << 4));
-      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = sc[cb][u][r] * fk4[u][r];
-          if (!full) v = ((vm >> (4 * u + r)) & 1u) ? v : -INFINITY;
-          s[u][r] = v;
-          tmax = fmaxf(tmax, v);
+          s[u][r] = sc[cb][u][r] * fk4[u][r];
+          tmax = fmaxf(tmax, s[u][r]);
         }
       }
       tmax = max_j(tmax);
@@ -621,7 +628,10 @@ void prefill_kernel(PrefillArgs a) {
         sc_cur[cb][1] = sc_next[cb][1];
       }
       if (x + 1 < ntm) scores(lbuf(b1), x + 1, sc_next, std::false_type{});
-      softmax_pv(lbuf(bx), x, live_cur, 0, sc_cur, std::false_type{});
+      if (pos_hi >= TILE * x) {  // some query of the wave sees the tile
+        if (live_cur != 0xFFFFFFFFu || TILE * x + TILE - 1 > pos_lo) mask_scores(x, live_cur, sc_cur);
+        softmax_pv(lbuf(bx), sc_cur, std::false_type{});
+      }
       store_tile(regs, live_n2, lbuf(b2));
       __syncthreads();
       live_cur = live_nx;
@@ -740,7 +750,10 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int cb = 0; cb < NQB; ++cb) sc[cb][0] = sc[cb][1] = f4{0.f, 0.f, 0.f, 0.f};
     scores(buf, Lq / TILE, sc, std::true_type{});
-    softmax_pv(buf, Lq / TILE, 0u, ntail, sc, std::true_type{});
+    if (pos_hi >= Lq) {
+      mask_scores(Lq / TILE, ntail >= 32 ? 0xFFFFFFFFu : (1u << ntail) - 1u, sc);
+      softmax_pv(buf, sc, std::true_type{});
+    }
   }
 
   // ---- out = acc / l, fp16 -------------------------------------------------
