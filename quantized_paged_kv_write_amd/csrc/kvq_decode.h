@@ -223,7 +223,10 @@ __device__ __forceinline__ void split_bf16x2(f2 x, uint32_t& hi, uint32_t& lo) {
   lo = __builtin_bit_cast(uint32_t, l);
 }
 // cs + the four bf16 values of a split pair (what the operands hold), with
-// two v_dot2_f32_bf16 against (1, 1)
+// two v_dot2_f32_bf16 against (1, 1).  The accumulating dot product does not
+// round like an IEEE add (measured on gfx950: a long chain of them drifts by
+// several 1e-4 relative), so callers sum one tile's operands in a fresh chain
+// and add that to the running sum with an fp32 add.
 __device__ __forceinline__ float add_split(float cs, uint32_t hi, uint32_t lo) {
   const bf2 one = {(__bf16)1.0f, (__bf16)1.0f};
   cs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, hi), one, cs, false);
@@ -685,7 +688,9 @@ void decode_split_kernel(DecodeArgs a) {
   f4 acc[VS::NPV];
 #pragma unroll
   for (int m = 0; m < VS::NPV; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  // l_run + l_err: probability sum of the lane's rows, kept with its rounding
+  // error (two_sum_acc), one add per tile
+  float m_run = -INFINITY, l_run = 0.f, l_err = 0.f;
   float cs_run[NCS];  // sum of the probability operands (hi + lo) of query head n, per value group
 #pragma unroll
   for (int g = 0; g < NCS; ++g) cs_run[g] = 0.f;
@@ -760,8 +765,7 @@ void decode_split_kernel(DecodeArgs a) {
         }
       }
     }
-    float l = l_run;
-    l = sum_j(l);
+    float l = sum_j(l_run) + sum_j(l_err);
     const size_t stride = (size_t)D + 2;
     float* pbase = a.part + ((size_t)(share + b) * a.Hq + hq0) * stride;
     if (j == 0 && n < NC) {
@@ -783,6 +787,7 @@ void decode_split_kernel(DecodeArgs a) {
     for (int m = 0; m < VS::NPV; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
     m_run = -INFINITY;
     l_run = 0.f;
+    l_err = 0.f;
 #pragma unroll
     for (int g = 0; g < NCS; ++g) cs_run[g] = 0.f;
     piece_start = true;
@@ -989,6 +994,7 @@ void decode_split_kernel(DecodeArgs a) {
     if (__ballot(m_new != m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 on the first live tile
       l_run *= alpha;
+      l_err *= alpha;
 #pragma unroll
       for (int g = 0; g < NCS; ++g) cs_run[g] *= alpha;
 #pragma unroll
@@ -1000,14 +1006,16 @@ void decode_split_kernel(DecodeArgs a) {
       m_run = m_new;
     }
     float p[2][NU];
+    float lt = 0.f;  // this tile's sum
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int i = 0; i < NU; ++i) {
         p[u][i] = __builtin_amdgcn_exp2f(s[u][i] - m_use);  // exp2(-inf) = 0 for masked rows
-        l_run += p[u][i];
+        lt += p[u][i];
       }
     }
+    two_sum_acc(l_run, l_err, lt);
 
     // ---- P V on the matrix cores -------------------------------------------
     // Probability operand of lane (j, n): 8 k-slots (tile rows T_j[e]) of
@@ -1022,6 +1030,7 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int grp = 0; grp < VS::NG; ++grp) {
         uint32_t ah[4], al[4];
+        float cst = 0.f;  // this tile's operand sum (a short chain, see add_split)
         if constexpr (HPC == 1) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -1029,7 +1038,7 @@ void decode_split_kernel(DecodeArgs a) {
             split_bf16x2(f2{p[u][r0] * s_fv[rows[u][r0] * VS::NG + grp],
                             p[u][r0 + 2] * s_fv[rows[u][r0 + 2] * VS::NG + grp]},
                          ah[q], al[q]);
-            cs_run[grp] = add_split(cs_run[grp], ah[q], al[q]);
+            cst = add_split(cst, ah[q], al[q]);
           }
         } else if constexpr (HPC == 2) {
           // rows hn, hn + 2 of u share dword 2 u + hn
@@ -1037,7 +1046,7 @@ void decode_split_kernel(DecodeArgs a) {
           for (int u = 0; u < 2; ++u) {
             uint32_t h, l;
             split_bf16x2(f2{p[u][0] * s_fv[rows[u][0] * VS::NG + grp], p[u][1] * s_fv[rows[u][1] * VS::NG + grp]}, h, l);
-            cs_run[grp] = add_split(cs_run[grp], h, l);
+            cst = add_split(cst, h, l);
             ah[2 * u] = hn ? 0u : h;
             ah[2 * u + 1] = hn ? h : 0u;
             al[2 * u] = hn ? 0u : l;
@@ -1047,13 +1056,14 @@ void decode_split_kernel(DecodeArgs a) {
           // row hn of u: dword 2 u + (hn & 1), half hn >> 1 (psel)
           uint32_t h, l;
           split_bf16x2(f2{p[0][0] * s_fv[rows[0][0] * VS::NG + grp], p[1][0] * s_fv[rows[1][0] * VS::NG + grp]}, h, l);
-          cs_run[grp] = add_split(cs_run[grp], h, l);
+          cst = add_split(cst, h, l);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             ah[q] = place(h, psel[q]);
             al[q] = place(l, psel[q]);
           }
         }
+        cs_run[grp] += cst;
         const b8 A_hi = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
         const b8 A_lo = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
         const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(cur + tbase + ((grp ^ tswz) << 4)));
@@ -1067,12 +1077,13 @@ void decode_split_kernel(DecodeArgs a) {
     } else {
       // dword q holds slots 2q, 2q + 1: rows r = 2 (q & 1), 2 (q & 1) + 1 of u = q >> 1
       uint32_t ah[4], al[4];
+      float cst = 0.f;  // this tile's operand sum (a short chain, see add_split)
       if constexpr (HPC == 1) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int u = q >> 1, r0 = 2 * (q & 1);
           split_bf16x2(f2{p[u][r0] * s_fv[rows[u][r0]], p[u][r0 + 1] * s_fv[rows[u][r0 + 1]]}, ah[q], al[q]);
-          if constexpr (FV == F_INT8) cs_run[0] = add_split(cs_run[0], ah[q], al[q]);
+          if constexpr (FV == F_INT8) cst = add_split(cst, ah[q], al[q]);
         }
       } else if constexpr (HPC == 2) {
         // row hn + 2 i of u: dword 2 u + i, half hn
@@ -1080,7 +1091,7 @@ void decode_split_kernel(DecodeArgs a) {
         for (int u = 0; u < 2; ++u) {
           uint32_t h, l;
           split_bf16x2(f2{p[u][0] * s_fv[rows[u][0]], p[u][1] * s_fv[rows[u][1]]}, h, l);
-          if constexpr (FV == F_INT8) cs_run[0] = add_split(cs_run[0], h, l);
+          if constexpr (FV == F_INT8) cst = add_split(cst, h, l);
           ah[2 * u] = place(h, psel[0]);
           ah[2 * u + 1] = place(h, psel[1]);
           al[2 * u] = place(l, psel[0]);
@@ -1090,13 +1101,14 @@ void decode_split_kernel(DecodeArgs a) {
         // row hn of u: dword 2 u + (hn >> 1), half hn & 1
         uint32_t h, l;
         split_bf16x2(f2{p[0][0] * s_fv[rows[0][0]], p[1][0] * s_fv[rows[1][0]]}, h, l);
-        if constexpr (FV == F_INT8) cs_run[0] = add_split(cs_run[0], h, l);
+        if constexpr (FV == F_INT8) cst = add_split(cst, h, l);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           ah[q] = place(h, psel[q]);
           al[q] = place(l, psel[q]);
         }
       }
+      if constexpr (FV == F_INT8) cs_run[0] += cst;
       const b8 A_hi = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
       const b8 A_lo = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
 #pragma unroll

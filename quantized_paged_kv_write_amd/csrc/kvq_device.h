@@ -164,6 +164,17 @@ __device__ __forceinline__ void fwht_row8(const float (&x)[8], uint32_t sbits, i
   if constexpr (LPR >= 32) stage(std::integral_constant<int, 16>{});
 }
 
+// s + e += x with the rounding error of the add kept in e (TwoSum, six
+// IEEE adds): a running sum of probabilities that starts with one large term
+// would otherwise drop every later term below half its ulp -- all of them
+// positive, so the sum would come out low, not just noisy.
+__device__ __forceinline__ void two_sum_acc(float& s, float& e, float x) {
+  const float t = s + x;
+  const float bx = t - s;
+  e += (s - (t - bx)) + (x - bx);
+  s = t;
+}
+
 // Record a device-side data error: the lowest lane of the wave whose `bad`
 // is set ORs `bit` into the error word (one vector atomic per wave at most).
 __device__ __forceinline__ void report_error(uint32_t* err, bool bad, uint32_t bit) {

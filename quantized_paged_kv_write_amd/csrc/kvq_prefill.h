@@ -136,11 +136,11 @@ __device__ __forceinline__ void split_f16x2_bf16(uint32_t h2v, uint32_t& hi, uin
 }
 
 // Waves per SIMD: two (each within 256 registers) where the kernel fits
-// them without spilling; one for INT4 values with rotated or KIVI keys
-// (extra query or key operands) and for KIVI keys at head_dim 256.
+// them without spilling; one for INT4 values with rotated keys (the extra
+// query operand) and for KIVI keys at head_dim 256.
 template <int FK, int FV, int D, bool ROTQ>
 constexpr int prefill_wpe() {
-  return (FV == F_INT4 && (ROTQ || FK == F_KIVI)) || (FK == F_KIVI && D == 256) ? 1 : 2;
+  return (FV == F_INT4 && ROTQ) || (FK == F_KIVI && D == 256) ? 1 : 2;
 }
 
 template <int FK, int FV, int D, bool ROTQ>
@@ -225,13 +225,16 @@ void prefill_kernel(PrefillArgs a) {
   const bool tail = KIVI && nt > ntm;                                // KIVI: the fp16 tail is visible
 
   f4 acc[NQB][VS::NPV];
-  float m_run[NQB], l_run[NQB], cs_run[NQB][NCS];
+  // l_run + l_err: the column's probability sum (this lane's tokens), kept
+  // with its rounding error (two_sum_acc), one add per tile
+  float m_run[NQB], l_run[NQB], l_err[NQB], cs_run[NQB][NCS];
 #pragma unroll
   for (int cb = 0; cb < NQB; ++cb) {
 #pragma unroll
     for (int m = 0; m < VS::NPV; ++m) acc[cb][m] = f4{0.f, 0.f, 0.f, 0.f};
     m_run[cb] = -INFINITY;
     l_run[cb] = 0.f;
+    l_err[cb] = 0.f;
 #pragma unroll
     for (int g = 0; g < NCS; ++g) cs_run[cb][g] = 0.f;
   }
@@ -479,20 +482,23 @@ void prefill_kernel(PrefillArgs a) {
       if (__ballot(m_new != m_run[cb])) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);  // 0 on the first visible tile
         l_run[cb] *= alpha;
+        l_err[cb] *= alpha;
 #pragma unroll
         for (int g = 0; g < NCS; ++g) cs_run[cb][g] *= alpha;
 #pragma unroll
         for (int m = 0; m < VS::NPV; ++m) acc[cb][m] *= alpha;
         m_run[cb] = m_new;
       }
+      float lt = 0.f;  // this tile's sum
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           p[cb][u][r] = __builtin_amdgcn_exp2f(s[u][r] - m_use);  // exp2(-inf) = 0 for masked tokens
-          l_run[cb] += p[cb][u][r];
+          lt += p[cb][u][r];
         }
       }
+      two_sum_acc(l_run[cb], l_err[cb], lt);
     }
     // ---- P V on the matrix cores ----
     if constexpr (TAILT) {
@@ -541,14 +547,16 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NQB; ++cb) {
           uint32_t ah[4], al[4];
+          float cst = 0.f;  // this tile's operand sum (a short chain, see add_split)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int u = q >> 1, r0 = q & 1;
             const int ta = 16 * u + 4 * j + r0;
             split_bf16x2(f2{p[cb][u][r0] * fv[grp * TILE + ta], p[cb][u][r0 + 2] * fv[grp * TILE + ta + 2]},
                          ah[q], al[q]);
-            cs_run[cb][grp] = add_split(cs_run[cb][grp], ah[q], al[q]);
+            cst = add_split(cst, ah[q], al[q]);
           }
+          cs_run[cb][grp] += cst;
           ph[cb] = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
           pl[cb] = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
         }
@@ -569,13 +577,15 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int cb = 0; cb < NQB; ++cb) {
         uint32_t ah[4], al[4];
+        float cst = 0.f;  // this tile's operand sum (a short chain, see add_split)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int u = q >> 1, r0 = 2 * (q & 1);
           const int ta = 16 * u + 4 * j + r0;
           split_bf16x2(f2{p[cb][u][r0] * fv[ta], p[cb][u][r0 + 1] * fv[ta + 1]}, ah[q], al[q]);
-          if constexpr (FV == F_INT8) cs_run[cb][0] = add_split(cs_run[cb][0], ah[q], al[q]);
+          if constexpr (FV == F_INT8) cst = add_split(cst, ah[q], al[q]);
         }
+        if constexpr (FV == F_INT8) cs_run[cb][0] += cst;
         ph[cb] = __builtin_bit_cast(b8, u4{ah[0], ah[1], ah[2], ah[3]});
         pl[cb] = __builtin_bit_cast(b8, u4{al[0], al[1], al[2], al[3]});
       }
@@ -587,6 +597,39 @@ void prefill_kernel(PrefillArgs a) {
         for (int cb = 0; cb < NQB; ++cb) {
           acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph[cb], acc[cb][m], 0, 0, 0);
           acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl[cb], acc[cb][m], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Remove the value-operand offset from acc now and restart the operand
+  // sums (INT8 / INT4 values): acc holds 2^-133 sum P u with u = c + 128
+  // (INT8) or c + 8 (INT4; odd channels 16 u), so the offset part is
+  // 2^-126 cs (2^-130 cs for even INT4 channels), cs = the column's operand
+  // sum since the last call.  Done every 16 tiles, it keeps acc near the size
+  // of the signal: a long chain of MFMA accumulations into a large offset
+  // drifts (the accumulation does not round like IEEE adds), and the offset
+  // would multiply that drift.
+  auto remove_offset = [&]() __attribute__((always_inline)) {
+    if constexpr (!VFP8) {
+#pragma unroll
+      for (int cb = 0; cb < NQB; ++cb) {
+#pragma unroll
+        for (int g = 0; g < NCS; ++g) {
+          const float cs = sum_j(cs_run[cb][g]);
+          cs_run[cb][g] = 0.f;
+          if constexpr (FV == F_INT8) {
+#pragma unroll
+            for (int m = 0; m < VS::NPV; ++m)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[cb][m][r] = __builtin_fmaf(cs, -0x1p-126f, acc[cb][m][r]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              acc[cb][2 * g][r] = __builtin_fmaf(cs, -0x1p-130f, acc[cb][2 * g][r]);
+              acc[cb][2 * g + 1][r] = __builtin_fmaf(cs, -0x1p-126f, acc[cb][2 * g + 1][r]);
+            }
+          }
         }
       }
     }
@@ -632,6 +675,7 @@ void prefill_kernel(PrefillArgs a) {
         if (live_cur != 0xFFFFFFFFu || TILE * x + TILE - 1 > pos_lo) mask_scores(x, live_cur, sc_cur);
         softmax_pv(lbuf(bx), sc_cur, std::false_type{});
       }
+      if ((x & 15) == 15) remove_offset();
       store_tile(regs, live_n2, lbuf(b2));
       __syncthreads();
       live_cur = live_nx;
@@ -759,7 +803,7 @@ void prefill_kernel(PrefillArgs a) {
   // ---- out = acc / l, fp16 -------------------------------------------------
 #pragma unroll
   for (int cb = 0; cb < NQB; ++cb) {
-    const float l = sum_j(l_run[cb]);
+    const float l = sum_j(l_run[cb]) + sum_j(l_err[cb]);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     if (Rw + 16 * cb + n >= rows) continue;
     uint16_t* o = a.out + qrow[cb] * D;

@@ -15,6 +15,27 @@ import numpy as np
 
 import oracle as o
 
+ATOL = 2e-3        # max |out_gpu(fp16) - o(fp64)| for outputs below 4 in magnitude
+ATOL_ARITH = 1e-3  # beyond the fp16 half-ulp of larger outputs
+
+
+def tolerance(ref):
+    """Per-element bar for an fp16 output against the fp64 reference o:
+    2e-3, or, where the fp16 format's own half-ulp at |o| exceeds 1e-3 (|o|
+    >= 4), that half-ulp plus 1e-3 -- the same arithmetic budget, since an
+    fp16 result cannot be closer to o than the rounding of o allows."""
+    a = np.abs(np.asarray(ref, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    half_ulp = 2.0 ** (e - 11)
+    return np.maximum(ATOL, half_ulp + ATOL_ARITH)
+
+
+def excess(got, ref):
+    """max(|got - ref| - tolerance(ref)): <= 0 when every element meets its bar."""
+    if got.size == 0:
+        return -1.0
+    return float(np.max(np.abs(got - ref) - tolerance(ref)))
+
 
 def check_piece(p: dict) -> dict:
     from threadpoolctl import threadpool_limits
@@ -72,5 +93,7 @@ def _check_piece(p: dict) -> dict:
         ref = o.causal_attention_fp64(p["pf_q"], K, V, p["pf_pos"])
         got = p["pf_out"].astype(np.float64)
         res["pf_err"] = float(np.max(np.abs(got - ref))) if got.size else 0.0
+        res["pf_excess"] = excess(got, ref)
+        res["pf_maxref"] = float(np.max(np.abs(ref))) if got.size else 0.0
         res["pf_rows"] = int(got.shape[0] * got.shape[1])
     return res

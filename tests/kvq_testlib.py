@@ -12,6 +12,7 @@ import oracle as o
 from quantized_paged_kv_write_amd import workloads as wl
 
 ATOL = 2e-3  # decode attention: max |out_gpu(fp16) - o(fp64)|
+from kvq_fullsize import excess, tolerance  # noqa: E402,F401  (the per-element bar, used for prefill)
 
 
 def garbage_like(shape, dtype, seed):
