@@ -55,6 +55,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef int i2 __attribute__((ext_vector_type(2)));
+typedef int i4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i2 lds_i2;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -327,14 +328,61 @@ struct Stage {
 template <int FK, int FV, int D, int HPC>
 struct TileRegs {
   using S = Stage<FK, FV, D>;
+  using VS = VShape<FV, D>;
   static constexpr int MCH = FK == F_KIVI ? HPC * D / 4 : 0;  // 16-byte chunks of page metadata
   static constexpr int KM = (MCH + 63) / 64;                  // per lane
+  static constexpr int NR = HPC >= 2 ? 2 * (4 / HPC) : 1;     // score rows per lane
+  static constexpr int VSB = 2 * VS::NG;                      // value-scale bytes per row
+  static constexpr int VW = VSB >= 4 ? VSB / 4 : 1;           // ... in registers
   u4 k[S::NLK];
   u4 v[S::NLV];
   uint32_t s[S::NGD];
   uint32_t par;  // bit rho: row rho's 16-bit scale is the high half of its dword
+  // direct scales (one page per tile, two or four heads per wave): the raw
+  // fp16 key scale and value scales of the lane's score rows
+  uint32_t fk[NR];
+  uint32_t fv[NR][VW];
   u4 m[KM > 0 ? KM : 1];
 };
+
+// Direct scales: with one page per tile and two or four KV heads per wave,
+// each lane loads the scales of its own score rows (two or four rows, see
+// score_row) straight into registers; otherwise every row's scales are
+// loaded once and passed on through LDS.
+template <int HPC, bool OP>
+constexpr bool direct_scales() {
+  return OP && HPC >= 2;
+}
+
+// Score row i (i = u (4 / HPC) + ii) of lane group j whose column's KV head
+// is hn: tile row 16 u + 4 j + r, r = hn + HPC ii.
+template <int HPC>
+__device__ __forceinline__ int score_row(int j, int hn, int i) {
+  constexpr int NU = 4 / HPC;
+  const int u = i / NU, ii = i % NU;
+  return 16 * u + 4 * j + (HPC == 1 ? ii : hn + HPC * ii);
+}
+
+// Raw buffer resource over `base` (word 3: 32-bit data format, so untyped
+// loads are valid); offsets stay within one page by construction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+constexpr int BUF_NT = 2;  // cache policy of a streaming load (nt)
+template <int BYTES, int AUX = 0>
+__device__ __forceinline__ void buf_load(uint32_t* dst, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (BYTES == 16) {
+    const u4 x = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
+    dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+  } else if constexpr (BYTES == 8) {
+    const u2 x = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX));
+    dst[0] = x.x; dst[1] = x.y;
+  } else if constexpr (BYTES == 4) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, AUX);
+  } else {
+    dst[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, AUX);
+  }
+}
 
 // Load one tile (keys, values, per-token scale dwords; KIVI page scales and
 // zeros) into registers; bid is the block id of token lane % 32's page.
@@ -352,7 +400,7 @@ struct TileRegs {
 // is out of range), so every address stays inside the cache; they are masked.
 template <int FK, int FV, int D, int HPC, bool OP>
 __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int t0, int tok_end, int h0,
-                                              TileRegs<FK, FV, D, HPC>& r) {
+                                              const uint32_t* sro, TileRegs<FK, FV, D, HPC>& r) {
   using S = Stage<FK, FV, D>;
   using KS = KShape<FK, D>;
   using VS = VShape<FV, D>;
@@ -372,32 +420,45 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
     const bool live = bok && t0 + (t >> hp) < tok_end;
     const uint64_t live_mask = __ballot(live);
     const uint32_t r_own = row0 + ro(t);
-    const uint8_t* kb = a.k_codes + (size_t)row0 * KS::RB;
-    const uint8_t* vb = a.v_codes + (size_t)row0 * VS::RB;
+    // buffer loads from the page base (scalar) at per-lane constant offsets
+    const auto rk = buf_rsrc(a.k_codes + (size_t)row0 * KS::RB);
+    const auto rv = buf_rsrc(a.v_codes + (size_t)row0 * VS::RB);
 #pragma unroll
     for (int i = 0; i < S::NLK; ++i) {
       const int p = 64 * i + lane;
       const int row = p / CHK;
       const int col = (p % CHK) ^ kswz<CHK>(row);
-      r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(kb + ro(row) * KS::RB + col * 16));
+      buf_load<16, BUF_NT>(reinterpret_cast<uint32_t*>(&r.k[i]), rk, ro(row) * KS::RB + col * 16);
     }
 #pragma unroll
     for (int i = 0; i < S::NLV; ++i) {
       const int p = 64 * i + lane;
       const int row = p / VS::CH;
       const int col = (p % VS::CH) ^ vswz<VS::CH>(row);
-      r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(vb + ro(row) * VS::RB + col * 16));
+      buf_load<16, BUF_NT>(reinterpret_cast<uint32_t*>(&r.v[i]), rv, ro(row) * VS::RB + col * 16);
     }
-    {
-      const uint16_t* src;
-      if (lane < 32) src = FK == F_KIVI ? a.v_scales : a.k_scales + (r_own & ~1u);
-      else src = a.v_scales + ((size_t)r_own * VS::NG & ~(size_t)1);
-      r.s[0] = *reinterpret_cast<const uint32_t*>(src);
-      r.par = (uint32_t)__ballot(live && (r_own & 1u));
-    }
+    if constexpr (direct_scales<HPC, OP>()) {
+      // the lane's score rows (flat-row offsets sro from row0)
+      using TR = TileRegs<FK, FV, D, HPC>;
+      const auto rks = buf_rsrc(a.k_scales + row0);
+      const auto rvs = buf_rsrc(a.v_scales + (size_t)row0 * VS::NG);
 #pragma unroll
-    for (int g = 1; g < S::NGD; ++g)
-      r.s[g] = *reinterpret_cast<const uint32_t*>(a.v_scales + (lane < 32 ? (size_t)r_own * VS::NG + 2 * g : 0));
+      for (int i = 0; i < TR::NR; ++i) {
+        if constexpr (FK != F_KIVI) buf_load<2>(&r.fk[i], rks, sro[i] * 2);
+        buf_load<TR::VSB>(r.fv[i], rvs, sro[i] * TR::VSB);
+      }
+    } else {
+      {
+        const uint16_t* src;
+        if (lane < 32) src = FK == F_KIVI ? a.v_scales : a.k_scales + (r_own & ~1u);
+        else src = a.v_scales + ((size_t)r_own * VS::NG & ~(size_t)1);
+        r.s[0] = *reinterpret_cast<const uint32_t*>(src);
+        r.par = (uint32_t)__ballot(live && (r_own & 1u));
+      }
+#pragma unroll
+      for (int g = 1; g < S::NGD; ++g)
+        r.s[g] = *reinterpret_cast<const uint32_t*>(a.v_scales + (lane < 32 ? (size_t)r_own * VS::NG + 2 * g : 0));
+    }
     if constexpr (FK == F_KIVI) {
       using TR = TileRegs<FK, FV, D, HPC>;
       constexpr int HALF = HPC * D / 8;
@@ -469,7 +530,7 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
 }
 
 // Store a loaded tile into the LDS stage `st` (layout of Stage).
-template <int FK, int FV, int D, int HPC>
+template <int FK, int FV, int D, int HPC, bool OP>
 __device__ __forceinline__ void store_tile(const TileRegs<FK, FV, D, HPC>& r, uint8_t* st) {
   using S = Stage<FK, FV, D>;
   const int lane = (int)threadIdx.x & 63;
@@ -477,11 +538,13 @@ __device__ __forceinline__ void store_tile(const TileRegs<FK, FV, D, HPC>& r, ui
   for (int i = 0; i < S::NLK; ++i) reinterpret_cast<u4*>(st + S::OFF_K)[64 * i + lane] = r.k[i];
 #pragma unroll
   for (int i = 0; i < S::NLV; ++i) reinterpret_cast<u4*>(st + S::OFF_V)[64 * i + lane] = r.v[i];
-  uint32_t* sd = reinterpret_cast<uint32_t*>(st + S::OFF_S);
-  sd[lane] = r.s[0];
+  if constexpr (!direct_scales<HPC, OP>()) {
+    uint32_t* sd = reinterpret_cast<uint32_t*>(st + S::OFF_S);
+    sd[lane] = r.s[0];
 #pragma unroll
-  for (int g = 1; g < S::NGD; ++g)
-    if (lane < 32) sd[32 + 32 * g + lane] = r.s[g];
+    for (int g = 1; g < S::NGD; ++g)
+      if (lane < 32) sd[32 + 32 * g + lane] = r.s[g];
+  }
   if constexpr (FK == F_KIVI) {
     using TR = TileRegs<FK, FV, D, HPC>;
 #pragma unroll
@@ -599,7 +662,9 @@ void decode_split_kernel(DecodeArgs a) {
   constexpr int NS = ST::NS, P = NS - 1;
   constexpr int L = NS > 2 ? 2 : 1;  // block ids are loaded L tiles ahead of their tile
   extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
-  const uint32_t wv = threadIdx.x >> 6;  // wave of the workgroup
+  // wave of the workgroup (uniform: so are the head group and every address
+  // derived from it, which then stay in scalar registers)
+  const uint32_t wv = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   uint8_t* const s_st = s_dyn + wv * ST::WAVE_LDS;
   // this tile's scales as fp32: key scale x sm_scale x log2 e, value scales
   float* const s_fk = reinterpret_cast<float*>(s_st + ST::BYTES);
@@ -662,6 +727,16 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int rho = 0; rho < 32; ++rho) colmask |= ((rho & hp_mask) == n / G ? 1u : 0u) << rho;
   }
+  // direct scales: the lane's score rows and their flat-row offsets from the
+  // tile's first row (one page per tile)
+  constexpr bool DSC = direct_scales<HPC, OP>();
+  constexpr int NR = TileRegs<FK, FV, D, HPC>::NR;
+  uint32_t sro[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int rho = score_row<HPC>(j, hn, i);
+    sro[i] = (uint32_t)((rho >> a.hp_log2) * a.H + (rho & hp_mask));
+  }
   // v_perm selectors that place the bf16 probabilities of column n's rows
   // into the probability operand (slots of other heads' rows get 0): psel[q]
   // builds operand dword q from the packed pair of split_bf16x2.
@@ -697,8 +772,18 @@ void decode_split_kernel(DecodeArgs a) {
   // Query operand (B of S^T = K Q^T), loaded at the start of each sequence's
   // piece: lane (j, n) holds query head n's channels of k-slots 8j..8j+7 in
   // the key operand's channel order.
-  h8 qop[KS::KB];
-  h8 qlo_r[ROTQ ? KS::KB : 1];  // rotated keys: the low half of the rotated query
+  // INT8 keys take the integer matrix core instead (I8K): the query is
+  // written as q = 2^-e (d1 2^14 + d2 2^7 + d3) with 7-bit digit planes
+  // d1..d3 (lane (j, n): 16 channels per 64-channel block), so the three
+  // products against the key codes are exact int32 sums and only their
+  // combination in fp32 rounds; the digits hold q to 2^-21 of its largest
+  // element (qe = 2^-e).
+  constexpr bool I8K = FK == F_INT8;
+  constexpr int KB64 = D / 64;
+  h8 qop[I8K ? 1 : KS::KB];
+  h8 qlo_r[ROTQ && !I8K ? KS::KB : 1];  // rotated keys: the low half of the rotated query
+  i4 qd[I8K ? 3 : 1][I8K ? KB64 : 1];
+  float qe = 1.f;
   bool piece_start = true;
   // KIVI: q * s of the current page (fp16 hi + lo) and q . z, column n's head
   h8 qhi[FK == F_KIVI ? KS::KB : 1], qlo[FK == F_KIVI ? KS::KB : 1];
@@ -732,7 +817,7 @@ void decode_split_kernel(DecodeArgs a) {
     ids_out = load_ids<OP>(a, cd, yi);
     const int yc = min(y, x_last);
     seek<FK>(ci, a, yc);
-    return load_tile<FK, FV, D, HPC, OP>(a, ids_in, (TILE * (yc - ci.lo)) >> a.hp_log2, ci.lq, h0, r);
+    return load_tile<FK, FV, D, HPC, OP>(a, ids_in, (TILE * (yc - ci.lo)) >> a.hp_log2, ci.lq, h0, sro, r);
   };
 #pragma unroll
   for (int i = 0; i < P; ++i) live[i] = load_group(x_begin + i, ids[(i + L) % NS], ids[i], regs[i]);
@@ -793,21 +878,74 @@ void decode_split_kernel(DecodeArgs a) {
     piece_start = true;
   };
 
+  const int slot = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 4) & 1);  // wave slot on the SIMD (HW_ID bit 0)
   int xr = x_begin;  // first tile of the current round
   // Step S_ of a round: tile x = xr + S_, held in register slot S_.
   auto step = [&](auto stage) __attribute__((always_inline)) {
     constexpr int S_ = decltype(stage)::value;
     const int x = xr + S_;
+    // Alternate the issue priority of the SIMD's two wave slots every tile.
+    // With equal priorities the older wave wins every issue conflict and
+    // finishes its (equal) share about a quarter earlier; the younger one
+    // then runs alone with nothing to hide its latencies.
+    if ((S_ & 1) ^ slot) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     // ---- start tile x + P ---------------------------------------------------
     live[(S_ + P) % NS] = load_group(x + P, ids[(S_ + P + L) % NS], ids[(S_ + P) % NS], regs[(S_ + P) % NS]);
     if (x >= x_end) return;
     // ---- tile x into LDS ------------------------------------------------------
     uint8_t* cur = s_st;
-    store_tile<FK, FV, D, HPC>(regs[S_], cur);
+    store_tile<FK, FV, D, HPC, OP>(regs[S_], cur);
     const uint64_t live_mask = live[S_];
     const uint32_t par = regs[S_].par;
     // ---- first tile of a sequence's piece: its query operand ---------------
     const bool new_piece = piece_start;
+    if (piece_start && I8K) {
+      // digit planes of the query (rotated keys: of hi + lo) for the lane's
+      // channels j D / 4 + 16 kb + e
+      const uint16_t* qrow = (ROTQ ? a.qrot : a.q) + ((size_t)cc.b * a.Hq + hq0 + (n < NC ? n : 0)) * D;
+      float qf[KB64][16];
+      float mx = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB64; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int c = j * (D / 4) + 16 * kb + e;
+          float x = h2f(qrow[c]);
+          if constexpr (ROTQ) x += h2f(qrow[(size_t)a.B * a.Hq * D + c]);
+          x = n < NC ? x : 0.f;
+          qf[kb][e] = x;
+          mx = fmaxf(mx, fabsf(x));
+        }
+      }
+      mx = max_j(mx);
+      // mx < 2^ex: X = rint(q 2^(20 - ex)) has |X| <= 2^20, digits in [-64, 64]
+      const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+      const float up = __builtin_ldexpf(1.f, 20 - ex);
+      qe = __builtin_ldexpf(1.f, ex - 20);
+#pragma unroll
+      for (int kb = 0; kb < KB64; ++kb) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t p1 = 0, p2 = 0, p3 = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const float X = __builtin_rintf(qf[kb][4 * w + b] * up);
+            const float d1 = __builtin_rintf(X * 0x1p-14f);
+            const float r1 = __builtin_fmaf(d1, -16384.f, X);
+            const float d2 = __builtin_rintf(r1 * 0x1p-7f);
+            const float d3 = __builtin_fmaf(d2, -128.f, r1);
+            p1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * b);
+            p2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * b);
+            p3 |= ((uint32_t)(int)d3 & 0xFFu) << (8 * b);
+          }
+          qd[0][kb][w] = (int)p1;
+          qd[1][kb][w] = (int)p2;
+          qd[2][kb][w] = (int)p3;
+        }
+      }
+      piece_start = false;
+    }
     if (piece_start) {
       const uint16_t* qrow = (ROTQ ? a.qrot : a.q) + ((size_t)cc.b * a.Hq + hq0 + (n < NC ? n : 0)) * D;
 #pragma unroll
@@ -818,7 +956,7 @@ void decode_split_kernel(DecodeArgs a) {
           qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < NC ? bits : 0));
         }
       }
-      if constexpr (ROTQ) {
+      if constexpr (ROTQ && !I8K) {
         const uint16_t* qlo = qrow + (size_t)a.B * a.Hq * D;
 #pragma unroll
         for (int kb = 0; kb < KS::KB; ++kb) {
@@ -834,18 +972,33 @@ void decode_split_kernel(DecodeArgs a) {
 
     // ---- scales -> fp32 (0 for masked tokens); FP8 codes of masked value
     //      rows zeroed (a garbage byte may be a NaN or infinity code)
+    // Direct scales: the score rows' scales are in registers (fkf: key scale
+    // x sm_scale x log2 e; fvm: value-scale dwords, 0 for masked rows, so a
+    // garbage scale never meets a zero probability).
+    float fkf[NR];
+    uint32_t fvm[NR][TileRegs<FK, FV, D, HPC>::VW];
+    if constexpr (DSC) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const bool lv = (live_mask >> score_row<HPC>(j, hn, i)) & 1;
+        if constexpr (FK != F_KIVI) fkf[i] = h2f(regs[S_].fk[i]) * (a.qscale * qe);
+#pragma unroll
+        for (int w = 0; w < TileRegs<FK, FV, D, HPC>::VW; ++w) fvm[i][w] = lv ? regs[S_].fv[i][w] : 0u;
+      }
+    }
     {
       const uint32_t* sdw = reinterpret_cast<const uint32_t*>(cur + ST::OFF_S);
       const int t = lane & 31;
       const bool lv = (live_mask >> t) & 1;
       const bool hi_half = (par >> t) & 1;
-      if (lane < 32) {
+      if (!DSC && lane < 32) {
         if constexpr (FK != F_KIVI) {
           const uint32_t d = sdw[t];
           s_fk[t] = lv ? h2f(hi_half ? d >> 16 : d & 0xFFFFu) * a.qscale : 0.f;
         }
       }
-      if constexpr (VS::NG == 1) {
+      if constexpr (DSC) {
+      } else if constexpr (VS::NG == 1) {
         if (lane >= 32) {
           const uint32_t d = sdw[32 + t];
           s_fv[t] = lv ? h2f(hi_half ? d >> 16 : d & 0xFFFFu) * VSC : 0.f;
@@ -941,9 +1094,25 @@ void decode_split_kernel(DecodeArgs a) {
 
     // ---- scores S^T[t][g] on the matrix cores ------------------------------
     f4 sc[2];
+    // INT8 keys: three integer products per row block (digit planes)
+    i4 si[I8K ? 3 : 1][2];
+    if constexpr (I8K) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int d = 0; d < 3; ++d) si[d][u] = i4{0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < KB64; ++kb) {
+          const i4 kop = i4{(int)kw[u][4 * kb], (int)kw[u][4 * kb + 1], (int)kw[u][4 * kb + 2], (int)kw[u][4 * kb + 3]};
+#pragma unroll
+          for (int d = 0; d < 3; ++d) si[d][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qd[d][kb], si[d][u], 0, 0, 0);
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       sc[u] = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (I8K) continue;
 #pragma unroll
       for (int kb = 0; kb < KS::KB; ++kb) {
         const h8 kop = key_operand<FK>(kw[u], kb);
@@ -973,11 +1142,33 @@ void decode_split_kernel(DecodeArgs a) {
         const int tr = 16 * u + 4 * j + r;
         rows[u][i] = tr;
         float raw;
-        if constexpr (HPC == 1) raw = sc[u][i];
+        if constexpr (I8K) {
+          // d1 2^14 + (d2 2^7 + d3) of the selected row: the low planes
+          // combine exactly in int32 (|d2 2^7 + d3| < 2^29)
+          int hi, lo;
+          auto sel = [&](int d) __attribute__((always_inline)) {
+            if constexpr (HPC == 1) return si[d][u][i];
+            else if constexpr (HPC == 2) return hn ? si[d][u][2 * i + 1] : si[d][u][2 * i];
+            else {
+              const int r01 = (hn & 1) ? si[d][u][1] : si[d][u][0];
+              const int r23 = (hn & 1) ? si[d][u][3] : si[d][u][2];
+              return (hn & 2) ? r23 : r01;
+            }
+          };
+          hi = sel(0);
+          lo = (sel(1) << 7) + sel(2);
+          raw = __builtin_fmaf((float)hi, 16384.f, (float)lo);
+        } else if constexpr (HPC == 1) raw = sc[u][i];
         else if constexpr (HPC == 2) raw = hn ? sc[u][2 * i + 1] : sc[u][2 * i];
-        else raw = hn == 0 ? sc[u][0] : hn == 1 ? sc[u][1] : hn == 2 ? sc[u][2] : sc[u][3];
+        else {
+          const float r01 = (hn & 1) ? sc[u][1] : sc[u][0];
+          const float r23 = (hn & 1) ? sc[u][3] : sc[u][2];
+          raw = (hn & 2) ? r23 : r01;
+        }
         float v;
         if constexpr (FK == F_KIVI) v = __builtin_fmaf(raw, kmul, qz);
+        else if constexpr (DSC) v = raw * fkf[u * NU + i];
+        else if constexpr (I8K) v = raw * (s_fk[tr] * qe);
         else v = raw * s_fk[tr];
         // a masked row's key codes may be anything, and a row of another KV
         // head than column n's does not belong to it: select, don't multiply
@@ -1024,6 +1215,17 @@ void decode_split_kernel(DecodeArgs a) {
     // for INT8/INT4; the bias times the probability sum is removed once,
     // after the last tile (cs_run).
     auto place = [](uint32_t b, uint32_t sel) __attribute__((always_inline)) { return __builtin_amdgcn_perm(b, b, sel); };
+    // value scale of score row (u, i), group grp, times 2^60 for the INT8 /
+    // INT4 operands (0 for masked rows)
+    auto vsc = [&](int u, int i, int grp) __attribute__((always_inline)) {
+      if constexpr (DSC) {
+        const uint32_t d = fvm[u * NU + i][VS::NG == 1 ? 0 : grp >> 1];
+        const uint32_t h = VS::NG == 1 ? (d & 0xFFFFu) : ((grp & 1) ? d >> 16 : d & 0xFFFFu);
+        return h2f(h) * VSC;
+      } else {
+        return s_fv[rows[u][i] * VS::NG + grp];
+      }
+    };
     if constexpr (FV == F_INT4) {
       // dword q holds slots (q >> 1) 4 + (q & 1) (rows r = q & 1, low half) and
       // that + 2 (r = (q & 1) + 2, high half) of u = q >> 1 (value_operand_int4)
@@ -1045,7 +1247,7 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             uint32_t h, l;
-            split_bf16x2(f2{p[u][0] * s_fv[rows[u][0] * VS::NG + grp], p[u][1] * s_fv[rows[u][1] * VS::NG + grp]}, h, l);
+            split_bf16x2(f2{p[u][0] * vsc(u, 0, grp), p[u][1] * vsc(u, 1, grp)}, h, l);
             cst = add_split(cst, h, l);
             ah[2 * u] = hn ? 0u : h;
             ah[2 * u + 1] = hn ? h : 0u;
@@ -1055,7 +1257,7 @@ void decode_split_kernel(DecodeArgs a) {
         } else {
           // row hn of u: dword 2 u + (hn & 1), half hn >> 1 (psel)
           uint32_t h, l;
-          split_bf16x2(f2{p[0][0] * s_fv[rows[0][0] * VS::NG + grp], p[1][0] * s_fv[rows[1][0] * VS::NG + grp]}, h, l);
+          split_bf16x2(f2{p[0][0] * vsc(0, 0, grp), p[1][0] * vsc(1, 0, grp)}, h, l);
           cst = add_split(cst, h, l);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -1090,7 +1292,7 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           uint32_t h, l;
-          split_bf16x2(f2{p[u][0] * s_fv[rows[u][0]], p[u][1] * s_fv[rows[u][1]]}, h, l);
+          split_bf16x2(f2{p[u][0] * vsc(u, 0, 0), p[u][1] * vsc(u, 1, 0)}, h, l);
           if constexpr (FV == F_INT8) cst = add_split(cst, h, l);
           ah[2 * u] = place(h, psel[0]);
           ah[2 * u + 1] = place(h, psel[1]);
@@ -1100,7 +1302,7 @@ void decode_split_kernel(DecodeArgs a) {
       } else {
         // row hn of u: dword 2 u + (hn >> 1), half hn & 1
         uint32_t h, l;
-        split_bf16x2(f2{p[0][0] * s_fv[rows[0][0]], p[1][0] * s_fv[rows[1][0]]}, h, l);
+        split_bf16x2(f2{p[0][0] * vsc(0, 0, 0), p[1][0] * vsc(1, 0, 0)}, h, l);
         if constexpr (FV == F_INT8) cst = add_split(cst, h, l);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
