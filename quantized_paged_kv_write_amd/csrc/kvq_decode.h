@@ -1340,7 +1340,9 @@ void decode_split_kernel(DecodeArgs a) {
 // tokens (fp16 keys and values in tail row b) are one more piece, computed
 // here by wave 0 in plain fp32.  MW waves share the records (16 when the
 // grid is small, so a few long record lists still fill the GPU); lanes own
-// channels.
+// channels.  One pass: each wave loads its records once and combines them
+// against its own maximum; the waves' partial sums are then combined against
+// the overall maximum (the same sums, grouped by wave).
 template <int D, bool KIVI, int MERGE_WAVES>
 __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   constexpr int CPL = D / 64;
@@ -1349,21 +1351,22 @@ __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   __shared__ float s_tail[D + 2];  // KIVI tail piece: m, l, acc[D]
   const int bh = (int)blockIdx.x, tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int b = bh / a.Hq, hq = bh - b * a.Hq;
-  if (hq == 0) {
-    // Data errors of sequence b: a context length outside [0, the tokens its
-    // block-table row addresses] (clamped), or a block id outside
-    // [0, num_blocks) on a page the split kernel reads (left out there).
+  // Data errors of sequence b: a context length outside [0, the tokens its
+  // block-table row addresses] (clamped), or a block id outside
+  // [0, num_blocks) on a page the split kernel reads (left out there).  The
+  // Hq workgroups of the sequence check every Hq-th page each; the ids load
+  // with the records and are reported at the end.
+  bool bad_id = false, bad_ctx = false;
+  {
     const int cap = a.max_blocks << a.log2_bs;
     const int raw = a.ctx_lens[b];
     const int L = min(max(raw, 0), cap);
     const int np = ((KIVI ? (L & ~31) : L) + a.bs - 1) >> a.log2_bs;
-    bool bad = false;
-    for (int p = tid; p < np; p += MERGE_WAVES * 64) {
+    for (int p = hq + a.Hq * tid; p < np; p += a.Hq * MERGE_WAVES * 64) {
       const int id = a.block_table[(size_t)b * a.max_blocks + p];
-      bad |= id < 0 || id >= a.nb;
+      bad_id |= id < 0 || id >= a.nb;
     }
-    report_error(a.err, bad, KVQ_DEVERR_BLOCK);
-    report_error(a.err, tid == 0 && (raw < 0 || raw > cap), KVQ_DEVERR_CTX);
+    bad_ctx = hq == 0 && tid == 0 && (raw < 0 || raw > cap);
   }
   int S, t0, t1;
   if (a.inline_plan) {
@@ -1425,58 +1428,82 @@ __global__ __launch_bounds__(MERGE_WAVES * 64) void merge_kernel(DecodeArgs a) {
   float tailv[CPL];  // rotated values: the KIVI tail's weighted values (wave 0)
 #pragma unroll
   for (int c = 0; c < CPL; ++c) tailv[c] = 0.f;
-  float M = tm;
-  for (int i = tid; i < nrec; i += MERGE_WAVES * 64) M = fmaxf(M, rec(i)[0]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if (lane == 0) s_m[w] = M;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < MERGE_WAVES; ++i) M = fmaxf(M, s_m[i]);
+  // this wave's records (i = w, w + MW, ...), combined against their maximum
+  // Mw (the KIVI tail joins wave 0's)
+  constexpr int RB = 8;  // records loaded per batch
+  float Mw = w == 0 ? tm : -INFINITY;
   float accv[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) accv[c] = 0.f;
   float l = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int i = w; i < nrec; i += MERGE_WAVES) {
-      const float* p = rec(i);
-      const float ms = p[0];
-      const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      l = __builtin_fmaf(p[1], wgt, l);
+  for (int i0 = w; i0 < nrec; i0 += RB * MERGE_WAVES) {
+    float ms[RB], ls[RB], av[RB][CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(p[2 + lane * CPL + c], wgt, accv[c]);
+    for (int k = 0; k < RB; ++k) {
+      const int i = i0 + k * MERGE_WAVES;
+      const float* p = rec(i < nrec ? i : 0);
+      ms[k] = i < nrec ? p[0] : -INFINITY;
+      ls[k] = p[1];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) av[k][c] = p[2 + lane * CPL + c];
     }
-    if (KIVI && w == 0 && tm != -INFINITY) {
-      const float wgt = exp2f(tm - M);
-      l = __builtin_fmaf(s_tail[1], wgt, l);
-      // the tail holds the original (unrotated) values: with rotated values
-      // it joins after the pages' sum is rotated back
+    float mb = Mw;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float t = s_tail[2 + lane * CPL + c] * wgt;
-        if (a.rot_v) tailv[c] = t;
-        else accv[c] += t;
-      }
+    for (int k = 0; k < RB; ++k) mb = fmaxf(mb, ms[k]);
+    if (mb == -INFINITY) continue;
+    // rescale what the wave holds to the new maximum
+    const float r = Mw == -INFINITY ? 0.f : exp2f(Mw - mb);
+    l *= r;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) accv[c] *= r;
+    Mw = mb;
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      const float wgt = ms[k] == -INFINITY ? 0.f : exp2f(ms[k] - mb);
+      l = __builtin_fmaf(ls[k], wgt, l);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) accv[c] = __builtin_fmaf(av[k][c], wgt, accv[c]);
     }
   }
+  if (lane == 0) s_m[w] = Mw;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) s_acc[w][lane * CPL + c] = accv[c];
   if (lane == 0) s_acc[w][D] = l;
+  report_error(a.err, bad_id, KVQ_DEVERR_BLOCK);
+  report_error(a.err, bad_ctx, KVQ_DEVERR_CTX);
   __syncthreads();
   if (w != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < MERGE_WAVES; ++i) M = fmaxf(M, s_m[i]);
+  float wg[MERGE_WAVES];
   float lt = 0.f;
 #pragma unroll
-  for (int i = 0; i < MERGE_WAVES; ++i) lt += s_acc[i][D];
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  uint16_t* o = a.out + (size_t)bh * D;
+  for (int i = 0; i < MERGE_WAVES; ++i) {
+    wg[i] = s_m[i] == -INFINITY ? 0.f : exp2f(s_m[i] - M);
+    lt = __builtin_fmaf(s_acc[i][D], wg[i], lt);
+  }
   float v[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     v[c] = 0.f;
 #pragma unroll
-    for (int i = 0; i < MERGE_WAVES; ++i) v[c] += s_acc[i][lane * CPL + c];
+    for (int i = 0; i < MERGE_WAVES; ++i) v[c] = __builtin_fmaf(s_acc[i][lane * CPL + c], wg[i], v[c]);
   }
+  if (KIVI && tm != -INFINITY) {
+    const float wgt = exp2f(tm - M);
+    lt = __builtin_fmaf(s_tail[1], wgt, lt);
+    // the tail holds the original (unrotated) values: with rotated values
+    // it joins after the pages' sum is rotated back
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float t = s_tail[2 + lane * CPL + c] * wgt;
+      if (a.rot_v) tailv[c] = t;
+      else v[c] += t;
+    }
+  }
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  uint16_t* o = a.out + (size_t)bh * D;
   if (a.rot_v) {
     // values stored rotated (y = H (sigma x)): the weighted sum of the stored
     // rows is rotated back, x = sigma (H y) / D, in fp32.  Channel c = lane
