@@ -55,7 +55,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef int i2 __attribute__((ext_vector_type(2)));
-typedef int i4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i2 lds_i2;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -772,18 +771,8 @@ void decode_split_kernel(DecodeArgs a) {
   // Query operand (B of S^T = K Q^T), loaded at the start of each sequence's
   // piece: lane (j, n) holds query head n's channels of k-slots 8j..8j+7 in
   // the key operand's channel order.
-  // INT8 keys take the integer matrix core instead (I8K): the query is
-  // written as q = 2^-e (d1 2^14 + d2 2^7 + d3) with 7-bit digit planes
-  // d1..d3 (lane (j, n): 16 channels per 64-channel block), so the three
-  // products against the key codes are exact int32 sums and only their
-  // combination in fp32 rounds; the digits hold q to 2^-21 of its largest
-  // element (qe = 2^-e).
-  constexpr bool I8K = FK == F_INT8;
-  constexpr int KB64 = D / 64;
-  h8 qop[I8K ? 1 : KS::KB];
-  h8 qlo_r[ROTQ && !I8K ? KS::KB : 1];  // rotated keys: the low half of the rotated query
-  i4 qd[I8K ? 3 : 1][I8K ? KB64 : 1];
-  float qe = 1.f;
+  h8 qop[KS::KB];
+  h8 qlo_r[ROTQ ? KS::KB : 1];  // rotated keys: the low half of the rotated query
   bool piece_start = true;
   // KIVI: q * s of the current page (fp16 hi + lo) and q . z, column n's head
   h8 qhi[FK == F_KIVI ? KS::KB : 1], qlo[FK == F_KIVI ? KS::KB : 1];
@@ -900,52 +889,6 @@ void decode_split_kernel(DecodeArgs a) {
     const uint32_t par = regs[S_].par;
     // ---- first tile of a sequence's piece: its query operand ---------------
     const bool new_piece = piece_start;
-    if (piece_start && I8K) {
-      // digit planes of the query (rotated keys: of hi + lo) for the lane's
-      // channels j D / 4 + 16 kb + e
-      const uint16_t* qrow = (ROTQ ? a.qrot : a.q) + ((size_t)cc.b * a.Hq + hq0 + (n < NC ? n : 0)) * D;
-      float qf[KB64][16];
-      float mx = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB64; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int c = j * (D / 4) + 16 * kb + e;
-          float x = h2f(qrow[c]);
-          if constexpr (ROTQ) x += h2f(qrow[(size_t)a.B * a.Hq * D + c]);
-          x = n < NC ? x : 0.f;
-          qf[kb][e] = x;
-          mx = fmaxf(mx, fabsf(x));
-        }
-      }
-      mx = max_j(mx);
-      // mx < 2^ex: X = rint(q 2^(20 - ex)) has |X| <= 2^20, digits in [-64, 64]
-      const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-      const float up = __builtin_ldexpf(1.f, 20 - ex);
-      qe = __builtin_ldexpf(1.f, ex - 20);
-#pragma unroll
-      for (int kb = 0; kb < KB64; ++kb) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t p1 = 0, p2 = 0, p3 = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const float X = __builtin_rintf(qf[kb][4 * w + b] * up);
-            const float d1 = __builtin_rintf(X * 0x1p-14f);
-            const float r1 = __builtin_fmaf(d1, -16384.f, X);
-            const float d2 = __builtin_rintf(r1 * 0x1p-7f);
-            const float d3 = __builtin_fmaf(d2, -128.f, r1);
-            p1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * b);
-            p2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * b);
-            p3 |= ((uint32_t)(int)d3 & 0xFFu) << (8 * b);
-          }
-          qd[0][kb][w] = (int)p1;
-          qd[1][kb][w] = (int)p2;
-          qd[2][kb][w] = (int)p3;
-        }
-      }
-      piece_start = false;
-    }
     if (piece_start) {
       const uint16_t* qrow = (ROTQ ? a.qrot : a.q) + ((size_t)cc.b * a.Hq + hq0 + (n < NC ? n : 0)) * D;
 #pragma unroll
@@ -956,7 +899,7 @@ void decode_split_kernel(DecodeArgs a) {
           qop[kb][e] = __builtin_bit_cast(_Float16, (uint16_t)(n < NC ? bits : 0));
         }
       }
-      if constexpr (ROTQ && !I8K) {
+      if constexpr (ROTQ) {
         const uint16_t* qlo = qrow + (size_t)a.B * a.Hq * D;
 #pragma unroll
         for (int kb = 0; kb < KS::KB; ++kb) {
@@ -981,7 +924,7 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         const bool lv = (live_mask >> score_row<HPC>(j, hn, i)) & 1;
-        if constexpr (FK != F_KIVI) fkf[i] = h2f(regs[S_].fk[i]) * (a.qscale * qe);
+        if constexpr (FK != F_KIVI) fkf[i] = h2f(regs[S_].fk[i]) * a.qscale;
 #pragma unroll
         for (int w = 0; w < TileRegs<FK, FV, D, HPC>::VW; ++w) fvm[i][w] = lv ? regs[S_].fv[i][w] : 0u;
       }
@@ -1094,25 +1037,9 @@ void decode_split_kernel(DecodeArgs a) {
 
     // ---- scores S^T[t][g] on the matrix cores ------------------------------
     f4 sc[2];
-    // INT8 keys: three integer products per row block (digit planes)
-    i4 si[I8K ? 3 : 1][2];
-    if constexpr (I8K) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int d = 0; d < 3; ++d) si[d][u] = i4{0, 0, 0, 0};
-#pragma unroll
-        for (int kb = 0; kb < KB64; ++kb) {
-          const i4 kop = i4{(int)kw[u][4 * kb], (int)kw[u][4 * kb + 1], (int)kw[u][4 * kb + 2], (int)kw[u][4 * kb + 3]};
-#pragma unroll
-          for (int d = 0; d < 3; ++d) si[d][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qd[d][kb], si[d][u], 0, 0, 0);
-        }
-      }
-    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       sc[u] = f4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (I8K) continue;
 #pragma unroll
       for (int kb = 0; kb < KS::KB; ++kb) {
         const h8 kop = key_operand<FK>(kw[u], kb);
@@ -1142,23 +1069,7 @@ void decode_split_kernel(DecodeArgs a) {
         const int tr = 16 * u + 4 * j + r;
         rows[u][i] = tr;
         float raw;
-        if constexpr (I8K) {
-          // d1 2^14 + (d2 2^7 + d3) of the selected row: the low planes
-          // combine exactly in int32 (|d2 2^7 + d3| < 2^29)
-          int hi, lo;
-          auto sel = [&](int d) __attribute__((always_inline)) {
-            if constexpr (HPC == 1) return si[d][u][i];
-            else if constexpr (HPC == 2) return hn ? si[d][u][2 * i + 1] : si[d][u][2 * i];
-            else {
-              const int r01 = (hn & 1) ? si[d][u][1] : si[d][u][0];
-              const int r23 = (hn & 1) ? si[d][u][3] : si[d][u][2];
-              return (hn & 2) ? r23 : r01;
-            }
-          };
-          hi = sel(0);
-          lo = (sel(1) << 7) + sel(2);
-          raw = __builtin_fmaf((float)hi, 16384.f, (float)lo);
-        } else if constexpr (HPC == 1) raw = sc[u][i];
+        if constexpr (HPC == 1) raw = sc[u][i];
         else if constexpr (HPC == 2) raw = hn ? sc[u][2 * i + 1] : sc[u][2 * i];
         else {
           const float r01 = (hn & 1) ? sc[u][1] : sc[u][0];
@@ -1168,7 +1079,6 @@ void decode_split_kernel(DecodeArgs a) {
         float v;
         if constexpr (FK == F_KIVI) v = __builtin_fmaf(raw, kmul, qz);
         else if constexpr (DSC) v = raw * fkf[u * NU + i];
-        else if constexpr (I8K) v = raw * (s_fk[tr] * qe);
         else v = raw * s_fk[tr];
         // a masked row's key codes may be anything, and a row of another KV
         // head than column n's does not belong to it: select, don't multiply
