@@ -501,6 +501,25 @@ def measure(w, args, steps, warmup, dev="cuda", want_inputs=False):
     return res, None
 
 
+def room_split_tokens(w, ctx_lens, reserve_waves):
+    """split_tokens for a decode call that leaves `reserve_waves` wave slots
+    of the GPU free (for a concurrent narrow copy kernel): the decode's
+    balanced partition, with as many shares as the remaining slots hold.  A
+    wave reads HP KV heads (the most with HP G <= 16 dividing H) in tiles of
+    32 / HP tokens; head dims up to 128 run two waves per SIMD."""
+    import torch
+    G = w.n_q_heads // w.n_kv_heads
+    hp = next(h for h in (4, 2, 1) if w.n_kv_heads % h == 0 and h * G <= 16)
+    tt = 32 // hp
+    lq = [(L & ~31) if w.k_dtype == "int4_kivi" else L for L in ctx_lens]
+    tiles = sum((L + tt - 1) // tt for L in lq)
+    groups = w.n_kv_heads // hp
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = (2 if w.head_dim <= 128 else 1) * 4 * cus - reserve_waves
+    shares = max(1, waves // groups)
+    return -(-tiles // shares) * tt
+
+
 def offload_measure(args, dev="cuda", engine="kernel"):
     """Offloaded pages with double-buffered prefetch ("Use Less Memory",
     section 4): the headline FP8 layer (27 x 32k) whose first --offload-pages
@@ -510,7 +529,9 @@ def offload_measure(args, dev="cuda", engine="kernel"):
     second stream) fills set (t + 1) % 2.  Reports the copy rate, the decode
     time with and without the concurrent prefetch, the overlapped and the
     serial step time, and whether every step's output equals the decode of
-    the pages that never left the device (bitwise)."""
+    the pages that never left the device (bitwise).  With the narrow copy
+    engine the decode calls leave the copy kernel's wave slots free
+    (room_split_tokens), so the two run side by side."""
     import torch
 
     import quantized_paged_kv_write_amd as kvq
@@ -550,11 +571,13 @@ def offload_measure(args, dev="cuda", engine="kernel"):
         tables.append(t2.to(dev))
     base_table = table.to(dev)
     out = torch.empty_like(q)
-    ws = torch.empty(kvq.decode_workspace_bytes(cache, B, w.n_q_heads, table.shape[1]), dtype=torch.uint8,
+    split = (room_split_tokens(w, [int(v) for v in ctx_d.cpu().tolist()], 4 * kvq.COPY_NARROW_WORKGROUPS)
+             if engine == "narrow" else 0)
+    ws = torch.empty(kvq.decode_workspace_bytes(cache, B, w.n_q_heads, table.shape[1], split), dtype=torch.uint8,
                      device=dev)
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
-    ref = kvq.decode_attn(cache, q, base_table, ctx_d).clone()
+    ref = kvq.decode_attn(cache, q, base_table, ctx_d, split_tokens=split).clone()
     torch.cuda.synchronize()
     page_bytes = 2 * w.block_size * w.n_kv_heads * (w.head_dim + 2)  # FP8 K and V codes + scales
     nbytes = n_off * page_bytes
@@ -573,17 +596,17 @@ def offload_measure(args, dev="cuda", engine="kernel"):
     copy_ms = e0.elapsed_time(e1) / reps
     # decode alone (over the staging sets)
     for r in range(3):
-        kvq.decode_attn(cache, q, tables[r % 2], ctx_d, out=out, workspace=ws)
+        kvq.decode_attn(cache, q, tables[r % 2], ctx_d, split_tokens=split, out=out, workspace=ws)
     torch.cuda.synchronize()
     e0.record(main)
     for r in range(reps):
-        kvq.decode_attn(cache, q, tables[r % 2], ctx_d, out=out, workspace=ws)
+        kvq.decode_attn(cache, q, tables[r % 2], ctx_d, split_tokens=split, out=out, workspace=ws)
     e1.record(main)
     torch.cuda.synchronize()
     dec_ms = e0.elapsed_time(e1) / reps
     equal = bool(torch.equal(out, ref))
     # serial: prefetch, then decode, on one stream
-    decs_s = [kvq.DecodeCall(cache, q, tables[i], ctx_d, out, ws) for i in range(2)]
+    decs_s = [kvq.DecodeCall(cache, q, tables[i], ctx_d, out, ws, split_tokens=split) for i in range(2)]
     cps_s = [kvq.CopyCall(pool, cache, host_ids, sets[i], engine=engine) for i in range(2)]
     torch.cuda.synchronize()
     e0.record(main)
@@ -605,7 +628,7 @@ def offload_measure(args, dev="cuda", engine="kernel"):
 
     # arguments marshalled once: the loop only calls into the library and
     # records events, so the host keeps ahead of the GPU
-    decs = [kvq.DecodeCall(cache, q, tables[i], ctx_d, out, ws) for i in range(2)]
+    decs = [kvq.DecodeCall(cache, q, tables[i], ctx_d, out, ws, split_tokens=split) for i in range(2)]
     cps = [kvq.CopyCall(pool, cache, host_ids, sets[i], engine=engine) for i in range(2)]
     torch.cuda.synchronize()
 
@@ -645,7 +668,8 @@ def offload_measure(args, dev="cuda", engine="kernel"):
     del cache, pool, ws
     torch.cuda.empty_cache()
     res = {
-        "workload": w.name, "copy_engine": engine, "pages_per_step": n_off, "bytes_per_step": nbytes,
+        "workload": w.name, "copy_engine": engine, "decode_split_tokens": split, "pages_per_step": n_off,
+        "bytes_per_step": nbytes,
         "prefetch_ms": round(copy_ms, 4), "prefetch_GBps_h2d": round(nbytes / (copy_ms * 1e6), 2),
         "decode_ms_alone": round(dec_ms, 4), "decode_ms_with_concurrent_prefetch": round(dec_conc_ms, 4),
         "step_ms_serial": round(serial_ms, 4), "step_ms_overlapped": round(overlap_ms, 4),
@@ -727,7 +751,7 @@ def main():
         r, _ = measure(wl.WORKLOADS[name], args, args.extra_steps, args.warmup, dev)
         workloads[name] = r
         torch.cuda.empty_cache()
-    offload = None if args.no_offload else {e: offload_measure(args, dev, e) for e in ("kernel", "dma")}
+    offload = None if args.no_offload else {e: offload_measure(args, dev, e) for e in ("narrow", "kernel", "dma")}
     probes = None if args.no_probes else stream_probes(dev)
 
     ms_per_step = head["ms_per_step"]

@@ -334,12 +334,21 @@ int kvq_prefill_attn(const kvq_cache* cache, const void* q,
  * the call, give an unspecified result.  KVQ_ERR_SHAPE if the geometries or
  * formats differ; KVQ_ERR_INVALID_ARG for a NULL buffer the formats need. */
 typedef enum kvq_copy_engine {
-  KVQ_COPY_KERNEL = 0, /* one copy-kernel launch for the whole list (pinned
-                          host memory through its device mapping); its
-                          waves are small enough to run beside a decode */
-  KVQ_COPY_DMA = 1     /* hipMemcpyAsync per run of consecutive ids and
-                          buffer: no compute units, more host time per call */
+  KVQ_COPY_KERNEL = 0,        /* one copy-kernel launch for the whole list
+                                 (pinned host memory through its device
+                                 mapping), one workgroup of 256 lanes per page */
+  KVQ_COPY_DMA = 1,           /* hipMemcpyAsync per run of consecutive ids and
+                                 buffer: no compute units, more host time per
+                                 call */
+  KVQ_COPY_KERNEL_NARROW = 2  /* the copy kernel on at most
+                                 KVQ_COPY_NARROW_WORKGROUPS workgroups of 256
+                                 lanes, each looping over pages: it holds at
+                                 most 4 x that many wave slots, so a decode
+                                 launched beside it with that many slots left
+                                 free (split_tokens) runs concurrently; a few
+                                 workgroups already saturate the host link */
 } kvq_copy_engine;
+#define KVQ_COPY_NARROW_WORKGROUPS 16
 int kvq_copy_blocks(const kvq_cache* src, const kvq_cache* dst,
                     const int32_t* src_blocks, const int32_t* dst_blocks,
                     int32_t n, int32_t engine, void* stream);

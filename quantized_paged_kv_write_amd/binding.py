@@ -45,7 +45,8 @@ class KvqCacheStruct(ctypes.Structure):
 
 
 ROTATE_K, ROTATE_V = 1, 2  # kvq_cache_flags
-COPY_ENGINES = {"kernel": 0, "dma": 1}  # kvq_copy_engine
+COPY_ENGINES = {"kernel": 0, "dma": 1, "narrow": 2}  # kvq_copy_engine
+COPY_NARROW_WORKGROUPS = 16  # KVQ_COPY_NARROW_WORKGROUPS
 
 
 class KvqError(RuntimeError):

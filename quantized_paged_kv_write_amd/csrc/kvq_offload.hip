@@ -59,11 +59,12 @@ int paged_buffers(const kvq_cache* s, const kvq_cache* d, std::vector<PagedBuffe
   return KVQ_OK;
 }
 
-// The copy kernel: one workgroup per page of the batch, each lane moving
-// 16-byte chunks of every paged buffer of that page, four in flight.  Pinned
-// host memory is read and written directly through its device mapping, so
-// one launch serves any list of pages; the kernel holds few registers and no
-// LDS, so its waves fit beside a decode launch on the same compute units.
+// The copy kernel: workgroup w moves pages w, w + grid, ... of the batch
+// (one page per workgroup by default, a few workgroups looping over the pages
+// for the narrow engine), each lane moving 16-byte chunks of every paged
+// buffer of a page, four in flight.  Pinned host memory is read and written
+// directly through its device mapping, so one launch serves any list of
+// pages.  The kernel holds few registers and no LDS.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxRuns = 160;
 struct CopyRun {
@@ -79,27 +80,29 @@ struct CopyArgs {
 };
 
 __global__ __launch_bounds__(256) void copy_pages_kernel(CopyArgs a) {
-  const int p = (int)blockIdx.x;  // page of the batch
+  const int pages = a.run_start[a.nruns];
   int r = 0;
-  while (r + 1 < a.nruns && a.run_start[r + 1] <= p) ++r;  // uniform scan over at most kMaxRuns runs
-  const int k = p - a.run_start[r];
-  const size_t sp = (size_t)(a.runs[r].src + k), dp = (size_t)(a.runs[r].dst + k);
-  for (int b = 0; b < a.nbuf; ++b) {
-    const uint32_t c = a.chunks[b];
-    const u32x4* s = a.src[b] + sp * c;
-    u32x4* d = a.dst[b] + dp * c;
-    uint32_t i = threadIdx.x;
-    for (; i + 768 < c; i += 1024) {
-      const u32x4 v0 = __builtin_nontemporal_load(s + i);
-      const u32x4 v1 = __builtin_nontemporal_load(s + i + 256);
-      const u32x4 v2 = __builtin_nontemporal_load(s + i + 512);
-      const u32x4 v3 = __builtin_nontemporal_load(s + i + 768);
-      __builtin_nontemporal_store(v0, d + i);
-      __builtin_nontemporal_store(v1, d + i + 256);
-      __builtin_nontemporal_store(v2, d + i + 512);
-      __builtin_nontemporal_store(v3, d + i + 768);
+  for (int p = (int)blockIdx.x; p < pages; p += (int)gridDim.x) {  // page of the batch
+    while (r + 1 < a.nruns && a.run_start[r + 1] <= p) ++r;  // uniform scan over at most kMaxRuns runs
+    const int k = p - a.run_start[r];
+    const size_t sp = (size_t)(a.runs[r].src + k), dp = (size_t)(a.runs[r].dst + k);
+    for (int b = 0; b < a.nbuf; ++b) {
+      const uint32_t c = a.chunks[b];
+      const u32x4* s = a.src[b] + sp * c;
+      u32x4* d = a.dst[b] + dp * c;
+      uint32_t i = threadIdx.x;
+      for (; i + 768 < c; i += 1024) {
+        const u32x4 v0 = __builtin_nontemporal_load(s + i);
+        const u32x4 v1 = __builtin_nontemporal_load(s + i + 256);
+        const u32x4 v2 = __builtin_nontemporal_load(s + i + 512);
+        const u32x4 v3 = __builtin_nontemporal_load(s + i + 768);
+        __builtin_nontemporal_store(v0, d + i);
+        __builtin_nontemporal_store(v1, d + i + 256);
+        __builtin_nontemporal_store(v2, d + i + 512);
+        __builtin_nontemporal_store(v3, d + i + 768);
+      }
+      for (; i < c; i += 256) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
     }
-    for (; i < c; i += 256) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
   }
 }
 
@@ -116,11 +119,12 @@ extern "C" int kvq_copy_blocks(const kvq_cache* src, const kvq_cache* dst, const
   for (int32_t i = 0; i < n; ++i)
     if (src_blocks[i] < 0 || src_blocks[i] >= src->num_blocks || dst_blocks[i] < 0 || dst_blocks[i] >= dst->num_blocks)
       return KVQ_ERR_INVALID_ARG;
-  if (engine != KVQ_COPY_KERNEL && engine != KVQ_COPY_DMA) return KVQ_ERR_INVALID_ARG;
+  if (engine != KVQ_COPY_KERNEL && engine != KVQ_COPY_DMA && engine != KVQ_COPY_KERNEL_NARROW)
+    return KVQ_ERR_INVALID_ARG;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return KVQ_ERR_NO_DEVICE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (engine == KVQ_COPY_KERNEL) {
+  if (engine == KVQ_COPY_KERNEL || engine == KVQ_COPY_KERNEL_NARROW) {
     for (const PagedBuffer& b : bufs)
       if ((b.page_bytes & 15) || (reinterpret_cast<uintptr_t>(b.src) & 15) || (reinterpret_cast<uintptr_t>(b.dst) & 15))
         return KVQ_ERR_INVALID_ARG;
@@ -146,7 +150,8 @@ extern "C" int kvq_copy_blocks(const kvq_cache* src, const kvq_cache* dst, const
         i = j;
       }
       a.run_start[a.nruns] = pages;
-      hipLaunchKernelGGL(copy_pages_kernel, dim3((unsigned)pages), dim3(256), 0, st, a);
+      const int32_t grid = engine == KVQ_COPY_KERNEL_NARROW ? std::min(pages, (int32_t)KVQ_COPY_NARROW_WORKGROUPS) : pages;
+      hipLaunchKernelGGL(copy_pages_kernel, dim3((unsigned)grid), dim3(256), 0, st, a);
       if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
     }
     return KVQ_OK;

@@ -232,7 +232,7 @@ def test_copy_blocks_argument_errors():
         return L.kvq_copy_blocks(ctypes.byref(s), ctypes.byref(d), si, di, n, engine, None)
 
     assert L.kvq_copy_blocks(None, ctypes.byref(b), ids, ids, 2, 0, None) == INVALID
-    assert cp(a, b, engine=2) == INVALID                # unknown engine
+    assert cp(a, b, engine=3) == INVALID                # unknown engine
     assert cp(a, _cache(head_dim=64)) == SHAPE          # geometries differ
     assert cp(a, _cache(v_dtype=2)) == SHAPE            # formats differ
     assert cp(a, b, di=bad) == INVALID                  # id out of range, nothing copied

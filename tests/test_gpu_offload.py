@@ -33,7 +33,7 @@ def _host_pool(dev, orc, n):
     return pool, opool
 
 
-@pytest.mark.parametrize("engine", ["kernel", "dma"])
+@pytest.mark.parametrize("engine", ["kernel", "dma", "narrow"])
 @pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("int4_kivi", "int4_g32"),
                                    ("fp8_e5m2", "int8")])
 def test_offload_and_prefetch_round_trip(kf, vf, engine):
@@ -74,7 +74,7 @@ def test_offload_and_prefetch_round_trip(kf, vf, engine):
     assert np.array_equal(ref1, ref0)
 
 
-@pytest.mark.parametrize("engine", ["kernel", "dma"])
+@pytest.mark.parametrize("engine", ["kernel", "dma", "narrow"])
 def test_prefetch_overlaps_decode_on_another_stream(engine):
     # Double buffering: while decode t reads staging set t % 2, the prefetch
     # of step t + 1 fills set (t + 1) % 2 on a second stream; decode t + 1
