@@ -1125,15 +1125,21 @@ void decode_split_kernel(DecodeArgs a) {
     // for INT8/INT4; the bias times the probability sum is removed once,
     // after the last tile (cs_run).
     auto place = [](uint32_t b, uint32_t sel) __attribute__((always_inline)) { return __builtin_amdgcn_perm(b, b, sel); };
-    // value scale of score row (u, i), group grp, times 2^60 for the INT8 /
-    // INT4 operands (0 for masked rows)
-    auto vsc = [&](int u, int i, int grp) __attribute__((always_inline)) {
+    // p x value scale of score row (u, i), group grp (x 2^60 for the INT8 /
+    // INT4 operands; 0 for masked rows), one rounding: with direct scales the
+    // fp16 scale is an operand of a mixed-precision FMA
+    float pv[2][NU];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < NU; ++i) pv[u][i] = p[u][i] * VSC;
+    auto pvs = [&](int u, int i, int grp) __attribute__((always_inline)) {
       if constexpr (DSC) {
         const uint32_t d = fvm[u * NU + i][VS::NG == 1 ? 0 : grp >> 1];
-        const uint32_t h = VS::NG == 1 ? (d & 0xFFFFu) : ((grp & 1) ? d >> 16 : d & 0xFFFFu);
-        return h2f(h) * VSC;
+        const uint16_t h = (uint16_t)((VS::NG > 1 && (grp & 1)) ? d >> 16 : d & 0xFFFFu);
+        return __builtin_fmaf(pv[u][i], (float)__builtin_bit_cast(_Float16, h), 0.f);
       } else {
-        return s_fv[rows[u][i] * VS::NG + grp];
+        return p[u][i] * s_fv[rows[u][i] * VS::NG + grp];
       }
     };
     if constexpr (FV == F_INT4) {
@@ -1157,7 +1163,7 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             uint32_t h, l;
-            split_bf16x2(f2{p[u][0] * vsc(u, 0, grp), p[u][1] * vsc(u, 1, grp)}, h, l);
+            split_bf16x2(f2{pvs(u, 0, grp), pvs(u, 1, grp)}, h, l);
             cst = add_split(cst, h, l);
             ah[2 * u] = hn ? 0u : h;
             ah[2 * u + 1] = hn ? h : 0u;
@@ -1167,7 +1173,7 @@ void decode_split_kernel(DecodeArgs a) {
         } else {
           // row hn of u: dword 2 u + (hn & 1), half hn >> 1 (psel)
           uint32_t h, l;
-          split_bf16x2(f2{p[0][0] * vsc(0, 0, grp), p[1][0] * vsc(1, 0, grp)}, h, l);
+          split_bf16x2(f2{pvs(0, 0, grp), pvs(1, 0, grp)}, h, l);
           cst = add_split(cst, h, l);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -1202,7 +1208,7 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           uint32_t h, l;
-          split_bf16x2(f2{p[u][0] * vsc(u, 0, 0), p[u][1] * vsc(u, 1, 0)}, h, l);
+          split_bf16x2(f2{pvs(u, 0, 0), pvs(u, 1, 0)}, h, l);
           if constexpr (FV == F_INT8) cst = add_split(cst, h, l);
           ah[2 * u] = place(h, psel[0]);
           ah[2 * u + 1] = place(h, psel[1]);
@@ -1212,7 +1218,7 @@ void decode_split_kernel(DecodeArgs a) {
       } else {
         // row hn of u: dword 2 u + (hn >> 1), half hn & 1
         uint32_t h, l;
-        split_bf16x2(f2{p[0][0] * vsc(0, 0, 0), p[1][0] * vsc(1, 0, 0)}, h, l);
+        split_bf16x2(f2{pvs(0, 0, 0), pvs(1, 0, 0)}, h, l);
         if constexpr (FV == F_INT8) cst = add_split(cst, h, l);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
