@@ -398,6 +398,10 @@ def measure(w, args, steps, warmup, dev="cuda", want_inputs=False):
             torch.cuda.synchronize()
 
     settle()
+    # two untimed writes first: the clocks settle on the write's own load
+    for _ in range(2):
+        kvq.write(cache, k_pre, v_pre, s_pre, q_pre)
+    torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(args.prefill_reps):
@@ -699,7 +703,7 @@ def main():
                     help="comma-separated workloads measured after the headline one, each reported in "
                          "'workloads' ('none' for none)")
     ap.add_argument("--extra-steps", type=int, default=20)
-    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed decode calls after the cache fill, before any timing")
     ap.add_argument("--caches", type=int, default=2, choices=(1, 2),

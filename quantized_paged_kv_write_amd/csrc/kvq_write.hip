@@ -11,9 +11,11 @@
 // KIVI-style keys ("12 KV Cache Quantization", section 5 "K is more sensitive
 // than V"; "Quantized KV caches in production", Numerical Formats; the
 // glossary's asymmetric quantization): the 32 rows of a page are quantized
-// together per channel when the page's last row arrives (kivi_seal_kernel);
-// rows of unfinished pages wait in the sequence's fp16 tail, written by the
-// value pass after the seal kernel has read the previous tail.
+// together per channel when the page's last row arrives (seal_pages);
+// rows of unfinished pages wait in the sequence's fp16 tail, written after
+// the seal has read the previous tail: by the value pass that follows the
+// seal kernel (calls of up to 2048 tokens), or by kivi_tail_kernel after one
+// launch that runs the seal and the value pass side by side (larger calls).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -99,7 +101,7 @@ __device__ __forceinline__ u32x2 encode8(const float (&y)[8]) {
 template <int FMT, int D, int ITER, bool TAIL, bool ROT>
 __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* __restrict__ src,
                                            uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
-                                           const uint16_t* __restrict__ stat) {
+                                           const uint16_t* __restrict__ stat, uint32_t bid) {
   using S = WShape<FMT, D>;
   const int lir = threadIdx.x % S::LPR;
   // the lane's 8 rotation signs: bits 8 lir .. 8 lir + 7 of rot_signs
@@ -111,7 +113,7 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
     sbits = (w >> (8 * (lir & 3))) & 0xFFu;
   }
   const uint32_t nrows = (uint32_t)(a.T * a.H);
-  const uint32_t row0 = blockIdx.x * (uint32_t)(S::RPP * ITER) + threadIdx.x / S::LPR;
+  const uint32_t row0 = bid * (uint32_t)(S::RPP * ITER) + threadIdx.x / S::LPR;
   u32x4 xin[ITER];
   int64_t slot[ITER];
   uint32_t tok[ITER];
@@ -236,9 +238,9 @@ template <int FK, int FV, int D, int ITER, bool ROTK, bool ROTV>
 __global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0) {
   const int tensor = (int)blockIdx.y + tensor0;
   if (tensor == 0) {
-    if constexpr (FK != F_KIVI) write_rows<FK, D, ITER, false, ROTK>(a, a.k, a.k_codes, a.k_scales, a.k_static);
+    if constexpr (FK != F_KIVI) write_rows<FK, D, ITER, false, ROTK>(a, a.k, a.k_codes, a.k_scales, a.k_static, blockIdx.x);
   } else {
-    write_rows<FV, D, ITER, FK == F_KIVI, ROTV>(a, a.v, a.v_codes, a.v_scales, a.v_static);
+    write_rows<FV, D, ITER, FK == F_KIVI, ROTV>(a, a.v, a.v_codes, a.v_scales, a.v_static, blockIdx.x);
   }
 }
 
@@ -257,20 +259,21 @@ __global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0
 // that they hold the page's tokens is in flight; rows that fail it are
 // reloaded from the tail.
 //
-// A workgroup holds NW = blockDim.x / 64 waves: heads c NW .. c NW + NW - 1
-// of one chunk, so the waves that read the neighbouring head segments of the
-// same token rows (and write neighbouring code rows) run on one compute
-// unit.  They never synchronize.
+// Seal workgroup `bid` holds nw waves (waves nw.. of the workgroup idle):
+// heads c nw .. c nw + nw - 1 of one chunk, so the waves that read the
+// neighbouring head segments of the same token rows (and write neighbouring
+// code rows) run on one compute unit.  They never synchronize.
 template <int D>
-__global__ __launch_bounds__(512) void kivi_seal_kernel(WriteArgs a) {
+__device__ __forceinline__ void seal_pages(const WriteArgs& a, uint32_t bid, int nw) {
   constexpr int PPL = D >= 256 ? D / 128 : 1;  // channel pairs per lane
   constexpr int LPR = D / 2 / PPL;             // lanes per row
   constexpr int RG = 64 / LPR;                 // row groups
   constexpr int RPL = 32 / RG;                 // rows per lane
-  const int nw = (int)(blockDim.x >> 6);
+  const int wave = (int)(threadIdx.x >> 6);
+  if (wave >= nw) return;
   const int wgs_per_chunk = a.H / nw;
-  const int h = (int)(blockIdx.x % (uint32_t)wgs_per_chunk) * nw + (int)(threadIdx.x >> 6);
-  const int64_t chunk = (int64_t)(blockIdx.x / (uint32_t)wgs_per_chunk);
+  const int h = (int)(bid % (uint32_t)wgs_per_chunk) * nw + wave;
+  const int64_t chunk = (int64_t)(bid / (uint32_t)wgs_per_chunk);
   const int C = a.seal_chunk;
   const int64_t t0 = chunk * C;
   const int lane = (int)threadIdx.x & 63;
@@ -287,7 +290,10 @@ __global__ __launch_bounds__(512) void kivi_seal_kernel(WriteArgs a) {
     const int j = __ffsll((unsigned long long)mask) - 1;
     mask &= mask - 1;
     const int64_t te = t0 + j;
-    const int64_t se = ((int64_t)__shfl((int)(my_slot >> 32), j) << 32) | (uint32_t)__shfl((int)my_slot, j);
+    // uniform (lane j's slot): read into scalar registers so the page's
+    // addresses stay scalar
+    const int64_t se = ((int64_t)__builtin_amdgcn_readfirstlane(__shfl((int)(my_slot >> 32), j)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane(__shfl((int)my_slot, j));
     const int32_t seq = __shfl(my_seq, j);
     if (seq < 0 || seq >= a.max_seqs) continue;
     const int64_t blk = se >> 5;
@@ -355,25 +361,38 @@ __global__ __launch_bounds__(512) void kivi_seal_kernel(WriteArgs a) {
       sc[c] = h2f(s16[c]);
       rc[c] = sc[c] != 0.0f ? recip_fp16(sc[c]) : 0.0f;
     }
-    uint8_t* cbase = a.k_codes + (size_t)blk * 32 * a.H * (D / 2);
+    // the page's code rows through a buffer resource: a per-lane offset and a
+    // uniform row offset, no 64-bit address arithmetic per store
+    const auto rco = __builtin_amdgcn_make_buffer_rsrc(a.k_codes + (size_t)blk * 32 * a.H * (D / 2), (short)0,
+                                                       0x7FFFFFFF, 0x00020000);
+    const int lane_off = (g * a.H + h) * (D / 2) + pl * PPL;
+    // 2 (x - z) and 2 s, r / 2: the quotient is the same (exact scaling), and
+    // 2 x - 2 z is one mixed-precision FMA on the fp16 x
+    float sc2[2 * PPL], rc2[2 * PPL], mn2[2 * PPL];
+#pragma unroll
+    for (int c = 0; c < 2 * PPL; ++c) {
+      sc2[c] = 2.0f * sc[c];
+      rc2[c] = 0.5f * rc[c];
+      mn2[c] = 2.0f * mn[c];
+    }
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const int row = g + RG * i;
       uint32_t w = 0;
 #pragma unroll
       for (int c = 0; c < 2 * PPL; ++c) {
-        // fl32(x - z) by one mixed-precision FMA on the fp16 x; then
-        // fl32(. / s).  No branch on s = 0: with r = 0 the division of the
-        // non-negative difference gives +0, so the code is 0.
+        // fl32(x - z), then fl32(. / s).  No branch on s = 0: with r = 0 the
+        // division of the non-negative difference gives +0, so the code is 0.
         const _Float16 xv = __builtin_bit_cast(hv2, x[i][c >> 1])[c & 1];
-        const float d = __builtin_fmaf((float)xv, 1.0f, -mn[c]);
-        const float y = exact_div(d, sc[c], rc[c]);
-        const uint32_t code = rne_low_bits(__builtin_amdgcn_fmed3f(y, 0.0f, 15.0f)) & 0xFu;  // clip, round half to even
-        w |= code << (4 * c);
+        const float d2 = __builtin_fmaf((float)xv, 2.0f, -mn2[c]);
+        const float y = exact_div(d2, sc2[c], rc2[c]);
+        // clip, round half to even: the integer is in the low byte (bits 4-7
+        // are 0), and bits above the stored ones are never read
+        const uint32_t code = rne_low_bits(__builtin_amdgcn_fmed3f(y, 0.0f, 15.0f));
+        w = c == 0 ? code : (code << (4 * c)) | w;
       }
-      uint8_t* dst = cbase + ((size_t)row * a.H + h) * (D / 2) + pl * PPL;
-      if constexpr (PPL == 1) *dst = (uint8_t)w;
-      else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+      const int roff = RG * i * a.H * (D / 2);
+      if constexpr (PPL == 1) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)w, rco, lane_off, roff, 0);
+      else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)w, rco, lane_off, roff, 0);
     }
     if (g == 0) {
       const size_t m = ((size_t)blk * a.H + h) * D + 2 * PPL * pl;
@@ -386,12 +405,77 @@ __global__ __launch_bounds__(512) void kivi_seal_kernel(WriteArgs a) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void kivi_seal_kernel(WriteArgs a) {
+  seal_pages<D>(a, blockIdx.x, (int)(blockDim.x >> 6));
+}
+
+// A large KIVI call in one launch: the value pass's workgroups, then the
+// seal's (key pages).  Neither writes the fp16 tail: kivi_tail_kernel does
+// that afterwards, once the seal has read the rows the tail held before the
+// call, so the value pass carries no tail lookups.  Measured on the
+// 131072-token KIVI layer: 8% faster than the seal kernel followed by a value
+// pass that writes the tail; interleaving the two kinds of workgroup in
+// block order was 2% slower than this order.  8 waves per SIMD: left to
+// itself the compiler gives the combined kernel 119 registers (4 waves),
+// which made it slower than the two kernels.
+template <int FV, int D, int ITER, bool ROTV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void kivi_write_kernel(WriteArgs a, uint32_t n_val, int nw) {
+  const uint32_t b = blockIdx.x;
+  if (b < n_val) write_rows<FV, D, ITER, false, ROTV>(a, a.v, a.v_codes, a.v_scales, a.v_static, b);
+  else seal_pages<D>(a, b - n_val, nw);
+}
+
+// Rows of the pages a large KIVI call leaves open (the page's last row is not
+// at its expected position in the call) go to the sequence's fp16 tail, key
+// and value.  One wave per 64 call tokens; the wave copies each such token's
+// H rows (contiguous in the call and in the tail row) with 16-byte accesses.
+template <int D>
+__global__ __launch_bounds__(256) void kivi_tail_kernel(WriteArgs a) {
+  const int lane = (int)threadIdx.x & 63;
+  const int64_t t0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 64;
+  const int64_t t = t0 + lane;
+  bool open = false;
+  int32_t seq = 0;
+  int off = 0;
+  if (t < a.T) {
+    const int64_t s = a.slots[t];
+    if (s >= 0 && s < a.capacity) {
+      seq = a.seq_idx[t];
+      const bool seq_ok = seq >= 0 && seq < a.max_seqs;
+      report_error(a.err, !seq_ok, KVQ_DEVERR_SEQ);
+      off = (int)(s % a.bs);
+      const int64_t te = t + (a.bs - 1 - off);
+      const bool sealed = te < a.T && a.seq_idx[te] == seq && a.slots[te] == s + (a.bs - 1 - off);
+      open = seq_ok && !sealed;
+    }
+  }
+  uint64_t m = __ballot(open);
+  const int nch = a.H * D / 8;  // 16-byte chunks of a token's H rows
+  while (m) {
+    const int j = __ffsll((unsigned long long)m) - 1;
+    m &= m - 1;
+    const int32_t sq = __shfl(seq, j);
+    const int oj = __shfl(off, j);
+    const u32x4* ks = reinterpret_cast<const u32x4*>(a.k + (size_t)(t0 + j) * a.H * D);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(a.v + (size_t)(t0 + j) * a.H * D);
+    u32x4* kd = reinterpret_cast<u32x4*>(a.k_tail + ((size_t)sq * a.bs + oj) * a.H * D);
+    u32x4* vd = reinterpret_cast<u32x4*>(a.v_tail + ((size_t)sq * a.bs + oj) * a.H * D);
+    for (int c = lane; c < nch; c += 64) {
+      kd[c] = ks[c];
+      vd[c] = vs[c];
+    }
+  }
+}
+
 namespace {
 
 // Rows per lane of write_sym_kernel.  Measured in one process (prefill
 // writes of the large workloads): one row per lane, i.e. more and shorter
 // workgroups, 5.45 -> 5.88 TB/s for the symmetric formats against 4 rows
-// per lane; the KIVI value pass (with its tail lookups) is fastest at 2.
+// per lane; the KIVI value pass is fastest at 2 (with its tail lookups, and
+// in the combined launch of large calls without them).
 template <int FK>
 constexpr int rows_per_lane() { return FK == F_KIVI ? 2 : 1; }
 
@@ -419,10 +503,30 @@ template <int FK, int FV, int D>
 hipError_t launch_all(const WriteArgs& a, hipStream_t s) {
   if constexpr (FK == F_KIVI) {
     const int64_t chunks = (a.T + a.seal_chunk - 1) / a.seal_chunk;
-    // waves per workgroup: the largest divisor of H up to 8 (heads of one chunk)
-    int nw = a.H < 8 ? a.H : 8;
+    // waves per seal workgroup: the largest divisor of H up to 4 (heads of
+    // one chunk; 4 measured 2-3% faster than 8)
+    int nw = a.H < 4 ? a.H : 4;
     while (a.H % nw) --nw;
     const int64_t wgs = chunks * (a.H / nw);
+    if (a.seal_chunk > 1) {
+      // large call: value pass and seal in one launch, then the tail rows
+      constexpr int kIter = rows_per_lane<FK>();
+      constexpr int RPP = 256 / (D / 8);
+      const int64_t vwgs = (a.T * a.H + RPP * kIter - 1) / (RPP * kIter);
+      const int64_t all = wgs + vwgs;
+      if (all >= (1ll << 31)) return hipErrorInvalidValue;
+      if (a.rot_v)
+        hipLaunchKernelGGL((kivi_write_kernel<FV, D, kIter, true>), dim3((unsigned)all), dim3(256), 0, s, a,
+                           (uint32_t)vwgs, nw);
+      else
+        hipLaunchKernelGGL((kivi_write_kernel<FV, D, kIter, false>), dim3((unsigned)all), dim3(256), 0, s, a,
+                           (uint32_t)vwgs, nw);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t twgs = (a.T + 255) / 256;
+      hipLaunchKernelGGL((kivi_tail_kernel<D>), dim3((unsigned)twgs), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
     if (wgs >= (1ll << 31)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((kivi_seal_kernel<D>), dim3((unsigned)wgs), dim3(64 * nw), 0, s, a);
     hipError_t e = hipGetLastError();

@@ -74,19 +74,25 @@ def test_write_static_reports_out_of_range_slots():
     assert kvq.get_device_error() == E["slot"]
 
 
-def test_kivi_write_reports_sequence_without_tail_row():
+@pytest.mark.parametrize("big", [False, True])
+def test_kivi_write_reports_sequence_without_tail_row(big):
+    # big: a call of more than 2048 tokens (seal and value pass in one launch,
+    # tail rows written by their own kernel)
     _clear()
     D, H, bs = 128, 2, 32
     rng = np.random.default_rng(5)
-    ctx = [40, 64, 20]
+    n0, n1, n2 = (1000, 1088, 20) if big else (40, 64, 20)
+    ctx = [n0, n1, n2]
     k = rng.standard_normal((sum(ctx), H, D)).astype(np.float16)
     v = rng.standard_normal((sum(ctx), H, D)).astype(np.float16)
-    slots = np.concatenate([np.arange(40), 64 + np.arange(64), 192 + np.arange(20)]).astype(np.int64)
-    seq = np.concatenate([np.zeros(40), np.full(64, 1), np.full(20, 2)]).astype(np.int32)
-    seq[40:104] = 7  # sequence 1 names tail row 7 of a 2-row tail: its keys go nowhere
-    dev, orc = new_caches(8, bs, H, D, "int4_kivi", "int4_g32", 2, DEV, seed=33)
+    b1 = -(-n0 // bs) * bs  # first slot of sequence 1 (its own pages)
+    b2 = b1 + -(-n1 // bs) * bs
+    slots = np.concatenate([np.arange(n0), b1 + np.arange(n1), b2 + np.arange(n2)]).astype(np.int64)
+    seq = np.concatenate([np.zeros(n0), np.full(n1, 1), np.full(n2, 2)]).astype(np.int32)
+    seq[n0:n0 + n1] = 7  # sequence 1 names tail row 7 of a 2-row tail: its keys go nowhere
+    dev, orc = new_caches(-(-(b2 + n2) // bs), bs, H, D, "int4_kivi", "int4_g32", 2, DEV, seed=33)
     keep_seq2 = seq.copy()
-    keep_seq2[104:] = 1  # the last sequence uses tail row 1
+    keep_seq2[n0 + n1:] = 1  # the last sequence uses tail row 1
     kvq.write(dev, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV), torch.from_numpy(slots).to(DEV),
               torch.from_numpy(keep_seq2).to(DEV))
     o.write(orc, k, v, slots, keep_seq2)
