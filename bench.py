@@ -114,7 +114,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, command: str) -> 
                            "fetch_counter_bytes": cal_f, "write_counter_bytes": cal_w,
                            "fetch_factor": kf, "write_factor": kw}, "kernels": {}}
     total = 0.0
-    for key in ("plan_kernel", "decode_split_kernel", "kivi_tail_kernel", "merge_kernel"):
+    for key in ("plan_kernel", "decode_split_kernel", "merge_kernel"):
         if not any(key in k for k in f):
             continue
         fb, nf = pick(f, key)

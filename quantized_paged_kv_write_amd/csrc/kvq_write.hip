@@ -429,42 +429,64 @@ void kivi_write_kernel(WriteArgs a, uint32_t n_val, int nw) {
 
 // Rows of the pages a large KIVI call leaves open (the page's last row is not
 // at its expected position in the call) go to the sequence's fp16 tail, key
-// and value.  One wave per 64 call tokens; the wave copies each such token's
-// H rows (contiguous in the call and in the tail row) with 16-byte accesses.
+// and value.  A workgroup takes 256 call tokens, a thread each: it decides
+// whether its token's page stays open and where the token's tail row is; the
+// open tokens are listed in LDS, and then all 256 threads copy their rows (H
+// rows of D values, contiguous in the call and in the tail row) in 16-byte
+// pieces, the loads of up to 32 tokens in flight per thread.  Most tokens of
+// a prefill close their page; a workgroup without an open token stops after
+// the check.
 template <int D>
 __global__ __launch_bounds__(256) void kivi_tail_kernel(WriteArgs a) {
-  const int lane = (int)threadIdx.x & 63;
-  const int64_t t0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 64;
-  const int64_t t = t0 + lane;
-  bool open = false;
-  int32_t seq = 0;
-  int off = 0;
+  __shared__ int64_t s_src[256];  // call token of the i-th open token
+  __shared__ int64_t s_dst[256];  // its tail row (offset in halves)
+  __shared__ int s_cnt[4];
+  const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
+  int64_t dst = -1;
   if (t < a.T) {
     const int64_t s = a.slots[t];
     if (s >= 0 && s < a.capacity) {
-      seq = a.seq_idx[t];
+      const int32_t seq = a.seq_idx[t];
       const bool seq_ok = seq >= 0 && seq < a.max_seqs;
       report_error(a.err, !seq_ok, KVQ_DEVERR_SEQ);
-      off = (int)(s % a.bs);
+      const int off = (int)(s % a.bs);
       const int64_t te = t + (a.bs - 1 - off);
       const bool sealed = te < a.T && a.seq_idx[te] == seq && a.slots[te] == s + (a.bs - 1 - off);
-      open = seq_ok && !sealed;
+      if (seq_ok && !sealed) dst = ((int64_t)seq * a.bs + off) * a.H * D;
     }
   }
-  uint64_t m = __ballot(open);
-  const int nch = a.H * D / 8;  // 16-byte chunks of a token's H rows
-  while (m) {
-    const int j = __ffsll((unsigned long long)m) - 1;
-    m &= m - 1;
-    const int32_t sq = __shfl(seq, j);
-    const int oj = __shfl(off, j);
-    const u32x4* ks = reinterpret_cast<const u32x4*>(a.k + (size_t)(t0 + j) * a.H * D);
-    const u32x4* vs = reinterpret_cast<const u32x4*>(a.v + (size_t)(t0 + j) * a.H * D);
-    u32x4* kd = reinterpret_cast<u32x4*>(a.k_tail + ((size_t)sq * a.bs + oj) * a.H * D);
-    u32x4* vd = reinterpret_cast<u32x4*>(a.v_tail + ((size_t)sq * a.bs + oj) * a.H * D);
-    for (int c = lane; c < nch; c += 64) {
-      kd[c] = ks[c];
-      vd[c] = vs[c];
+  const uint64_t m = __ballot(dst >= 0);
+  if (lane == 0) s_cnt[w] = __popcll(m);
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    base += i < w ? s_cnt[i] : 0;
+    total += s_cnt[i];
+  }
+  if (total == 0) return;  // the same for every thread of the workgroup
+  if (dst >= 0) {
+    const int pos = base + __popcll(m & ((1ull << lane) - 1));
+    s_src[pos] = t;
+    s_dst[pos] = dst;
+  }
+  __syncthreads();
+  const int nch = a.H * D / 8;  // 16-byte pieces of one token's H rows (keys, then values)
+  for (int c = tid; c < 2 * nch; c += 256) {
+    const bool isv = c >= nch;
+    const size_t cofs = (size_t)(isv ? c - nch : c) * 8;  // in halves
+    const uint16_t* src = isv ? a.v : a.k;
+    uint16_t* dstb = isv ? a.v_tail : a.k_tail;
+    for (int k0 = 0; k0 < total; k0 += 32) {
+      u32x4 buf[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (k0 + u < total)
+          buf[u] = *reinterpret_cast<const u32x4*>(src + (size_t)s_src[k0 + u] * a.H * D + cofs);
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (k0 + u < total) *reinterpret_cast<u32x4*>(dstb + s_dst[k0 + u] + cofs) = buf[u];
     }
   }
 }

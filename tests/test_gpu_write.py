@@ -151,6 +151,33 @@ def test_write_kivi_incremental_decode_steps():
     assert compare_buffers(dev, orc) == {}
 
 
+def test_write_kivi_large_decode_step():
+    # A decode step of more than 2048 sequences (one large call, one token
+    # per sequence): most tokens stay in their sequence's tail, and the
+    # sequences at page offset 31 complete a page whose other rows come from
+    # the tail written by the previous (also large) call.
+    n, H, D, bs = 2100, 2, 128, 32
+    rng = np.random.default_rng(23)
+    off = rng.integers(0, 32, n)
+    off[:70] = 31
+    k = (rng.standard_normal((int(off.sum()) + n, H, D)) * 1.5).astype(np.float16)
+    v = rng.standard_normal(k.shape).astype(np.float16)
+    seq_first = np.repeat(np.arange(n), off).astype(np.int32)
+    slot_first = np.concatenate([32 * i + np.arange(o_) for i, o_ in enumerate(off)]).astype(np.int64)
+    seq_step = np.arange(n, dtype=np.int32)
+    slot_step = (32 * np.arange(n) + off).astype(np.int64)
+    dev, orc = new_caches(n, bs, H, D, "int4_kivi", "int4_g32", n, DEV, seed=24)
+    import quantized_paged_kv_write_amd as kvq
+    m = len(seq_first)
+    assert m > 2048
+    for lo, hi, sl, sq in ((0, m, slot_first, seq_first), (m, m + n, slot_step, seq_step)):
+        kvq.write(dev, torch.from_numpy(k[lo:hi]).to(DEV), torch.from_numpy(v[lo:hi]).to(DEV),
+                  torch.from_numpy(sl).to(DEV), torch.from_numpy(sq).to(DEV))
+        o.write(orc, k[lo:hi], v[lo:hi], sl, sq)
+    torch.cuda.synchronize()
+    assert compare_buffers(dev, orc) == {}
+
+
 def test_write_kivi_large_calls():
     # Calls of more than 2048 tokens (one seal wave per 32 call tokens):
     # sequences start inside a chunk, pages straddle the two calls (their
