@@ -89,7 +89,8 @@ typedef enum kvq_device_error {
  *                the maximum of the FNUZ variant; gfx950 uses OCP E4M3FN.)
  * KVQ_INT4_G32   symmetric, one fp16 scale per 32 consecutive channels of a
  *                (token, head) row, q_max 7; two codes per byte, even channel
- *                in the low nibble, two's complement ([P2] 5).
+ *                in the low nibble, two's complement ([P2] 5).  Keys or
+ *                values.
  * KVQ_INT4_KIVI  keys only: asymmetric per channel over the 32 tokens of a
  *                page ([P2] 5, [P3], [P4]); requires block_size == 32.  Per
  *                (page, head, channel): scale = fp16(fl32(max-min)/15), zero =
@@ -302,8 +303,7 @@ int kvq_prefill_workspace_bytes(const kvq_cache* cache, int64_t total_q,
  * Scores and the softmax are accumulated in fp32 and the result is rounded
  * to fp16 once; a given call gives bitwise the same result every time.
  * KVQ_ERR_SHAPE when total_q x n_q_heads x head_dim reaches 2^31 or
- * max_q_len x n_q_heads / n_kv_heads reaches 2^30; KVQ_ERR_UNSUPPORTED for
- * KVQ_INT4_G32 keys. */
+ * max_q_len x n_q_heads / n_kv_heads reaches 2^30. */
 int kvq_prefill_attn(const kvq_cache* cache, const void* q,
                      const int32_t* q_start, const int32_t* block_table,
                      int32_t max_blocks_per_seq, const int32_t* ctx_lens,

@@ -523,7 +523,7 @@ def write_static(cache: OracleCache, k16: np.ndarray, v16: np.ndarray, slot_mapp
     and V instead of the per-token amax ([P3] Implementation Best Practices,
     calibrated scaling factors; [P4] static calibration).  Symmetric formats only; every written row
     stores its head's scale in its scale slot, so reading is unchanged."""
-    assert cache.k_fmt in SYM_FORMATS and cache.k_fmt != INT4_G32 and cache.v_fmt in SYM_FORMATS
+    assert cache.k_fmt in SYM_FORMATS and cache.v_fmt in SYM_FORMATS
     slots = np.asarray(slot_mapping, dtype=np.int64)
     valid = np.nonzero(slot_in_range(cache, slots))[0]
     bs = cache.bs

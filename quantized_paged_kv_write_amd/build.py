@@ -29,6 +29,8 @@ SOURCES = {
     "kvq_decode_kfp8.hip": [],
     "kvq_decode_kkivi.hip": [],
     "kvq_decode_ke5m2.hip": [],
+    "kvq_decode_kint4.hip": [],
+    "kvq_decode_kint4_rot.hip": [],
     "kvq_decode_kint8_rot.hip": [],
     "kvq_decode_kfp8_rot.hip": [],
     "kvq_decode_ke5m2_rot.hip": [],
@@ -38,6 +40,7 @@ SOURCES = {
     "kvq_prefill_kfp8.hip": [],
     "kvq_prefill_kkivi.hip": [],
     "kvq_prefill_ke5m2.hip": [],
+    "kvq_prefill_kint4.hip": [],
 }
 
 COMMON = [

@@ -120,7 +120,6 @@ int write_impl(const kvq_cache* cache, const void* k, const void* v, const int64
                void* stream) {
   int rc = check_cache(cache);
   if (rc != KVQ_OK) return rc;
-  if (cache->k_dtype == KVQ_INT4_G32) return KVQ_ERR_UNSUPPORTED;  // INT4 keys: KIVI only
   if (k_static && cache->k_dtype == KVQ_INT4_KIVI) return KVQ_ERR_UNSUPPORTED;  // KIVI keys are dynamic
   if (num_tokens < 0) return KVQ_ERR_INVALID_ARG;
   if (num_tokens == 0) return KVQ_OK;
@@ -196,7 +195,6 @@ int decode_impl(const kvq_cache* cache, const void* q, const int32_t* block_tabl
                 void* out, void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
   int rc = check_cache(cache);
   if (rc != KVQ_OK) return rc;
-  if (cache->k_dtype == KVQ_INT4_G32) return KVQ_ERR_UNSUPPORTED;
   if (batch < 0 || n_q_heads <= 0 || max_blocks_per_seq <= 0 || split_tokens < 0) return KVQ_ERR_INVALID_ARG;
   if (n_q_heads % cache->n_kv_heads != 0) return KVQ_ERR_SHAPE;
   const int32_t G = n_q_heads / cache->n_kv_heads;
@@ -288,7 +286,6 @@ int kvq_prefill_attn(const kvq_cache* cache, const void* q, const int32_t* q_sta
                      size_t workspace_bytes, void* stream) {
   int rc = check_cache(cache);
   if (rc != KVQ_OK) return rc;
-  if (cache->k_dtype == KVQ_INT4_G32) return KVQ_ERR_UNSUPPORTED;
   if (batch < 0 || total_q < 0 || n_q_heads <= 0 || max_blocks_per_seq <= 0 || max_q_len < 0)
     return KVQ_ERR_INVALID_ARG;
   if (n_q_heads % cache->n_kv_heads != 0) return KVQ_ERR_SHAPE;

@@ -66,10 +66,14 @@ constexpr int AUTO_MIN_TILES = 4;
 
 template <int FK, int D>
 struct KShape {
-  static constexpr int RB = FK == F_KIVI ? D / 2 : D;  // key row bytes
+  static constexpr int RB = FK == F_KIVI || FK == F_INT4 ? D / 2 : D;  // key row bytes
   static constexpr int LB = RB / 4;                    // bytes per lane (quarter row)
   static constexpr int NW = LB / 4;                    // dwords per lane
   static constexpr int KB = D / 32;                    // MFMA k-blocks
+  // INT4 keys: one scale per 32 channels (k-block kb is scale group kb);
+  // a row's scales fill NGKD whole dwords
+  static constexpr int NGK = FK == F_INT4 ? D / 32 : 1;
+  static constexpr int NGKD = FK == F_INT4 ? D / 64 : 1;
 };
 
 template <int FV, int D>
@@ -113,7 +117,22 @@ __device__ __forceinline__ void e5m2_to_h4(uint32_t d, uint32_t& lo, uint32_t& h
 template <int FK>
 __device__ __forceinline__ h8 key_operand(const uint32_t* w, int kb) {
   u4 r;
-  if constexpr (FK == F_KIVI) {
+  if constexpr (FK == F_INT4) {
+    // 8 two's-complement nibbles of one dword, channels 32 kb + 8 j .. + 7
+    // (byte b: channel 2b low, 2b + 1 high); pair i = channels (i, i + 4).
+    // (nibble ^ 8) under the fp16 exponent of 1024 is 1024 + c + 8, exactly;
+    // one packed subtract of 1032 leaves c.  f(x, m, k) = (x & m) ^ k has the
+    // truth table 0x6A (x = 0xF0, m = 0xCC, k = 0xAA).
+    const uint32_t d = w[kb];
+    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+    auto pair = [&](uint32_t x) __attribute__((always_inline)) {
+      return h2_bits(as_h2(__builtin_amdgcn_bitop3_b32(x, 0x000F000Fu, 0x64086408u, 0x6A)) - bias);
+    };
+    r.x = pair(d);
+    r.y = pair(d >> 4);
+    r.z = pair(d >> 8);
+    r.w = pair(d >> 12);
+  } else if constexpr (FK == F_KIVI) {
     // 8 unsigned nibbles of one dword; pair i = channels (i, i + 4).  A
     // nibble in mantissa bits 0-3 of an fp16 is the subnormal n 2^-24, in
     // bits 4-7 it is 16 n 2^-24, both exact: even channels (x, z) give
@@ -145,6 +164,7 @@ __device__ __forceinline__ h8 key_operand(const uint32_t* w, int kb) {
 // order; the query operand is laid out to match).
 template <int FK, int D>
 __device__ __forceinline__ int key_channel(int j, int kb, int e) {
+  if constexpr (FK == F_INT4) return 32 * kb + 8 * j + ((e & 1) ? 4 + (e >> 1) : (e >> 1));
   const int base = j * (D / 4) + 8 * kb;
   if constexpr (FK == F_KIVI) return base + ((e & 1) ? 4 + (e >> 1) : (e >> 1));
   return base + e;
@@ -304,18 +324,18 @@ struct Stage {
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = KT;
   static constexpr int OFF_S = KT + VT;              // raw scale dwords (see load_tile)
-  static constexpr int OFF_M = OFF_S + 4 * TILE * (1 + NGD);
+  static constexpr int OFF_M = OFF_S + 4 * TILE * (KS::NGKD + NGD);
   static constexpr int BYTES = OFF_M + KIVI_BYTES;
-  // one wave's LDS: the stage, then this tile's key scales (TILE fp32) and
-  // value scales (TILE NG fp32)
-  static constexpr int WAVE_LDS = (BYTES + 4 * TILE + 4 * TILE * VS::NG + 15) / 16 * 16;
+  // one wave's LDS: the stage, then this tile's key scales (TILE NGK fp32)
+  // and value scales (TILE NG fp32)
+  static constexpr int WAVE_LDS = (BYTES + 4 * TILE * KS::NGK + 4 * TILE * VS::NG + 15) / 16 * 16;
   // Waves per SIMD and register slots for tiles.  Head dims up to 128 run
   // two waves per SIMD (each within 256 registers), so one wave's compute
   // hides the other's waits; a wave then holds NS = 2 tiles (one in flight
   // while one is stored to LDS and computed).  Head dim 256 runs one wave per
   // SIMD with up to 4 tiles held, within about 136 registers.
   static constexpr int WPE = D <= 128 ? 2 : 1;
-  static constexpr int TILE_REGS = 4 * (NLK + NLV) + NGD + 1 + (FK == F_KIVI ? 4 * (D / 64) : 0);
+  static constexpr int TILE_REGS = 4 * (NLK + NLV) + NGD + KS::NGKD + (FK == F_KIVI ? 4 * (D / 64) : 0);
   static constexpr int NS_FIT = 136 / TILE_REGS;
   static constexpr int NS = WPE == 2 ? 2 : (NS_FIT < 2 ? 2 : (NS_FIT > 4 ? 4 : NS_FIT));
 };
@@ -336,6 +356,7 @@ struct TileRegs {
   u4 k[S::NLK];
   u4 v[S::NLV];
   uint32_t s[S::NGD];
+  uint32_t sk[KShape<FK, D>::NGKD > 1 ? KShape<FK, D>::NGKD - 1 : 1];  // INT4 keys: key-scale dwords 1..
   uint32_t par;  // bit rho: row rho's 16-bit scale is the high half of its dword
   // direct scales (one page per tile, two or four heads per wave): the raw
   // fp16 key scale and value scales of the lane's score rows
@@ -498,11 +519,18 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
   // scale dwords (LDS dword index): [rho] the dword holding row rho's key
   // scale, [32 + rho] the first value-scale dword of row rho, [32 + 32 k +
   // rho] its value-scale dword k >= 1 (INT4 groups; lanes < 32).  A lone
-  // fp16 scale sits in half (flat row & 1) of its dword (par).
+  // fp16 scale sits in half (flat row & 1) of its dword (par).  INT4 keys:
+  // [rho] is the first of row rho's key-scale dwords (groups 0, 1), and
+  // [32 (1 + NGD) + 32 (k - 1) + rho] its key-scale dword k >= 1.
   {
     const uint16_t* src;
-    if (lane < 32) src = FK == F_KIVI ? a.v_scales : a.k_scales + (live ? (r_own & ~1u) : 0);
-    else src = a.v_scales + (live ? ((size_t)r_own * VS::NG & ~(size_t)1) : 0);
+    if (lane < 32) {
+      if constexpr (FK == F_KIVI) src = a.v_scales;
+      else if constexpr (FK == F_INT4) src = a.k_scales + (live ? (size_t)r_own * KS::NGK : 0);
+      else src = a.k_scales + (live ? (r_own & ~1u) : 0);
+    } else {
+      src = a.v_scales + (live ? ((size_t)r_own * VS::NG & ~(size_t)1) : 0);
+    }
     r.s[0] = *reinterpret_cast<const uint32_t*>(src);
     r.par = (uint32_t)__ballot(live && (r_own & 1u));
   }
@@ -510,6 +538,12 @@ __device__ __forceinline__ uint64_t load_tile(const DecodeArgs& a, int bid, int 
   for (int g = 1; g < S::NGD; ++g)
     r.s[g] = *reinterpret_cast<const uint32_t*>(a.v_scales +
                                                 (live && lane < 32 ? (size_t)r_own * VS::NG + 2 * g : 0));
+  if constexpr (FK == F_INT4) {
+#pragma unroll
+    for (int g = 1; g < KS::NGKD; ++g)
+      r.sk[g - 1] = *reinterpret_cast<const uint32_t*>(a.k_scales +
+                                                       (live && lane < 32 ? (size_t)r_own * KS::NGK + 2 * g : 0));
+  }
   if constexpr (FK == F_KIVI) {
     // the tile lies in one page (block_size 32): the D scales of heads
     // h0 .. h0 + HPC - 1 (contiguous), then their D zeros; chunk c of 16 bytes
@@ -543,6 +577,11 @@ __device__ __forceinline__ void store_tile(const TileRegs<FK, FV, D, HPC>& r, ui
 #pragma unroll
     for (int g = 1; g < S::NGD; ++g)
       if (lane < 32) sd[32 + 32 * g + lane] = r.s[g];
+    if constexpr (FK == F_INT4) {
+#pragma unroll
+      for (int g = 1; g < KShape<FK, D>::NGKD; ++g)
+        if (lane < 32) sd[32 * (1 + S::NGD) + 32 * (g - 1) + lane] = r.sk[g - 1];
+    }
   }
   if constexpr (FK == F_KIVI) {
     using TR = TileRegs<FK, FV, D, HPC>;
@@ -667,7 +706,7 @@ void decode_split_kernel(DecodeArgs a) {
   uint8_t* const s_st = s_dyn + wv * ST::WAVE_LDS;
   // this tile's scales as fp32: key scale x sm_scale x log2 e, value scales
   float* const s_fk = reinterpret_cast<float*>(s_st + ST::BYTES);
-  float* const s_fv = s_fk + TILE;
+  float* const s_fv = s_fk + TILE * KS::NGK;
 
   // Wave (share, group of HP KV heads).  The workgroups of one share (when
   // a share needs more than one) are consecutive workgroups of one XCD
@@ -935,7 +974,15 @@ void decode_split_kernel(DecodeArgs a) {
       const bool lv = (live_mask >> t) & 1;
       const bool hi_half = (par >> t) & 1;
       if (!DSC && lane < 32) {
-        if constexpr (FK != F_KIVI) {
+        if constexpr (FK == F_INT4) {
+          // row t's key scales, group g at s_fk[t NGK + g]
+#pragma unroll
+          for (int g = 0; g < KS::NGKD; ++g) {
+            const uint32_t d = g == 0 ? sdw[t] : sdw[32 * (1 + ST::NGD) + 32 * (g - 1) + t];
+            s_fk[t * KS::NGK + 2 * g] = lv ? h2f(d & 0xFFFFu) * a.qscale : 0.f;
+            s_fk[t * KS::NGK + 2 * g + 1] = lv ? h2f(d >> 16) * a.qscale : 0.f;
+          }
+        } else if constexpr (FK != F_KIVI) {
           const uint32_t d = sdw[t];
           s_fk[t] = lv ? h2f(hi_half ? d >> 16 : d & 0xFFFFu) * a.qscale : 0.f;
         }
@@ -974,7 +1021,15 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int row = 16 * u + n;
-      if constexpr (KS::LB >= 16) {
+      if constexpr (FK == F_INT4) {
+        // k-block kb is the row's 16-byte chunk kb (scale group kb); lane
+        // group j takes its dword j (channels 32 kb + 8 j .. + 7)
+#pragma unroll
+        for (int kb = 0; kb < KS::KB; ++kb) {
+          const int col = kb ^ kswz<CHK>(row);
+          kw[u][kb] = *reinterpret_cast<const uint32_t*>(cur + ST::OFF_K + (row * CHK + col) * 16 + 4 * j);
+        }
+      } else if constexpr (KS::LB >= 16) {
 #pragma unroll
         for (int q = 0; q < KS::LB / 16; ++q) {
           const int col = (j * KS::LB / 16 + q) ^ kswz<CHK>(row);
@@ -1037,13 +1092,18 @@ void decode_split_kernel(DecodeArgs a) {
 
     // ---- scores S^T[t][g] on the matrix cores ------------------------------
     f4 sc[2];
+    // INT4 keys: one product per k-block (scale group), scaled per row below
+    f4 sck[FK == F_INT4 ? KS::KB : 1][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       sc[u] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KS::KB; ++kb) {
         const h8 kop = key_operand<FK>(kw[u], kb);
-        if constexpr (FK == F_KIVI) {
+        if constexpr (FK == F_INT4) {
+          sck[kb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[kb], f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          if constexpr (ROTQ) sck[kb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qlo_r[kb], sck[kb][u], 0, 0, 0);
+        } else if constexpr (FK == F_KIVI) {
           sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qhi[kb], sc[u], 0, 0, 0);
           sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qlo[kb], sc[u], 0, 0, 0);
         } else if constexpr (ROTQ) {
@@ -1068,16 +1128,22 @@ void decode_split_kernel(DecodeArgs a) {
         const int r = HPC == 1 ? i : hn + HPC * i;
         const int tr = 16 * u + 4 * j + r;
         rows[u][i] = tr;
-        float raw;
-        if constexpr (HPC == 1) raw = sc[u][i];
-        else if constexpr (HPC == 2) raw = hn ? sc[u][2 * i + 1] : sc[u][2 * i];
-        else {
-          const float r01 = (hn & 1) ? sc[u][1] : sc[u][0];
-          const float r23 = (hn & 1) ? sc[u][3] : sc[u][2];
-          raw = (hn & 2) ? r23 : r01;
-        }
+        auto pick = [&](const f4& x) __attribute__((always_inline)) {
+          if constexpr (HPC == 1) return x[i];
+          else if constexpr (HPC == 2) return hn ? x[2 * i + 1] : x[2 * i];
+          else {
+            const float r01 = (hn & 1) ? x[1] : x[0];
+            const float r23 = (hn & 1) ? x[3] : x[2];
+            return (hn & 2) ? r23 : r01;
+          }
+        };
+        const float raw = FK == F_INT4 ? 0.f : pick(sc[u]);
         float v;
-        if constexpr (FK == F_KIVI) v = __builtin_fmaf(raw, kmul, qz);
+        if constexpr (FK == F_INT4) {
+          v = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < KS::KB; ++kb) v = __builtin_fmaf(pick(sck[kb][u]), s_fk[tr * KS::NGK + kb], v);
+        } else if constexpr (FK == F_KIVI) v = __builtin_fmaf(raw, kmul, qz);
         else if constexpr (DSC) v = raw * fkf[u * NU + i];
         else v = raw * s_fk[tr];
         // a masked row's key codes may be anything, and a row of another KV
@@ -1596,7 +1662,8 @@ hipError_t launch4(DecodeArgs a, hipStream_t st) {
 
 template <int FK, int FV, int D, bool ROTQ>
 hipError_t launch3(const DecodeArgs& a, hipStream_t st) {
-  constexpr bool OP_PAYS = FV == F_INT4 || FK == F_KIVI;
+  // (INT4 keys: the general path, whose scales pass through LDS)
+  constexpr bool OP_PAYS = (FV == F_INT4 || FK == F_KIVI) && FK != F_INT4;
   switch (a.hp_log2) {
     // Tiles of 32 / HP tokens lie in one page when the page holds at least
     // that many (always for HP = 4: block_size >= 8).  The one-page address

@@ -132,6 +132,7 @@ hipError_t launch_decode(const kvq_cache& c, const DecodeArgs& a, hipStream_t s)
       case F_INT8: return decode_keys_int8_rot(c.v_dtype, c.head_dim, a, s);
       case F_FP8: return decode_keys_fp8_rot(c.v_dtype, c.head_dim, a, s);
       case F_E5M2: return decode_keys_e5m2_rot(c.v_dtype, c.head_dim, a, s);
+      case F_INT4: return decode_keys_int4_rot(c.v_dtype, c.head_dim, a, s);
     }
     return hipErrorInvalidValue;
   }
@@ -140,6 +141,7 @@ hipError_t launch_decode(const kvq_cache& c, const DecodeArgs& a, hipStream_t s)
     case F_FP8: return decode_keys_fp8(c.v_dtype, c.head_dim, a, s);
     case F_KIVI: return decode_keys_kivi(c.v_dtype, c.head_dim, a, s);
     case F_E5M2: return decode_keys_e5m2(c.v_dtype, c.head_dim, a, s);
+    case F_INT4: return decode_keys_int4(c.v_dtype, c.head_dim, a, s);
   }
   return hipErrorInvalidValue;
 }

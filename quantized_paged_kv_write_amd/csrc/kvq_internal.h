@@ -138,10 +138,12 @@ hipError_t decode_keys_int8(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_fp8(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_kivi(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_e5m2(int fv, int D, const DecodeArgs& a, hipStream_t s);
+hipError_t decode_keys_int4(int fv, int D, const DecodeArgs& a, hipStream_t s);
 // rotated keys (the query operand is the rotated query, fp16 hi + lo)
 hipError_t decode_keys_int8_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_fp8_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
 hipError_t decode_keys_e5m2_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
+hipError_t decode_keys_int4_rot(int fv, int D, const DecodeArgs& a, hipStream_t s);
 
 // The rotated query q' = H (sigma q) / D of `rows` fp16 rows of head_dim D,
 // written as fp16 hi (rows, D) at qrot and lo (rows, D) right after it.
@@ -154,6 +156,7 @@ hipError_t prefill_keys_int8(int fv, int D, bool rot, const PrefillArgs& a, hipS
 hipError_t prefill_keys_fp8(int fv, int D, bool rot, const PrefillArgs& a, hipStream_t s);
 hipError_t prefill_keys_kivi(int fv, int D, bool rot, const PrefillArgs& a, hipStream_t s);
 hipError_t prefill_keys_e5m2(int fv, int D, bool rot, const PrefillArgs& a, hipStream_t s);
+hipError_t prefill_keys_int4(int fv, int D, bool rot, const PrefillArgs& a, hipStream_t s);
 
 
 }  // namespace kvq

@@ -48,20 +48,23 @@ namespace kvq {
 template <int FK, int FV, int D>
 struct PLayout {
   static constexpr bool KIVI = FK == F_KIVI;
+  // 4-bit keys (KIVI, INT4 group-32) are dequantized when stored: k_hat as
+  // fp16 hi and lo planes
+  static constexpr bool PLANES = KIVI || FK == F_INT4;
   using VS = VShape<FV, D>;
   static constexpr int NQB = D <= 128 ? 2 : 1;  // 16-column blocks per wave
   static constexpr int NWAVE = 4;
   static constexpr int THREADS = 64 * NWAVE;
   static constexpr int ROWS = NWAVE * 16 * NQB;  // query rows per workgroup
   // LDS: three buffers of [keys fp16 | value codes | key scales fp32 | value
-  // scales fp32] (KIVI keys: fp16 hi plane then lo plane), then (KIVI) the
+  // scales fp32] (4-bit keys: fp16 hi plane then lo plane), then (KIVI) the
   // tail's values transposed, fp16 [D][32].  Value scales of INT4 groups are
   // stored group-major, [group][token].
-  static constexpr int KRB = 2 * D;             // key row bytes in LDS: fp16 (KIVI: per plane)
+  static constexpr int KRB = 2 * D;             // key row bytes in LDS: fp16 (4-bit keys: per plane)
   static constexpr int KCH = KRB / 16;          // 16-byte chunks per key row
   static constexpr int KPLANE = TILE * KRB;
   static constexpr int OFF_K = 0;
-  static constexpr int OFF_V = (KIVI ? 2 : 1) * KPLANE;
+  static constexpr int OFF_V = (PLANES ? 2 : 1) * KPLANE;
   static constexpr int OFF_FK = OFF_V + TILE * VS::RB;
   static constexpr int OFF_FV = OFF_FK + 4 * TILE;
   static constexpr int BUF = (OFF_FV + 4 * TILE * VS::NG + 15) / 16 * 16;
@@ -73,9 +76,10 @@ struct PLayout {
   static constexpr int NLK = (NK + THREADS - 1) / THREADS;
   static constexpr int NV = TILE * VS::CH;
   static constexpr int NLV = (NV + THREADS - 1) / THREADS;
-  // KIVI: thread (t, cg) = (tid / 8, tid % 8) handles channels cg KE ..
-  // cg KE + KE - 1 of token t: KE / 2 code bytes, KM 16-byte chunks of fp16
-  // scales, zeros (or of the tail's key and value rows)
+  // 4-bit keys: thread (t, cg) = (tid / 8, tid % 8) handles channels cg KE
+  // .. cg KE + KE - 1 of token t: KE / 2 code bytes; KIVI: KM 16-byte chunks
+  // of fp16 scales, zeros (or of the tail's key and value rows); INT4
+  // group-32: the channels' one group scale (KE <= 32 and KE divides 32)
   static constexpr int KE = D / 8;
   static constexpr int KM = KE / 8;
 };
@@ -101,11 +105,12 @@ __device__ __forceinline__ uint32_t u4_word(const u4& v, int i) {
 template <int FK, int FV, int D>
 struct PRegs {
   using PL = PLayout<FK, FV, D>;
-  u4 k[PL::KIVI ? 1 : PL::NLK];  // key code chunks (8-bit keys); KIVI: the thread's code bytes in k[0]
+  u4 k[PL::PLANES ? 1 : PL::NLK];  // key code chunks (8-bit keys); 4-bit keys: the thread's code bytes in k[0]
   u4 ks[PL::KIVI ? PL::KM : 1];  // KIVI: scales of the thread's channels (tail tile: the key row)
   u4 kz[PL::KIVI ? PL::KM : 1];  // KIVI: zero points (tail tile: the value row)
   u4 v[PL::NLV];
   uint16_t fk;                   // wave 0, lanes < 32: fp16 key scale of token lane
+  uint16_t kg;                   // INT4 group-32 keys: the scale of the thread's channels' group
   u4 fv;                         // wave 0, lanes >= 32: fp16 value scales of token lane - 32
 };
 
@@ -140,7 +145,7 @@ __device__ __forceinline__ void split_f16x2_bf16(uint32_t h2v, uint32_t& hi, uin
 // query operand) and for KIVI keys at head_dim 256.
 template <int FK, int FV, int D, bool ROTQ>
 constexpr int prefill_wpe() {
-  return (FV == F_INT4 && ROTQ) || (FK == F_KIVI && D == 256) ? 1 : 2;
+  return (FV == F_INT4 && ROTQ) || ((FK == F_KIVI || FK == F_INT4) && D == 256) ? 1 : 2;
 }
 
 template <int FK, int FV, int D, bool ROTQ>
@@ -261,7 +266,7 @@ void prefill_kernel(PrefillArgs a) {
     const uint32_t flat =
         ok ? (((uint32_t)id << a.log2_bs) + (uint32_t)(tok & (a.bs - 1))) * (uint32_t)a.H + (uint32_t)h : 0u;
     const uint32_t live = (uint32_t)__ballot(ok);
-    if constexpr (!KIVI) {
+    if constexpr (!PL::PLANES) {
 #pragma unroll
       for (int i = 0; i < PL::NLK; ++i) {
         const int p = tid + PL::THREADS * i;
@@ -275,6 +280,9 @@ void prefill_kernel(PrefillArgs a) {
       const int t = tid >> 3, cg = tid & 7;
       const uint32_t fr = (uint32_t)__shfl((int)flat, t);
       r.k[0] = load_n<D / 16>(a.k_codes + (size_t)fr * (D / 2) + cg * (D / 16));
+      if constexpr (FK == F_INT4) {
+        r.kg = a.k_scales[(size_t)fr * (D / 32) + (cg * PL::KE) / 32];
+      } else {
       // the tile is one page (block_size 32): its scales and zeros for head h
       const int id0 = __builtin_amdgcn_readfirstlane(id);
       const bool ok0 = (live & 1u) != 0u;
@@ -283,6 +291,7 @@ void prefill_kernel(PrefillArgs a) {
       for (int k = 0; k < PL::KM; ++k) {
         r.ks[k] = *reinterpret_cast<const u4*>(a.k_scales + mrow + 8 * k);
         r.kz[k] = *reinterpret_cast<const u4*>(a.k_zeros + mrow + 8 * k);
+      }
       }
     }
 #pragma unroll
@@ -298,7 +307,7 @@ void prefill_kernel(PrefillArgs a) {
     if (wv == 0) {
       // every lane loads both (lanes < 32 keep the key scale, the others
       // the value scales), so no branch waits on a load
-      if constexpr (!KIVI) r.fk = a.k_scales[flat];
+      if constexpr (!PL::PLANES) r.fk = a.k_scales[flat];
       r.fv = load_n<2 * VS::NG>(a.v_scales + (size_t)flat * VS::NG);
     }
     return live;
@@ -306,7 +315,7 @@ void prefill_kernel(PrefillArgs a) {
 
   // Store a loaded page tile into LDS buffer `buf` (layout PLayout).
   auto store_tile = [&](const PRegs<FK, FV, D>& r, uint32_t live, uint8_t* buf) __attribute__((always_inline)) {
-    if constexpr (!KIVI) {
+    if constexpr (!PL::PLANES) {
 #pragma unroll
       for (int i = 0; i < PL::NLK; ++i) {
         const int p = tid + PL::THREADS * i;
@@ -330,20 +339,28 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
     } else {
-      // k_hat = c s + z in fp32 (one rounding), stored as fp16 hi + lo with
-      // hi = RN(min(|k_hat|, 65504)), lo = RN(k_hat - hi)
+      // KIVI: k_hat = c s + z in fp32 (one rounding); INT4 group-32: k_hat =
+      // c s, exact (at most 3 + 11 significant bits).  Stored as fp16 hi + lo
+      // with hi = RN(min(|k_hat|, 65504)), lo = RN(k_hat - hi)
       const int t = tid >> 3, cg = tid & 7;
       const bool lv = (live >> t) & 1u;
       uint32_t hw[PL::KE / 2], lw[PL::KE / 2];
 #pragma unroll
       for (int e2 = 0; e2 < PL::KE / 2; ++e2) {
         const uint32_t codes = u4_word(r.k[0], e2 / 4) >> (8 * (e2 % 4));  // byte e2: channels 2 e2, 2 e2 + 1
-        const uint32_t sw = u4_word(r.ks[e2 / 4], e2 % 4), zw = u4_word(r.kz[e2 / 4], e2 % 4);
         uint32_t hh[2], ll[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const float c = (float)((codes >> (4 * q)) & 0xFu);
-          const float x = lv ? __builtin_fmaf(c, h2f(sw >> (16 * q)), h2f((zw >> (16 * q)) & 0xFFFFu)) : 0.f;
+          float x;
+          if constexpr (FK == F_INT4) {
+            // two's-complement nibble
+            const float c = (float)((int)(((codes >> (4 * q)) & 0xFu) ^ 8u) - 8);
+            x = lv ? c * h2f(r.kg) : 0.f;
+          } else {
+            const uint32_t sw = u4_word(r.ks[e2 / 4], e2 % 4), zw = u4_word(r.kz[e2 / 4], e2 % 4);
+            const float c = (float)((codes >> (4 * q)) & 0xFu);
+            x = lv ? __builtin_fmaf(c, h2f(sw >> (16 * q)), h2f((zw >> (16 * q)) & 0xFFFFu)) : 0.f;
+          }
           const float xs = fminf(fmaxf(x, -65504.f), 65504.f);
           hh[q] = f2h_bits_of_f32(xs);
           ll[q] = f2h_bits(x - h2f(hh[q]));
@@ -380,7 +397,7 @@ void prefill_kernel(PrefillArgs a) {
         // codes when the scale is 0), so such a row scores 0 with any factor;
         // dead rows and zero scales store factor 1, so that a masked (-inf)
         // raw score stays -inf when scaled.
-        if constexpr (!KIVI) fk[t] = (lv && (r.fk & 0x7FFFu) != 0u) ? h2f(r.fk) * a.qscale : 1.f;
+        if constexpr (!PL::PLANES) fk[t] = (lv && (r.fk & 0x7FFFu) != 0u) ? h2f(r.fk) * a.qscale : 1.f;
       } else {
 #pragma unroll
         for (int g = 0; g < VS::NG; ++g)
@@ -415,7 +432,7 @@ void prefill_kernel(PrefillArgs a) {
           sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qop[cb][kb], sc[cb][u], 0, 0, 0);
           if constexpr (ROTQ) sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qlo[cb][kb], sc[cb][u], 0, 0, 0);
         }
-        if constexpr (KIVI && !TAILT) {
+        if constexpr (PL::PLANES && !TAILT) {
           const h8 kl = *reinterpret_cast<const h8*>(buf + off + PL::KPLANE);
 #pragma unroll
           for (int cb = 0; cb < NQB; ++cb)
@@ -460,7 +477,7 @@ void prefill_kernel(PrefillArgs a) {
     f4 fk4[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      if constexpr (KIVI) fk4[u] = f4{a.qscale, a.qscale, a.qscale, a.qscale};
+      if constexpr (PL::PLANES) fk4[u] = f4{a.qscale, a.qscale, a.qscale, a.qscale};
       else fk4[u] = *reinterpret_cast<const f4*>(fk + 16 * u + 4 * j);
     }
     float p[NQB][2][4];

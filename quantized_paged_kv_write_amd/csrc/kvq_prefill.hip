@@ -16,6 +16,7 @@ hipError_t launch_prefill(const kvq_cache& c, const PrefillArgs& a, hipStream_t 
     case KVQ_FP8_E4M3FN: return prefill_keys_fp8(c.v_dtype, c.head_dim, rot, a, s);
     case KVQ_INT4_KIVI: return prefill_keys_kivi(c.v_dtype, c.head_dim, rot, a, s);
     case KVQ_FP8_E5M2: return prefill_keys_e5m2(c.v_dtype, c.head_dim, rot, a, s);
+    case KVQ_INT4_G32: return prefill_keys_int4(c.v_dtype, c.head_dim, rot, a, s);
   }
   return hipErrorInvalidValue;
 }

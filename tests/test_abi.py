@@ -70,7 +70,7 @@ def test_write_argument_errors():
     assert _write(_cache(k_dtype=4, block_size=16, max_seqs=2)) == SHAPE  # KIVI needs 32-token pages
     assert _write(_cache(k_dtype=4, block_size=32, max_seqs=0)) == SHAPE
     assert _write(_cache(k_dtype=4, block_size=32, max_seqs=2)) == INVALID  # zeros / tails missing
-    assert _write(_cache(k_dtype=3)) == UNSUPPORTED  # INT4 group-32 keys not offered
+    assert _write(_cache(k_dtype=3), T=0) == OK  # INT4 group-32 keys (no-op call)
     assert _write(_cache(), T=-1) == INVALID
     assert _write(_cache(), T=0) == OK  # no-op
     assert L.kvq_write(ctypes.byref(_cache()), None, FAKE, FAKE, None, 4, None) == INVALID
@@ -91,7 +91,7 @@ def test_write_static_argument_errors():
     assert _write_static(_cache(), vs=None) == INVALID
     kc = _cache(k_dtype=4, block_size=32, max_seqs=2, k_zeros=FAKE, k_tail=FAKE, v_tail=FAKE)
     assert _write_static(kc) == UNSUPPORTED  # KIVI keys take no calibrated scale
-    assert _write_static(_cache(k_dtype=3)) == UNSUPPORTED
+    assert _write_static(_cache(k_dtype=3), T=0) == OK  # INT4 group-32 keys take a calibrated scale
     assert _write_static(_cache(v_dtype=9)) == INVALID
     assert _write_static(_cache(), T=-1) == INVALID
     assert _write_static(_cache(k_dtype=2, v_dtype=3), T=0) == OK  # no-op
@@ -140,6 +140,16 @@ def test_decode_argument_errors():
     assert dec(q=None) == INVALID
     assert dec(batch=0) == OK            # empty batch: nothing to do
     assert dec(mb=0) == INVALID
+    c = _cache(k_dtype=3)
+    assert dec(batch=0) == OK            # INT4 group-32 keys decode
+
+
+def test_prefill_accepts_int4_group32_keys():
+    # an empty chunk batch over INT4 group-32 keys passes every check
+    c = _cache(k_dtype=3)
+    rc = kvq.lib().kvq_prefill_attn(ctypes.byref(c), FAKE, FAKE, FAKE, 4, FAKE, 0, 0, 4, 4, 0.1, FAKE, FAKE,
+                                    1 << 30, None)
+    assert rc == OK
 
 
 @pytest.mark.skipif(kvq.binding.torch.cuda.device_count() > 0, reason="only meaningful without a GPU")

@@ -13,7 +13,8 @@ DEV = "cuda"
 
 COMBOS = [("int8", "int8"), ("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("fp8_e4m3fn", "int4_g32"),
           ("int8", "fp8_e4m3fn"), ("int4_kivi", "int4_g32"), ("int4_kivi", "int8"), ("int4_kivi", "fp8_e4m3fn"),
-          ("fp8_e5m2", "fp8_e5m2"), ("fp8_e5m2", "int4_g32"), ("int8", "fp8_e5m2"), ("int4_kivi", "fp8_e5m2")]
+          ("fp8_e5m2", "fp8_e5m2"), ("fp8_e5m2", "int4_g32"), ("int8", "fp8_e5m2"), ("int4_kivi", "fp8_e5m2"),
+          ("int4_g32", "int4_g32"), ("int4_g32", "fp8_e4m3fn"), ("int4_g32", "int8")]
 RAGGED = [0, 1, 15, 16, 17, 31, 32, 33, 100, 257]
 
 
@@ -54,7 +55,8 @@ def test_decode_gqa_group_sizes(G):
 
 
 @pytest.mark.parametrize("H,G", [(8, 4), (4, 4), (8, 8), (8, 2), (8, 1), (6, 2), (4, 16)])
-@pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("int4_kivi", "int4_g32")])
+@pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("int4_kivi", "int4_g32"),
+                                   ("int4_g32", "int4_g32")])
 def test_decode_head_groups(H, G, kf, vf):
     # a wave reads HP = 4, 2 or 1 KV heads (the most with HP G <= 16 and
     # H % HP == 0): (token, head) tile rows, head-matched score columns; for
@@ -147,7 +149,7 @@ def test_decode_full_size_sampled(name):
     assert worst <= ATOL, worst
 
 
-@pytest.mark.parametrize("kf", ["int8", "fp8_e4m3fn", "fp8_e5m2", "int4_kivi"])
+@pytest.mark.parametrize("kf", ["int8", "fp8_e4m3fn", "fp8_e5m2", "int4_kivi", "int4_g32"])
 @pytest.mark.parametrize("qmode", ["sharp_positive", "flat"])
 def test_decode_query_scales(kf, qmode):
     """Queries far from N(0,1): all-positive and 8x larger (a sharp softmax,

@@ -16,7 +16,7 @@ DEV = "cuda"
 
 COMBOS = [("int8", "int8"), ("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("fp8_e4m3fn", "int4_g32"),
           ("int4_kivi", "int4_g32"), ("int4_kivi", "int8"), ("int4_kivi", "fp8_e5m2"), ("fp8_e5m2", "fp8_e5m2"),
-          ("int8", "fp8_e5m2")]
+          ("int8", "fp8_e5m2"), ("int4_g32", "int4_g32"), ("int4_g32", "fp8_e4m3fn")]
 # context lengths and chunk lengths: an empty context, one token, chunks
 # shorter than, equal to and longer than the context, ragged pages
 CTX = [0, 1, 33, 100, 257, 70, 64]
@@ -75,7 +75,7 @@ def test_prefill_block_sizes(bs):
 
 
 @pytest.mark.parametrize("kf,vf", [("int8", "int4_g32"), ("fp8_e4m3fn", "fp8_e5m2"), ("int4_kivi", "int4_g32"),
-                                   ("int8", "int8")])
+                                   ("int8", "int8"), ("int4_g32", "int8")])
 def test_prefill_rotated(kf, vf):
     s = sign_bits(128, 5)
     rk = None if kf == "int4_kivi" else s

@@ -30,7 +30,7 @@ def _setup(kf, vf, D, ctx, rk, rv, H=2, G=4, seed=0):
 
 @pytest.mark.parametrize("kf,vf,rk,rv", [("int8", "int4_g32", True, True), ("fp8_e4m3fn", "fp8_e4m3fn", True, False),
                                          ("fp8_e5m2", "int8", False, True), ("int4_kivi", "int4_g32", False, True),
-                                         ("int8", "fp8_e5m2", True, True)])
+                                         ("int8", "fp8_e5m2", True, True), ("int4_g32", "int4_g32", True, True)])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_rotated_write_and_decode(kf, vf, rk, rv, D):
     inp, dev, orc = _setup(kf, vf, D, RAGGED, rk, rv, seed=D + (3 if rk else 0) + (5 if rv else 0))

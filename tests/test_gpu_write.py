@@ -14,7 +14,8 @@ DEV = "cuda"
 
 COMBOS = [("int8", "int8"), ("fp8_e4m3fn", "fp8_e4m3fn"), ("int8", "int4_g32"), ("fp8_e4m3fn", "int4_g32"),
           ("int8", "fp8_e4m3fn"), ("int4_kivi", "int4_g32"), ("int4_kivi", "int8"), ("int4_kivi", "fp8_e4m3fn"),
-          ("fp8_e5m2", "fp8_e5m2"), ("fp8_e5m2", "int4_g32"), ("int8", "fp8_e5m2"), ("int4_kivi", "fp8_e5m2")]
+          ("fp8_e5m2", "fp8_e5m2"), ("fp8_e5m2", "int4_g32"), ("int8", "fp8_e5m2"), ("int4_kivi", "fp8_e5m2"),
+          ("int4_g32", "int4_g32"), ("int4_g32", "fp8_e4m3fn"), ("int4_g32", "int8")]
 
 
 def _small(kf, vf, D, bs, ctx, H=2, G=2, seed=0, outliers=2, sinks=2):
@@ -76,7 +77,7 @@ def _edge_rows(D, rng):
 
 
 @pytest.mark.parametrize("kf,vf", [("int8", "int4_g32"), ("fp8_e4m3fn", "int8"), ("int8", "fp8_e4m3fn"),
-                                   ("fp8_e5m2", "int8"), ("int8", "fp8_e5m2")])
+                                   ("fp8_e5m2", "int8"), ("int8", "fp8_e5m2"), ("int4_g32", "int8")])
 def test_write_edge_values(kf, vf):
     D, H, bs = 128, 2, 16
     rng = np.random.default_rng(3)
@@ -247,7 +248,7 @@ def test_write_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("kf,vf", [("int8", "int8"), ("fp8_e4m3fn", "fp8_e4m3fn"), ("fp8_e5m2", "int4_g32"),
-                                   ("int8", "fp8_e5m2")])
+                                   ("int8", "fp8_e5m2"), ("int4_g32", "int4_g32")])
 @pytest.mark.parametrize("D", [64, 128])
 def test_write_static_scales(kf, vf, D):
     """kvq_write_static: calibrated per-head scales at half the median
@@ -277,7 +278,7 @@ def test_write_static_scales(kf, vf, D):
     assert decode_error(got, ref)[0] <= 2e-3
 
 
-@pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "fp8_e5m2"), ("int8", "int4_g32")])
+@pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "fp8_e5m2"), ("int8", "int4_g32"), ("int4_g32", "fp8_e4m3fn")])
 def test_write_static_every_fp16_pattern(kf, vf):
     """With a calibrated scale of 1 every quotient is the fp16 input itself,
     so writing all finite fp16 bit patterns checks the hardware encoders
