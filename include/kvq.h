@@ -154,7 +154,7 @@ typedef struct kvq_cache {
 /* kvq_cache.flags.  Walsh-Hadamard rotation ([P3] Numerical Formats: QuaRot's
  * randomized orthogonal Walsh-Hadamard transforms spread outlier channels
  * before 4-bit quantization; Accuracy, Latency, and Serving Economics: INT4
- * with Hadamard rotations keeps baseline quality).  A rotated tensor stores,
+ * after rotation stays close to unquantized quality).  A rotated tensor stores,
  * for each (token, head) row x, the row y = H (sigma * x) -- H the Sylvester
  * Hadamard matrix of order head_dim (entries +-1), sigma the signs of
  * rot_signs -- with every entry computed exactly and rounded once to fp32,

@@ -331,7 +331,7 @@ def kivi_dequant(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndar
 # Walsh-Hadamard rotation ([P3] "Numerical Formats": QuaRot applies randomized
 # orthogonal Walsh-Hadamard transforms that spread outlier peaks over all
 # channels before uniform 4-bit quantization; "Accuracy, Latency, and
-# Serving Economics": INT4 with Hadamard rotations keeps baseline quality).
+# Serving Economics": rotated INT4 stays close to unquantized quality).
 # Reading: the rotation of a head_dim row x is R x with R = H diag(sigma) /
 # sqrt(D), H the Sylvester Hadamard matrix (entries +-1) and sigma a vector
 # of random signs drawn by the caller ("randomized").  The cache stores the
