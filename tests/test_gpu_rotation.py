@@ -111,3 +111,16 @@ def test_rotation_improves_per_token_key_quality():
             err = max(err, float(np.sqrt(np.mean((got[b] - ref) ** 2))))
         errs[rk] = err
     assert errs[True] < 0.6 * errs[False], errs
+
+
+def test_rotated_values_in_a_large_kivi_call():
+    # a call of more than 2048 tokens: the value pass and the seal share one
+    # launch and the tail rows (unrotated) follow; rotated values bit-exact
+    ctx = [1500, 700, 95]
+    inp, dev, orc = _setup("int4_kivi", "int4_g32", 128, ctx, False, True, seed=77)
+    assert sum(ctx) > 2048
+    torch.cuda.synchronize()
+    assert compare_buffers(dev, orc) == {}
+    got, ref = decode_both(inp, dev, orc, DEV)
+    err, err16 = decode_error(got, ref)
+    assert err <= ATOL, (err, err16)
