@@ -65,7 +65,12 @@ struct PLayout {
   static constexpr int KPLANE = TILE * KRB;
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = (PLANES ? 2 : 1) * KPLANE;
-  static constexpr int OFF_FK = OFF_V + TILE * VS::RB;
+  // 8-bit values at head dims up to 128 are staged as their exact bf16
+  // operands (converted once per workgroup when stored, read with the 16-bit
+  // transpose read), 2 D bytes per token row; otherwise the codes themselves
+  static constexpr bool V16 = FV != F_INT4 && D <= 128;
+  static constexpr int VRB = V16 ? 2 * D : VS::RB;  // value row bytes in LDS
+  static constexpr int OFF_FK = OFF_V + TILE * VRB;
   static constexpr int OFF_FV = OFF_FK + 4 * TILE;
   static constexpr int BUF = (OFF_FV + 4 * TILE * VS::NG + 15) / 16 * 16;
   static constexpr int NBUF = 3;  // tiles x (softmax, P V), x + 1 (scores), x + 2 (being stored)
@@ -128,6 +133,17 @@ __device__ __forceinline__ b8 value_operand_biased(i2 t) {
     return __builtin_bit_cast(b8, r);
   }
 }
+
+// bf16-staged value rows: 32-byte block m of token row t is stored at block
+// m ^ (t mod NB), NB = min(D / 16, 8), so the 16 token rows one transpose
+// read touches spread over the LDS banks.
+template <int D>
+__device__ __forceinline__ int v16swz(int row) {
+  constexpr int NB = D / 16 < 8 ? D / 16 : 8;
+  return row & (NB - 1);
+}
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4v lds_s4v;
 
 // fp16 pair -> bf16 hi (truncated) and lo = x - hi; both exact (an fp16
 // value has 11 significant bits, hi keeps 8)
@@ -299,7 +315,7 @@ void prefill_kernel(PrefillArgs a) {
       const int p = tid + PL::THREADS * i;
       if (PL::NV % PL::THREADS == 0 || p < PL::NV) {
         const int row = p / VS::CH;
-        const int col = (p % VS::CH) ^ vswz<VS::CH>(row);
+        const int col = PL::V16 ? p % VS::CH : (p % VS::CH) ^ vswz<VS::CH>(row);
         const uint32_t fr = (uint32_t)__shfl((int)flat, row);
         r.v[i] = *reinterpret_cast<const u4*>(a.v_codes + (size_t)fr * VS::RB + col * 16);
       }
@@ -384,7 +400,32 @@ void prefill_kernel(PrefillArgs a) {
         const bool lv = (live >> (p / VS::CH)) & 1u;
         u4 v = lv ? r.v[i] : u4{0u, 0u, 0u, 0u};
         if constexpr (FV == F_INT8) v ^= 0x80808080u;  // codes c + 128 (unsigned), see value_operand_biased
-        reinterpret_cast<u4*>(buf + PL::OFF_V)[p] = v;
+        if constexpr (PL::V16) {
+          // 16 codes of token row p / CH, channels 16 (p % CH) ..: their bf16
+          // operands (value_operand_8bit's values, in channel order) into
+          // the row's 32-byte block (p % CH) ^ v16swz<D>(row)
+          const int row = p / VS::CH, col = p % VS::CH;
+          const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
+          uint32_t bw[8];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            if constexpr (FV == F_INT8) {
+              bw[2 * w] = __builtin_amdgcn_perm(0u, cw[w], 0x0C010C00u);
+              bw[2 * w + 1] = __builtin_amdgcn_perm(0u, cw[w], 0x0C030C02u);
+            } else if constexpr (FV == F_FP8) {
+              bw[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[w], 1.0f, false));
+              bw[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[w], 1.0f, true));
+            } else {
+              bw[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(cw[w], 1.0f, false));
+              bw[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(cw[w], 1.0f, true));
+            }
+          }
+          u4* dst = reinterpret_cast<u4*>(buf + PL::OFF_V + row * PL::VRB + ((col ^ v16swz<D>(row)) << 5));
+          dst[0] = u4{bw[0], bw[1], bw[2], bw[3]};
+          dst[1] = u4{bw[4], bw[5], bw[6], bw[7]};
+        } else {
+          reinterpret_cast<u4*>(buf + PL::OFF_V)[p] = v;
+        }
       }
     }
     if (wv == 0) {
@@ -407,7 +448,12 @@ void prefill_kernel(PrefillArgs a) {
   };
 
   // Value transpose reads (as in decode): lane (j, i) points at row T_j[i / 2]
-  // of the value tile, byte 8 (i % 2) of the chunk.
+  // of the value tile, byte 8 (i % 2) of the chunk.  bf16-staged values
+  // (V16): lane (j, n) of the 16-bit transpose read points at token row
+  // 4 j + n / 4 (tokens 16 + 4 j + n / 4 for the second read), channels
+  // 16 m + 4 (n % 4) ..: the read hands lane n of each 16-lane group element
+  // n % 4 of the rows of lanes n / 4, n / 4 + 4, + 8, + 12, i.e. channel
+  // 16 m + n of tokens T_j[0..3] (then T_j[4..7]).
   const int trow = 16 * ((n >> 1) >> 2) + 4 * j + ((n >> 1) & 3);
   const int tbase = PL::OFF_V + trow * VS::RB + 8 * (n & 1);
   const int tswz = vswz<VS::CH>(trow);
@@ -608,8 +654,18 @@ void prefill_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int m = 0; m < VS::NPV; ++m) {
-        const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(buf + tbase + ((m ^ tswz) << 4)));
-        const b8 vop = value_operand_biased<FV>(raw);
+        b8 vop;
+        if constexpr (PL::V16) {
+          const int ta = 4 * j + (n >> 2);  // token row of the first read; the second reads ta + 16
+          const int off = PL::OFF_V + ta * PL::VRB + ((m ^ v16swz<D>(ta)) << 5) + 8 * (n & 3);
+          const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(buf + off));
+          const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(buf + off + 16 * PL::VRB));
+          const u2 w0 = __builtin_bit_cast(u2, lo), w1 = __builtin_bit_cast(u2, hi);
+          vop = __builtin_bit_cast(b8, u4{w0.x, w0.y, w1.x, w1.y});
+        } else {
+          const i2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(buf + tbase + ((m ^ tswz) << 4)));
+          vop = value_operand_biased<FV>(raw);
+        }
 #pragma unroll
         for (int cb = 0; cb < NQB; ++cb) {
           acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph[cb], acc[cb][m], 0, 0, 0);
