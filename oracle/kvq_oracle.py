@@ -292,10 +292,10 @@ def unpack_int4(packed: np.ndarray, signed: bool) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# KIVI-style keys ([P2] section 5 "K is more sensitive than V": per-channel
-# quantization for K, per-token for V; [P3] "Numerical Formats": KIVI applies
-# per-channel quantization to keys; [P4]: asymmetric quantization maps the
-# observed min and max onto the full integer range).
+# KIVI-style keys ([P2] section 5 "K is more sensitive than V": keys are
+# quantized channel by channel, values token by token; [P3] "Numerical
+# Formats": KIVI's keys are quantized per channel; [P4]: the asymmetric
+# scheme stretches the observed [min, max] over the whole integer range).
 # One group = 32 consecutive tokens of one head; per channel:
 #   s = (max - min) / 15 (fp32, stored fp16),  z = min (stored fp16, exact),
 #   code = clip(round((x - z) / s), 0, 15),     x_hat = code * s + z.
@@ -328,9 +328,9 @@ def kivi_dequant(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndar
 
 
 # --------------------------------------------------------------------------
-# Walsh-Hadamard rotation ([P3] "Numerical Formats": QuaRot applies randomized
-# orthogonal Walsh-Hadamard transforms that spread outlier peaks over all
-# channels before uniform 4-bit quantization; "Accuracy, Latency, and
+# Walsh-Hadamard rotation ([P3] "Numerical Formats": QuaRot rotates rows with
+# randomized orthogonal Walsh-Hadamard transforms, so an outlier channel's
+# energy is shared by every channel before the 4-bit quantizer; "Accuracy, Latency, and
 # Serving Economics": rotated INT4 stays close to unquantized quality).
 # Reading: the rotation of a head_dim row x is R x with R = H diag(sigma) /
 # sqrt(D), H the Sylvester Hadamard matrix (entries +-1) and sigma a vector
