@@ -74,6 +74,11 @@ WORKLOADS = {
 # (per-token INT8 keys with channel outliers are where the rotation helps).
 WORKLOADS["llama3_70b_int8_rot"] = WORKLOADS["llama3_70b_int8"].with_(name="llama3_70b_int8_rot", rotate_k=True,
                                                                        rotate_v=True, base="llama3_70b_int8")
+# The KIVI layer's shape with symmetric INT4 group-32 keys and values, both
+# Walsh-Hadamard rotated (the 4-bit alternative to per-channel keys).
+WORKLOADS["llama3_8b_int4_rot"] = WORKLOADS["llama3_8b_kivi_int4"].with_(
+    name="llama3_8b_int4_rot", block_size=16, k_dtype="int4_g32", rotate_k=True, rotate_v=True,
+    base="llama3_8b_kivi_int4")
 ORDER = ["tiny_int8", "llama3_8b_fp8", "llama3_8b_int8k_int4v", "llama3_70b_int8", "llama3_8b_kivi_int4",
          "llama3_8b_e5m2", "llama3_70b_int8_rot"]
 
