@@ -127,18 +127,18 @@ __device__ __forceinline__ double swz_xor(double v) {
   return __hiloint2double(hi, lo);
 }
 
-// Walsh-Hadamard transform y = H (sigma * x) of one row spread over LPR
-// consecutive lanes (aligned, LPR <= 32), 8 channels per lane: lane l of the
-// row holds channels 8 l .. 8 l + 7.  H is the Sylvester matrix: for each
-// index bit, the pair (i, i + 2^k) with bit k of i clear becomes (x_i + x_j,
-// x_i - x_j).  Bits 0-2 of the channel are inside the lane, bits 3.. are the
-// lane bits.  Every partial sum is a sum of at most 256 fp16 values, exact in
-// float64, so the result is the exact transform; sbits: the lane's 8 sign
-// bits (bit j set negates channel 8 l + j).
+// Walsh-Hadamard transform y = H x of one row spread over LPR consecutive
+// lanes (aligned, LPR <= 32), 8 channels per lane: lane l of the row holds
+// channels 8 l .. 8 l + 7 (fp16 values, the caller has applied the random
+// signs).  H is the Sylvester matrix: for each index bit, the pair
+// (i, i + 2^k) with bit k of i clear becomes (x_i + x_j, x_i - x_j).  Bits
+// 0-2 of the channel are inside the lane, bits 3.. are the lane bits.  Every
+// partial sum is a sum of at most 256 fp16 values, exact in float64, so the
+// result is the exact transform.
 template <int LPR>
-__device__ __forceinline__ void fwht_row8(const float (&x)[8], uint32_t sbits, int lir, double (&y)[8]) {
+__device__ __forceinline__ void fwht_row8(const float (&x)[8], int lir, double (&y)[8]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) y[j] = (double)((sbits >> j) & 1 ? -x[j] : x[j]);
+  for (int j = 0; j < 8; ++j) y[j] = (double)x[j];
 #pragma unroll
   for (int s = 1; s < 8; s <<= 1) {
 #pragma unroll
