@@ -92,7 +92,7 @@ def test_rotated_extreme_rows():
 
 
 def test_rotation_improves_per_token_key_quality():
-    # The point of the rotation: keys with channel-consistent outliers (x20)
+    # The point of the rotation: keys whose outliers sit in the same few channels (x20)
     # quantized per token lose the small channels; rotated first, the
     # outliers spread over all channels.  The error of the decode output
     # against unquantized attention drops (about 2.4x on these inputs in the
