@@ -235,15 +235,15 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* _
   }
 }
 
-// grid.y: 0 = keys, 1 = values (keys are skipped for KIVI: grid.y = 1 and
-// tensor0 = 1).
-template <int FK, int FV, int D, int ITER, bool ROTK, bool ROTV>
-__global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, int tensor0) {
-  const int tensor = (int)blockIdx.y + tensor0;
-  if (tensor == 0) {
-    if constexpr (FK != F_KIVI) write_rows<FK, D, ITER, false, ROTK>(a, a.k, a.k_codes, a.k_scales, a.k_static, blockIdx.x);
+// Workgroups [0, nk) write key rows (IK per lane), the rest value rows (IV
+// per lane); nk = 0 for KIVI keys, which the seal writes.
+template <int FK, int FV, int D, int IK, int IV, bool ROTK, bool ROTV>
+__global__ __launch_bounds__(256) void write_sym_kernel(WriteArgs a, uint32_t nk) {
+  const uint32_t b = blockIdx.x;
+  if (b < nk) {
+    if constexpr (FK != F_KIVI) write_rows<FK, D, IK, false, ROTK>(a, a.k, a.k_codes, a.k_scales, a.k_static, b);
   } else {
-    write_rows<FV, D, ITER, FK == F_KIVI, ROTV>(a, a.v, a.v_codes, a.v_scales, a.v_static, blockIdx.x);
+    write_rows<FV, D, IV, FK == F_KIVI, ROTV>(a, a.v, a.v_codes, a.v_scales, a.v_static, b - nk);
   }
 }
 
@@ -496,36 +496,39 @@ __global__ __launch_bounds__(256) void kivi_tail_kernel(WriteArgs a) {
 
 namespace {
 
-// Rows per lane of write_sym_kernel.  Measured in one process (prefill
-// writes of the large workloads): one row per lane, i.e. more and shorter
-// workgroups, 5.45 -> 5.88 TB/s for the symmetric formats against 4 rows
-// per lane; the KIVI value pass is fastest at 2 (with its tail lookups, and
-// in the combined launch of large calls without them).  Rotated rows are
-// bound by the issue of the transform's vector instructions, and two rows
-// per lane share the lane's sign masks and butterfly constants: 7% faster
-// than one (2.76-3.24 GB writes; four rows: no further change).
-template <int FK, bool ROT>
-constexpr int rows_per_lane() { return FK == F_KIVI || ROT ? 2 : 1; }
+// Rows per lane of a tensor's rows in write_sym_kernel.  Measured in one
+// process (prefill writes of the large workloads): one row per lane, i.e.
+// more and shorter workgroups, 5.45 -> 5.88 TB/s for the 8-bit formats
+// against 4 rows per lane, and 2-3% faster than 2; INT4 group-32 rows (four
+// group maxima and scales per row) 3% faster at 2 than at 1; the KIVI value
+// pass is fastest at 2 (with its tail lookups, and in the combined launch of
+// large calls without them).  Rotated rows are bound by the issue of the
+// transform's vector instructions, and two rows per lane share the lane's
+// sign masks and butterfly constants: 7% faster than one (2.76-3.24 GB
+// writes; four rows: no further change).
+template <int FMT, bool ROT, bool KIVI_V>
+constexpr int rows_per_lane() { return FMT == F_INT4 || ROT || KIVI_V ? 2 : 1; }
+
+template <int FK, int FV, int D, bool ROTK, bool ROTV>
+hipError_t launch_sym_rot(const WriteArgs& a, hipStream_t s) {
+  constexpr int IK = rows_per_lane<FK, ROTK, false>(), IV = rows_per_lane<FV, ROTV, FK == F_KIVI>();
+  constexpr int RPP = 256 / (D / 8);
+  const int64_t rows = a.T * a.H;
+  const int64_t nk = FK == F_KIVI ? 0 : (rows + RPP * IK - 1) / (RPP * IK);
+  const int64_t all = nk + (rows + RPP * IV - 1) / (RPP * IV);
+  if (all >= (1ll << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, IK, IV, ROTK, ROTV>), dim3((unsigned)all), dim3(256), 0, s, a,
+                     (uint32_t)nk);
+  return hipGetLastError();
+}
 
 template <int FK, int FV, int D>
 hipError_t launch_sym(const WriteArgs& a, hipStream_t s) {
-  const bool rot = a.rot_k || a.rot_v;
-  constexpr int kIter = rows_per_lane<FK, false>(), kIterR = rows_per_lane<FK, true>();
-  constexpr int RPP = 256 / (D / 8);
-  const int64_t rows = a.T * a.H;
-  const int64_t blocks = (rows + RPP * (rot ? kIterR : kIter) - 1) / (RPP * (rot ? kIterR : kIter));
-  const int tensors = FK == F_KIVI ? 1 : 2;
-  const int tensor0 = FK == F_KIVI ? 1 : 0;
-  const dim3 grid((unsigned)blocks, tensors);
-  if (a.rot_k && a.rot_v)
-    hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIterR, FK != F_KIVI, true>), grid, dim3(256), 0, s, a, tensor0);
-  else if (a.rot_k)
-    hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIterR, FK != F_KIVI, false>), grid, dim3(256), 0, s, a, tensor0);
-  else if (a.rot_v)
-    hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIterR, false, true>), grid, dim3(256), 0, s, a, tensor0);
-  else
-    hipLaunchKernelGGL((write_sym_kernel<FK, FV, D, kIter, false, false>), grid, dim3(256), 0, s, a, tensor0);
-  return hipGetLastError();
+  constexpr bool RK = FK != F_KIVI;  // KIVI keys are never rotated
+  if (a.rot_k && a.rot_v) return launch_sym_rot<FK, FV, D, RK, true>(a, s);
+  if (a.rot_k) return launch_sym_rot<FK, FV, D, RK, false>(a, s);
+  if (a.rot_v) return launch_sym_rot<FK, FV, D, false, true>(a, s);
+  return launch_sym_rot<FK, FV, D, false, false>(a, s);
 }
 
 template <int FK, int FV, int D>
@@ -539,7 +542,7 @@ hipError_t launch_all(const WriteArgs& a, hipStream_t s) {
     const int64_t wgs = chunks * (a.H / nw);
     if (a.seal_chunk > 1) {
       // large call: value pass and seal in one launch, then the tail rows
-      constexpr int kIter = rows_per_lane<FK, false>();
+      constexpr int kIter = rows_per_lane<FV, false, true>();
       constexpr int RPP = 256 / (D / 8);
       const int64_t vwgs = (a.T * a.H + RPP * kIter - 1) / (RPP * kIter);
       const int64_t all = wgs + vwgs;
