@@ -417,7 +417,7 @@ def _make_seq_cache(kf, vf, L, bs, H, D, table, seed=0, seqs=1):
 
 
 @pytest.mark.parametrize("kf,vf", [(o.INT8, o.INT8), (o.FP8_E4M3FN, o.FP8_E4M3FN), (o.FP8_E5M2, o.FP8_E5M2),
-                                   (o.INT8, o.INT4_G32),
+                                   (o.INT8, o.INT4_G32), (o.INT4_G32, o.INT4_G32), (o.INT4_G32, o.FP8_E4M3FN),
                                    (o.INT4_KIVI, o.INT4_G32)])
 def test_paged_gather_equals_direct_quantization(kf, vf):
     # Writing through a shuffled block table and reading back through it gives
@@ -588,6 +588,35 @@ def test_static_write_layout():
     assert np.array_equal(c.k_codes[blk[m], off[m]].view(np.int8), codes)
     skipped = np.setdiff1d(np.arange(4 * bs), slots[m])
     assert np.all(c.k_codes[skipped // bs, skipped % bs] == 0)
+
+
+def test_static_write_int4_group32_keys():
+    # INT4 group-32 keys with calibrated per-head scales: every group slot of
+    # a written row holds its head's scale, and the read-back keys obey the
+    # symmetric-quantizer bounds: |x - x_hat| <= s/2 where |x|/s <= 7, and
+    # x_hat = +-7 s (the sign of x) beyond.
+    rng = np.random.default_rng(43)
+    H, D, bs, n = 2, 64, 16, 30
+    k16 = (rng.standard_normal((n, H, D)) * 0.3).astype(np.float16)
+    v16 = rng.standard_normal((n, H, D)).astype(np.float16)
+    slots = rng.permutation(3 * bs)[:n].astype(np.int64)
+    ks = np.array([0.05, 0.02], np.float16)  # head 1 saturates often
+    vs = np.array([0.02, 0.03], np.float16)
+    c = o.OracleCache(3, bs, H, D, o.INT4_G32, o.INT8)
+    o.write_static(c, k16, v16, slots, ks, vs)
+    blk, off = slots // bs, slots % bs
+    assert c.k_scales.shape[-1] == D // 32
+    assert np.all(c.k_scales[blk, off].view(np.uint16) == ks.view(np.uint16)[None, :, None])
+    for i in range(n):
+        for h in range(H):
+            x = k16[i, h].astype(np.float64)
+            s_ = float(ks[h])
+            xh = o.dequant_sym(o.unpack_int4(c.k_codes[blk[i], off[i], h], signed=True),
+                               c.k_scales[blk[i], off[i], h], o.INT4_G32)
+            inside = np.abs(x) / s_ <= 7
+            assert np.all(np.abs(x - xh)[inside] <= s_ / 2 * (1 + 2.0 ** -20))
+            assert np.array_equal(xh[~inside], 7 * s_ * np.sign(x[~inside]))
+    assert (np.abs(k16[:, 1].astype(np.float64)) / float(ks[1]) > 7).any()
 
 
 # --------------------------------------------------------------------------
