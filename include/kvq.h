@@ -179,7 +179,9 @@ typedef enum kvq_cache_flags {
  * order and consecutively (as a prefill chunk or one token per decode step
  * does); a page is quantized when the call holds its last row, taking its
  * earlier rows from this call or from the tail written by earlier calls.
- * num_tokens == 0 is a no-op. */
+ * num_tokens == 0 is a no-op; num_tokens * n_kv_heads must be below 2^31
+ * (else KVQ_ERR_SHAPE).  Calls beyond 2^24 (token, head) rows are run as
+ * consecutive launches over token ranges, with the same result as one. */
 int kvq_write(const kvq_cache* cache, const void* k, const void* v,
               const int64_t* slot_mapping, const int32_t* seq_idx,
               int64_t num_tokens, void* stream);

@@ -3,6 +3,7 @@
 // call synchronizes.
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -152,13 +153,30 @@ int write_impl(const kvq_cache* cache, const void* k, const void* v, const int64
   a.k_tail = static_cast<uint16_t*>(cache->k_tail);
   a.v_tail = static_cast<uint16_t*>(cache->v_tail);
   a.max_seqs = cache->max_seqs;
-  // KIVI seal waves: one per call token for small calls (decode steps), one
-  // per 32 tokens otherwise
-  a.seal_chunk = num_tokens <= 2048 ? 1 : 32;
   a.rot_k = (cache->flags & KVQ_ROTATE_K) ? 1 : 0;
   a.rot_v = (cache->flags & KVQ_ROTATE_V) ? 1 : 0;
   for (int i = 0; i < 8; ++i) a.rot_signs[i] = cache->rot_signs[i];
-  return launch_write(*cache, a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+  // One launch takes at most 2^24 (token, head) rows, so that its grid stays
+  // far below the 2^32 work-items of a dispatch.  Larger calls run as
+  // consecutive calls on the same stream over consecutive token ranges:
+  // tokens are independent, and a KIVI page split between two ranges is
+  // completed by the second from the tail the first wrote, as across calls.
+  const int64_t rows_per_launch = 1ll << 24;
+  const int64_t step = std::max<int64_t>(1, rows_per_launch / cache->n_kv_heads);
+  const size_t row_elems = (size_t)cache->n_kv_heads * cache->head_dim;
+  for (int64_t t0 = 0; t0 < num_tokens; t0 += step) {
+    const int64_t n = std::min(step, num_tokens - t0);
+    a.k = static_cast<const uint16_t*>(k) + (size_t)t0 * row_elems;
+    a.v = static_cast<const uint16_t*>(v) + (size_t)t0 * row_elems;
+    a.slots = slot_mapping + t0;
+    a.seq_idx = seq_idx ? seq_idx + t0 : nullptr;
+    a.T = n;
+    // KIVI seal waves: one per call token for small calls (decode steps),
+    // one per 32 tokens otherwise
+    a.seal_chunk = n <= 2048 ? 1 : 32;
+    if (launch_write(*cache, a, static_cast<hipStream_t>(stream)) != hipSuccess) return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
 }
 
 }  // namespace

@@ -201,6 +201,55 @@ def test_write_kivi_large_calls():
     assert compare_buffers(dev, orc) == {}
 
 
+@pytest.mark.parametrize("kf,vf", [("fp8_e4m3fn", "int4_g32"), ("int4_kivi", "int8")])
+def test_write_call_beyond_one_launch(kf, vf):
+    # A call of more than 2^24 (token, head) rows runs as launches over
+    # consecutive token ranges.  With 6 heads the first range ends inside a
+    # 32-token page, so that KIVI page is completed by the second launch from
+    # the tail the first wrote.  Every row near the range end, sampled rows
+    # elsewhere, the KIVI pages around the range end and the open tail are
+    # checked against the oracle.
+    import quantized_paged_kv_write_amd as kvq
+    H, D = 6, 64
+    step = (1 << 24) // H
+    T = step + 1017
+    assert T * H > (1 << 24) and step % 32 != 0
+    bs = 32 if kf == "int4_kivi" else 16
+    g = torch.Generator(device=DEV).manual_seed(5)
+    k = torch.randn((T, H, D), generator=g, device=DEV, dtype=torch.float16)
+    v = torch.randn((T, H, D), generator=g, device=DEV, dtype=torch.float16)
+    slots = torch.arange(T, dtype=torch.int64, device=DEV)
+    seq = torch.zeros(T, dtype=torch.int32, device=DEV)
+    cache = kvq.PagedKVCache((T + bs - 1) // bs, bs, H, D, kf, vf, max_seqs=1, device=DEV)
+    kvq.write(cache, k, v, slots, seq)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    toks = np.unique(np.concatenate([np.arange(step - 70, step + 70), rng.integers(0, T, 2000), [0, T - 1]]))
+    tt = torch.from_numpy(toks).to(DEV)
+    blk, off = tt // bs, tt % bs
+    checks = [("v", v, vf)] + ([] if kf == "int4_kivi" else [("k", k, kf)])
+    for name, x, fmt in checks:
+        codes, s16 = o.quantize_sym(to_np16(x[tt]), fmt)
+        stored = o.pack_int4(codes) if fmt == "int4_g32" else codes.view(np.uint8)
+        assert np.array_equal(getattr(cache, name + "_codes")[blk, off].cpu().numpy(), stored), name
+        assert np.array_equal(getattr(cache, name + "_scales")[blk, off].cpu().numpy().view(np.uint16),
+                              s16.view(np.uint16)), name
+    if kf != "int4_kivi":
+        return
+    pages = [step // 32 - 1, step // 32, step // 32 + 1, 0] + list(rng.integers(0, T // 32, 3))
+    for pb in pages:
+        k16 = to_np16(k[32 * pb:32 * pb + 32])
+        for h in range(H):
+            c, s16, z16 = o.kivi_quantize_group(k16[:, h])
+            assert np.array_equal(cache.k_codes[pb, :, h].cpu().numpy(), o.pack_int4(c)), (pb, h)
+            assert np.array_equal(cache.k_scales[pb, h].cpu().numpy().view(np.uint16), s16.view(np.uint16))
+            assert np.array_equal(cache.k_zeros[pb, h].cpu().numpy().view(np.uint16), z16.view(np.uint16))
+    nt = T % 32
+    assert nt > 0
+    assert np.array_equal(to_np16(cache.k_tail[0, :nt]), to_np16(k[T - nt:]))
+    assert np.array_equal(to_np16(cache.v_tail[0, :nt]), to_np16(v[T - nt:]))
+
+
 @pytest.mark.parametrize("name", [n for n in wl.ORDER[1:] if not wl.WORKLOADS[n].base])
 def test_write_full_size_sampled(name):
     """The full workload written in one call on the GPU; sampled rows (and,
